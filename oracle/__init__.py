@@ -1,0 +1,180 @@
+"""fp64 CPU oracle for grouped-query attention (ctypes binding to gqa_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg are the only importers.  The library under
+``prefill_split_gqa_amd`` never imports this package, and this package never
+imports the library.
+
+Inputs may be numpy arrays or CPU torch tensors of any floating dtype; they
+are widened exactly to float64 before the C code sees them.  Outputs are
+unrounded float64 numpy arrays.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gqa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libgqa_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile gqa_oracle.c with gcc into oracle/libgqa_oracle.so."""
+    if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+           "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    build(force=False)
+    lib = ctypes.CDLL(_LIB_PATH)
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.gqa_oracle_attend.argtypes = [dp, dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.POINTER(ctypes.c_int32), ctypes.c_int, ctypes.c_double,
+                                      dp, ctypes.c_int]
+    lib.gqa_oracle_attend.restype = ctypes.c_int
+    lib.gqa_oracle_q4_unpack.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_int, ctypes.c_void_p]
+    lib.gqa_oracle_q4_unpack.restype = ctypes.c_int
+    lib.gqa_oracle_q4_dequant.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.gqa_oracle_q4_dequant.restype = ctypes.c_int
+    lib.gqa_oracle_f16_to_f32.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long]
+    lib.gqa_oracle_f16_to_f32.restype = ctypes.c_int
+    lib.gqa_oracle_max_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def max_threads() -> int:
+    return int(_load().gqa_oracle_max_threads())
+
+
+def _f64(x) -> np.ndarray:
+    """Exact widening of a numpy array or CPU torch tensor to contiguous float64."""
+    if hasattr(x, "detach"):  # torch tensor
+        x = x.detach()
+        if x.device.type != "cpu":
+            raise ValueError("oracle inputs must live in host memory")
+        import torch
+
+        x = x.to(torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _u8(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.uint8))
+
+
+def _f16bits(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        import torch
+
+        x = x.detach().cpu().to(torch.float16).numpy()
+    x = np.asarray(x)
+    if x.dtype != np.float16:
+        raise ValueError("scales/biases must be float16")
+    return np.ascontiguousarray(x).view(np.uint16)
+
+
+def attend(q, k, v, kv_lens=None, causal: bool = False, scale: Optional[float] = None,
+           return_probs: bool = False, nthreads: int = 0):
+    """Grouped-query attention in fp64.
+
+    q [B,Hq,Tq,D]; k, v [B,Hkv,s_cap,D]; kv_lens: None (= s_cap), an int, or a
+    length-B sequence of valid key counts.  ``causal`` aligns the Tq queries
+    to the end of each request's keys.  ``scale`` defaults to the float32
+    value of 1/sqrt(D).  Returns O [B,Hq,Tq,D] (and the softmax weights
+    [B,Hq,Tq,s_cap] when ``return_probs``).
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4 or k.shape != v.shape:
+        raise ValueError("expected q [B,Hq,Tq,D] and k, v [B,Hkv,S,D]")
+    B, Hq, Tq, D = q.shape
+    Bk, Hkv, s_cap, Dk = k.shape
+    if Bk != B or Dk != D:
+        raise ValueError("batch or head-dim mismatch")
+    if kv_lens is None:
+        lens = np.full(B, s_cap, dtype=np.int32)
+    elif np.isscalar(kv_lens):
+        lens = np.full(B, int(kv_lens), dtype=np.int32)
+    else:
+        lens = np.ascontiguousarray(np.asarray(kv_lens, dtype=np.int32).reshape(B))
+    if scale is None:
+        scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
+    out = np.empty((B, Hq, Tq, D), dtype=np.float64)
+    probs = np.empty((B, Hq, Tq, s_cap), dtype=np.float64) if return_probs else None
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = _load().gqa_oracle_attend(
+        q.ctypes.data_as(dp), k.ctypes.data_as(dp), v.ctypes.data_as(dp), out.ctypes.data_as(dp),
+        B, Hq, Hkv, Tq, D, s_cap, lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        1 if causal else 0, float(scale),
+        probs.ctypes.data_as(dp) if probs is not None else None, int(nthreads))
+    if rc != 0:
+        raise ValueError("gqa_oracle_attend rejected its arguments (code %d)" % rc)
+    return (out, probs) if return_probs else out
+
+
+def f16_to_f32(x) -> np.ndarray:
+    bits = _f16bits(x)
+    out = np.empty(bits.shape, dtype=np.float32)
+    rc = _load().gqa_oracle_f16_to_f32(bits.ctypes.data, out.ctypes.data, bits.size)
+    if rc != 0:
+        raise ValueError("bad arguments")
+    return out
+
+
+def q4_unpack(packed) -> np.ndarray:
+    """uint8 [..., D/2] -> uint8 codes [..., D]."""
+    p = _u8(packed)
+    D = p.shape[-1] * 2
+    n_rows = p.size // max(p.shape[-1], 1)
+    codes = np.empty(p.shape[:-1] + (D,), dtype=np.uint8)
+    rc = _load().gqa_oracle_q4_unpack(p.ctypes.data, n_rows, D, codes.ctypes.data)
+    if rc != 0:
+        raise ValueError("bad arguments")
+    return codes
+
+
+def q4_dequant(packed, scales, biases, group: int) -> np.ndarray:
+    """float32 [..., D] = scale*code + bias per group (one rounding)."""
+    p = _u8(packed)
+    s = _f16bits(scales)
+    b = _f16bits(biases)
+    D = p.shape[-1] * 2
+    n_rows = p.size // max(p.shape[-1], 1)
+    if s.shape != p.shape[:-1] + (D // group,) or b.shape != s.shape:
+        raise ValueError("scales/biases must be [..., D/group]")
+    out = np.empty(p.shape[:-1] + (D,), dtype=np.float32)
+    rc = _load().gqa_oracle_q4_dequant(p.ctypes.data, s.ctypes.data, b.ctypes.data, n_rows, D,
+                                       int(group), out.ctypes.data)
+    if rc != 0:
+        raise ValueError("bad arguments")
+    return out
+
+
+def q4_attend(q, k_codes, k_scales, k_biases, v_codes, v_scales, v_biases, group: int,
+              kv_lens=None, scale: Optional[float] = None, nthreads: int = 0):
+    """Decode attention over a 4-bit cache: dequantize K and V, then attend."""
+    k = q4_dequant(k_codes, k_scales, k_biases, group)
+    v = q4_dequant(v_codes, v_scales, v_biases, group)
+    return attend(q, k, v, kv_lens=kv_lens, causal=False, scale=scale, nthreads=nthreads)

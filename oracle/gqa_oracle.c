@@ -1,0 +1,257 @@
+/*
+ * gqa_oracle.c -- plain, slow fp64 CPU reference for grouped-query
+ * scaled-dot-product attention and for the group-affine 4-bit KV encoding.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The tests, the smoke check and the benchmark's
+ * CPU-baseline leg are the only callers.  Nothing here is shared with the HIP
+ * library: no headers, no helpers, no constants.
+ *
+ * What is computed (one output row per (b, h, i)):
+ *
+ *   O[b,h,i,:] = sum_{j in J} softmax_j( scale * <Q[b,h,i,:], K[b,g,j,:]> ) V[b,g,j,:]
+ *
+ *   g = floor(h / G), G = Hq / Hkv   (query heads come in contiguous groups
+ *                                     that share one KV head)
+ *   J = { j : j < n_b  and  (not causal  or  j <= i + (n_b - Tq)) }
+ *
+ * with n_b the number of valid key rows of request b.  Sources:
+ *  - "2x faster Qwen2 decode on Metal in Candle", section "Why It Matters: 7x
+ *    KV Expansion": the fused kernel reads the few KV heads directly through a
+ *    GQA stride instead of materialising one copy per query head.
+ *  - "Fused attention makes a 4,096-token Qwen2 prefill on Metal 4.5x faster",
+ *    section "Cause and workaround", points 1 and 2: K/V are given before
+ *    repeat_kv (query heads a multiple of KV heads) and, with the causal flag,
+ *    the queries are aligned to the end of the keys so that a chunk at an
+ *    offset sees every earlier key.
+ *  - same page, "Cause": the unfused path is repeat_kv, a matmul, scale, mask,
+ *    softmax and a second matmul -- the plain definition written out below.
+ *
+ * A row whose visible set J is empty (possible only for a zero-length request)
+ * gets an all-zero output.
+ *
+ * Arithmetic: every stored element is widened exactly to double by the
+ * caller; dot products, exp (libm) and sums run in double in ascending index
+ * order; the result is returned unrounded.
+ *
+ * Pins: every function here is checked by tests/test_oracle_*.py against a
+ * brute force with explicitly repeated KV heads, a library attention routine,
+ * closed forms and invariants (see the test files' headers).
+ */
+
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG 1
+#define ORACLE_ERR_NOMEM 2
+
+int gqa_oracle_version(void) { return 1; }
+
+int gqa_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * q     [B, Hq,  Tq,    D]
+ * k, v  [B, Hkv, s_cap, D]   (only rows j < n_b are read)
+ * out   [B, Hq,  Tq,    D]
+ * kv_lens[b] = n_b, 0 <= n_b <= s_cap
+ * probs (optional, may be NULL) [B, Hq, Tq, s_cap]: the softmax weights,
+ *       zero where a key is not visible.
+ * nthreads <= 0 means the OpenMP default.
+ */
+int gqa_oracle_attend(const double *q, const double *k, const double *v, double *out,
+                      int B, int Hq, int Hkv, int Tq, int D, int s_cap,
+                      const int32_t *kv_lens, int causal, double scale,
+                      double *probs, int nthreads)
+{
+    if (!q || !k || !v || !out || !kv_lens)
+        return ORACLE_ERR_ARG;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Tq < 1 || D < 1 || s_cap < 1)
+        return ORACLE_ERR_ARG;
+    if (Hq % Hkv != 0)
+        return ORACLE_ERR_ARG;
+    for (int b = 0; b < B; ++b)
+        if (kv_lens[b] < 0 || kv_lens[b] > s_cap)
+            return ORACLE_ERR_ARG;
+
+    const int G = Hq / Hkv;
+    const long n_rows = (long)B * Hq * Tq;
+    int failed = 0;
+
+#ifdef _OPENMP
+    int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel num_threads(nt)
+#endif
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)s_cap);
+        if (!s) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            failed = 1;
+        }
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (long r = 0; r < n_rows; ++r) {
+            if (!s)
+                continue;
+            const int i = (int)(r % Tq);
+            const int h = (int)((r / Tq) % Hq);
+            const int b = (int)(r / ((long)Tq * Hq));
+            const int g = h / G;
+            const int n = kv_lens[b];
+
+            /* visible keys: j < n, and j <= i + (n - Tq) when causal */
+            long limit = n;
+            if (causal) {
+                long last = (long)i + ((long)n - Tq);
+                if (last + 1 < limit)
+                    limit = last + 1;
+                if (limit < 0)
+                    limit = 0;
+            }
+
+            const double *qi = q + (size_t)r * D;
+            const double *kb = k + ((size_t)b * Hkv + g) * (size_t)s_cap * D;
+            const double *vb = v + ((size_t)b * Hkv + g) * (size_t)s_cap * D;
+            double *oi = out + (size_t)r * D;
+            double *pi = probs ? probs + (size_t)r * s_cap : NULL;
+
+            if (pi)
+                for (int j = 0; j < s_cap; ++j)
+                    pi[j] = 0.0;
+
+            if (limit == 0) {
+                for (int d = 0; d < D; ++d)
+                    oi[d] = 0.0;
+                continue;
+            }
+
+            /* scores */
+            double m = -INFINITY;
+            for (long j = 0; j < limit; ++j) {
+                const double *kj = kb + (size_t)j * D;
+                double dot = 0.0;
+                for (int d = 0; d < D; ++d)
+                    dot += qi[d] * kj[d];
+                s[j] = scale * dot;
+                if (s[j] > m)
+                    m = s[j];
+            }
+
+            /* softmax weights (shifted by the row maximum) and their sum */
+            double l = 0.0;
+            for (long j = 0; j < limit; ++j) {
+                s[j] = exp(s[j] - m);
+                l += s[j];
+            }
+
+            /* weighted sum of value rows */
+            for (int d = 0; d < D; ++d)
+                oi[d] = 0.0;
+            for (long j = 0; j < limit; ++j) {
+                const double *vj = vb + (size_t)j * D;
+                for (int d = 0; d < D; ++d)
+                    oi[d] += s[j] * vj[d];
+            }
+            for (int d = 0; d < D; ++d)
+                oi[d] /= l;
+
+            if (pi)
+                for (long j = 0; j < limit; ++j)
+                    pi[j] = s[j] / l;
+        }
+        free(s);
+    }
+    return failed ? ORACLE_ERR_NOMEM : ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Group-affine 4-bit KV encoding (VeloxQuant-MLX "attention" posts: the
+ * fused group-affine decode+attention kernel behind the KIVI-style cache, and
+ * its call that passes codes, scales and biases with the group size).
+ *
+ * Layout of one cache row of D elements: D/2 bytes, element 2j in the low
+ * nibble of byte j and element 2j+1 in the high nibble; one f16 scale s and
+ * one f16 bias b per group of `group` consecutive elements.  The value of
+ * element e with code c in group e/group is  s*c + b,  rounded once to
+ * float32 (s*c is exact in float32: an 11-bit significand times a 4-bit
+ * integer, so this equals a fused multiply-add).
+ * ------------------------------------------------------------------------- */
+
+/* IEEE 754 binary16 -> binary32, from the format's definition (exact). */
+static float half_bits_to_float(uint16_t hbits)
+{
+    const int sign = (hbits >> 15) & 1;
+    const int expo = (hbits >> 10) & 0x1F;
+    const int frac = hbits & 0x3FF;
+    double mag;
+    if (expo == 0)
+        mag = ldexp((double)frac, -24);                 /* subnormal or zero */
+    else if (expo == 31)
+        mag = frac ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(1024 + frac), expo - 25);  /* (1 + frac/1024) * 2^(expo-15) */
+    return (float)(sign ? -mag : mag);
+}
+
+int gqa_oracle_f16_to_f32(const uint16_t *in, float *out, long n)
+{
+    if (!in || !out || n < 0)
+        return ORACLE_ERR_ARG;
+    for (long i = 0; i < n; ++i)
+        out[i] = half_bits_to_float(in[i]);
+    return ORACLE_OK;
+}
+
+/* codes [n_rows, D] (one byte per element, 0..15) from packed [n_rows, D/2] */
+int gqa_oracle_q4_unpack(const uint8_t *packed, long n_rows, int D, uint8_t *codes)
+{
+    if (!packed || !codes || n_rows < 0 || D < 2 || D % 2)
+        return ORACLE_ERR_ARG;
+    for (long r = 0; r < n_rows; ++r) {
+        const uint8_t *row = packed + (size_t)r * (D / 2);
+        for (int e = 0; e < D; ++e) {
+            const uint8_t byte = row[e / 2];
+            codes[(size_t)r * D + e] = (e % 2 == 0) ? (uint8_t)(byte & 0x0F) : (uint8_t)(byte >> 4);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* out [n_rows, D] float32 = s*c + b per element (single rounding) */
+int gqa_oracle_q4_dequant(const uint8_t *packed, const uint16_t *scales, const uint16_t *biases,
+                          long n_rows, int D, int group, float *out)
+{
+    if (!packed || !scales || !biases || !out || n_rows < 0 || D < 2 || D % 2 ||
+        group < 1 || D % group)
+        return ORACLE_ERR_ARG;
+    const int n_groups = D / group;
+    uint8_t *codes = (uint8_t *)malloc((size_t)D);
+    if (!codes)
+        return ORACLE_ERR_NOMEM;
+    for (long r = 0; r < n_rows; ++r) {
+        gqa_oracle_q4_unpack(packed + (size_t)r * (D / 2), 1, D, codes);
+        for (int e = 0; e < D; ++e) {
+            const int grp = e / group;
+            const float s = half_bits_to_float(scales[(size_t)r * n_groups + grp]);
+            const float b = half_bits_to_float(biases[(size_t)r * n_groups + grp]);
+            out[(size_t)r * D + e] = fmaf(s, (float)codes[e], b);
+        }
+    }
+    free(codes);
+    return ORACLE_OK;
+}
