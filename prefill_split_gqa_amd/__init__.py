@@ -1,0 +1,224 @@
+"""Python binding of libgqa.so (fused grouped-query attention for MI355X).
+
+The functions carry the C entry points' names and only marshal arguments:
+they read sizes from tensor shapes, check devices and dtypes, and pass
+``data_ptr()`` values and torch's current HIP stream to the library.  Every
+step of the attention runs in the library's kernels; there is no fallback
+path, and a missing ``libgqa.so`` raises :class:`GqaError`.
+
+PyTorch supplies device memory and streams only.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgqa.so")
+
+GQA_OK, GQA_ERR_NULL, GQA_ERR_SHAPE, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP, GQA_ERR_ALIGN = range(7)
+GQA_F32, GQA_BF16, GQA_F16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: GQA_F32, torch.bfloat16: GQA_BF16, torch.float16: GQA_F16}
+
+EXPORTED = (
+    "gqa_abi_version",
+    "gqa_status_string",
+    "gqa_decode_workspace_bytes",
+    "gqa_workspace_init",
+    "gqa_decode_attend",
+    "gqa_decode_attend_batched",
+    "gqa_prefill_causal",
+    "gqa_decode_attend_q4",
+    "gqa_dequant_q4",
+)
+
+
+class GqaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, status_string(status) if _lib else "?", status))
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libgqa.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise GqaError(-1, "loading %s (not built: run python -m prefill_split_gqa_amd.build)" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.gqa_abi_version.restype = i
+    lib.gqa_status_string.argtypes = [i]
+    lib.gqa_status_string.restype = ctypes.c_char_p
+    lib.gqa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.gqa_decode_workspace_bytes.restype = sz
+    lib.gqa_workspace_init.argtypes = [vp, sz, vp]
+    lib.gqa_workspace_init.restype = i
+    lib.gqa_decode_attend.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.gqa_decode_attend.restype = i
+    lib.gqa_decode_attend_batched.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.gqa_decode_attend_batched.restype = i
+    lib.gqa_prefill_causal.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    lib.gqa_prefill_causal.restype = i
+    lib.gqa_decode_attend_q4.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
+    lib.gqa_decode_attend_q4.restype = i
+    lib.gqa_dequant_q4.argtypes = [vp, vp, vp, vp, i, i, i, vp]
+    lib.gqa_dequant_q4.restype = i
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().gqa_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != GQA_OK:
+        raise GqaError(status, what)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dense(name: str, t: torch.Tensor, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %d-d tensor" % (name, ndim))
+
+
+def default_scale(D: int) -> float:
+    """1/sqrt(D) rounded to float32 (the value the kernels receive)."""
+    return float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32))
+
+
+def gqa_abi_version() -> int:
+    return int(load().gqa_abi_version())
+
+
+def gqa_decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, s_cap: int) -> int:
+    return int(load().gqa_decode_workspace_bytes(B, Hq, Hkv, D, s_cap))
+
+
+def make_workspace(B: int, Hq: int, Hkv: int, D: int, s_cap: int, device="cuda") -> torch.Tensor:
+    """A zero-filled (hence ready) decode workspace for these sizes."""
+    n = gqa_decode_workspace_bytes(B, Hq, Hkv, D, s_cap)
+    if n == 0:
+        raise ValueError("invalid decode sizes")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def gqa_workspace_init(workspace: torch.Tensor) -> None:
+    _check(load().gqa_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(workspace)), "gqa_workspace_init")
+
+
+def gqa_decode_attend(q, k, v, out, kv_len: int, workspace, scale: Optional[float] = None) -> torch.Tensor:
+    """q, out [B,Hq,1,D]; k, v [B,Hkv,s_cap,D] (same dtype); attends over rows < kv_len."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _dense(n, t, 4)
+    B, Hq, Tq, D = q.shape
+    _, Hkv, s_cap, _ = k.shape
+    if Tq != 1 or out.shape != q.shape or k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("shape mismatch")
+    dt = _DTYPE_CODE.get(q.dtype, -1)
+    if not (q.dtype == k.dtype == v.dtype == out.dtype):
+        raise ValueError("q, k, v and out must share one dtype")
+    scale = default_scale(D) if scale is None else scale
+    _check(load().gqa_decode_attend(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, D, int(kv_len), s_cap,
+                                    float(scale), dt, _ptr(workspace), workspace.numel(), _stream(q)),
+           "gqa_decode_attend")
+    return out
+
+
+def gqa_decode_attend_batched(q, k, v, out, kv_lens, workspace, scale: Optional[float] = None) -> torch.Tensor:
+    """As gqa_decode_attend with a device int32 [B] of per-request lengths."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _dense(n, t, 4)
+    _dense("kv_lens", kv_lens, 1)
+    B, Hq, Tq, D = q.shape
+    _, Hkv, s_cap, _ = k.shape
+    if Tq != 1 or out.shape != q.shape or k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("shape mismatch")
+    if kv_lens.dtype != torch.int32 or kv_lens.numel() != B:
+        raise ValueError("kv_lens must be int32 [B]")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype):
+        raise ValueError("q, k, v and out must share one dtype")
+    dt = _DTYPE_CODE.get(q.dtype, -1)
+    scale = default_scale(D) if scale is None else scale
+    _check(load().gqa_decode_attend_batched(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(kv_lens), B, Hq, Hkv, D,
+                                            s_cap, float(scale), dt, _ptr(workspace), workspace.numel(),
+                                            _stream(q)), "gqa_decode_attend_batched")
+    return out
+
+
+def gqa_prefill_causal(q, k, v, out, Tk: Optional[int] = None, scale: Optional[float] = None) -> torch.Tensor:
+    """q, out [B,Hq,Tq,D]; k, v [B,Hkv,s_cap,D]; queries aligned to the end of the first Tk keys."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _dense(n, t, 4)
+    B, Hq, Tq, D = q.shape
+    _, Hkv, s_cap, _ = k.shape
+    if out.shape != q.shape or k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("shape mismatch")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype):
+        raise ValueError("q, k, v and out must share one dtype")
+    Tk = s_cap if Tk is None else int(Tk)
+    dt = _DTYPE_CODE.get(q.dtype, -1)
+    scale = default_scale(D) if scale is None else scale
+    _check(load().gqa_prefill_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, D, Tq, Tk, s_cap,
+                                     float(scale), dt, _stream(q)), "gqa_prefill_causal")
+    return out
+
+
+def gqa_decode_attend_q4(q, k_codes, k_scales, k_biases, v_codes, v_scales, v_biases, out, group_size: int,
+                         kv_len: int, workspace, scale: Optional[float] = None) -> torch.Tensor:
+    """q, out f16 [B,Hq,1,D]; codes uint8 [B,Hkv,s_cap,D/2]; scales, biases f16 [B,Hkv,s_cap,D/group]."""
+    for n, t in (("q", q), ("out", out), ("k_codes", k_codes), ("v_codes", v_codes), ("k_scales", k_scales),
+                 ("k_biases", k_biases), ("v_scales", v_scales), ("v_biases", v_biases)):
+        _dense(n, t, 4)
+    B, Hq, Tq, D = q.shape
+    _, Hkv, s_cap, half = k_codes.shape
+    if Tq != 1 or out.shape != q.shape or half * 2 != D or v_codes.shape != k_codes.shape:
+        raise ValueError("shape mismatch")
+    if q.dtype != torch.float16 or out.dtype != torch.float16:
+        raise ValueError("q and out must be float16")
+    if k_codes.dtype != torch.uint8 or v_codes.dtype != torch.uint8:
+        raise ValueError("codes must be uint8")
+    gshape = (B, Hkv, s_cap, D // group_size)
+    for n, t in (("k_scales", k_scales), ("k_biases", k_biases), ("v_scales", v_scales), ("v_biases", v_biases)):
+        if t.dtype != torch.float16 or tuple(t.shape) != gshape:
+            raise ValueError("%s must be float16 %s" % (n, gshape))
+    scale = default_scale(D) if scale is None else scale
+    _check(load().gqa_decode_attend_q4(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(k_biases), _ptr(v_codes),
+                                       _ptr(v_scales), _ptr(v_biases), _ptr(out), B, Hq, Hkv, D, int(group_size),
+                                       int(kv_len), s_cap, float(scale), _ptr(workspace), workspace.numel(),
+                                       _stream(q)), "gqa_decode_attend_q4")
+    return out
+
+
+def gqa_dequant_q4(codes, scales, biases, out, group_size: int) -> torch.Tensor:
+    """codes uint8 [..., D/2], scales/biases f16 [..., D/group] -> out float32 [..., D]."""
+    for n, t in (("codes", codes), ("scales", scales), ("biases", biases), ("out", out)):
+        if t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous GPU tensor" % n)
+    D = codes.shape[-1] * 2
+    n_rows = codes.numel() // max(codes.shape[-1], 1)
+    if out.dtype != torch.float32 or out.numel() != n_rows * D:
+        raise ValueError("out must be float32 with D elements per row")
+    _check(load().gqa_dequant_q4(_ptr(codes), _ptr(scales), _ptr(biases), _ptr(out), n_rows, D,
+                                 int(group_size), _stream(codes)), "gqa_dequant_q4")
+    return out

@@ -1,0 +1,169 @@
+// common.h -- internal definitions shared by the gfx950 kernels and the C-ABI
+// layer of libgqa.so.  Not installed; the public interface is include/gqa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gqa {
+
+// ---------------------------------------------------------------------------
+// Storage types.  bf16 and f16 travel as raw 16-bit words so that loads stay
+// plain integer vector loads; conversion to fp32 happens in registers.
+// ---------------------------------------------------------------------------
+struct bf16_t { uint16_t bits; };
+struct f16_t { uint16_t bits; };
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b)
+{
+    _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)b);
+    return (float)h;
+}
+
+// fp32 -> storage, round to nearest even (gfx950 converts natively).
+template <typename T> __device__ __forceinline__ void store_elem(T *p, float x);
+template <> __device__ __forceinline__ void store_elem<float>(float *p, float x) { *p = x; }
+template <> __device__ __forceinline__ void store_elem<bf16_t>(bf16_t *p, float x)
+{
+    __bf16 h = (__bf16)x;
+    p->bits = __builtin_bit_cast(uint16_t, h);
+}
+template <> __device__ __forceinline__ void store_elem<f16_t>(f16_t *p, float x)
+{
+    _Float16 h = (_Float16)x;
+    p->bits = __builtin_bit_cast(uint16_t, h);
+}
+
+// Unpack the 32-bit words of a loaded vector into fp32 elements.
+template <typename T> struct Unpack;
+template <> struct Unpack<float> {
+    static constexpr int per_word = 1;
+    __device__ __forceinline__ static void run(uint32_t w, float *out) { out[0] = __uint_as_float(w); }
+};
+template <> struct Unpack<bf16_t> {
+    static constexpr int per_word = 2;
+    __device__ __forceinline__ static void run(uint32_t w, float *out)
+    {
+        out[0] = __uint_as_float(w << 16);
+        out[1] = __uint_as_float(w & 0xFFFF0000u);
+    }
+};
+template <> struct Unpack<f16_t> {
+    static constexpr int per_word = 2;
+    __device__ __forceinline__ static void run(uint32_t w, float *out)
+    {
+        out[0] = f16_bits_to_f32(w & 0xFFFFu);
+        out[1] = f16_bits_to_f32(w >> 16);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Cross-lane helpers (wave64).
+// DPP row controls (gfx9 encoding): quad_perm [1,0,3,2] = 0xB1 (lane^1),
+// quad_perm [2,3,0,1] = 0x4E (lane^2), row_half_mirror = 0x141,
+// row_mirror = 0x140.  The four steps below sum a value over each
+// 16-lane row.
+// ---------------------------------------------------------------------------
+template <int CTRL> __device__ __forceinline__ float dpp_f32(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row16_sum(float x)
+{
+    x += dpp_f32<0xB1>(x);
+    x += dpp_f32<0x4E>(x);
+    x += dpp_f32<0x141>(x);
+    x += dpp_f32<0x140>(x);
+    return x;
+}
+
+__device__ __forceinline__ float shfl_xor_f32(float x, int mask)
+{
+    return __shfl_xor(x, mask, 64);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Decode split plan.  The host sizes the workspace and the grid from it and
+// the kernel derives every index from the same numbers, so a request's split
+// boundaries depend only on (s_cap, Hq, Hkv) -- never on B or on the other
+// requests' lengths.
+// ---------------------------------------------------------------------------
+constexpr int kDecodeThreads = 512;     // 8 waves = 32 row-groups of 16 lanes
+constexpr int kDecodeRowGroups = kDecodeThreads / 16;
+constexpr int kDecodeMaxSplits = 64;    // partials merged by one workgroup (one round trip)
+constexpr int kDecodeTargetWGs = 128;   // measured best at 7B geometry, KV length 4096
+
+struct DecodePlan {
+    int G;            // query heads per KV head
+    int GT;           // query heads handled by one workgroup (divides G, <= 8)
+    int ht_per_kv;    // G / GT
+    int HT;           // Hkv * ht_per_kv: workgroup columns per request
+    int L;            // keys per split (multiple of kDecodeRowGroups)
+    int n_split_max;  // ceil(s_cap / L)
+    // workspace layout (byte offsets)
+    size_t off_o, off_ml, off_cnt, bytes;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline bool make_decode_plan(int B, int Hq, int Hkv, int D, int s_cap, int target_wgs, int max_splits,
+                             DecodePlan *p)
+{
+    if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || s_cap < 1 || Hq % Hkv || target_wgs < 1 || max_splits < 1)
+        return false;
+    p->G = Hq / Hkv;
+    p->GT = 1;
+    for (int t = 8; t >= 1; --t)
+        if (p->G % t == 0) { p->GT = t; break; }
+    p->ht_per_kv = p->G / p->GT;
+    p->HT = Hkv * p->ht_per_kv;
+    long ns = target_wgs / p->HT;
+    if (ns < 1) ns = 1;
+    if (ns > max_splits) ns = max_splits;
+    const long rows = kDecodeRowGroups;
+    const long per = (s_cap + rows * ns - 1) / (rows * ns);  // rows per row-group per split
+    p->L = (int)(per * rows);
+    p->n_split_max = (int)((s_cap + p->L - 1) / p->L);
+    const size_t cols = (size_t)B * p->HT;
+    size_t off = 0;
+    p->off_o = off;   off = align_up(off + cols * p->n_split_max * p->GT * (size_t)D * 4, 256);
+    p->off_ml = off;  off = align_up(off + cols * p->n_split_max * p->GT * 2 * 4, 256);
+    p->off_cnt = off; off = align_up(off + cols * 4, 256);
+    p->bytes = off;
+    return true;
+}
+
+// Arguments of the split-K decode kernels (passed by value).
+struct DecodeArgs {
+    const void *q;
+    const void *k;       // dense K, or 4-bit codes
+    const void *v;       // dense V, or 4-bit codes
+    const void *k_scales, *k_biases, *v_scales, *v_biases;  // 4-bit cache only
+    void *out;
+    const int32_t *kv_lens;  // device lengths, or nullptr
+    int kv_len;              // uniform length when kv_lens == nullptr
+    int Hq, Hkv, s_cap;
+    int group;               // 4-bit cache group size (0 for dense caches)
+    float qscale;            // scale * log2(e)
+    DecodePlan plan;
+    float *part_o, *part_ml; // per split: [GT][D] outputs, [GT][2] (max, sum)
+    unsigned *cnt;           // one arrival counter per (request, head tile)
+    size_t ws_bytes;
+};
+
+// Launchers (defined in the .hip files; return a hipError_t).
+hipError_t launch_decode(int dtype, int D, int B, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode_q4(int D, int group, int B, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_dequant_q4(const uint8_t *codes, const void *scales, const void *biases, float *out,
+                             int n_rows, int D, int group, hipStream_t s);
+hipError_t launch_prefill(int dtype, int D, const void *q, const void *k, const void *v, void *out,
+                          int B, int Hq, int Hkv, int Tq, int Tk, int s_cap, float scale, hipStream_t s);
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+
+}  // namespace gqa

@@ -1,0 +1,241 @@
+// gqa_abi.hip -- the extern "C" entry points declared in include/gqa.h.
+//
+// Every check on sizes, pointers and dtypes runs before the first HIP call,
+// so an invalid call returns a status without touching the device (and can be
+// exercised on a machine with no GPU).  The device check (gfx950 only; the
+// decode page's companion finding returns an explicit error on a device the
+// fused kernel does not support rather than falling back) runs next, then the
+// kernels are enqueued on the caller's stream.
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/gqa.h"
+#include "common.h"
+
+using namespace gqa;
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int env_int(const char *name, int dflt)
+{
+    const char *s = std::getenv(name);
+    const int x = s ? std::atoi(s) : 0;
+    return x > 0 ? x : dflt;
+}
+
+// Launch-shape knobs (defaults fill the chip once at full length); the
+// environment overrides exist for tuning sweeps only.
+int decode_target_wgs()
+{
+    static const int v = env_int("GQA_DECODE_TARGET_WGS", kDecodeTargetWGs);
+    return v;
+}
+int decode_max_splits()
+{
+    static const int v = env_int("GQA_DECODE_MAX_SPLITS", kDecodeMaxSplits);
+    return v < kDecodeMaxSplits ? v : kDecodeMaxSplits;  // the merge holds at most this many
+}
+
+bool plan_decode(int B, int Hq, int Hkv, int D, int s_cap, DecodePlan *p)
+{
+    if (!make_decode_plan(B, Hq, Hkv, D, s_cap, decode_target_wgs(), decode_max_splits(), p)) return false;
+    // grid limits, and buffer-resource ranges of the partial arrays
+    return p->HT <= 65535 && p->n_split_max <= 65535 && p->bytes < ((size_t)1 << 31);
+}
+
+// 1 = gfx950, 0 = other device, -1 = HIP error.  Cached per device ordinal.
+int device_supported()
+{
+    static std::mutex mu;
+    static int cache[64];
+    static bool init = false;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!init) {
+        for (int &c : cache) c = 2;  // unknown
+        init = true;
+    }
+    if (dev < 0 || dev >= 64) return -1;
+    if (cache[dev] == 2) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return -1;
+        cache[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+    }
+    return cache[dev];
+}
+
+int check_device()
+{
+    const int d = device_supported();
+    if (d < 0) return GQA_ERR_HIP;
+    if (d == 0) return GQA_ERR_UNSUPPORTED;
+    return GQA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ERR_HIP; }
+
+bool dense_dtype(int dtype) { return dtype == GQA_F32 || dtype == GQA_BF16 || dtype == GQA_F16; }
+
+int check_decode_common(const void *q, const void *k, const void *v, void *out, int B, int Hq, int Hkv, int D,
+                        int s_cap, float scale, void *ws, size_t ws_bytes, DecodePlan *plan)
+{
+    if (!q || !k || !v || !out) return GQA_ERR_NULL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || s_cap < 1) return GQA_ERR_SHAPE;
+    if (!std::isfinite(scale)) return GQA_ERR_SHAPE;
+    if (D != 64 && D != 128) return GQA_ERR_UNSUPPORTED;
+    if (B > 65535 || (size_t)B * Hkv * (size_t)s_cap * D >= ((size_t)1 << 40)) return GQA_ERR_SHAPE;
+    if (!plan_decode(B, Hq, Hkv, D, s_cap, plan)) return GQA_ERR_SHAPE;
+    if (!ws || ws_bytes < plan->bytes) return GQA_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(ws)) return GQA_ERR_ALIGN;
+    return GQA_OK;
+}
+
+void fill_ws(DecodeArgs &a, void *ws)
+{
+    char *base = (char *)ws;
+    a.part_o = (float *)(base + a.plan.off_o);
+    a.part_ml = (float *)(base + a.plan.off_ml);
+    a.cnt = (unsigned *)(base + a.plan.off_cnt);
+    a.ws_bytes = a.plan.bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_abi_version(void) { return kAbiVersion; }
+
+const char *gqa_status_string(int status)
+{
+    switch (status) {
+    case GQA_OK: return "ok";
+    case GQA_ERR_NULL: return "a required pointer is NULL";
+    case GQA_ERR_SHAPE: return "sizes are inconsistent or out of range";
+    case GQA_ERR_UNSUPPORTED: return "dtype, head dimension or device not supported";
+    case GQA_ERR_WORKSPACE: return "workspace missing or too small";
+    case GQA_ERR_HIP: return "HIP runtime error";
+    case GQA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    default: return "unknown status";
+    }
+}
+
+size_t gqa_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int s_cap)
+{
+    if (D != 64 && D != 128) return 0;
+    DecodePlan p;
+    if (!plan_decode(B, Hq, Hkv, D, s_cap, &p)) return 0;
+    return p.bytes;
+}
+
+int gqa_workspace_init(void *workspace, size_t bytes, void *stream)
+{
+    if (!workspace) return GQA_ERR_NULL;
+    if (!aligned16(workspace)) return GQA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return hip_status(launch_fill_zero(workspace, bytes, (hipStream_t)stream));
+}
+
+int gqa_decode_attend(const void *q, const void *k, const void *v, void *out, int B, int Hq, int Hkv, int D,
+                      int kv_len, int s_cap, float scale, int dtype, void *workspace, size_t workspace_bytes,
+                      void *stream)
+{
+    DecodePlan plan;
+    if (int st = check_decode_common(q, k, v, out, B, Hq, Hkv, D, s_cap, scale, workspace, workspace_bytes, &plan))
+        return st;
+    if (kv_len < 1 || kv_len > s_cap) return GQA_ERR_SHAPE;
+    if (!dense_dtype(dtype)) return GQA_ERR_UNSUPPORTED;
+    if (int st = check_device()) return st;
+    DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.out = out;
+    a.kv_lens = nullptr; a.kv_len = kv_len;
+    a.Hq = Hq; a.Hkv = Hkv; a.s_cap = s_cap; a.group = 0;
+    a.qscale = scale * 1.4426950408889634f;
+    a.plan = plan;
+    fill_ws(a, workspace);
+    return hip_status(launch_decode(dtype, D, B, a, (hipStream_t)stream));
+}
+
+int gqa_decode_attend_batched(const void *q, const void *k, const void *v, void *out, const int32_t *kv_lens,
+                              int B, int Hq, int Hkv, int D, int s_cap, float scale, int dtype, void *workspace,
+                              size_t workspace_bytes, void *stream)
+{
+    if (!kv_lens) return GQA_ERR_NULL;
+    DecodePlan plan;
+    if (int st = check_decode_common(q, k, v, out, B, Hq, Hkv, D, s_cap, scale, workspace, workspace_bytes, &plan))
+        return st;
+    if (!aligned16(kv_lens)) return GQA_ERR_ALIGN;
+    if (!dense_dtype(dtype)) return GQA_ERR_UNSUPPORTED;
+    if (int st = check_device()) return st;
+    DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.out = out;
+    a.kv_lens = kv_lens; a.kv_len = 0;
+    a.Hq = Hq; a.Hkv = Hkv; a.s_cap = s_cap; a.group = 0;
+    a.qscale = scale * 1.4426950408889634f;
+    a.plan = plan;
+    fill_ws(a, workspace);
+    return hip_status(launch_decode(dtype, D, B, a, (hipStream_t)stream));
+}
+
+int gqa_prefill_causal(const void *q, const void *k, const void *v, void *out, int B, int Hq, int Hkv, int D,
+                       int Tq, int Tk, int s_cap, float scale, int dtype, void *stream)
+{
+    if (!q || !k || !v || !out) return GQA_ERR_NULL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return GQA_ERR_SHAPE;
+    if (Tq < 1 || Tq > Tk || Tk > s_cap) return GQA_ERR_SHAPE;
+    if (!std::isfinite(scale)) return GQA_ERR_SHAPE;
+    if (D != 64 && D != 128) return GQA_ERR_UNSUPPORTED;
+    if (dtype != GQA_BF16 && dtype != GQA_F16) return GQA_ERR_UNSUPPORTED;
+    if ((long)((Tq + 127) / 128) * Hq >= (1L << 31) || B > 65535) return GQA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return hip_status(launch_prefill(dtype, D, q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, (hipStream_t)stream));
+}
+
+int gqa_decode_attend_q4(const void *q, const uint8_t *k_codes, const void *k_scales, const void *k_biases,
+                         const uint8_t *v_codes, const void *v_scales, const void *v_biases, void *out, int B,
+                         int Hq, int Hkv, int D, int group_size, int kv_len, int s_cap, float scale,
+                         void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!k_scales || !k_biases || !v_scales || !v_biases) return GQA_ERR_NULL;
+    DecodePlan plan;
+    if (int st = check_decode_common(q, k_codes, v_codes, out, B, Hq, Hkv, D, s_cap, scale, workspace,
+                                     workspace_bytes, &plan))
+        return st;
+    if (kv_len < 1 || kv_len > s_cap) return GQA_ERR_SHAPE;
+    if (group_size != 32 && group_size != 64 && group_size != 128) return GQA_ERR_UNSUPPORTED;
+    if (D % group_size != 0) return GQA_ERR_SHAPE;
+    if (!aligned16(k_scales) || !aligned16(k_biases) || !aligned16(v_scales) || !aligned16(v_biases))
+        return GQA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    DecodeArgs a{};
+    a.q = q; a.k = k_codes; a.v = v_codes; a.out = out;
+    a.k_scales = k_scales; a.k_biases = k_biases; a.v_scales = v_scales; a.v_biases = v_biases;
+    a.kv_lens = nullptr; a.kv_len = kv_len;
+    a.Hq = Hq; a.Hkv = Hkv; a.s_cap = s_cap; a.group = group_size;
+    a.qscale = scale * 1.4426950408889634f;
+    a.plan = plan;
+    fill_ws(a, workspace);
+    return hip_status(launch_decode_q4(D, group_size, B, a, (hipStream_t)stream));
+}
+
+int gqa_dequant_q4(const uint8_t *codes, const void *scales, const void *biases, float *out, int n_rows, int D,
+                   int group_size, void *stream)
+{
+    if (!codes || !scales || !biases || !out) return GQA_ERR_NULL;
+    if (n_rows < 0) return GQA_ERR_SHAPE;
+    if (D < 2 || D % 2) return GQA_ERR_SHAPE;
+    if (group_size != 32 && group_size != 64 && group_size != 128) return GQA_ERR_UNSUPPORTED;
+    if (D % group_size != 0) return GQA_ERR_SHAPE;
+    if (int st = check_device()) return st;
+    return hip_status(launch_dequant_q4(codes, scales, biases, out, n_rows, D, group_size, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+"""Small helpers shared by the GPU parity tests (comparison and guard bands)."""
+
+import sys
+
+import numpy as np
+import torch
+
+TOL_F32 = 2e-5   # max-abs bound for fp32 outputs
+TOL_16 = 2e-2    # max-abs bound for bf16 / f16 outputs
+
+
+def tol_for(dtype) -> float:
+    return TOL_F32 if dtype == torch.float32 else TOL_16
+
+
+def note(msg: str) -> None:
+    """Flush a line naming the case before a GPU step (survives a crash)."""
+    sys.stdout.write(msg + "\n")
+    sys.stdout.flush()
+
+
+def max_abs_err(got: torch.Tensor, want: np.ndarray) -> float:
+    g = got.detach().float().cpu().double().numpy()
+    assert g.shape == want.shape, (g.shape, want.shape)
+    assert np.isfinite(g).all(), "non-finite output"
+    return float(np.abs(g - want).max()) if g.size else 0.0
+
+
+def assert_close(got: torch.Tensor, want: np.ndarray, tol: float, what: str) -> float:
+    err = max_abs_err(got, want)
+    note("  %s: max-abs error %.3e (bound %.1e)" % (what, err, tol))
+    assert err <= tol, "%s: max-abs error %.3e > %.1e" % (what, err, tol)
+    return err
+
+
+class Guarded:
+    """An output tensor with sentinel-filled guard bands on both sides."""
+
+    PAD = 256  # elements (keeps 16-byte alignment for every dtype used)
+
+    def __init__(self, shape, dtype, device="cuda", sentinel=1234.5):
+        n = int(np.prod(shape))
+        self.buf = torch.full((n + 2 * self.PAD,), sentinel, dtype=dtype, device=device)
+        self.sentinel = sentinel
+        self.n = n
+        self.t = self.buf[self.PAD:self.PAD + n].view(*shape)
+
+    def check(self):
+        b = self.buf.float().cpu()
+        s = torch.tensor(self.sentinel, dtype=self.buf.dtype).float()
+        assert (b[:self.PAD] == s).all() and (b[self.PAD + self.n:] == s).all(), "write outside the output"

@@ -1,0 +1,143 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+* libgqa.so loads and exports every function include/gqa.h declares;
+* status strings and the workspace-size function behave;
+* every invalid-argument path returns its status before any HIP call.
+  Only invalid calls are made here (a fully valid call would launch work),
+  and no pointer passed is ever dereferenced on the host.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import prefill_split_gqa_amd as gqa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa.h")
+
+FAKE = ctypes.c_void_p(0x10000)      # 16-byte aligned, never dereferenced
+FAKE_ODD = ctypes.c_void_p(0x10004)  # misaligned
+NULL = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gqa.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(gqa.EXPORTED)
+
+
+def test_version_and_status_strings(lib):
+    assert gqa.gqa_abi_version() == 1
+    for st in range(7):
+        assert gqa.status_string(st)
+    assert gqa.status_string(99) == "unknown status"
+
+
+def test_workspace_bytes():
+    n = gqa.gqa_decode_workspace_bytes(1, 28, 4, 128, 4096)
+    assert n > 0 and n % 256 == 0
+    # grows with the batch, depends only on the arguments
+    assert gqa.gqa_decode_workspace_bytes(8, 28, 4, 128, 4096) > n
+    assert gqa.gqa_decode_workspace_bytes(1, 28, 4, 128, 4096) == n
+    assert gqa.gqa_decode_workspace_bytes(1, 28, 5, 128, 4096) == 0   # Hq % Hkv
+    assert gqa.gqa_decode_workspace_bytes(1, 28, 4, 96, 4096) == 0    # unsupported D
+    assert gqa.gqa_decode_workspace_bytes(0, 28, 4, 128, 4096) == 0
+
+
+def _decode(lib, q=FAKE, k=FAKE, v=FAKE, out=FAKE, B=1, Hq=28, Hkv=4, D=128, kv_len=10, s_cap=16,
+            scale=0.1, dtype=0, ws=FAKE, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = gqa.gqa_decode_workspace_bytes(max(B, 1), Hq if Hq > 0 else 1, max(Hkv, 1), 128, max(s_cap, 1))
+    return lib.gqa_decode_attend(q, k, v, out, B, Hq, Hkv, D, kv_len, s_cap, ctypes.c_float(scale), dtype, ws,
+                                 ws_bytes, NULL)
+
+
+def test_decode_validation(lib):
+    assert _decode(lib, q=NULL) == gqa.GQA_ERR_NULL
+    assert _decode(lib, out=NULL) == gqa.GQA_ERR_NULL
+    assert _decode(lib, Hkv=3) == gqa.GQA_ERR_SHAPE
+    assert _decode(lib, B=0) == gqa.GQA_ERR_SHAPE
+    assert _decode(lib, kv_len=0) == gqa.GQA_ERR_SHAPE
+    assert _decode(lib, kv_len=17) == gqa.GQA_ERR_SHAPE
+    assert _decode(lib, scale=float("nan")) == gqa.GQA_ERR_SHAPE
+    assert _decode(lib, D=96) == gqa.GQA_ERR_UNSUPPORTED
+    assert _decode(lib, dtype=7) == gqa.GQA_ERR_UNSUPPORTED
+    assert _decode(lib, ws=NULL) == gqa.GQA_ERR_WORKSPACE
+    assert _decode(lib, ws_bytes=16) == gqa.GQA_ERR_WORKSPACE
+    assert _decode(lib, k=FAKE_ODD) == gqa.GQA_ERR_ALIGN
+
+
+def test_batched_validation(lib):
+    wsb = gqa.gqa_decode_workspace_bytes(2, 32, 8, 128, 64)
+
+    def call(lens=FAKE, B=2, Hkv=8, dtype=1, ws_bytes=wsb):
+        return lib.gqa_decode_attend_batched(FAKE, FAKE, FAKE, FAKE, lens, B, 32, Hkv, 128, 64,
+                                             ctypes.c_float(0.1), dtype, FAKE, ws_bytes, NULL)
+
+    assert call(lens=NULL) == gqa.GQA_ERR_NULL
+    assert call(Hkv=5) == gqa.GQA_ERR_SHAPE
+    assert call(ws_bytes=wsb - 1) == gqa.GQA_ERR_WORKSPACE
+    assert call(lens=FAKE_ODD) == gqa.GQA_ERR_ALIGN
+    assert call(dtype=3) == gqa.GQA_ERR_UNSUPPORTED
+
+
+def test_prefill_validation(lib):
+    def call(q=FAKE, Hq=14, Hkv=2, D=64, Tq=8, Tk=8, s_cap=8, dtype=1, scale=0.125):
+        return lib.gqa_prefill_causal(q, FAKE, FAKE, FAKE, 1, Hq, Hkv, D, Tq, Tk, s_cap, ctypes.c_float(scale),
+                                      dtype, NULL)
+
+    assert call(q=NULL) == gqa.GQA_ERR_NULL
+    assert call(Tq=9) == gqa.GQA_ERR_SHAPE        # Tq > Tk
+    assert call(Tk=9) == gqa.GQA_ERR_SHAPE        # Tk > s_cap
+    assert call(Tq=0) == gqa.GQA_ERR_SHAPE
+    assert call(Hkv=3) == gqa.GQA_ERR_SHAPE
+    assert call(scale=float("inf")) == gqa.GQA_ERR_SHAPE
+    assert call(dtype=0) == gqa.GQA_ERR_UNSUPPORTED  # fp32 prefill is not provided
+    assert call(D=80) == gqa.GQA_ERR_UNSUPPORTED
+    assert call(q=FAKE_ODD) == gqa.GQA_ERR_ALIGN
+
+
+def test_q4_validation(lib):
+    wsb = gqa.gqa_decode_workspace_bytes(1, 64, 8, 128, 64)
+
+    def call(ks=FAKE, group=64, D=128, kv_len=10, ws_bytes=wsb):
+        return lib.gqa_decode_attend_q4(FAKE, FAKE, ks, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 8, D, group, kv_len, 64,
+                                        ctypes.c_float(0.1), FAKE, ws_bytes, NULL)
+
+    assert call(ks=NULL) == gqa.GQA_ERR_NULL
+    assert call(group=48) == gqa.GQA_ERR_UNSUPPORTED
+    assert call(group=128, D=64) == gqa.GQA_ERR_SHAPE
+    assert call(kv_len=65) == gqa.GQA_ERR_SHAPE
+    assert call(ws_bytes=0) == gqa.GQA_ERR_WORKSPACE
+    assert call(ks=FAKE_ODD) == gqa.GQA_ERR_ALIGN
+    assert lib.gqa_dequant_q4(NULL, FAKE, FAKE, FAKE, 4, 128, 64, NULL) == gqa.GQA_ERR_NULL
+    assert lib.gqa_dequant_q4(FAKE, FAKE, FAKE, FAKE, 4, 128, 48, NULL) == gqa.GQA_ERR_UNSUPPORTED
+    assert lib.gqa_dequant_q4(FAKE, FAKE, FAKE, FAKE, -1, 128, 64, NULL) == gqa.GQA_ERR_SHAPE
+
+
+def test_workspace_init_validation(lib):
+    assert lib.gqa_workspace_init(NULL, 256, NULL) == gqa.GQA_ERR_NULL
+    assert lib.gqa_workspace_init(FAKE_ODD, 256, NULL) == gqa.GQA_ERR_ALIGN
+
+
+def test_library_does_not_link_the_oracle():
+    # the product library and the oracle share nothing
+    with open(gqa.LIB_PATH, "rb") as f:
+        blob = f.read()
+    assert b"gqa_oracle" not in blob

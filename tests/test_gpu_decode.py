@@ -1,0 +1,181 @@
+"""GPU parity of the split-K decode entry points against the fp64 oracle.
+
+Covers the single-token decode workloads (Qwen2.5-0.5B heads at KV length
+128; Qwen2.5-7B heads swept 128..4096, fp32, the configuration the benchmark
+times), batched decode with per-request lengths (Qwen3-4B heads, bf16,
+B = 1, 2, 4, 8 in a 4096-row cache), and small ragged shapes for every dtype,
+head dim and several group sizes.  Also: NaN-filled cache rows past the
+valid length, guard bands around the output, run-to-run bit equality with a
+reused workspace, and batched output bit-identical to per-request calls.
+Bounds: max-abs 2e-5 for fp32 outputs, 2e-2 for bf16/f16.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.helpers import Guarded, assert_close, note, tol_for
+from workloads import configs as W
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def run_decode(gqa, q, k, v, kv_len, scale=None):
+    B, Hq, _, D = q.shape
+    Hkv, s_cap = k.shape[1], k.shape[2]
+    ws = gqa.make_workspace(B, Hq, Hkv, D, s_cap)
+    g = Guarded(q.shape, q.dtype)
+    gqa.gqa_decode_attend(q.cuda(), k.cuda(), v.cuda(), g.t, kv_len, ws, scale=scale)
+    torch.cuda.synchronize()
+    g.check()
+    return g.t
+
+
+def test_decode_0p5b_s128(gpu_lib):
+    w = W.by_name("decode_0p5b")
+    q, k, v = W.decode_inputs(w, 128, 0)
+    note("decode_0p5b S=128")
+    got = run_decode(gpu_lib, q, k, v, 128)
+    want = oracle.attend(q, k, v, scale=w.scale())
+    assert_close(got, want, 2e-5, "decode_0p5b")
+
+
+@pytest.mark.parametrize("S", [128, 256, 512, 1024, 2048, 4096])
+def test_decode_7b_sweep(gpu_lib, S):
+    w = W.by_name("decode_7b")
+    for layer in (0, 27):
+        q, k, v = W.decode_inputs(w, S, layer)
+        note("decode_7b S=%d layer=%d" % (S, layer))
+        got = run_decode(gpu_lib, q, k, v, S)
+        want = oracle.attend(q, k, v, scale=w.scale())
+        assert_close(got, want, 2e-5, "decode_7b S=%d layer %d" % (S, layer))
+
+
+GEOMS = [(1, 1), (4, 4), (8, 2), (12, 2), (14, 2), (32, 8), (16, 1), (10, 2), (28, 4)]
+LENS = [1, 5, 31, 32, 33, 100, 777]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_small_ragged(gpu_lib, dtype, D):
+    rng = np.random.default_rng({"f32": 0, "bf16": 1, "f16": 2}[dtype] * 1000 + D)
+    for Hq, Hkv in GEOMS:
+        for n in LENS:
+            s_cap = n + int(rng.integers(0, 40))
+            B = 1 + int(rng.integers(0, 2))
+            q = torch.from_numpy(rng.standard_normal((B, Hq, 1, D), dtype=np.float32)).to(DT[dtype])
+            k = torch.from_numpy(rng.standard_normal((B, Hkv, s_cap, D), dtype=np.float32)).to(DT[dtype])
+            v = torch.from_numpy(rng.standard_normal((B, Hkv, s_cap, D), dtype=np.float32)).to(DT[dtype])
+            k[:, :, n:] = float("nan")
+            v[:, :, n:] = float("nan")
+            note("decode %s D=%d Hq=%d Hkv=%d n=%d s_cap=%d B=%d" % (dtype, D, Hq, Hkv, n, s_cap, B))
+            got = run_decode(gpu_lib, q, k, v, n)
+            want = oracle.attend(q, k, v, kv_lens=n)
+            assert_close(got, want, tol_for(DT[dtype]), "n=%d Hq=%d Hkv=%d" % (n, Hq, Hkv))
+
+
+def test_decode_single_key_is_value_row(gpu_lib):
+    q = torch.randn(1, 28, 1, 128)
+    k = torch.randn(1, 4, 64, 128)
+    v = torch.randn(1, 4, 64, 128)
+    got = run_decode(gpu_lib, q, k, v, 1).cpu()
+    want = v[:, :, :1].repeat_interleave(7, dim=1)
+    assert torch.equal(got, want)
+
+
+def test_decode_deterministic_with_reused_workspace(gpu_lib):
+    w = W.by_name("decode_7b")
+    q, k, v = (t.cuda() for t in W.decode_inputs(w, 4096, 3))
+    ws = gpu_lib.make_workspace(1, 28, 4, 128, 4096)
+    outs = []
+    for _ in range(3):
+        o = torch.empty_like(q)
+        gpu_lib.gqa_decode_attend(q, k, v, o, 4096, ws)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+def test_workspace_init_entry_point(gpu_lib):
+    q = torch.randn(1, 8, 1, 64, device="cuda")
+    k = torch.randn(1, 2, 300, 64, device="cuda")
+    v = torch.randn(1, 2, 300, 64, device="cuda")
+    ws = torch.full((gpu_lib.gqa_decode_workspace_bytes(1, 8, 2, 64, 300),), 7, dtype=torch.uint8, device="cuda")
+    gpu_lib.gqa_workspace_init(ws)
+    o = torch.empty_like(q)
+    gpu_lib.gqa_decode_attend(q, k, v, o, 300, ws)
+    torch.cuda.synchronize()
+    assert_close(o, oracle.attend(q.cpu(), k.cpu(), v.cpu()), 2e-5, "after workspace init")
+
+
+# ---------------------------------------------------------------- batched
+
+def run_batched(gqa, q, k, v, lens):
+    B, Hq, _, D = q.shape
+    Hkv, s_cap = k.shape[1], k.shape[2]
+    ws = gqa.make_workspace(B, Hq, Hkv, D, s_cap)
+    g = Guarded(q.shape, q.dtype)
+    lens_d = torch.as_tensor(np.asarray(lens, dtype=np.int32)).cuda()
+    gqa.gqa_decode_attend_batched(q.cuda(), k.cuda(), v.cuda(), g.t, lens_d, ws)
+    torch.cuda.synchronize()
+    g.check()
+    return g.t
+
+
+@pytest.mark.parametrize("B", [1, 2, 4, 8])
+def test_batched_qwen3_4b(gpu_lib, B):
+    w = W.by_name("batched_qwen3_4b")
+    for layer in (0, 35):
+        q, k, v, lens = W.batched_inputs(w, B, layer)
+        note("batched B=%d layer=%d lens=%s" % (B, layer, list(lens)))
+        got = run_batched(gpu_lib, q, k, v, lens)
+        want = oracle.attend(q, k, v, kv_lens=lens)
+        assert_close(got, want, 2e-2, "batched B=%d layer %d" % (B, layer))
+        # bit-identical to one single-request call per request (same s_cap)
+        qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+        for b in range(B):
+            ws = gpu_lib.make_workspace(1, w.Hq, w.Hkv, w.D, w.s_cap)
+            o1 = torch.empty_like(qd[b:b + 1])
+            gpu_lib.gqa_decode_attend(qd[b:b + 1], kd[b:b + 1], vd[b:b + 1], o1, int(lens[b]), ws)
+            torch.cuda.synchronize()
+            assert torch.equal(o1, got[b:b + 1]), "request %d differs from its single call" % b
+        # requests carry distinct data: no output is another's copy
+        for b in range(1, B):
+            assert not torch.equal(got[b], got[0])
+
+
+def test_batched_lengths_zero_clamped_and_ragged(gpu_lib):
+    B, Hq, Hkv, D, s_cap = 6, 16, 4, 128, 200
+    q = torch.randn(B, Hq, 1, D).to(torch.bfloat16)
+    k = torch.randn(B, Hkv, s_cap, D).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, s_cap, D).to(torch.bfloat16)
+    lens = np.array([0, 1, 33, 200, 5000, -3], np.int32)   # 5000 and -3 are clamped
+    got = run_batched(gpu_lib, q, k, v, lens).cpu()
+    eff = np.clip(lens, 0, s_cap)
+    want = oracle.attend(q, k, v, kv_lens=eff)
+    assert_close(got, want, 2e-2, "ragged batch")
+    assert (got[0] == 0).all() and (got[5] == 0).all()
+
+
+def test_workspace_reuse_with_changing_inputs(gpu_lib):
+    """Back-to-back calls on one workspace with different inputs: a merge that
+    read a previous call's partials (or a counter left non-zero) would show up
+    as a mismatch here.  Every call's output is checked."""
+    rng = np.random.default_rng(99)
+    B, Hq, Hkv, D, s_cap = 1, 28, 4, 128, 4096
+    ws = gpu_lib.make_workspace(B, Hq, Hkv, D, s_cap)
+    cases = []
+    for i in range(24):
+        n = int(rng.integers(1, s_cap + 1)) if i % 3 else s_cap
+        q = torch.from_numpy(rng.standard_normal((B, Hq, 1, D), dtype=np.float32))
+        k = torch.from_numpy(rng.standard_normal((B, Hkv, s_cap, D), dtype=np.float32))
+        v = torch.from_numpy(rng.standard_normal((B, Hkv, s_cap, D), dtype=np.float32))
+        o = torch.empty((B, Hq, 1, D), device="cuda")
+        gpu_lib.gqa_decode_attend(q.cuda(), k.cuda(), v.cuda(), o, n, ws)  # no sync between calls
+        cases.append((q, k, v, n, o))
+    torch.cuda.synchronize()
+    for q, k, v, n, o in cases:
+        assert_close(o, oracle.attend(q, k, v, kv_lens=n), 2e-5, "reuse n=%d" % n)

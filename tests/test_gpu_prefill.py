@@ -1,0 +1,113 @@
+"""GPU parity of the causal prefill entry point against the fp64 oracle.
+
+Workloads: Qwen2.5-0.5B heads (14 query / 2 KV heads, dim 64), bf16, T in
+{513, 2049, 4097} with Tq = Tk = T, and the chunk of 256 queries at offset
+3841 into 4097 keys (queries aligned to the end of the keys, "Cause and
+workaround" point 2 of the Fornace prefill page).  T = 513 and 2049 and the
+chunk are compared on every output; T = 4097 on every output too (the oracle
+takes a few seconds on all cores).  Small shapes cover ragged tiles, Tq < Tk,
+D = 128, f16, several group sizes and B > 1.  Bound: max-abs 2e-2 (bf16/f16
+outputs).  Row 0 of a square prefill sees one key and must equal that key's
+value row exactly; the chunk must match the tail of the full prefill within
+the bound.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.helpers import Guarded, assert_close, note
+from workloads import configs as W
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(gqa, q, k, v, Tk=None):
+    g = Guarded(q.shape, q.dtype)
+    gqa.gqa_prefill_causal(q.cuda(), k.cuda(), v.cuda(), g.t, Tk=Tk)
+    torch.cuda.synchronize()
+    g.check()
+    return g.t
+
+
+@pytest.mark.parametrize("T", [513, 2049, 4097])
+def test_prefill_0p5b(gpu_lib, T):
+    w = W.by_name("prefill_0p5b")
+    q, k, v = W.prefill_inputs(w, T)
+    note("prefill_0p5b T=%d" % T)
+    got = run_prefill(gpu_lib, q, k, v)
+    want = oracle.attend(q, k, v, causal=True, scale=w.scale())
+    assert_close(got, want, 2e-2, "prefill T=%d" % T)
+    # row 0 sees only key 0
+    g = got.cpu()
+    assert torch.equal(g[0, :, 0], v[0, :, 0].repeat_interleave(w.G, dim=0))
+
+
+def test_prefill_chunk_at_offset(gpu_lib):
+    w = W.by_name("prefill_0p5b")
+    c = W.PREFILL_CHUNK
+    q, k, v = W.prefill_inputs(w, c["Tk"])
+    qc = q[:, :, c["offset"]:].contiguous()
+    note("prefill chunk Tq=%d Tk=%d" % (c["Tq"], c["Tk"]))
+    got = run_prefill(gpu_lib, qc, k, v)
+    want = oracle.attend(qc, k, v, causal=True, scale=w.scale())
+    assert_close(got, want, 2e-2, "chunk")
+    full = run_prefill(gpu_lib, q, k, v)
+    diff = (full[:, :, c["offset"]:].float() - got.float()).abs().max().item()
+    note("  chunk vs tail of full prefill: %.3e" % diff)
+    assert diff <= 2e-2
+
+
+CASES = [
+    # B, Hq, Hkv, D, Tq, Tk, s_cap
+    (1, 1, 1, 64, 1, 1, 1),
+    (1, 2, 1, 64, 1, 300, 300),
+    (1, 14, 2, 64, 5, 5, 9),
+    (2, 4, 2, 64, 127, 127, 130),
+    (1, 4, 4, 64, 128, 128, 128),
+    (1, 7, 1, 64, 129, 200, 256),
+    (1, 8, 8, 128, 200, 200, 200),
+    (2, 12, 2, 128, 65, 333, 400),
+    (1, 16, 1, 128, 257, 257, 257),
+    (1, 14, 2, 64, 64, 1000, 1000),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_prefill_small_ragged(gpu_lib, dtype):
+    rng = np.random.default_rng(17 if dtype == torch.bfloat16 else 18)
+    for B, Hq, Hkv, D, Tq, Tk, s_cap in CASES:
+        q = torch.from_numpy(rng.standard_normal((B, Hq, Tq, D), dtype=np.float32)).to(dtype)
+        k = torch.from_numpy(rng.standard_normal((B, Hkv, s_cap, D), dtype=np.float32)).to(dtype)
+        v = torch.from_numpy(rng.standard_normal((B, Hkv, s_cap, D), dtype=np.float32)).to(dtype)
+        k[:, :, Tk:] = float("nan")
+        v[:, :, Tk:] = float("nan")
+        note("prefill %s B=%d Hq=%d Hkv=%d D=%d Tq=%d Tk=%d s_cap=%d" % (dtype, B, Hq, Hkv, D, Tq, Tk, s_cap))
+        got = run_prefill(gpu_lib, q, k, v, Tk=Tk)
+        want = oracle.attend(q, k, v, kv_lens=Tk, causal=True)
+        assert_close(got, want, 2e-2, "Tq=%d Tk=%d" % (Tq, Tk))
+
+
+def test_prefill_large_scores(gpu_lib):
+    # scores spread far beyond the lazy-rescale threshold: the running max
+    # must be raised (rows with strongly increasing scores along the keys)
+    T, D = 300, 64
+    q = torch.ones(1, 2, T, D) * 0.5
+    k = (torch.arange(T, dtype=torch.float32)[:, None] / 20.0).expand(T, D).reshape(1, 1, T, D).contiguous()
+    v = torch.randn(1, 1, T, D)
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    got = run_prefill(gpu_lib, q, k, v)
+    want = oracle.attend(q, k, v, causal=True)
+    assert_close(got, want, 2e-2, "large scores")
+
+
+def test_prefill_deterministic(gpu_lib):
+    w = W.by_name("prefill_0p5b")
+    q, k, v = (t.cuda() for t in W.prefill_inputs(w, 2049))
+    a = torch.empty_like(q)
+    b = torch.empty_like(q)
+    gpu_lib.gqa_prefill_causal(q, k, v, a)
+    gpu_lib.gqa_prefill_causal(q, k, v, b)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
