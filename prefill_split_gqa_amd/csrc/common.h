@@ -97,7 +97,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 constexpr int kDecodeThreads = 512;     // 8 waves = 32 row-groups of 16 lanes
 constexpr int kDecodeRowGroups = kDecodeThreads / 16;
 constexpr int kDecodeMaxSplits = 64;    // partials merged by one workgroup (one round trip)
-constexpr int kDecodeTargetWGs = 128;   // measured best at 7B geometry, KV length 4096
+constexpr int kDecodeTargetWGs = 256;   // one workgroup per CU at full length
 
 struct DecodePlan {
     int G;            // query heads per KV head
@@ -134,7 +134,7 @@ inline bool make_decode_plan(int B, int Hq, int Hkv, int D, int s_cap, int targe
     size_t off = 0;
     p->off_o = off;   off = align_up(off + cols * p->n_split_max * p->GT * (size_t)D * 4, 256);
     p->off_ml = off;  off = align_up(off + cols * p->n_split_max * p->GT * 2 * 4, 256);
-    p->off_cnt = off; off = align_up(off + cols * 4, 256);
+    p->off_cnt = off;  // end of the partial arrays
     p->bytes = off;
     return true;
 }
@@ -153,7 +153,6 @@ struct DecodeArgs {
     float qscale;            // scale * log2(e)
     DecodePlan plan;
     float *part_o, *part_ml; // per split: [GT][D] outputs, [GT][2] (max, sum)
-    unsigned *cnt;           // one arrival counter per (request, head tile)
     size_t ws_bytes;
 };
 

@@ -18,11 +18,25 @@
 // End of a workgroup: the four row-groups of a wave are merged with the
 // gfx950 cross-half lane swaps (a reduce-scatter: after two swap+add steps
 // each lane owns a quarter of the wave's output slice), the eight waves
-// through LDS, giving one (max, sum, output) partial per split.  The last
-// workgroup of a (request, head tile) to finish merges every split's
-// partial with the log-sum-exp rule, in split order, so results do not
-// depend on timing.
+// through LDS, giving one (max, sum, output) partial per split.
 //
+// Cross-split merge: one CU can pull only ~70 GB/s, so a single workgroup
+// reading every split's partial would be the tail of the launch.  Instead the
+// grid carries, after all streaming workgroups, one merge workgroup per
+// (request, query head).  It waits until every split of its (request, head
+// tile) has published its partial for that head, reads only that head's
+// slice and merges it with the log-sum-exp rule in a fixed order (results do
+// not depend on timing).  A split publishes its outputs, waits for them to
+// complete, then writes its (max, sum) pair: the sum is >= 1 (the split's
+// maximum row contributes exp2(0)) and never 0, so a non-zero sum word means
+// "published".  The merge workgroup zeroes the words it consumed, leaving the
+// workspace ready for the next call; no counters or atomics are involved.
+// The wait always ends: workgroups are dispatched in linear-id order on every
+// XCD, so all streaming workgroups are dispatched before any merge workgroup
+// that waits for them, and they never wait on anything; the wait is also
+// bounded, and a merge workgroup that gives up writes NaN so that the failure
+// cannot pass silently.
+
 // Cross-workgroup exchange without cache maintenance: on gfx950 each XCD has
 // its own L2, and a device-scope fence writes back / invalidates that L2
 // (tens of microseconds across a full launch).  Instead, every value that
@@ -51,6 +65,17 @@ __device__ __forceinline__ float q4_dequant_value(float scale, float bias, uint3
     return __builtin_fmaf(scale, (float)code, bias);
 }
 
+// K/V rows are read with buffer loads whose resource covers exactly the
+// rows [0, end) of this (request, KV head): a row past the split's end reads
+// as zeros without a branch (and without a memory access), so every load of a
+// chunk is issued unconditionally.
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, size_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
+}
+
 // Dense K/V rows of D elements of type T.
 template <typename T, int D>
 struct DenseKV {
@@ -60,37 +85,32 @@ struct DenseKV {
     static constexpr int NU = BPL / U;                            // loads per lane per row
     static constexpr int EU = U / (int)sizeof(T);                 // elements per load
     static constexpr int WPU = U / 4;                             // words per load
+    static constexpr int ROW = D * (int)sizeof(T);                // bytes per row
     struct Raw { uint32_t w[NU * WPU]; };
 
     __device__ __forceinline__ static int dim(int lr, int e) { return ((e / EU) * 16 + lr) * EU + (e % EU); }
 
     struct Src {
-        const T *base;  // row 0 of this (request, KV head)
+        __amdgpu_buffer_rsrc_t rs;  // rows [0, end) of this (request, KV head)
     };
-    __device__ __forceinline__ static Src make_src(const DecodeArgs &a, bool is_v, size_t head_row0, int)
+    __device__ __forceinline__ static Src make_src(const DecodeArgs &a, bool is_v, size_t head_row0, int end, int)
     {
-        return Src{(const T *)(is_v ? a.v : a.k) + head_row0 * D};
+        return Src{make_rsrc((const T *)(is_v ? a.v : a.k) + head_row0 * D, (size_t)end * ROW)};
     }
 
     __device__ __forceinline__ static void load(Raw &r, const Src &s, int row, int lr)
     {
-        const char *p = (const char *)(s.base + (size_t)row * D);
 #pragma unroll
         for (int j = 0; j < NU; ++j) {
-            const char *pj = p + (size_t)(j * 16 + lr) * U;
+            const int off = row * ROW + (j * 16 + lr) * U;
             if constexpr (U == 16) {
-                uint4 x = *(const uint4 *)pj;
-                r.w[j * 4 + 0] = x.x; r.w[j * 4 + 1] = x.y; r.w[j * 4 + 2] = x.z; r.w[j * 4 + 3] = x.w;
+                auto x = __builtin_amdgcn_raw_buffer_load_b128(s.rs, off, 0, 0);
+                r.w[j * 4 + 0] = x[0]; r.w[j * 4 + 1] = x[1]; r.w[j * 4 + 2] = x[2]; r.w[j * 4 + 3] = x[3];
             } else {
-                uint2 x = *(const uint2 *)pj;
-                r.w[j * 2 + 0] = x.x; r.w[j * 2 + 1] = x.y;
+                auto x = __builtin_amdgcn_raw_buffer_load_b64(s.rs, off, 0, 0);
+                r.w[j * 2 + 0] = x[0]; r.w[j * 2 + 1] = x[1];
             }
         }
-    }
-    __device__ __forceinline__ static void zero(Raw &r)
-    {
-#pragma unroll
-        for (int i = 0; i < NU * WPU; ++i) r.w[i] = 0;
     }
     __device__ __forceinline__ static void unpack(const Raw &r, float *x)
     {
@@ -99,13 +119,23 @@ struct DenseKV {
         for (int i = 0; i < NU * WPU; ++i) Unpack<T>::run(r.w[i], x + i * PW);
     }
     // a query row has the same element type and lane layout as a K row
-    __device__ __forceinline__ static void load_q(float *x, const void *q, size_t row, int lr)
+    typedef Raw QRaw;
+    __device__ __forceinline__ static void load_q(QRaw &r, const void *q, size_t row, int lr)
     {
-        Raw r;
-        Src qs{(const T *)q + row * D};
-        load(r, qs, 0, lr);
-        unpack(r, x);
+        const char *p = (const char *)q + row * ROW;
+#pragma unroll
+        for (int j = 0; j < NU; ++j) {
+            const char *pj = p + (j * 16 + lr) * U;
+            if constexpr (U == 16) {
+                const uint4 x = *(const uint4 *)pj;
+                r.w[j * 4 + 0] = x.x; r.w[j * 4 + 1] = x.y; r.w[j * 4 + 2] = x.z; r.w[j * 4 + 3] = x.w;
+            } else {
+                const uint2 x = *(const uint2 *)pj;
+                r.w[j * 2 + 0] = x.x; r.w[j * 2 + 1] = x.y;
+            }
+        }
     }
+    __device__ __forceinline__ static void unpack_q(const QRaw &r, float *x) { unpack(r, x); }
 };
 
 // 4-bit group-affine K/V rows: D/2 bytes of codes plus D/group f16 scales and
@@ -114,55 +144,59 @@ template <int D>
 struct Q4KV {
     static constexpr int EPL = D / 16;
     static constexpr int CB = EPL / 2;  // code bytes per lane (4 or 2)
-    struct Raw { uint32_t codes; uint32_t sb; };  // sb: scale bits | bias bits << 16
+    struct Raw { uint32_t codes; uint32_t scale; uint32_t bias; };
 
     __device__ __forceinline__ static int dim(int lr, int e) { return lr * EPL + e; }
 
     struct Src {
-        const uint8_t *codes;
-        const uint16_t *scales, *biases;
+        __amdgpu_buffer_rsrc_t codes, scales, biases;  // rows [0, end)
         int n_groups;      // D / group
         int lane_group;    // group index of this lane's elements
     };
-    __device__ __forceinline__ static Src make_src(const DecodeArgs &a, bool is_v, size_t head_row0, int lr)
+    __device__ __forceinline__ static Src make_src(const DecodeArgs &a, bool is_v, size_t head_row0, int end, int lr)
     {
         Src r;
         r.n_groups = D / a.group;
         r.lane_group = (lr * EPL) / a.group;
-        r.codes = (const uint8_t *)(is_v ? a.v : a.k) + head_row0 * (D / 2);
-        r.scales = (const uint16_t *)(is_v ? a.v_scales : a.k_scales) + head_row0 * r.n_groups;
-        r.biases = (const uint16_t *)(is_v ? a.v_biases : a.k_biases) + head_row0 * r.n_groups;
+        r.codes = make_rsrc((const uint8_t *)(is_v ? a.v : a.k) + head_row0 * (D / 2), (size_t)end * (D / 2));
+        r.scales = make_rsrc((const uint16_t *)(is_v ? a.v_scales : a.k_scales) + head_row0 * r.n_groups,
+                             (size_t)end * r.n_groups * 2);
+        r.biases = make_rsrc((const uint16_t *)(is_v ? a.v_biases : a.k_biases) + head_row0 * r.n_groups,
+                             (size_t)end * r.n_groups * 2);
         return r;
     }
 
     __device__ __forceinline__ static void load(Raw &r, const Src &s, int row, int lr)
     {
-        const uint8_t *c = s.codes + (size_t)row * (D / 2) + lr * CB;
-        if constexpr (CB == 4) r.codes = *(const uint32_t *)c;
-        else r.codes = *(const uint16_t *)c;
-        const size_t gi = (size_t)row * s.n_groups + s.lane_group;
-        r.sb = (uint32_t)s.scales[gi] | ((uint32_t)s.biases[gi] << 16);
+        const int off = row * (D / 2) + lr * CB;
+        if constexpr (CB == 4) r.codes = __builtin_amdgcn_raw_buffer_load_b32(s.codes, off, 0, 0);
+        else r.codes = __builtin_amdgcn_raw_buffer_load_b16(s.codes, off, 0, 0);
+        const int goff = (row * s.n_groups + s.lane_group) * 2;
+        r.scale = __builtin_amdgcn_raw_buffer_load_b16(s.scales, goff, 0, 0);
+        r.bias = __builtin_amdgcn_raw_buffer_load_b16(s.biases, goff, 0, 0);
     }
-    __device__ __forceinline__ static void zero(Raw &r) { r.codes = 0; r.sb = 0; }
     // f16 query: the lane's D/16 consecutive elements in one vector load
-    __device__ __forceinline__ static void load_q(float *x, const void *q, size_t row, int lr)
+    struct QRaw { uint32_t w[EPL / 2]; };
+    __device__ __forceinline__ static void load_q(QRaw &r, const void *q, size_t row, int lr)
     {
         const uint16_t *p = (const uint16_t *)q + row * D + lr * EPL;
-        uint32_t w[EPL / 2];
         if constexpr (EPL == 8) {
             const uint4 v = *(const uint4 *)p;
-            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+            r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
         } else {
             const uint2 v = *(const uint2 *)p;
-            w[0] = v.x; w[1] = v.y;
+            r.w[0] = v.x; r.w[1] = v.y;
         }
+    }
+    __device__ __forceinline__ static void unpack_q(const QRaw &r, float *x)
+    {
 #pragma unroll
-        for (int i = 0; i < EPL / 2; ++i) Unpack<f16_t>::run(w[i], x + 2 * i);
+        for (int i = 0; i < EPL / 2; ++i) Unpack<f16_t>::run(r.w[i], x + 2 * i);
     }
     __device__ __forceinline__ static void unpack(const Raw &r, float *x)
     {
-        const float sc = f16_bits_to_f32(r.sb & 0xFFFFu);
-        const float bi = f16_bits_to_f32(r.sb >> 16);
+        const float sc = f16_bits_to_f32(r.scale & 0xFFFFu);
+        const float bi = f16_bits_to_f32(r.bias & 0xFFFFu);
 #pragma unroll
         for (int e = 0; e < EPL; ++e) x[e] = q4_dequant_value(sc, bi, (r.codes >> (4 * e)) & 0xFu);
     }
@@ -224,25 +258,20 @@ __device__ __forceinline__ float rowgroup_sum(float x)
     return a + b;
 }
 
-// Waits until this workgroup's device-scope stores have completed, then
-// takes a ticket; true in every thread of the last of `expected` arrivals.
-__device__ __forceinline__ bool take_ticket(unsigned *counter, unsigned expected, int *s_flag)
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
-    __syncthreads();                // ... and so have every other wave's
-    if (threadIdx.x == 0) {
-        const unsigned t = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = (t == expected - 1);
-        if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
-        *s_flag = last;
-    }
-    __syncthreads();
-    return *s_flag != 0;
-}
+constexpr unsigned kMergeSpinLimit = 1u << 22;  // polls before a merge workgroup gives up
+
+// Kernel launch shape of the decode grid: streaming workgroups first, then
+// merge workgroups (one per request and query head).
+struct DecodeGrid {
+    int gx;        // splits per (request, head tile) in the grid
+    int n_stream;  // gx * HT * B
+};
+
+template <typename TQ, int D, int GT>
+__device__ void merge_role(const DecodeArgs &a, int m);
 
 template <class KV, typename TQ, int D, int GT>
-__global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArgs a)
+__global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArgs a, DecodeGrid grid)
 {
     constexpr int EPL = D / 16;
     constexpr int RC = 2;                     // rows per row-group per chunk
@@ -253,11 +282,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
     static_assert(KV::EPL == EPL, "lane layout mismatch");
     static_assert(NF % 4 == 0 && NQ <= kDecodeThreads, "tile shape");
 
+    if ((int)blockIdx.x >= grid.n_stream) {
+        merge_role<TQ, D, GT>(a, (int)blockIdx.x - grid.n_stream);
+        return;
+    }
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, rgq = lane >> 4, lr = lane & 15;
     const int rg = wave * 4 + rgq;  // row-group within the workgroup
-    const int s = blockIdx.x, ht = blockIdx.y, b = blockIdx.z;
     const DecodePlan &P = a.plan;
+    const int s = (int)blockIdx.x % grid.gx;
+    const int ht = ((int)blockIdx.x / grid.gx) % P.HT;
+    const int b = (int)blockIdx.x / (grid.gx * P.HT);
 
     int n = a.kv_len;
     if (a.kv_lens) {
@@ -279,30 +314,33 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
     const int end = min(start + P.L, n);
 
     const size_t head_row0 = ((size_t)b * a.Hkv + g) * (size_t)a.s_cap;
-    const typename KV::Src src = KV::make_src(a, false, head_row0, lr);
-    const typename KV::Src srcv = KV::make_src(a, true, head_row0, lr);
+    const typename KV::Src src = KV::make_src(a, false, head_row0, end, lr);
+    const typename KV::Src srcv = KV::make_src(a, true, head_row0, end, lr);
 
     typename KV::Raw kr[2][RC], vr[2][RC];
     auto load_chunk = [&](int buf, int c0) {
 #pragma unroll
         for (int rr = 0; rr < RC; ++rr) {
-            const int row = c0 + rr * kDecodeRowGroups + rg;
-            if (row < end) {
-                KV::load(kr[buf][rr], src, row, lr);
-                KV::load(vr[buf][rr], srcv, row, lr);
-            } else {
-                KV::zero(kr[buf][rr]);
-                KV::zero(vr[buf][rr]);
-            }
+            const int row = c0 + rr * kDecodeRowGroups + rg;  // rows >= end read as zero
+            KV::load(kr[buf][rr], src, row, lr);
+            KV::load(vr[buf][rr], srcv, row, lr);
         }
     };
+
+    // Issue order matters: vector-memory waits are in order, so the queries
+    // go first (their wait then does not wait for K/V), then the first two
+    // chunks, all before anything is consumed.
+    typename KV::QRaw qraw[GT];
+#pragma unroll
+    for (int h = 0; h < GT; ++h) KV::load_q(qraw[h], a.q, (size_t)b * a.Hq + h0 + h, lr);
     load_chunk(0, start);
+    if (start + CHUNK < end) load_chunk(1, start + CHUNK);
 
     // Queries of the GT heads, pre-multiplied by scale*log2(e).
     float qf[GT][EPL];
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
-        KV::load_q(qf[h], a.q, (size_t)b * a.Hq + h0 + h, lr);
+        KV::unpack_q(qraw[h], qf[h]);
 #pragma unroll
         for (int e = 0; e < EPL; ++e) qf[h][e] *= a.qscale;
     }
@@ -367,20 +405,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
         }
     };
 
-    // Two-deep register pipeline over the chunks of this split.
+    // Two-deep register pipeline over the chunks of this split: chunks c and
+    // c+1 are in flight while chunk c is consumed.
     for (int c0 = start; c0 < end; c0 += 2 * CHUNK) {
         const int c1 = c0 + CHUNK;
-        if (c1 < end) load_chunk(1, c1);
         process_chunk(0, c0);
         if (c1 >= end) break;
         if (c1 + CHUNK < end) load_chunk(0, c1 + CHUNK);
         process_chunk(1, c1);
+        if (c1 + 2 * CHUNK < end) load_chunk(1, c1 + 2 * CHUNK);
     }
 
     // ---- merge the 4 row-groups of each wave ----
     __shared__ __attribute__((aligned(16))) float so[NW][GT][D];
     __shared__ float sm[NW][GT], sl[NW][GT];
-    __shared__ int s_last;
     float of[NF];
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
@@ -434,78 +472,124 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
         return;
     }
 
-    // ---- publish the partial with device-scope stores ----
+    // ---- publish the partial with device-scope stores: outputs first, then
+    //      (after they have completed) the (max, sum) word that flags them ----
     const __amdgpu_buffer_rsrc_t ws_o =
-        __builtin_amdgcn_make_buffer_rsrc(a.part_o, 0, (int)(P.off_ml - P.off_o), 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(a.part_o, 0, (int)(P.off_ml - P.off_o), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t ws_ml =
-        __builtin_amdgcn_make_buffer_rsrc(a.part_ml, 0, (int)(P.off_cnt - P.off_ml), 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(a.part_ml, 0, (int)(P.off_cnt - P.off_ml), kRsrcWord3);
     const size_t colbase = (size_t)col * P.n_split_max;
     if (tid < NQ) {
         const int off_o = (int)((((colbase + s) * GT + qh) * D + qd) * 4);
         __builtin_amdgcn_raw_buffer_store_b128(
             __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, make_float4(O0, O1, O2, O3)), ws_o,
             off_o, 0, kSC1);
-        if (qd == 0) {
-            const int off_ml = (int)(((colbase + s) * GT + qh) * 2 * 4);
-            __builtin_amdgcn_raw_buffer_store_b64(
-                __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, make_float2(Mw, Lw)), ws_ml,
-                off_ml, 0, kSC1);
-        }
     }
-    if (!take_ticket(&a.cnt[col], (unsigned)n_split, &s_last)) return;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's output stores have completed
+    __syncthreads();                // ... and so have every other wave's
+    if (tid < NQ && qd == 0) {
+        const int off_ml = (int)(((colbase + s) * GT + qh) * 2 * 4);
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, make_float2(Mw, Lw)), ws_ml, off_ml, 0,
+            kSC1);
+    }
+}
 
-    // ---- last arrival: merge every split's partial in one round trip ----
-    // Thread t handles output item t % 256 over the splits of half t / 256
-    // (up to kDecodeMaxSplits / 2 each); the (max, sum) pairs of every split
-    // are staged in LDS by the same round trip.  The merge order is fixed:
-    // each half sums its splits in order, then half 0 adds half 1.
-    constexpr int HALF = kDecodeMaxSplits / 2;
-    static_assert(kDecodeThreads == 512 && NQ <= 256, "merge layout");
-    __shared__ float2 sml[kDecodeMaxSplits][GT];
-    __shared__ float4 sacc[256];
-    __shared__ float sls[256];
-    const int item = tid & 255, hf = tid >> 8;
-    const int mh = item / (D / 4), md = (item % (D / 4)) * 4;
-    const int s_first = hf * HALF;
-    const int s_count = max(0, min(HALF, n_split - s_first));
-    float4 po[HALF];
-    if (item < NQ) {
-#pragma unroll
-        for (int j = 0; j < HALF; ++j) {
-            const int sj = j < s_count ? s_first + j : 0;
-            const int off_o = (int)((((colbase + sj) * GT + mh) * D + md) * 4);
-            po[j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ws_o, off_o, 0, kSC1));
-        }
+// Merge workgroup m: request b, query head h0 + hh of head tile ht.
+// Thread t handles 4 dims (t % (D/4)) of the splits j = t / (D/4) + k * NG;
+// the NG strided groups are then added in group order.
+template <typename TQ, int D, int GT>
+__device__ void merge_role(const DecodeArgs &a, int m)
+{
+    constexpr int D4 = D / 4;
+    constexpr int NG = kDecodeThreads / D4;              // split groups
+    constexpr int PER = (kDecodeMaxSplits + NG - 1) / NG; // splits per group
+    __shared__ float2 sml[kDecodeMaxSplits];
+    __shared__ float4 sacc[NG][D4];
+    __shared__ float sls[NG][D4];
+    __shared__ int s_go;
+    const DecodePlan &P = a.plan;
+    const int tid = threadIdx.x;
+    const int hh = m % GT;
+    const int col = m / GT;
+    const int ht = col % P.HT;
+    const int b = col / P.HT;
+    int n = a.kv_len;
+    if (a.kv_lens) {
+        n = a.kv_lens[b];
+        n = n < 0 ? 0 : (n > a.s_cap ? a.s_cap : n);
     }
-    if (tid < n_split * GT) {
-        const int ms = tid / GT, mhh = tid % GT;
-        const int off_ml = (int)(((colbase + ms) * GT + mhh) * 2 * 4);
-        sml[ms][mhh] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(ws_ml, off_ml, 0, kSC1));
+    const int n_split = (n + P.L - 1) / P.L;
+    if (n_split <= 1) return;  // written directly by the streaming workgroup
+    const int g = ht / P.ht_per_kv;
+    const int h = g * P.G + (ht % P.ht_per_kv) * GT + hh;
+    TQ *out = (TQ *)a.out + ((size_t)b * a.Hq + h) * D;
+
+    // wait until every split has published this head's partial: thread j
+    // polls split j's (max, sum) word (the sum is never 0 once written)
+    const size_t colbase = (size_t)col * P.n_split_max;
+    const __amdgpu_buffer_rsrc_t ws_ml = make_rsrc(a.part_ml + colbase * GT * 2, (size_t)n_split * GT * 8);
+    if (tid == 0) s_go = 1;
+    __syncthreads();
+    if (tid < n_split) {
+        unsigned it = 0;
+        float2 ml = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(ws_ml, (tid * GT + hh) * 8, 0, kSC1));
+        while (__float_as_uint(ml.y) == 0u && ++it < kMergeSpinLimit) {
+            __builtin_amdgcn_s_sleep(2);
+            ml = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(ws_ml, (tid * GT + hh) * 8, 0, kSC1));
+        }
+        sml[tid] = ml;
+        if (__float_as_uint(ml.y) == 0u) s_go = 0;
     }
     __syncthreads();
+    const int d4 = tid % D4, grp = tid / D4;
+    if (!s_go) {  // not reachable with in-order dispatch; never pass silently
+        if (grp == 0) store4(out + d4 * 4, __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
+        return;
+    }
+
+    const __amdgpu_buffer_rsrc_t ws_o =
+        make_rsrc(a.part_o + colbase * GT * D, (size_t)n_split * GT * D * 4);  // splits past n_split read 0
+    float4 po[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int j = grp + k * NG;
+        const int off = (int)((((size_t)j * GT + hh) * D + d4 * 4) * 4);
+        po[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ws_o, off, 0, kSC1));
+    }
     float M = kNegInf;
-    if (item < NQ)
-        for (int j = 0; j < n_split; ++j) M = fmaxf(M, sml[j][mh].x);
+    for (int j = 0; j < n_split; ++j) M = fmaxf(M, sml[j].x);
     float Ls = 0.0f;
     float4 R = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if (item < NQ) {
 #pragma unroll
-        for (int j = 0; j < HALF; ++j) {
-            if (j >= s_count) continue;
-            const float2 ml = sml[s_first + j][mh];
+    for (int k = 0; k < PER; ++k) {
+        const int j = grp + k * NG;
+        if (j < n_split) {
+            const float2 ml = sml[j];
             const float w = rel_weight(ml.x, M);
             Ls += w * ml.y;
-            R.x += w * po[j].x; R.y += w * po[j].y; R.z += w * po[j].z; R.w += w * po[j].w;
+            R.x += w * po[k].x; R.y += w * po[k].y; R.z += w * po[k].z; R.w += w * po[k].w;
         }
     }
-    if (hf == 1) { sacc[item] = R; sls[item] = Ls; }
+    sacc[grp][d4] = R;
+    sls[grp][d4] = Ls;
     __syncthreads();
-    if (hf == 0 && item < NQ) {
-        const float4 R1 = sacc[item];
-        Ls += sls[item];
-        R.x += R1.x; R.y += R1.y; R.z += R1.z; R.w += R1.w;
-        store4(out + (size_t)mh * D + md, R.x / Ls, R.y / Ls, R.z / Ls, R.w / Ls);
+    if (grp == 0) {
+#pragma unroll
+        for (int q = 1; q < NG; ++q) {
+            const float4 x = sacc[q][d4];
+            Ls += sls[q][d4];
+            R.x += x.x; R.y += x.y; R.z += x.z; R.w += x.w;
+        }
+        store4(out + d4 * 4, R.x / Ls, R.y / Ls, R.z / Ls, R.w / Ls);
     }
+    // consume the flags: this head's (max, sum) words go back to zero (the
+    // reads above have completed: their values were used)
+    if (tid < n_split)
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, make_float2(0.0f, 0.0f)), ws_ml,
+            (tid * GT + hh) * 8, 0, kSC1);
 }
 
 // ---------------------------------------------------------------------------
@@ -514,9 +598,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
 template <class KV, typename TQ, int D, int GT>
 static hipError_t launch_one(int B, const DecodeArgs &a, hipStream_t stream)
 {
-    const int gx = a.kv_lens ? a.plan.n_split_max : (a.kv_len + a.plan.L - 1) / a.plan.L;
-    dim3 grid(gx, a.plan.HT, B);
-    hipLaunchKernelGGL((decode_splitk_kernel<KV, TQ, D, GT>), grid, dim3(kDecodeThreads), 0, stream, a);
+    DecodeGrid g;
+    g.gx = a.kv_lens ? a.plan.n_split_max : (a.kv_len + a.plan.L - 1) / a.plan.L;
+    g.n_stream = g.gx * a.plan.HT * B;
+    // merge workgroups are needed only when a request can have several splits
+    const int n_merge = a.plan.n_split_max > 1 && g.gx > 1 ? B * a.plan.HT * GT : 0;
+    hipLaunchKernelGGL((decode_splitk_kernel<KV, TQ, D, GT>), dim3(g.n_stream + n_merge), dim3(kDecodeThreads), 0,
+                       stream, a, g);
     return hipGetLastError();
 }
 

@@ -91,7 +91,8 @@ int check_decode_common(const void *q, const void *k, const void *v, void *out, 
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || s_cap < 1) return GQA_ERR_SHAPE;
     if (!std::isfinite(scale)) return GQA_ERR_SHAPE;
     if (D != 64 && D != 128) return GQA_ERR_UNSUPPORTED;
-    if (B > 65535 || (size_t)B * Hkv * (size_t)s_cap * D >= ((size_t)1 << 40)) return GQA_ERR_SHAPE;
+    // a KV head's rows are addressed with 32-bit buffer offsets
+    if (B > 65535 || (size_t)s_cap * D * 4 >= ((size_t)1 << 31)) return GQA_ERR_SHAPE;
     if (!plan_decode(B, Hq, Hkv, D, s_cap, plan)) return GQA_ERR_SHAPE;
     if (!ws || ws_bytes < plan->bytes) return GQA_ERR_WORKSPACE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(ws)) return GQA_ERR_ALIGN;
@@ -103,7 +104,6 @@ void fill_ws(DecodeArgs &a, void *ws)
     char *base = (char *)ws;
     a.part_o = (float *)(base + a.plan.off_o);
     a.part_ml = (float *)(base + a.plan.off_ml);
-    a.cnt = (unsigned *)(base + a.plan.off_cnt);
     a.ws_bytes = a.plan.bytes;
 }
 
