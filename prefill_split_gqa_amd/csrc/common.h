@@ -81,6 +81,16 @@ __device__ __forceinline__ float row16_sum(float x)
     return x;
 }
 
+// Sum over each 32-lane half of the wave: the 16-lane sum, then the two
+// rows of the half added with the gfx950 row swap (which hands each row the
+// other row's value).
+__device__ __forceinline__ float row32_sum(float x)
+{
+    x = row16_sum(x);
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float shfl_xor_f32(float x, int mask)
 {
     return __shfl_xor(x, mask, 64);
@@ -94,8 +104,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // boundaries depend only on (s_cap, Hq, Hkv) -- never on B or on the other
 // requests' lengths.
 // ---------------------------------------------------------------------------
-constexpr int kDecodeThreads = 512;     // 8 waves = 32 row-groups of 16 lanes
-constexpr int kDecodeRowGroups = kDecodeThreads / 16;
+constexpr int kDecodeThreads = 512;     // 8 waves
+constexpr int kDecodeLPR = 32;          // lanes per key row (a row-group)
+constexpr int kDecodeRowGroups = kDecodeThreads / kDecodeLPR;
 constexpr int kDecodeMaxSplits = 64;    // partials merged by one workgroup (one round trip)
 constexpr int kDecodeTargetWGs = 256;   // one workgroup per CU at full length
 

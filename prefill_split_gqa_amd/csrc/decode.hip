@@ -79,8 +79,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, si
 // Dense K/V rows of D elements of type T.
 template <typename T, int D>
 struct DenseKV {
-    static constexpr int EPL = D / 16;                            // elements per lane
-    static constexpr int BPL = D * (int)sizeof(T) / 16;           // bytes per lane
+    static constexpr int EPL = D / kDecodeLPR;                    // elements per lane
+    static constexpr int BPL = D * (int)sizeof(T) / kDecodeLPR;   // bytes per lane
     static constexpr int U = BPL >= 16 ? 16 : BPL;                // bytes per load
     static constexpr int NU = BPL / U;                            // loads per lane per row
     static constexpr int EU = U / (int)sizeof(T);                 // elements per load
@@ -88,7 +88,7 @@ struct DenseKV {
     static constexpr int ROW = D * (int)sizeof(T);                // bytes per row
     struct Raw { uint32_t w[NU * WPU]; };
 
-    __device__ __forceinline__ static int dim(int lr, int e) { return ((e / EU) * 16 + lr) * EU + (e % EU); }
+    __device__ __forceinline__ static int dim(int lr, int e) { return ((e / EU) * kDecodeLPR + lr) * EU + (e % EU); }
 
     struct Src {
         __amdgpu_buffer_rsrc_t rs;  // rows [0, end) of this (request, KV head)
@@ -102,13 +102,15 @@ struct DenseKV {
     {
 #pragma unroll
         for (int j = 0; j < NU; ++j) {
-            const int off = row * ROW + (j * 16 + lr) * U;
+            const int off = row * ROW + (j * kDecodeLPR + lr) * U;
             if constexpr (U == 16) {
                 auto x = __builtin_amdgcn_raw_buffer_load_b128(s.rs, off, 0, 0);
                 r.w[j * 4 + 0] = x[0]; r.w[j * 4 + 1] = x[1]; r.w[j * 4 + 2] = x[2]; r.w[j * 4 + 3] = x[3];
-            } else {
+            } else if constexpr (U == 8) {
                 auto x = __builtin_amdgcn_raw_buffer_load_b64(s.rs, off, 0, 0);
                 r.w[j * 2 + 0] = x[0]; r.w[j * 2 + 1] = x[1];
+            } else {
+                r.w[j] = __builtin_amdgcn_raw_buffer_load_b32(s.rs, off, 0, 0);
             }
         }
     }
@@ -118,32 +120,27 @@ struct DenseKV {
 #pragma unroll
         for (int i = 0; i < NU * WPU; ++i) Unpack<T>::run(r.w[i], x + i * PW);
     }
-    // a query row has the same element type and lane layout as a K row
+    // a query row has the same element type and lane layout as a K row; the
+    // workgroup's query rows are staged in LDS (sq) first
     typedef Raw QRaw;
-    __device__ __forceinline__ static void load_q(QRaw &r, const void *q, size_t row, int lr)
+    __device__ __forceinline__ static void load_q_lds(QRaw &r, const uint32_t *sq, int h, int lr)
     {
-        const char *p = (const char *)q + row * ROW;
 #pragma unroll
         for (int j = 0; j < NU; ++j) {
-            const char *pj = p + (j * 16 + lr) * U;
-            if constexpr (U == 16) {
-                const uint4 x = *(const uint4 *)pj;
-                r.w[j * 4 + 0] = x.x; r.w[j * 4 + 1] = x.y; r.w[j * 4 + 2] = x.z; r.w[j * 4 + 3] = x.w;
-            } else {
-                const uint2 x = *(const uint2 *)pj;
-                r.w[j * 2 + 0] = x.x; r.w[j * 2 + 1] = x.y;
-            }
+            const uint32_t *pj = sq + (h * ROW + (j * kDecodeLPR + lr) * U) / 4;
+#pragma unroll
+            for (int w = 0; w < WPU; ++w) r.w[j * WPU + w] = pj[w];
         }
     }
     __device__ __forceinline__ static void unpack_q(const QRaw &r, float *x) { unpack(r, x); }
 };
 
 // 4-bit group-affine K/V rows: D/2 bytes of codes plus D/group f16 scales and
-// biases.  Lane lr owns the D/16 consecutive elements starting at lr*D/16.
+// biases.  Lane lr owns the D/32 consecutive elements starting at lr*D/32.
 template <int D>
 struct Q4KV {
-    static constexpr int EPL = D / 16;
-    static constexpr int CB = EPL / 2;  // code bytes per lane (4 or 2)
+    static constexpr int EPL = D / kDecodeLPR;
+    static constexpr int CB = EPL / 2;  // code bytes per lane (2 or 1)
     struct Raw { uint32_t codes; uint32_t scale; uint32_t bias; };
 
     __device__ __forceinline__ static int dim(int lr, int e) { return lr * EPL + e; }
@@ -169,24 +166,19 @@ struct Q4KV {
     __device__ __forceinline__ static void load(Raw &r, const Src &s, int row, int lr)
     {
         const int off = row * (D / 2) + lr * CB;
-        if constexpr (CB == 4) r.codes = __builtin_amdgcn_raw_buffer_load_b32(s.codes, off, 0, 0);
-        else r.codes = __builtin_amdgcn_raw_buffer_load_b16(s.codes, off, 0, 0);
+        if constexpr (CB == 2) r.codes = __builtin_amdgcn_raw_buffer_load_b16(s.codes, off, 0, 0);
+        else r.codes = __builtin_amdgcn_raw_buffer_load_b8(s.codes, off, 0, 0);
         const int goff = (row * s.n_groups + s.lane_group) * 2;
         r.scale = __builtin_amdgcn_raw_buffer_load_b16(s.scales, goff, 0, 0);
         r.bias = __builtin_amdgcn_raw_buffer_load_b16(s.biases, goff, 0, 0);
     }
-    // f16 query: the lane's D/16 consecutive elements in one vector load
+    // f16 query: the lane's D/32 consecutive elements, from the staged rows
     struct QRaw { uint32_t w[EPL / 2]; };
-    __device__ __forceinline__ static void load_q(QRaw &r, const void *q, size_t row, int lr)
+    __device__ __forceinline__ static void load_q_lds(QRaw &r, const uint32_t *sq, int h, int lr)
     {
-        const uint16_t *p = (const uint16_t *)q + row * D + lr * EPL;
-        if constexpr (EPL == 8) {
-            const uint4 v = *(const uint4 *)p;
-            r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
-        } else {
-            const uint2 v = *(const uint2 *)p;
-            r.w[0] = v.x; r.w[1] = v.y;
-        }
+        const uint32_t *p = sq + (h * D + lr * EPL) / 2;
+#pragma unroll
+        for (int w = 0; w < EPL / 2; ++w) r.w[w] = p[w];
     }
     __device__ __forceinline__ static void unpack_q(const QRaw &r, float *x)
     {
@@ -240,21 +232,17 @@ __device__ __forceinline__ void swap16(float a, float b, float &lo, float &hi)
     lo = __uint_as_float(r[0]);
     hi = __uint_as_float(r[1]);
 }
-// max / sum over the 4 row-groups of a wave (lanes l, l^16, l^32, l^48)
+// max / sum over the 2 row-groups of a wave (lanes l and l^32)
 __device__ __forceinline__ float rowgroup_max(float x)
 {
     float a, b;
     swap32(x, x, a, b);
-    x = fmaxf(a, b);
-    swap16(x, x, a, b);
     return fmaxf(a, b);
 }
 __device__ __forceinline__ float rowgroup_sum(float x)
 {
     float a, b;
     swap32(x, x, a, b);
-    x = a + b;
-    swap16(x, x, a, b);
     return a + b;
 }
 
@@ -273,22 +261,22 @@ __device__ void merge_role(const DecodeArgs &a, int m);
 template <class KV, typename TQ, int D, int GT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArgs a, DecodeGrid grid)
 {
-    constexpr int EPL = D / 16;
+    constexpr int EPL = D / kDecodeLPR;
     constexpr int RC = 2;                     // rows per row-group per chunk
     constexpr int CHUNK = RC * kDecodeRowGroups;
     constexpr int NW = kDecodeThreads / 64;   // waves
     constexpr int NF = GT * EPL;              // output registers per lane
     constexpr int NQ = GT * D / 4;            // 4-wide output items
     static_assert(KV::EPL == EPL, "lane layout mismatch");
-    static_assert(NF % 4 == 0 && NQ <= kDecodeThreads, "tile shape");
+    static_assert(NF % 2 == 0 && NQ <= kDecodeThreads && kDecodeLPR == 32, "tile shape");
 
     if ((int)blockIdx.x >= grid.n_stream) {
         merge_role<TQ, D, GT>(a, (int)blockIdx.x - grid.n_stream);
         return;
     }
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, rgq = lane >> 4, lr = lane & 15;
-    const int rg = wave * 4 + rgq;  // row-group within the workgroup
+    const int wave = tid >> 6, lane = tid & 63, rgq = lane >> 5, lr = lane & 31;
+    const int rg = wave * 2 + rgq;  // row-group (half wave) within the workgroup
     const DecodePlan &P = a.plan;
     const int s = (int)blockIdx.x % grid.gx;
     const int ht = ((int)blockIdx.x / grid.gx) % P.HT;
@@ -329,18 +317,31 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
 
     // Issue order matters: vector-memory waits are in order, so the queries
     // go first (their wait then does not wait for K/V), then the first two
-    // chunks, all before anything is consumed.
-    typename KV::QRaw qraw[GT];
-#pragma unroll
-    for (int h = 0; h < GT; ++h) KV::load_q(qraw[h], a.q, (size_t)b * a.Hq + h0 + h, lr);
+    // chunks, all before anything is consumed.  The GT query rows are read
+    // once per workgroup (16 bytes per thread) and staged in LDS: loading
+    // them per wave would push as many bytes through each CU's load path as
+    // the K/V split itself.
+    constexpr int QB = GT * D * (int)sizeof(TQ);  // bytes of this workgroup's query rows
+    __shared__ __attribute__((aligned(16))) uint32_t sq[QB / 4];
+    // (every load below is unconditional -- threads past the query block
+    // re-read its first 16 bytes, rows past the split read as zero -- so the
+    // compiler's in-order wait counts stay exact)
+    const bool q_loader = tid < QB / 16;
+    const uint4 qv = *((const uint4 *)((const char *)a.q + ((size_t)b * a.Hq + h0) * D * sizeof(TQ)) +
+                       (q_loader ? tid : 0));
+    asm volatile("" ::: "memory");  // keep the query load ahead of the K/V loads
     load_chunk(0, start);
-    if (start + CHUNK < end) load_chunk(1, start + CHUNK);
+    load_chunk(1, start + CHUNK);
+    if (q_loader) *((uint4 *)sq + tid) = qv;
+    __syncthreads();
 
     // Queries of the GT heads, pre-multiplied by scale*log2(e).
     float qf[GT][EPL];
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
-        KV::unpack_q(qraw[h], qf[h]);
+        typename KV::QRaw qraw;
+        KV::load_q_lds(qraw, sq, h, lr);
+        KV::unpack_q(qraw, qf[h]);
 #pragma unroll
         for (int e = 0; e < EPL; ++e) qf[h][e] *= a.qscale;
     }
@@ -367,7 +368,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
                 float acc = 0.0f;
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) acc = __builtin_fmaf(qf[h][e], kf[e], acc);
-                acc = row16_sum(acc);
+                acc = row32_sum(acc);
                 sc[rr][h] = valid[rr] ? acc : kNegInf;
             }
         }
@@ -411,12 +412,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
         const int c1 = c0 + CHUNK;
         process_chunk(0, c0);
         if (c1 >= end) break;
-        if (c1 + CHUNK < end) load_chunk(0, c1 + CHUNK);
+        const bool more = c1 + CHUNK < end;  // uniform
+        if (more) load_chunk(0, c1 + CHUNK);
         process_chunk(1, c1);
-        if (c1 + 2 * CHUNK < end) load_chunk(1, c1 + 2 * CHUNK);
+        if (more) load_chunk(1, c1 + 2 * CHUNK);
     }
 
-    // ---- merge the 4 row-groups of each wave ----
+    // ---- merge the 2 row-groups of each wave ----
     __shared__ __attribute__((aligned(16))) float so[NW][GT][D];
     __shared__ float sm[NW][GT], sl[NW][GT];
     float of[NF];
@@ -429,25 +431,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
         for (int e = 0; e < EPL; ++e) of[h * EPL + e] = o[h][e] * al;
         if (lane == 0) { sm[wave][h] = mw; sl[wave][h] = lw; }
     }
-    float w1[NF / 2], w2[NF / 4];
-#pragma unroll
-    for (int f = 0; f < NF / 2; ++f) {
-        float lo, hi;
-        swap32(of[f], of[f + NF / 2], lo, hi);
-        w1[f] = lo + hi;
-    }
-#pragma unroll
-    for (int f = 0; f < NF / 4; ++f) {
-        float lo, hi;
-        swap16(w1[f], w1[f + NF / 4], lo, hi);
-        w2[f] = lo + hi;
-    }
     {
-        const int fbase = (lane >> 5) * (NF / 2) + ((lane >> 4) & 1) * (NF / 4);
+        // reduce-scatter: lanes of the low half keep of[0, NF/2), the high half of[NF/2, NF)
+        const int fbase = (lane >> 5) * (NF / 2);
 #pragma unroll
-        for (int f = 0; f < NF / 4; ++f) {
+        for (int f = 0; f < NF / 2; ++f) {
+            float lo, hi;
+            swap32(of[f], of[f + NF / 2], lo, hi);
             const int ff = fbase + f;
-            so[wave][ff / EPL][KV::dim(lr, ff % EPL)] = w2[f];
+            so[wave][ff / EPL][KV::dim(lr, ff % EPL)] = lo + hi;
         }
     }
     __syncthreads();
