@@ -28,6 +28,9 @@ COMMON_FLAGS = [
     "-Wall",
     # packed fp32 VALU forms stay disabled in every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators live in ordinary VGPRs, so the softmax and the
+    # rescale of the running output need no AGPR<->VGPR copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

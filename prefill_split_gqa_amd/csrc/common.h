@@ -98,6 +98,16 @@ __device__ __forceinline__ float shfl_xor_f32(float x, int mask)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Raw buffer resources: a load whose byte offset falls outside [0, bytes)
+// returns zeros and touches no memory, which lets tiles past the end of a
+// sequence be loaded without a branch.
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, size_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
+}
+
 // ---------------------------------------------------------------------------
 // Decode split plan.  The host sizes the workspace and the grid from it and
 // the kernel derives every index from the same numbers, so a request's split

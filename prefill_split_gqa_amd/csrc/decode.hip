@@ -69,12 +69,6 @@ __device__ __forceinline__ float q4_dequant_value(float scale, float bias, uint3
 // rows [0, end) of this (request, KV head): a row past the split's end reads
 // as zeros without a branch (and without a memory access), so every load of a
 // chunk is issued unconditionally.
-constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 data format
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, size_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
-}
 
 // Dense K/V rows of D elements of type T.
 template <typename T, int D>

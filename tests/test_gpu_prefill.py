@@ -23,9 +23,9 @@ from workloads import configs as W
 pytestmark = pytest.mark.gpu
 
 
-def run_prefill(gqa, q, k, v, Tk=None):
+def run_prefill(gqa, q, k, v, Tk=None, scale=None):
     g = Guarded(q.shape, q.dtype)
-    gqa.gqa_prefill_causal(q.cuda(), k.cuda(), v.cuda(), g.t, Tk=Tk)
+    gqa.gqa_prefill_causal(q.cuda(), k.cuda(), v.cuda(), g.t, Tk=Tk, scale=scale)
     torch.cuda.synchronize()
     g.check()
     return g.t
@@ -111,3 +111,19 @@ def test_prefill_deterministic(gpu_lib):
     gpu_lib.gqa_prefill_causal(q, k, v, b)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 0.9])
+def test_prefill_scale_sign(gpu_lib, scale):
+    # the running maximum is kept over sign(scale) * q.k: a negative scale
+    # takes the minimum raw score, a zero scale gives the plain mean of the
+    # visible value rows, a large one spreads the exponents far apart
+    rng = np.random.default_rng(23)
+    B, Hq, Hkv, D, Tq, Tk = 1, 4, 2, 64, 150, 260
+    q = torch.from_numpy(rng.standard_normal((B, Hq, Tq, D), dtype=np.float32)).to(torch.bfloat16)
+    k = torch.from_numpy(rng.standard_normal((B, Hkv, Tk, D), dtype=np.float32)).to(torch.bfloat16)
+    v = torch.from_numpy(rng.standard_normal((B, Hkv, Tk, D), dtype=np.float32)).to(torch.bfloat16)
+    note("prefill scale=%g" % scale)
+    got = run_prefill(gpu_lib, q, k, v, scale=scale)
+    want = oracle.attend(q, k, v, causal=True, scale=scale)
+    assert_close(got, want, 2e-2, "scale=%g" % scale)
