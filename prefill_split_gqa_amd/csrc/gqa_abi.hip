@@ -194,8 +194,9 @@ int gqa_prefill_causal(const void *q, const void *k, const void *v, void *out, i
     if (D != 64 && D != 128) return GQA_ERR_UNSUPPORTED;
     if (dtype != GQA_BF16 && dtype != GQA_F16) return GQA_ERR_UNSUPPORTED;
     if ((long)((Tq + 127) / 128) * Hq >= (1L << 31) || B > 65535) return GQA_ERR_SHAPE;
-    // a head's rows (plus one tile past the end) are addressed with 32-bit byte offsets
-    if ((size_t)(s_cap + 128) * D * 2 >= ((size_t)1 << 31)) return GQA_ERR_SHAPE;
+    // a head's rows (plus the few tiles past the end that prefetches name) are
+    // addressed with 32-bit byte offsets
+    if ((size_t)(s_cap + 512) * D * 2 >= ((size_t)1 << 31)) return GQA_ERR_SHAPE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_ERR_ALIGN;
     if (int st = check_device()) return st;
     return hip_status(launch_prefill(dtype, D, q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, (hipStream_t)stream));
