@@ -6,27 +6,44 @@
 // aligned to the end of the keys (row i sees keys j <= i + Tk - Tq), and never
 // stores the score matrix.
 //
-// Work decomposition: a workgroup owns 128 query rows of one query head and
-// has 8 waves: row-wave w (32 rows) appears twice, once in each half of the
-// workgroup, and the two halves walk the first and the second half of the
-// visible key tiles (64 keys each) side by side.  At the end the second
-// half's running (output, max, sum) goes through LDS and is merged into the
-// first half's, which normalises and stores.  Splitting the keys halves the
-// longest chain of dependent tiles (the last row block sees every key) while
-// the merge costs one LDS round trip.  Each half stages its K tiles row-major
-// in LDS and its V tiles transposed (V^T, keys contiguous), double-buffered,
-// with the next tile's global loads in flight while the current tile is
-// computed.
+// Work decomposition.  A workgroup owns 128 query rows of one query head and
+// has 8 waves.  The visible key tiles (64 keys each) are cut into NSPLIT
+// contiguous ranges ("splits"); each split is walked by the row-waves that
+// together cover the 128 rows (D = 64: 4 splits x 2 waves of 64 rows;
+// D = 128: 2 splits x 4 waves of 32 rows).  At the end every split but the
+// first hands its running (output, max, sum) to the first through LDS, which
+// merges, normalises and stores.  Splitting the keys shortens the longest
+// chain of dependent tiles (the last row block sees every key).
 //
-// Per tile and wave, on v_mfma_f32_32x32x16 (bf16 or f16 inputs, fp32 sums):
+// Per tile, on v_mfma_f32_32x32x16 (bf16 or f16 inputs, fp32 sums), for each
+// 32-row block of a wave:
 //   S^T[key][row] = K Q^T          (A = K rows from LDS, B = Q rows in registers)
 //   online softmax per row in fp32 (exp2 with scale*log2(e) folded in; the
 //   reference max is only raised when a score exceeds it by more than 2^8)
-//   O^T[d][row] += V^T P^T         (A = V^T from LDS, B = P in registers)
+//   O^T[d][row] += V^T P^T         (A = V^T fragments from LDS, B = P in registers)
 // Computing S transposed makes its accumulator layout (a lane holds keys of
 // one row) exactly the layout the second product wants for P, so P never
-// leaves registers.  Only tiles that cross the diagonal are masked.
-// Workgroups are issued longest-row-block first to shorten the causal tail.
+// leaves registers.  A wave with 64 rows uses every K and V fragment it reads
+// from LDS twice: the LDS bytes per matrix instruction are what limits a
+// wave (one wave reads LDS at about 20 bytes per clock), and 64-row waves
+// halve them.
+//
+// Data movement.  K and V tiles go from HBM straight into LDS with buffer
+// loads that write LDS (no staging registers), row-major, each row's 16-byte
+// chunks XOR-swizzled and every 8 rows padded by 64 bytes, so that the
+// fragment reads below avoid bank conflicts.  K fragments are plain 16-byte
+// reads; V^T fragments come from the transposing LDS read
+// (ds_read_b64_tr_b16), which hands each lane four 16-bit values of one
+// column from four consecutive rows.  Rows past Tk load as zeros (buffer
+// range check).  K runs one tile ahead of V, each double-buffered.
+//
+// Schedule.  Each wave alternates a V phase (next tiles' loads issued;
+// softmax of the current tile in place) and an M phase (P to 16 bits; the
+// P V^T product; S^T of the next tile), one workgroup barrier after each
+// phase.  The splits of the second half of the workgroup run one phase
+// behind the first half, so on each SIMD one wave issues matrix instructions
+// while the other runs the exponentials.  Only tiles that cross the diagonal
+// are masked.  Workgroups are issued longest-row-block first.
 
 #include <type_traits>
 
@@ -41,6 +58,12 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8v_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Per-dtype matrix-core product, fp32 -> 16-bit pair conversion (one
 // v_cvt_pk per pair) and the sum of a packed pair (v_dot2 against 1.0).
@@ -61,6 +84,10 @@ template <> struct MfmaOps<bf16_t> {
         const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
         return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
     }
+    __device__ __forceinline__ static uint4 pack8(f32x8_t x)
+    {
+        return __builtin_bit_cast(uint4, __builtin_convertvector(x, bf16x8v_t));
+    }
 };
 template <> struct MfmaOps<f16_t> {
     typedef f16x8_t vec;
@@ -78,41 +105,83 @@ template <> struct MfmaOps<f16_t> {
         const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
         return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), one, acc, false);
     }
+    __device__ __forceinline__ static uint4 pack8(f32x8_t x)
+    {
+        return __builtin_bit_cast(uint4, __builtin_convertvector(x, f16x8v_t));
+    }
 };
 
 template <typename V> __device__ __forceinline__ V as_vec(uint4 x) { return __builtin_bit_cast(V, x); }
 
-// Position of key kk (0..63 within a tile) in a V^T row in LDS.  Each
-// 16-key block is stored as keys [0-3, 8-11, 4-7, 12-15]: the eight keys
-// that lane group lg of the second product pairs with its P values (keys
-// 4lg..4lg+3 and 8+4lg..8+4lg+3 of the block, the order in which the score
-// accumulator holds them) then sit in eight consecutive elements.
-__device__ __forceinline__ int vt_pos(int kk)
-{
-    const int w = kk & 15, a = w >> 2;
-    return (kk & ~15) + 8 * (a & 1) + 4 * (a >> 1) + (w & 3);
-}
+constexpr int kPfBM = 128;  // query rows per workgroup: 4 row-waves of 32 rows
+constexpr int kPfBN = 64;   // keys per tile
+constexpr int kPfNRW = 4;   // row-waves per key split
 
-constexpr int kPfBM = 128;          // query rows per workgroup (4 row-waves of 32)
-constexpr int kPfBN = 64;           // keys per tile
-constexpr int kPfHalfThreads = 256; // one key half: 4 waves
-constexpr int kPfThreads = 512;     // two key halves
-constexpr int kPfKPad = 8;          // 16-bit elements of padding per K row in LDS
-constexpr int kPfVPad = 8;          // per V^T row
+// Key splits per head dimension (the LDS holds two tiles per split).
+template <int D> struct PfCfg;
+template <> struct PfCfg<64> { static constexpr int NSPLIT = 4; };   // 16 waves, 4 per SIMD
+template <> struct PfCfg<128> { static constexpr int NSPLIT = 2; };  // 8 waves
+template <int D> constexpr int pf_threads() { return PfCfg<D>::NSPLIT * kPfNRW * 64; }
 
-// LDS layout: for each key half, two buffers of [K tile | V^T tile]; after
-// the key loop the same memory holds the second half's partial results.
-template <int D> struct PfSmem {
-    static constexpr int KS = D + kPfKPad;      // K row stride (elements)
-    static constexpr int VS = kPfBN + kPfVPad;  // V^T row stride (elements)
-    static constexpr int K_ELEMS = kPfBN * KS;
-    static constexpr int BUF = K_ELEMS + D * VS;
-    static constexpr int TOTAL = 2 * 2 * BUF;
-    static constexpr int MERGE_FLOATS = 4 * (D / 32) * 16 * 64 + 4 * 64 * 2;
-    static_assert(MERGE_FLOATS * 4 <= TOTAL * 2, "merge area exceeds the tile buffers");
+// LDS layout (bytes).  A tile is 64 rows of D 16-bit elements: groups of 8
+// rows (8 * ROW bytes) followed by 64 bytes of padding.  Per split: K
+// buffers 0, 1 then V buffers 0, 1.  After the key loop the same memory
+// holds the partial results of splits 1..NSPLIT-1.
+template <int D> struct PfLds {
+    static constexpr int NSPLIT = PfCfg<D>::NSPLIT;
+    static constexpr int NRW = kPfNRW;
+    static constexpr int ROW = D * 2;
+    static constexpr int GROUP = 8 * ROW + 64;
+    static constexpr int TILE = 8 * GROUP;
+    static constexpr int SPLIT = 4 * TILE;
+    static constexpr int TOTAL = NSPLIT * SPLIT;
+    static constexpr int MERGE_O = (NSPLIT - 1) * NRW * (D / 32) * 16 * 64 * 4;
+    static constexpr int MERGE_ML = (NSPLIT - 1) * NRW * 64 * 2 * 4;
+    static_assert(MERGE_O + MERGE_ML <= TOTAL, "merge area exceeds the tile buffers");
+    static_assert(TOTAL <= 160 * 1024, "LDS");
 };
 
-// Softmax part of one 64-key tile for the wave's 32 rows, in place.
+// XOR applied to the 16-byte chunk index of a row, from the row's position
+// in its group of 8.  Any 8 consecutive rows get 8 distinct values (the K
+// fragment reads: 8 rows, one chunk each), and any 4 consecutive rows that
+// start at a multiple of 4 get distinct values of swz >> 1 (the transposing
+// V reads: 4 rows, an aligned pair of chunks each).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+// Buffer loads that write LDS (buffer_load_dwordx4 ... lds): lane l's 16
+// bytes at byte offset voff go to LDS address lds_base + 16*l; an offset
+// outside the descriptor's range writes zeros (the whole offset is in the
+// vector register, where the range check applies).  They are issued from inline
+// assembly so that the compiler does not treat them as pending LDS stores
+// (it would otherwise wait for every one of them at each workgroup barrier);
+// the kernel waits for them itself (s_waitcnt vmcnt) before the barrier
+// that precedes their readers.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+struct BufDesc { u32x4_t w; };
+
+__device__ __forceinline__ BufDesc buf_desc(const void *base, size_t bytes)
+{
+    const unsigned long long a = (unsigned long long)(uintptr_t)base;
+    BufDesc d;
+    d.w[0] = __builtin_amdgcn_readfirstlane((unsigned)a);
+    d.w[1] = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32)) & 0xFFFFu;  // stride 0
+    d.w[2] = __builtin_amdgcn_readfirstlane((unsigned)bytes);
+    d.w[3] = kRsrcWord3;
+    return d;
+}
+
+__device__ __forceinline__ void lds_load16(const BufDesc &d, unsigned lds_base, int voff)
+{
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(d.w), "{m0}"(lds_base) : "memory");
+}
+
+template <int D> __device__ __forceinline__ int tile_off(int row, int chunk)
+{
+    typedef PfLds<D> L;
+    return (row >> 3) * L::GROUP + (row & 7) * L::ROW + ((chunk ^ swz(row & 7)) << 4);
+}
+
+// Softmax part of one 64-key tile for one 32-row block, in place.
 //
 // st holds S^T (raw q.k) in the accumulator layout: lane (ln, lg) has, for
 // sub-tile u and register j, key 32u + 8(j/4) + 4lg + (j%4) of the tile, row
@@ -155,28 +224,32 @@ __device__ __forceinline__ void softmax_inplace(f32x16_t (&st)[2], f32x16_t (&ac
 }
 
 template <typename T, int D, bool NEG>
-__global__ __launch_bounds__(kPfThreads) void prefill_causal_kernel(const uint16_t *__restrict__ q,
-                                                                    const uint16_t *__restrict__ k,
-                                                                    const uint16_t *__restrict__ v,
-                                                                    uint16_t *__restrict__ out, int Hq, int Hkv,
-                                                                    int Tq, int Tk, int s_cap, float qscale,
-                                                                    int n_rb)
+__global__ __launch_bounds__(pf_threads<D>()) void prefill_causal_kernel(const uint16_t *__restrict__ q,
+                                                                         const uint16_t *__restrict__ k,
+                                                                         const uint16_t *__restrict__ v,
+                                                                         uint16_t *__restrict__ out, int Hq, int Hkv,
+                                                                         int Tq, int Tk, int s_cap, float qscale,
+                                                                         int n_rb)
 {
     typedef MfmaOps<T> Ops;
     typedef typename Ops::vec vec;
-    typedef PfSmem<D> L;
-    constexpr int KS = L::KS;
-    constexpr int VS = L::VS;
-    constexpr int NKB = D / 16;  // k-blocks of the QK^T product
-    constexpr int NDB = D / 32;  // 32-wide d-blocks of the output
+    typedef PfLds<D> L;
+    constexpr int NSPLIT = L::NSPLIT;  // key splits
+    constexpr int NRW = L::NRW;        // row-waves per split
+    constexpr int NKB = D / 16;        // k-blocks of the QK^T product
+    constexpr int NDB = D / 32;        // 32-wide d-blocks of the output
+    constexpr int CPR = D / 8;         // 16-byte chunks per row
+    constexpr int RPI = 1024 / L::ROW; // rows per LDS-writing load (64 lanes x 16 bytes)
+    constexpr int IPT = kPfBN / RPI;   // such loads per tile
+    constexpr int IPW = 2 * IPT / NRW; // loads per wave per step (one K and one V tile per split)
     constexpr float kInf = __builtin_huge_valf();
-    __shared__ __attribute__((aligned(16))) uint16_t smem[L::TOTAL];
+    static_assert(2 * IPT % NRW == 0 && IPT % IPW == 0, "load split");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int half = wave >> 2;  // which half of the key tiles this wave walks
-    const int rw = wave & 3;     // row-wave within the block
-    const int htid = tid & (kPfHalfThreads - 1);
+    const int split = wave / NRW;  // key split this wave walks
+    const int rw = wave % NRW;     // row-wave within the split
     const int lane = tid & 63;
     const int ln = lane & 31, lg = lane >> 5;
 
@@ -193,18 +266,20 @@ __global__ __launch_bounds__(kPfThreads) void prefill_causal_kernel(const uint16
     const int row_hi = min(r0 + kPfBM, Tq);         // one past the last valid row of the block
     const int kend = min(Tk, row_hi + off);         // keys any valid row of the block can see
     const int n_tiles = (kend + kPfBN - 1) / kPfBN;
-    const int n = (n_tiles + 1) / 2;                // steps; the first half has n tiles, the second the rest
-    const int t_begin = half ? n : 0;
+    const int n = (n_tiles + NSPLIT - 1) / NSPLIT;  // steps; split sp walks tiles [sp*n, sp*n + n)
+    const int t_begin = split * n;
     const int n_full = min(n_tiles, max(0, (r0 + off + 1) / kPfBN));  // tiles every row sees in full
-    uint16_t *const hsm = smem + half * 2 * L::BUF;  // this half's two buffers
+    unsigned char *const ssm = smem + split * L::SPLIT;  // this split's K0 K1 V0 V1
+    const int my_row = rw0 + ln;
+    const int my_lim = my_row + off;  // last visible key of this lane's row
 
     const uint16_t *qh = q + ((size_t)b * Hq + h) * (size_t)Tq * D;
     const uint16_t *kh = k + ((size_t)b * Hkv + g) * (size_t)s_cap * D;
     const uint16_t *vh = v + ((size_t)b * Hkv + g) * (size_t)s_cap * D;
     // rows at or past Tq (queries) and Tk (keys) read as zeros
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qh, (size_t)Tq * D * 2);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh, (size_t)Tk * D * 2);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh, (size_t)Tk * D * 2);
+    const BufDesc dk = buf_desc(kh, (size_t)Tk * D * 2);
+    const BufDesc dv = buf_desc(vh, (size_t)Tk * D * 2);
 
     // Q rows of this wave as MFMA B operands: lane (row ln, group lg) holds
     // dims [16*kb + 8*lg, +8) of its row.
@@ -214,65 +289,29 @@ __global__ __launch_bounds__(kPfThreads) void prefill_causal_kernel(const uint16
         qreg[kb] = as_vec<vec>(__builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, ((rw0 + ln) * D + kb * 16 + lg * 8) * 2, 0, 0)));
 
-    // global -> register -> LDS staging of K and V tiles by the 256 threads
-    // of a half.  Tile indices past the end load zeros (range-checked
-    // buffers) or keys no valid row sees, into buffers nobody reads any more,
-    // so neither step branches.
-    constexpr int K_ITEMS = kPfBN * D / 8;          // 16-byte pieces per K tile
-    constexpr int K_PER_T = K_ITEMS / kPfHalfThreads;
-    constexpr int V_ITEMS = (kPfBN / 2) * (D / 8);  // (key pair, 8-dim chunk)
-    constexpr int V_PER_T = V_ITEMS / kPfHalfThreads;
-    static_assert(K_ITEMS % kPfHalfThreads == 0 && V_ITEMS % kPfHalfThreads == 0, "tile/thread mismatch");
-    uint4 kreg[2][K_PER_T], vreg[2][V_PER_T][2];  // two staging sets: loads run two steps ahead
-
-    auto load_k = [&](int kt, int set) {
-        const int k0 = kt * kPfBN;
+    // ---- tile loads: HBM -> LDS, IPW loads of 1 KB per wave and step ----
+    // Load i of a tile covers rows [i*RPI, i*RPI + RPI); lane l writes the
+    // 16 bytes at LDS position (row i*RPI + l/CPR, slot l%CPR), which hold
+    // the row's chunk slot ^ swz(row & 7).  The row-waves of a split share
+    // the K and V loads of one tile between them.
+    const bool loads_v = rw * IPW >= IPT;  // this wave's share of a step's loads: all K or all V
+    int dma_voff[IPW];                     // lane part of each load's byte offset
+    unsigned dma_lds[IPW];                 // LDS destination of each load in buffer 0
 #pragma unroll
-        for (int i = 0; i < K_PER_T; ++i) {
-            const int idx = htid + i * kPfHalfThreads;
-            const int key = k0 + idx / (D / 8), c8 = idx % (D / 8);
-            kreg[set][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, (key * D + c8 * 8) * 2, 0, 0));
-        }
-    };
-    auto load_v = [&](int kt, int set) {
-        const int k0 = kt * kPfBN;
+    for (int ii = 0; ii < IPW; ++ii) {
+        const int i = rw * IPW + ii;  // 0 .. 2*IPT-1: K loads, then V loads
+        const int row_first = (loads_v ? i - IPT : i) * RPI;
+        const int row = row_first + lane / CPR;
+        const int chunk = (lane % CPR) ^ swz(row & 7);
+        dma_voff[ii] = (row * D + chunk * 8) * 2;
+        dma_lds[ii] = (unsigned)(uintptr_t)(lds_void_t *)(ssm + (loads_v ? 2 : 0) * L::TILE +
+                                                          (row_first >> 3) * L::GROUP + (row_first & 7) * L::ROW);
+    }
+    auto issue_tile_loads = [&](int kt, int buf) {
+        const int toff = kt * kPfBN * D * 2;
 #pragma unroll
-        for (int i = 0; i < V_PER_T; ++i) {
-            const int idx = htid + i * kPfHalfThreads;
-            const int kp = idx % (kPfBN / 2), c8 = idx / (kPfBN / 2);
-            const int key = k0 + 2 * kp;
-            vreg[set][i][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, (key * D + c8 * 8) * 2, 0, 0));
-            vreg[set][i][1] =
-                __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, ((key + 1) * D + c8 * 8) * 2, 0, 0));
-        }
-    };
-    auto k_buf = [&](int buf) { return hsm + buf * L::BUF; };
-    auto v_buf = [&](int buf) { return hsm + buf * L::BUF + L::K_ELEMS; };
-    auto store_k = [&](int buf, int set) {
-        uint16_t *Ks = k_buf(buf);
-#pragma unroll
-        for (int i = 0; i < K_PER_T; ++i) {
-            const int idx = htid + i * kPfHalfThreads;
-            const int key = idx / (D / 8), c8 = idx % (D / 8);
-            *(uint4 *)(&Ks[key * KS + c8 * 8]) = kreg[set][i];
-        }
-    };
-    auto store_v = [&](int buf, int set) {
-        uint16_t *Vt = v_buf(buf);
-#pragma unroll
-        for (int i = 0; i < V_PER_T; ++i) {
-            const int idx = htid + i * kPfHalfThreads;
-            const int kp = idx % (kPfBN / 2), c8 = idx / (kPfBN / 2);
-            const int pos = vt_pos(2 * kp);
-            const uint32_t *a = (const uint32_t *)&vreg[set][i][0];
-            const uint32_t *c = (const uint32_t *)&vreg[set][i][1];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                // dims 8*c8 + 2w (low halves of the two keys) and 8*c8 + 2w + 1 (high halves)
-                *(uint32_t *)(&Vt[(c8 * 8 + 2 * w) * VS + pos]) = __builtin_amdgcn_perm(c[w], a[w], 0x05040100u);
-                *(uint32_t *)(&Vt[(c8 * 8 + 2 * w + 1) * VS + pos]) = __builtin_amdgcn_perm(c[w], a[w], 0x07060302u);
-            }
-        }
+        for (int ii = 0; ii < IPW; ++ii)
+            lds_load16(loads_v ? dv : dk, dma_lds[ii] + buf * L::TILE, dma_voff[ii] + toff);
     };
 
     f32x16_t acc[NDB];
@@ -280,16 +319,64 @@ __global__ __launch_bounds__(kPfThreads) void prefill_causal_kernel(const uint16
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[db][j] = 0.0f;
-    f32x16_t st[2];  // S^T of the current tile, then its probabilities
     float m_run = -kInf;  // running max of the oriented raw scores of this lane's row
     float l_part = 0.0f;
     const float aq = fabsf(qscale);
     const float thr = fminf(8.0f / aq, 3.0e38f);  // lazy-rescale threshold, raw units (qscale != 0)
-    const int my_row = rw0 + ln;
-    const int my_lim = my_row + off;  // last visible key of this lane's row
 
-    // Keys of a tile that crosses the diagonal get sigma*(-inf) where masked.
-    auto mask_tile = [&](int kt) {
+    // Lane-dependent LDS byte offsets of the fragments within a tile; the
+    // rest of each address (buffer, sub-tile, k-block row group) is a
+    // constant the reads take as an immediate offset.
+    //   K, row u*32 + ln, chunk 2kb + lg:  tile_off(ln, 2kb + lg) + u*4*GROUP
+    //   V, rows 16t + 8h + 4lg + j/4:     (see v_frag) + (2t + h)*GROUP
+    int koff[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) koff[kb] = tile_off<D>(ln, 2 * kb + lg);
+
+    // K fragment (A operand of S^T): key row u*32 + ln, dims kb*16 + lg*8 .. +8
+    auto k_frag = [&](const unsigned char *Kt, int u, int kb) {
+        return *(const uint4 *)(Kt + koff[kb] + u * 4 * L::GROUP);
+    };
+    // V^T fragment (A operand of O^T += V^T P^T) for k-block t, d-block db.
+    // The operand's slots 0..3 are keys 16t + 4lg + 0..3 and slots 4..7 keys
+    // 16t + 8 + 4lg + 0..3 of column d = 32db + (lane % 32), matching the
+    // order in which P sits in the score accumulator.  A transposing read
+    // gives output lane i (of 16) element i%4 of the 8 bytes named by source
+    // lane 4k + i/4 as its slot k, so source lane j names row
+    // 16t + 8h + 4lg + j/4 (h: which half of the slots) at column
+    // 32db + 16*((lane/16)%2) + 4*(j%4).
+    int voff[NDB];
+    {
+        const int gam = lane >> 4, j = lane & 15;
+        const int row0 = 4 * lg + (j >> 2);  // < 8: rows 16t + 8h + row0 share its swizzle
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            voff[db] = tile_off<D>(row0, 4 * db + 2 * (gam & 1) + ((j & 3) >> 1)) + (j & 1) * 8;
+    }
+    auto v_frag = [&](const unsigned char *Vt, int t, int db) {
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t *)(Vt + voff[db] + (2 * t) * L::GROUP));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t *)(Vt + voff[db] + (2 * t + 1) * L::GROUP));
+        const uint2 a = __builtin_bit_cast(uint2, lo), c = __builtin_bit_cast(uint2, hi);
+        return make_uint4(a.x, a.y, c.x, c.y);
+    };
+
+    // One tile of the wave's 32 rows from buffer buf: S^T = K Q^T, mask (tiles
+    // crossing the diagonal), online softmax, O^T += V^T P^T.  Fragments are
+    // read from LDS as they are needed; the other waves on the SIMD (four
+    // per SIMD for D = 64) hide the latency.
+    auto tile_step = [&](int kt, int buf) {
+        const unsigned char *Kt = ssm + buf * L::TILE;
+        const unsigned char *Vt = ssm + (2 + buf) * L::TILE;
+        f32x16_t st[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) st[u][j] = 0.0f;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) st[u] = Ops::mfma(as_vec<vec>(k_frag(Kt, u, kb)), qreg[kb], st[u]);
+        }
         if (kt >= n_full) {
             // (kept a real branch: the empty asm stops the compiler from
             // turning the mask into selects executed on every tile)
@@ -301,187 +388,86 @@ __global__ __launch_bounds__(kPfThreads) void prefill_causal_kernel(const uint16
                 for (int j = 0; j < 16; ++j)
                     if (key0 + 32 * u + 8 * (j >> 2) + (j & 3) > my_lim) st[u][j] = NEG ? kInf : -kInf;
         }
-    };
-    // S^T = K Q^T for tile kt from K fragments already in registers
-    auto qk_frags = [&](int kt, const uint4 (&kf)[2][NKB]) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) st[u][j] = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) st[u] = Ops::mfma(as_vec<vec>(kf[u][kb]), qreg[kb], st[u]);
-        mask_tile(kt);
-    };
-    // S^T = K Q^T for tile kt (this half's K buffer buf)
-    auto qk = [&](int kt, int buf) {
-        const uint16_t *Ks = k_buf(buf);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) st[u][j] = 0.0f;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            uint4 kf[NKB];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) kf[kb] = *(const uint4 *)(&Ks[(u * 32 + ln) * KS + kb * 16 + lg * 8]);
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) st[u] = Ops::mfma(as_vec<vec>(kf[kb]), qreg[kb], st[u]);
-        }
-        mask_tile(kt);
-    };
-
-    // The two phases of step s of a half (tile t_begin + s):
-    //   V(s): LDS stores of K(s+1), V(s) (loaded two steps earlier, staging
-    //         set s&1); loads of K(s+3), V(s+2) issued into the same set;
-    //         softmax of tile s in place
-    //   M(s): P of tile s rounded to 16 bits and summed; O^T += V^T P^T;
-    //         S^T of tile s+1
-    // K runs one tile ahead of V: M(s) reads K buffer (s+1)&1 and V buffer
-    // s&1; V(s) writes the same two buffers, whose previous tiles M(s-1)
-    // read.  A global load has two whole steps to arrive before its store.
-    // SET is s&1, a template argument so that the staging registers are
-    // named statically (the step loop is unrolled by two).
-    auto v_phase = [&](int s, auto set_tag) {
-        constexpr int SET = decltype(set_tag)::value;
-        if (s > 0) {
-            store_k((s + 1) & 1, SET);
-            store_v(s & 1, SET);
-        }
-        load_k(t_begin + s + 3, SET);
-        load_v(t_begin + s + 2, SET);
         softmax_inplace<NEG>(st, acc, m_run, l_part, qscale, thr);
-    };
-    auto m_phase = [&](int s) {
-        const uint16_t *Vt = v_buf(s & 1);
-        const uint16_t *Ks = k_buf((s + 1) & 1);
-        // D = 64: every LDS fragment of the phase is requested up front (64
-        // registers), so the reads overlap each other instead of each
-        // matrix instruction waiting for the one it needs.
-        constexpr bool PRE = D == 64;
-        uint4 vf[4][NDB], kf[2][NKB];
-        if constexpr (PRE) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    vf[t][db] = *(const uint4 *)(&Vt[(db * 32 + ln) * VS + 16 * t + 8 * lg]);
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-                    kf[u][kb] = *(const uint4 *)(&Ks[(u * 32 + ln) * KS + kb * 16 + lg * 8]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // P of tile s to 16 bits (paired conversion) and its row sums (four
-        // independent partial sums); O^T += V^T P^T in four 16-key k-blocks
+        // P to 16 bits (paired conversion) and its row sums (independent
+        // partial sums); O^T += V^T P^T in four 16-key k-blocks
         float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int u = t >> 1, hh = t & 1;
-            uint32_t pw[4];
+            f32x8_t x;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pw[i] = Ops::pack2(st[u][8 * hh + 2 * i], st[u][8 * hh + 2 * i + 1]);
-                lsum[i] = Ops::sum2(pw[i], lsum[i]);
-            }
-            const uint4 pb = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+            for (int i = 0; i < 8; ++i) x[i] = st[u][8 * hh + i];
+            const uint4 pb = Ops::pack8(x);
+            lsum[0] = Ops::sum2(pb.x, lsum[0]);
+            lsum[1] = Ops::sum2(pb.y, lsum[1]);
+            lsum[2] = Ops::sum2(pb.z, lsum[2]);
+            lsum[3] = Ops::sum2(pb.w, lsum[3]);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                if constexpr (!PRE) vf[t][db] = *(const uint4 *)(&Vt[(db * 32 + ln) * VS + 16 * t + 8 * lg]);
-                acc[db] = Ops::mfma(as_vec<vec>(vf[t][db]), as_vec<vec>(pb), acc[db]);
-            }
+            for (int db = 0; db < NDB; ++db)
+                acc[db] = Ops::mfma(as_vec<vec>(v_frag(Vt, t, db)), as_vec<vec>(pb), acc[db]);
         }
         l_part += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
-        // S^T of tile s+1
-        if constexpr (PRE) {
-            qk_frags(t_begin + s + 1, kf);
-        } else {
-            qk(t_begin + s + 1, (s + 1) & 1);
-        }
     };
 
-    // prologue: K and V of tile 0, K of tile 1 into LDS; K of tile 2 and V
-    // of tile 1 in flight into staging set 1 (stored by V(1))
-    load_k(t_begin, 0);
-    load_v(t_begin, 0);
-    store_k(0, 0);
-    store_v(0, 0);
-    load_k(t_begin + 1, 0);
-    store_k(1, 0);
-    load_k(t_begin + 2, 1);
-    load_v(t_begin + 1, 1);
+    // Step s: the loads of tile t+1 go to the buffer that step s-1 read
+    // (every wave has passed the barrier that ended step s-1); tile t is
+    // computed from the other buffer; the step ends by waiting for its own
+    // loads and a barrier.  Steps past a split's last tile work on keys at
+    // or past kend (masked for every valid row) or past Tk (zeros), and add
+    // nothing.
+    issue_tile_loads(t_begin, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-
-    // Ping-pong: the second half runs one phase behind the first, so on each
-    // SIMD one wave issues matrix instructions while the other (same row
-    // block, other key half) runs the softmax.  Both halves run the same
-    // sequence qk(0) | V(0) | M(0) | ... | V(n-1) | M(n-1), one barrier
-    // after each phase; the second half passes one extra barrier before it
-    // starts and the first half one after it ends (a barrier only counts
-    // arrivals, so the waves need not be at the same instruction).  The
-    // second half has one tile fewer when n_tiles is odd; its extra tile
-    // holds keys at or past kend, masked for every valid row.
-    // phase_end() is a barrier that the compiler may not move work across:
-    // the phases only overlap as intended if each stays between its barriers.
-    auto phase_end = [&]() {
-        __builtin_amdgcn_sched_barrier(0);
+    for (int s = 0; s < n; s += 2) {  // unrolled by two: buffer indices are constants
+        issue_tile_loads(t_begin + s + 1, 1);
+        tile_step(t_begin + s, 0);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    if (half == 1) phase_end();
-    qk(t_begin, 0);
-    phase_end();
-    int s = 0;
-    for (; s + 1 < n; s += 2) {
-        v_phase(s, std::integral_constant<int, 0>());
-        phase_end();
-        m_phase(s);
-        phase_end();
-        v_phase(s + 1, std::integral_constant<int, 1>());
-        phase_end();
-        m_phase(s + 1);
-        phase_end();
+        if (s + 1 < n) {
+            issue_tile_loads(t_begin + s + 2, 0);
+            tile_step(t_begin + s + 1, 1);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
     }
-    if (s < n) {
-        v_phase(s, std::integral_constant<int, 0>());
-        phase_end();
-        m_phase(s);
-        phase_end();
-    }
-    if (half == 0) phase_end();
 
-    // ---- merge the second half's partial results into the first half ----
-    // (the last phase ended on a barrier, so the tile buffers are free)
-    float *xo = (float *)smem;                   // [row-wave][NDB*16 registers][64 lanes]
-    float *xml = xo + 4 * NDB * 16 * 64;         // [row-wave][64 lanes][max, sum]
-    if (half == 1) {
+    // ---- merge splits 1..NSPLIT-1 into split 0 through LDS ----
+    float *xo = (float *)smem;                  // [split-1][rw][db][j][lane]
+    float *xml = (float *)(smem + L::MERGE_O);  // [split-1][rw][lane][max, sum]
+    if (split > 0) {
+        const int slot = (split - 1) * NRW + rw;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) xo[((rw * NDB + db) * 16 + j) * 64 + lane] = acc[db][j];
-        xml[(rw * 64 + lane) * 2 + 0] = m_run;
-        xml[(rw * 64 + lane) * 2 + 1] = l_part;
+            for (int j = 0; j < 16; ++j) xo[((slot * NDB + db) * 16 + j) * 64 + lane] = acc[db][j];
+        xml[(slot * 64 + lane) * 2 + 0] = m_run;
+        xml[(slot * 64 + lane) * 2 + 1] = l_part;
     }
     __syncthreads();
-    if (half == 1) return;
-    {
-        const float mB = xml[(rw * 64 + lane) * 2 + 0];
-        const float lB = xml[(rw * 64 + lane) * 2 + 1];
-        const float m = fmaxf(m_run, mB);
-        const float wA = m_run == -__builtin_huge_valf() ? 0.0f : fast_exp2(aq * (m_run - m));
-        const float wB = mB == -__builtin_huge_valf() ? 0.0f : fast_exp2(aq * (mB - m));
-        l_part = wA * l_part + wB * lB;
+    if (split > 0) return;
+    float m = m_run;
+#pragma unroll
+    for (int sp = 1; sp < NSPLIT; ++sp) m = fmaxf(m, xml[(((sp - 1) * NRW + rw) * 64 + lane) * 2 + 0]);
+    const float w0 = m_run == -kInf ? 0.0f : fast_exp2(aq * (m_run - m));
+    float l = w0 * l_part;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[db][j] *= w0;
+#pragma unroll
+    for (int sp = 1; sp < NSPLIT; ++sp) {
+        const int slot = (sp - 1) * NRW + rw;
+        const float ms = xml[(slot * 64 + lane) * 2 + 0];
+        const float ws = ms == -kInf ? 0.0f : fast_exp2(aq * (ms - m));
+        l += ws * xml[(slot * 64 + lane) * 2 + 1];
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                acc[db][j] = wA * acc[db][j] + wB * xo[((rw * NDB + db) * 16 + j) * 64 + lane];
+            for (int j = 0; j < 16; ++j) acc[db][j] += ws * xo[((slot * NDB + db) * 16 + j) * 64 + lane];
     }
-
     // ---- normalise and store: lane holds O^T[d][row] for d = 32db + 8i + 4lg + r ----
-    float l_tot = l_part + __shfl_xor(l_part, 32, 64);
+    const float l_tot = l + __shfl_xor(l, 32, 64);
     if (my_row < Tq) {
         const float inv = 1.0f / l_tot;
         uint16_t *orow = out + (((size_t)b * Hq + h) * (size_t)Tq + my_row) * D;
@@ -511,11 +497,11 @@ static hipError_t launch_pf(const void *q, const void *k, const void *v, void *o
     if (qscale == 0.0f) qscale = 1.17549435e-38f;
     dim3 grid(n_rb * Hq, B);
     if (qscale < 0.0f)
-        hipLaunchKernelGGL((prefill_causal_kernel<T, D, true>), grid, dim3(kPfThreads), 0, s, (const uint16_t *)q,
+        hipLaunchKernelGGL((prefill_causal_kernel<T, D, true>), grid, dim3(pf_threads<D>()), 0, s, (const uint16_t *)q,
                            (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)out, Hq, Hkv, Tq, Tk, s_cap,
                            qscale, n_rb);
     else
-        hipLaunchKernelGGL((prefill_causal_kernel<T, D, false>), grid, dim3(kPfThreads), 0, s, (const uint16_t *)q,
+        hipLaunchKernelGGL((prefill_causal_kernel<T, D, false>), grid, dim3(pf_threads<D>()), 0, s, (const uint16_t *)q,
                            (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)out, Hq, Hkv, Tq, Tk, s_cap,
                            qscale, n_rb);
     return hipGetLastError();
