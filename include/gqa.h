@@ -81,17 +81,18 @@ const char *gqa_status_string(int status);
 
 /*
  * Bytes of device workspace the decode entry points need for these sizes
- * (split-K partial results and merge counters).  Returns 0 when the sizes
- * are invalid.  The value depends only on the arguments.
+ * (split-K partial outputs and per-split (max, sum) words, a non-zero sum
+ * marking a published partial).  Returns 0 when the sizes are invalid.  The
+ * value depends only on the arguments.
  */
 size_t gqa_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int s_cap);
 
 /*
  * Prepare a workspace for its first use: zero-fills `bytes` bytes at
  * `workspace` with a kernel on `stream`.  The decode entry points leave the
- * workspace's counters at zero when their work completes, so this is needed
- * once per allocation (a zero-filled allocation needs no call).  Two calls
- * whose work may overlap in time must not share a workspace.
+ * workspace's (max, sum) words at zero when their work completes, so this is
+ * needed once per allocation (a zero-filled allocation needs no call).  Two
+ * calls whose work may overlap in time must not share a workspace.
  */
 int gqa_workspace_init(void *workspace, size_t bytes, void *stream);
 

@@ -128,7 +128,7 @@ struct DecodePlan {
     int L;            // keys per split (multiple of kDecodeRowGroups)
     int n_split_max;  // ceil(s_cap / L)
     // workspace layout (byte offsets)
-    size_t off_o, off_ml, off_cnt, bytes;
+    size_t off_o, off_ml, off_end, bytes;
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -155,7 +155,7 @@ inline bool make_decode_plan(int B, int Hq, int Hkv, int D, int s_cap, int targe
     size_t off = 0;
     p->off_o = off;   off = align_up(off + cols * p->n_split_max * p->GT * (size_t)D * 4, 256);
     p->off_ml = off;  off = align_up(off + cols * p->n_split_max * p->GT * 2 * 4, 256);
-    p->off_cnt = off;  // end of the partial arrays
+    p->off_end = off;  // end of the partial arrays
     p->bytes = off;
     return true;
 }

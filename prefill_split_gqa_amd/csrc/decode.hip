@@ -5,20 +5,23 @@
 // KV Expansion" on the Candle decode page: the fused kernel reads each KV
 // head once through a GQA stride; here the heads of a group share the load).
 //
-// Lane layout: each key row is read by a 16-lane row-group with 16-byte
-// (or 8-byte) coalesced loads; a wave reads 4 consecutive rows per load
-// instruction and the workgroup 32 rows per step.  Each lane owns D/16
-// elements of the row; a dot product is finished with four DPP steps inside
-// the 16-lane row.  Each row-group keeps its own online-softmax state
-// (reference max, sum, output slice) in registers; the reference max is only
-// raised when a score exceeds it by more than 2^8 (log2 domain), so the
-// rescale of the output registers is rare and the result is exact up to
-// rounding.  Two 64-row chunks of K and V are in flight per workgroup.
+// Lane layout: each key row is read by a 32-lane row-group with 16-byte
+// (or 8-byte) coalesced loads; a wave reads 2 rows per load instruction and
+// the workgroup 16 rows per step.  Each lane owns D/32 elements of the row;
+// a dot product is finished with four DPP steps inside a 16-lane row and one
+// gfx950 row swap (v_permlane16_swap).  Each row-group keeps its own
+// online-softmax state (reference max, sum, output slice) in registers; the
+// reference max is only raised when a score exceeds it by more than 2^8
+// (log2 domain), so the rescale of the output registers is rare and the
+// result is exact up to rounding.  The GT query rows are staged in LDS once
+// per workgroup.  Two 32-row chunks of K and V are in flight per workgroup,
+// read through buffer resources bounded to the split, so a row past the end
+// reads as zeros and every load is issued unconditionally.
 //
-// End of a workgroup: the four row-groups of a wave are merged with the
-// gfx950 cross-half lane swaps (a reduce-scatter: after two swap+add steps
-// each lane owns a quarter of the wave's output slice), the eight waves
-// through LDS, giving one (max, sum, output) partial per split.
+// End of a workgroup: the two row-groups of a wave are merged with the
+// gfx950 cross-half lane swap (v_permlane32_swap, a reduce-scatter: each
+// lane then owns half of the wave's output slice), the eight waves through
+// LDS, giving one (max, sum, output) partial per split.
 //
 // Cross-split merge: one CU can pull only ~70 GB/s, so a single workgroup
 // reading every split's partial would be the tail of the launch.  Instead the
@@ -41,10 +44,10 @@
 // its own L2, and a device-scope fence writes back / invalidates that L2
 // (tens of microseconds across a full launch).  Instead, every value that
 // crosses workgroups is written and read with device-scope (sc1) accesses,
-// which are coherent at device scope by themselves; the writer waits for its
-// stores to complete before taking its ticket with a device-scope atomic
-// add, and the merger only reads after its ticket shows that every partial
-// was published.
+// which are coherent at device scope by themselves; a split waits for its
+// output stores to complete (s_waitcnt) before it writes its (max, sum)
+// word, and the merge workgroup reads the outputs only after it has seen
+// every split's word.
 //
 // The 4-bit cache variant (VeloxQuant-MLX "attention" posts, Part 4: codes,
 // scales, biases and the group size go to the kernel, which dequantizes in
@@ -463,7 +466,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
     const __amdgpu_buffer_rsrc_t ws_o =
         __builtin_amdgcn_make_buffer_rsrc(a.part_o, 0, (int)(P.off_ml - P.off_o), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t ws_ml =
-        __builtin_amdgcn_make_buffer_rsrc(a.part_ml, 0, (int)(P.off_cnt - P.off_ml), kRsrcWord3);
+        __builtin_amdgcn_make_buffer_rsrc(a.part_ml, 0, (int)(P.off_end - P.off_ml), kRsrcWord3);
     const size_t colbase = (size_t)col * P.n_split_max;
     if (tid < NQ) {
         const int off_o = (int)((((colbase + s) * GT + qh) * D + qd) * 4);
