@@ -159,7 +159,8 @@ def bench_prefill(torch, gqa, oracle, W, T, steps, warmup, flush, n_check_rows=2
     q, k, v = W.prefill_inputs(w, T)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     out = torch.empty_like(qd)
-    gqa.gqa_prefill_causal(qd, kd, vd, out)
+    ws = gqa.make_prefill_workspace(1, w.Hq, w.Hkv, w.D, T, T)
+    gqa.gqa_prefill_causal(qd, kd, vd, out, ws)
     torch.cuda.synchronize()
     # parity gate on sampled rows: row i is decode over keys 0..i
     rows = sorted(set([0, 1, T - 1] + list(np.random.default_rng(T).integers(0, T, n_check_rows - 3))))
@@ -167,7 +168,7 @@ def bench_prefill(torch, gqa, oracle, W, T, steps, warmup, flush, n_check_rows=2
     for i in rows:
         want = oracle.attend(q[:, :, i:i + 1], k[:, :, :i + 1], v[:, :, :i + 1], scale=w.scale())
         err = max(err, float(np.abs(out[:, :, i:i + 1].float().cpu().double().numpy() - want).max()))
-    ms = time_steps(torch, lambda: gqa.gqa_prefill_causal(qd, kd, vd, out), steps, warmup, flush)
+    ms = time_steps(torch, lambda: gqa.gqa_prefill_causal(qd, kd, vd, out, ws), steps, warmup, flush)
     return {"T": T, "gate_max_abs": err, "gate_ok": err <= 2e-2, "ms": ms, "flops": prefill_flops(T, T)}
 
 

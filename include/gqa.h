@@ -80,19 +80,29 @@ int gqa_abi_version(void);
 const char *gqa_status_string(int status);
 
 /*
- * Bytes of device workspace the decode entry points need for these sizes
- * (split-K partial outputs and per-split (max, sum) words, a non-zero sum
- * marking a published partial).  Returns 0 when the sizes are invalid.  The
- * value depends only on the arguments.
+ * Workspaces.  Every workspace starts with a flag region of 16 MiB: the
+ * words through which workgroups of one call meet (decode (max, sum) words,
+ * a non-zero sum marking a published partial; prefill arrival counters)
+ * live only there, and every call leaves the ones it used at zero.  Partial
+ * results follow the region.  Since the region's place and size never
+ * depend on a call's sizes, one workspace may serve any sequence of decode
+ * and prefill calls of any sizes, as long as it is large enough for each
+ * call and their work does not overlap in time.
+ *
+ * Bytes of device workspace the decode entry points need for these sizes:
+ * the flag region plus one fp32 partial output per (request, query head,
+ * split).  Returns 0 when the sizes are invalid, which includes (max, sum)
+ * words that would not fit the flag region (8 bytes per request, query head
+ * and split; at most 64 splits).  The value depends only on the arguments.
  */
 size_t gqa_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int s_cap);
 
 /*
  * Prepare a workspace for its first use: zero-fills `bytes` bytes at
- * `workspace` with a kernel on `stream`.  The decode entry points leave the
- * workspace's (max, sum) words at zero when their work completes, so this is
- * needed once per allocation (a zero-filled allocation needs no call).  Two
- * calls whose work may overlap in time must not share a workspace.
+ * `workspace` with a kernel on `stream`.  Every entry point leaves the flag
+ * region at zero when its work completes, so this is needed once per
+ * allocation (a zero-filled allocation needs no call).  Two calls whose work
+ * may overlap in time must not share a workspace.
  */
 int gqa_workspace_init(void *workspace, size_t bytes, void *stream);
 
@@ -130,6 +140,17 @@ int gqa_decode_attend_batched(const void *q, const void *k, const void *v, void 
                               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Bytes of device workspace gqa_prefill_causal needs for these sizes: the
+ * flag region (one u32 arrival counter per request, query head and 128-row
+ * block that is split into key chunks) plus the fp32 partial results of
+ * those chunks; when no row block is split, the flag region alone.  Returns
+ * 0 when the sizes are invalid.  The value depends only on the arguments.
+ * Like the decode workspace it must start zero-filled (torch.zeros, or
+ * gqa_workspace_init once per allocation).
+ */
+size_t gqa_prefill_workspace_bytes(int B, int Hq, int Hkv, int D, int Tq, int Tk);
+
+/*
  * Causal prefill with the queries aligned to the end of the keys.
  *
  *   q, out  [B, Hq, Tq, D]       dtype
@@ -138,13 +159,18 @@ int gqa_decode_attend_batched(const void *q, const void *k, const void *v, void 
  *
  * so a chunk of Tq queries at offset Tk - Tq sees every earlier key.
  * Requires B >= 1, Hkv >= 1, Hq % Hkv == 0, D in {64, 128},
- * 1 <= Tq <= Tk <= s_cap, dtype in {GQA_BF16, GQA_F16} (products on the
+ * 1 <= Tq <= Tk <= s_cap, Tq <= 131072, dtype in {GQA_BF16, GQA_F16} (products on the
  * matrix cores, fp32 accumulation; probabilities are rounded to the input
- * dtype before the second product).
+ * dtype before the second product), and a caller-owned, 16-byte aligned
+ * workspace of at least gqa_prefill_workspace_bytes(B, Hq, Hkv, D, Tq, Tk)
+ * bytes (GQA_ERR_WORKSPACE otherwise).  Two calls whose work may overlap in
+ * time must not share a workspace.  The result does not depend on timing:
+ * the key chunks of a row block are merged in chunk order.
  */
 int gqa_prefill_causal(const void *q, const void *k, const void *v, void *out,
                        int B, int Hq, int Hkv, int D, int Tq, int Tk, int s_cap,
-                       float scale, int dtype, void *stream);
+                       float scale, int dtype,
+                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Decode over a 4-bit group-affine quantized KV cache.

@@ -29,6 +29,7 @@ EXPORTED = (
     "gqa_abi_version",
     "gqa_status_string",
     "gqa_decode_workspace_bytes",
+    "gqa_prefill_workspace_bytes",
     "gqa_workspace_init",
     "gqa_decode_attend",
     "gqa_decode_attend_batched",
@@ -61,13 +62,15 @@ def load() -> ctypes.CDLL:
     lib.gqa_status_string.restype = ctypes.c_char_p
     lib.gqa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.gqa_decode_workspace_bytes.restype = sz
+    lib.gqa_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.gqa_prefill_workspace_bytes.restype = sz
     lib.gqa_workspace_init.argtypes = [vp, sz, vp]
     lib.gqa_workspace_init.restype = i
     lib.gqa_decode_attend.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
     lib.gqa_decode_attend.restype = i
     lib.gqa_decode_attend_batched.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.gqa_decode_attend_batched.restype = i
-    lib.gqa_prefill_causal.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    lib.gqa_prefill_causal.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     lib.gqa_prefill_causal.restype = i
     lib.gqa_decode_attend_q4.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
     lib.gqa_decode_attend_q4.restype = i
@@ -166,10 +169,25 @@ def gqa_decode_attend_batched(q, k, v, out, kv_lens, workspace, scale: Optional[
     return out
 
 
-def gqa_prefill_causal(q, k, v, out, Tk: Optional[int] = None, scale: Optional[float] = None) -> torch.Tensor:
-    """q, out [B,Hq,Tq,D]; k, v [B,Hkv,s_cap,D]; queries aligned to the end of the first Tk keys."""
+def gqa_prefill_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, Tq: int, Tk: int) -> int:
+    return int(load().gqa_prefill_workspace_bytes(B, Hq, Hkv, D, Tq, Tk))
+
+
+def make_prefill_workspace(B: int, Hq: int, Hkv: int, D: int, Tq: int, Tk: int, device="cuda") -> torch.Tensor:
+    """A zero-filled (hence ready) prefill workspace for these sizes."""
+    n = gqa_prefill_workspace_bytes(B, Hq, Hkv, D, Tq, Tk)
+    if n == 0:
+        raise ValueError("invalid prefill sizes")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def gqa_prefill_causal(q, k, v, out, workspace, Tk: Optional[int] = None,
+                       scale: Optional[float] = None) -> torch.Tensor:
+    """q, out [B,Hq,Tq,D]; k, v [B,Hkv,s_cap,D]; queries aligned to the end of the first Tk keys.
+    workspace: uint8 device tensor of gqa_prefill_workspace_bytes(...) bytes, zero-filled once."""
     for n, t in (("q", q), ("k", k), ("v", v), ("out", out)):
         _dense(n, t, 4)
+    _dense("workspace", workspace, 1)
     B, Hq, Tq, D = q.shape
     _, Hkv, s_cap, _ = k.shape
     if out.shape != q.shape or k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
@@ -180,7 +198,8 @@ def gqa_prefill_causal(q, k, v, out, Tk: Optional[int] = None, scale: Optional[f
     dt = _DTYPE_CODE.get(q.dtype, -1)
     scale = default_scale(D) if scale is None else scale
     _check(load().gqa_prefill_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, D, Tq, Tk, s_cap,
-                                     float(scale), dt, _stream(q)), "gqa_prefill_causal")
+                                     float(scale), dt, _ptr(workspace), workspace.numel(), _stream(q)),
+           "gqa_prefill_causal")
     return out
 
 

@@ -102,6 +102,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // returns zeros and touches no memory, which lets tiles past the end of a
 // sequence be loaded without a branch.
 constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 data format
+constexpr int kSC1 = 16;                 // cache policy bit of buffer accesses: device-scope coherence
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, size_t bytes)
 {
@@ -120,6 +121,14 @@ constexpr int kDecodeRowGroups = kDecodeThreads / kDecodeLPR;
 constexpr int kDecodeMaxSplits = 64;    // partials merged by one workgroup (one round trip)
 constexpr int kDecodeTargetWGs = 256;   // one workgroup per CU at full length
 
+// Every workspace begins with a flag region of fixed size.  The words that
+// workgroups use to meet one another (decode (max, sum) words, prefill
+// arrival counters) live only there, and every call leaves the ones it used
+// at zero; partial results go after the region.  Because the region's place
+// and size never depend on a call's sizes, the partial results of one call
+// can never land where another call, of any sizes, looks for its flags.
+constexpr size_t kWsFlagBytes = (size_t)16 << 20;
+
 struct DecodePlan {
     int G;            // query heads per KV head
     int GT;           // query heads handled by one workgroup (divides G, <= 8)
@@ -127,11 +136,12 @@ struct DecodePlan {
     int HT;           // Hkv * ht_per_kv: workgroup columns per request
     int L;            // keys per split (multiple of kDecodeRowGroups)
     int n_split_max;  // ceil(s_cap / L)
-    // workspace layout (byte offsets)
-    size_t off_o, off_ml, off_end, bytes;
+    // workspace layout: (max, sum) words at offset 0 (flag region), partial
+    // outputs from kWsFlagBytes on
+    size_t ml_bytes, off_o, o_bytes, bytes;
 };
 
-inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+__host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 inline bool make_decode_plan(int B, int Hq, int Hkv, int D, int s_cap, int target_wgs, int max_splits,
                              DecodePlan *p)
@@ -151,13 +161,13 @@ inline bool make_decode_plan(int B, int Hq, int Hkv, int D, int s_cap, int targe
     const long per = (s_cap + rows * ns - 1) / (rows * ns);  // rows per row-group per split
     p->L = (int)(per * rows);
     p->n_split_max = (int)((s_cap + p->L - 1) / p->L);
-    const size_t cols = (size_t)B * p->HT;
-    size_t off = 0;
-    p->off_o = off;   off = align_up(off + cols * p->n_split_max * p->GT * (size_t)D * 4, 256);
-    p->off_ml = off;  off = align_up(off + cols * p->n_split_max * p->GT * 2 * 4, 256);
-    p->off_end = off;  // end of the partial arrays
-    p->bytes = off;
-    return true;
+    const size_t parts = (size_t)B * p->HT * p->n_split_max * p->GT;  // (request, query head, split)
+    p->ml_bytes = parts * 2 * 4;
+    p->off_o = kWsFlagBytes;
+    p->o_bytes = parts * (size_t)D * 4;
+    p->bytes = align_up(p->off_o + p->o_bytes, 256);
+    // the flags must fit their region; partials are addressed with 32-bit offsets
+    return p->ml_bytes <= kWsFlagBytes && p->o_bytes < ((size_t)1 << 31);
 }
 
 // Arguments of the split-K decode kernels (passed by value).
@@ -183,7 +193,8 @@ hipError_t launch_decode_q4(int D, int group, int B, const DecodeArgs &a, hipStr
 hipError_t launch_dequant_q4(const uint8_t *codes, const void *scales, const void *biases, float *out,
                              int n_rows, int D, int group, hipStream_t s);
 hipError_t launch_prefill(int dtype, int D, const void *q, const void *k, const void *v, void *out,
-                          int B, int Hq, int Hkv, int Tq, int Tk, int s_cap, float scale, hipStream_t s);
+                          int B, int Hq, int Hkv, int Tq, int Tk, int s_cap, float scale, void *ws, hipStream_t s);
+size_t prefill_workspace_bytes(int B, int Hq, int D, int Tq, int Tk);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 
 }  // namespace gqa

@@ -209,7 +209,6 @@ __device__ __forceinline__ void store4(T16 *p, float a, float b, float c, float 
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLazyRescale = 8.0f;  // log2 units
-constexpr int kSC1 = 16;              // cache policy bit: device-scope coherence
 
 __device__ __forceinline__ float rel_weight(float m_part, float m_total)
 {
@@ -464,9 +463,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
     // ---- publish the partial with device-scope stores: outputs first, then
     //      (after they have completed) the (max, sum) word that flags them ----
     const __amdgpu_buffer_rsrc_t ws_o =
-        __builtin_amdgcn_make_buffer_rsrc(a.part_o, 0, (int)(P.off_ml - P.off_o), kRsrcWord3);
+        __builtin_amdgcn_make_buffer_rsrc(a.part_o, 0, (int)P.o_bytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t ws_ml =
-        __builtin_amdgcn_make_buffer_rsrc(a.part_ml, 0, (int)(P.off_end - P.off_ml), kRsrcWord3);
+        __builtin_amdgcn_make_buffer_rsrc(a.part_ml, 0, (int)P.ml_bytes, kRsrcWord3);
     const size_t colbase = (size_t)col * P.n_split_max;
     if (tid < NQ) {
         const int off_o = (int)((((colbase + s) * GT + qh) * D + qd) * 4);

@@ -19,7 +19,7 @@ using namespace gqa;
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -103,7 +103,7 @@ void fill_ws(DecodeArgs &a, void *ws)
 {
     char *base = (char *)ws;
     a.part_o = (float *)(base + a.plan.off_o);
-    a.part_ml = (float *)(base + a.plan.off_ml);
+    a.part_ml = (float *)base;  // the flag region
     a.ws_bytes = a.plan.bytes;
 }
 
@@ -184,8 +184,16 @@ int gqa_decode_attend_batched(const void *q, const void *k, const void *v, void 
     return hip_status(launch_decode(dtype, D, B, a, (hipStream_t)stream));
 }
 
+size_t gqa_prefill_workspace_bytes(int B, int Hq, int Hkv, int D, int Tq, int Tk)
+{
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Tq < 1 || Tq > Tk) return 0;
+    if (D != 64 && D != 128) return 0;
+    return prefill_workspace_bytes(B, Hq, D, Tq, Tk);
+}
+
 int gqa_prefill_causal(const void *q, const void *k, const void *v, void *out, int B, int Hq, int Hkv, int D,
-                       int Tq, int Tk, int s_cap, float scale, int dtype, void *stream)
+                       int Tq, int Tk, int s_cap, float scale, int dtype, void *workspace, size_t workspace_bytes,
+                       void *stream)
 {
     if (!q || !k || !v || !out) return GQA_ERR_NULL;
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return GQA_ERR_SHAPE;
@@ -193,13 +201,19 @@ int gqa_prefill_causal(const void *q, const void *k, const void *v, void *out, i
     if (!std::isfinite(scale)) return GQA_ERR_SHAPE;
     if (D != 64 && D != 128) return GQA_ERR_UNSUPPORTED;
     if (dtype != GQA_BF16 && dtype != GQA_F16) return GQA_ERR_UNSUPPORTED;
-    if ((long)((Tq + 127) / 128) * Hq >= (1L << 31) || B > 65535) return GQA_ERR_SHAPE;
-    // a head's rows (plus the few tiles past the end that prefetches name) are
+    // the launch table names row blocks in 10 bits, and the 1-D grid has at
+    // most 1024 items per (request, head)
+    if (Tq > 1024 * 128 || (long)B * Hq * 1024 >= (1L << 31)) return GQA_ERR_SHAPE;
+    // a head's rows (plus the tile past the end that a prefetch names) are
     // addressed with 32-bit byte offsets
     if ((size_t)(s_cap + 512) * D * 2 >= ((size_t)1 << 31)) return GQA_ERR_SHAPE;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_ERR_ALIGN;
+    const size_t need = prefill_workspace_bytes(B, Hq, D, Tq, Tk);
+    if (!workspace || workspace_bytes < need) return GQA_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace))
+        return GQA_ERR_ALIGN;
     if (int st = check_device()) return st;
-    return hip_status(launch_prefill(dtype, D, q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, (hipStream_t)stream));
+    return hip_status(
+        launch_prefill(dtype, D, q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, workspace, (hipStream_t)stream));
 }
 
 int gqa_decode_attend_q4(const void *q, const uint8_t *k_codes, const void *k_scales, const void *k_biases,

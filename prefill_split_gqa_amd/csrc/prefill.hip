@@ -45,7 +45,10 @@
 // while the other runs the exponentials.  Only tiles that cross the diagonal
 // are masked.  Workgroups are issued longest-row-block first.
 
+#include <algorithm>
 #include <type_traits>
+#include <utility>
+#include <vector>
 
 #include "common.h"
 
@@ -113,32 +116,42 @@ template <> struct MfmaOps<f16_t> {
 
 template <typename V> __device__ __forceinline__ V as_vec(uint4 x) { return __builtin_bit_cast(V, x); }
 
-constexpr int kPfBM = 128;  // query rows per workgroup: 4 row-waves of 32 rows
-constexpr int kPfBN = 64;   // keys per tile
-constexpr int kPfNRW = 4;   // row-waves per key split
+constexpr int kPfBM = 128;       // query rows per workgroup: 4 row-waves of 32 rows
+constexpr int kPfBN = 64;        // keys per tile
+constexpr int kPfThreads = 256;  // 4 waves
+constexpr int kPfMaxItems = 1024;     // (row block, key chunk) work items in the launch table
 
-// Key splits per head dimension (the LDS holds two tiles per split).
-template <int D> struct PfCfg;
-template <> struct PfCfg<64> { static constexpr int NSPLIT = 4; };   // 16 waves, 4 per SIMD
-template <> struct PfCfg<128> { static constexpr int NSPLIT = 2; };  // 8 waves
-template <int D> constexpr int pf_threads() { return PfCfg<D>::NSPLIT * kPfNRW * 64; }
+// The launch's work items, longest first: entry r is (row block << 6) |
+// chunk; grid block x runs item x / (B * Hq) for request and head
+// x % (B * Hq).  ch is the most key tiles a chunk holds; row blocks rb0 and
+// later (those with more than ch tiles) are split, each into at most max_nc
+// chunks.
+struct PfItems {
+    int n;
+    int ch;
+    int rb0;
+    int max_nc;
+    unsigned short e[kPfMaxItems];
+};
 
 // LDS layout (bytes).  A tile is 64 rows of D 16-bit elements: groups of 8
-// rows (8 * ROW bytes) followed by 64 bytes of padding.  Per split: K
-// buffers 0, 1 then V buffers 0, 1.  After the key loop the same memory
-// holds the partial results of splits 1..NSPLIT-1.
+// rows (8 * ROW bytes) followed by 64 bytes of padding.  K buffers 0, 1 then
+// V buffers 0, 1.
 template <int D> struct PfLds {
-    static constexpr int NSPLIT = PfCfg<D>::NSPLIT;
-    static constexpr int NRW = kPfNRW;
     static constexpr int ROW = D * 2;
     static constexpr int GROUP = 8 * ROW + 64;
     static constexpr int TILE = 8 * GROUP;
-    static constexpr int SPLIT = 4 * TILE;
-    static constexpr int TOTAL = NSPLIT * SPLIT;
-    static constexpr int MERGE_O = (NSPLIT - 1) * NRW * (D / 32) * 16 * 64 * 4;
-    static constexpr int MERGE_ML = (NSPLIT - 1) * NRW * 64 * 2 * 4;
-    static_assert(MERGE_O + MERGE_ML <= TOTAL, "merge area exceeds the tile buffers");
-    static_assert(TOTAL <= 160 * 1024, "LDS");
+    static constexpr int TOTAL = 4 * TILE;
+};
+
+// Workspace of the key-chunk merge: one u32 arrival counter per (request,
+// head, row block), then one partial per (request, head, row block, chunk):
+// the 4 waves' fp32 O^T accumulators in register order ([wave][d-block][j]
+// [lane]) and each lane's (max, sum).
+template <int D> struct PfSlot {
+    static constexpr int O_FLOATS = 4 * (D / 32) * 16 * 64;
+    static constexpr int ML_FLOATS = 4 * 64 * 2;
+    static constexpr int BYTES = (O_FLOATS + ML_FLOATS) * 4;
 };
 
 // XOR applied to the 16-byte chunk index of a row, from the row's position
@@ -224,40 +237,41 @@ __device__ __forceinline__ void softmax_inplace(f32x16_t (&st)[2], f32x16_t (&ac
 }
 
 template <typename T, int D, bool NEG>
-__global__ __launch_bounds__(pf_threads<D>()) void prefill_causal_kernel(const uint16_t *__restrict__ q,
-                                                                         const uint16_t *__restrict__ k,
-                                                                         const uint16_t *__restrict__ v,
-                                                                         uint16_t *__restrict__ out, int Hq, int Hkv,
-                                                                         int Tq, int Tk, int s_cap, float qscale,
-                                                                         int n_rb)
+__global__ __launch_bounds__(kPfThreads) void prefill_causal_kernel(const uint16_t *__restrict__ q,
+                                                                    const uint16_t *__restrict__ k,
+                                                                    const uint16_t *__restrict__ v,
+                                                                    uint16_t *__restrict__ out, int Hq, int Hkv,
+                                                                    int Tq, int Tk, int s_cap, float qscale,
+                                                                    int n_rb, unsigned char *__restrict__ ws,
+                                                                    int B, PfItems items)
 {
     typedef MfmaOps<T> Ops;
     typedef typename Ops::vec vec;
     typedef PfLds<D> L;
-    constexpr int NSPLIT = L::NSPLIT;  // key splits
-    constexpr int NRW = L::NRW;        // row-waves per split
+    typedef PfSlot<D> SL;
+    constexpr int NRW = 4;             // row-waves
     constexpr int NKB = D / 16;        // k-blocks of the QK^T product
     constexpr int NDB = D / 32;        // 32-wide d-blocks of the output
     constexpr int CPR = D / 8;         // 16-byte chunks per row
     constexpr int RPI = 1024 / L::ROW; // rows per LDS-writing load (64 lanes x 16 bytes)
     constexpr int IPT = kPfBN / RPI;   // such loads per tile
-    constexpr int IPW = 2 * IPT / NRW; // loads per wave per step (one K and one V tile per split)
+    constexpr int IPW = 2 * IPT / NRW; // loads per wave per step (one K and one V tile)
     constexpr float kInf = __builtin_huge_valf();
     static_assert(2 * IPT % NRW == 0 && IPT % IPW == 0, "load split");
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int split = wave / NRW;  // key split this wave walks
-    const int rw = wave % NRW;     // row-wave within the split
+    const int rw = wave;  // row-wave
     const int lane = tid & 63;
     const int ln = lane & 31, lg = lane >> 5;
 
-    // longest row blocks first, every head's before the next length
-    const int bx = blockIdx.x;
-    const int h = bx % Hq;
-    const int rb = n_rb - 1 - bx / Hq;
-    const int b = blockIdx.y;
+    // work item (row block, key chunk) and (request, head) of this workgroup
+    const int bh = blockIdx.x % (B * Hq);
+    const int item = items.e[blockIdx.x / (B * Hq)];
+    const int rb = item >> 6, chunk = item & 63;
+    const int h = bh % Hq;
+    const int b = bh / Hq;
     const int G = Hq / Hkv;
     const int g = h / G;
     const int off = Tk - Tq;
@@ -266,10 +280,11 @@ __global__ __launch_bounds__(pf_threads<D>()) void prefill_causal_kernel(const u
     const int row_hi = min(r0 + kPfBM, Tq);         // one past the last valid row of the block
     const int kend = min(Tk, row_hi + off);         // keys any valid row of the block can see
     const int n_tiles = (kend + kPfBN - 1) / kPfBN;
-    const int n = (n_tiles + NSPLIT - 1) / NSPLIT;  // steps; split sp walks tiles [sp*n, sp*n + n)
-    const int t_begin = split * n;
+    const int nc = (n_tiles + items.ch - 1) / items.ch;  // chunks of this row block
+    const int per = (n_tiles + nc - 1) / nc;        // tiles per chunk
+    const int t_begin = min(n_tiles, chunk * per);
+    const int n = min(n_tiles, t_begin + per) - t_begin;
     const int n_full = min(n_tiles, max(0, (r0 + off + 1) / kPfBN));  // tiles every row sees in full
-    unsigned char *const ssm = smem + split * L::SPLIT;  // this split's K0 K1 V0 V1
     const int my_row = rw0 + ln;
     const int my_lim = my_row + off;  // last visible key of this lane's row
 
@@ -292,8 +307,8 @@ __global__ __launch_bounds__(pf_threads<D>()) void prefill_causal_kernel(const u
     // ---- tile loads: HBM -> LDS, IPW loads of 1 KB per wave and step ----
     // Load i of a tile covers rows [i*RPI, i*RPI + RPI); lane l writes the
     // 16 bytes at LDS position (row i*RPI + l/CPR, slot l%CPR), which hold
-    // the row's chunk slot ^ swz(row & 7).  The row-waves of a split share
-    // the K and V loads of one tile between them.
+    // the row's chunk slot ^ swz(row & 7).  The 4 waves share the K and V
+    // loads of one tile.
     const bool loads_v = rw * IPW >= IPT;  // this wave's share of a step's loads: all K or all V
     int dma_voff[IPW];                     // lane part of each load's byte offset
     unsigned dma_lds[IPW];                 // LDS destination of each load in buffer 0
@@ -302,9 +317,9 @@ __global__ __launch_bounds__(pf_threads<D>()) void prefill_causal_kernel(const u
         const int i = rw * IPW + ii;  // 0 .. 2*IPT-1: K loads, then V loads
         const int row_first = (loads_v ? i - IPT : i) * RPI;
         const int row = row_first + lane / CPR;
-        const int chunk = (lane % CPR) ^ swz(row & 7);
-        dma_voff[ii] = (row * D + chunk * 8) * 2;
-        dma_lds[ii] = (unsigned)(uintptr_t)(lds_void_t *)(ssm + (loads_v ? 2 : 0) * L::TILE +
+        const int cslot = (lane % CPR) ^ swz(row & 7);
+        dma_voff[ii] = (row * D + cslot * 8) * 2;
+        dma_lds[ii] = (unsigned)(uintptr_t)(lds_void_t *)(smem + (loads_v ? 2 : 0) * L::TILE +
                                                           (row_first >> 3) * L::GROUP + (row_first & 7) * L::ROW);
     }
     auto issue_tile_loads = [&](int kt, int buf) {
@@ -325,14 +340,21 @@ __global__ __launch_bounds__(pf_threads<D>()) void prefill_causal_kernel(const u
     const float thr = fminf(8.0f / aq, 3.0e38f);  // lazy-rescale threshold, raw units (qscale != 0)
 
     // Lane-dependent LDS byte offsets of the fragments within a tile; the
-    // rest of each address (buffer, sub-tile, k-block row group) is a
-    // constant the reads take as an immediate offset.
+    // rest of each address (buffer, sub-tile, row group) is a constant the
+    // reads take as an immediate offset.
     //   K, row u*32 + ln, chunk 2kb + lg:  tile_off(ln, 2kb + lg) + u*4*GROUP
-    //   V, rows 16t + 8h + 4lg + j/4:     (see v_frag) + (2t + h)*GROUP
+    //   V, rows 16t + 8h + 4lg + j/4:     voff[db] + (2t + h)*GROUP
     int koff[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) koff[kb] = tile_off<D>(ln, 2 * kb + lg);
-
+    int voff[NDB];
+    {
+        const int gam = lane >> 4, j = lane & 15;
+        const int row0 = 4 * lg + (j >> 2);  // < 8: rows 16t + 8h + row0 share its swizzle
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            voff[db] = tile_off<D>(row0, 4 * db + 2 * (gam & 1) + ((j & 3) >> 1)) + (j & 1) * 8;
+    }
     // K fragment (A operand of S^T): key row u*32 + ln, dims kb*16 + lg*8 .. +8
     auto k_frag = [&](const unsigned char *Kt, int u, int kb) {
         return *(const uint4 *)(Kt + koff[kb] + u * 4 * L::GROUP);
@@ -345,14 +367,6 @@ __global__ __launch_bounds__(pf_threads<D>()) void prefill_causal_kernel(const u
     // lane 4k + i/4 as its slot k, so source lane j names row
     // 16t + 8h + 4lg + j/4 (h: which half of the slots) at column
     // 32db + 16*((lane/16)%2) + 4*(j%4).
-    int voff[NDB];
-    {
-        const int gam = lane >> 4, j = lane & 15;
-        const int row0 = 4 * lg + (j >> 2);  // < 8: rows 16t + 8h + row0 share its swizzle
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-            voff[db] = tile_off<D>(row0, 4 * db + 2 * (gam & 1) + ((j & 3) >> 1)) + (j & 1) * 8;
-    }
     auto v_frag = [&](const unsigned char *Vt, int t, int db) {
         const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4_t *)(Vt + voff[db] + (2 * t) * L::GROUP));
@@ -364,11 +378,11 @@ __global__ __launch_bounds__(pf_threads<D>()) void prefill_causal_kernel(const u
 
     // One tile of the wave's 32 rows from buffer buf: S^T = K Q^T, mask (tiles
     // crossing the diagonal), online softmax, O^T += V^T P^T.  Fragments are
-    // read from LDS as they are needed; the other waves on the SIMD (four
-    // per SIMD for D = 64) hide the latency.
+    // read from LDS as they are needed; the waves of the other workgroups on
+    // the CU (four workgroups per CU for D = 64) hide the latency.
     auto tile_step = [&](int kt, int buf) {
-        const unsigned char *Kt = ssm + buf * L::TILE;
-        const unsigned char *Vt = ssm + (2 + buf) * L::TILE;
+        const unsigned char *Kt = smem + buf * L::TILE;
+        const unsigned char *Vt = smem + (2 + buf) * L::TILE;
         f32x16_t st[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -389,7 +403,7 @@ __global__ __launch_bounds__(pf_threads<D>()) void prefill_causal_kernel(const u
                     if (key0 + 32 * u + 8 * (j >> 2) + (j & 3) > my_lim) st[u][j] = NEG ? kInf : -kInf;
         }
         softmax_inplace<NEG>(st, acc, m_run, l_part, qscale, thr);
-        // P to 16 bits (paired conversion) and its row sums (independent
+        // P to 16 bits (one vector conversion) and its row sums (independent
         // partial sums); O^T += V^T P^T in four 16-key k-blocks
         float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -413,10 +427,8 @@ __global__ __launch_bounds__(pf_threads<D>()) void prefill_causal_kernel(const u
     // Step s: the loads of tile t+1 go to the buffer that step s-1 read
     // (every wave has passed the barrier that ended step s-1); tile t is
     // computed from the other buffer; the step ends by waiting for its own
-    // loads and a barrier.  Steps past a split's last tile work on keys at
-    // or past kend (masked for every valid row) or past Tk (zeros), and add
-    // nothing.
-    issue_tile_loads(t_begin, 0);
+    // loads and a barrier.
+    if (n > 0) issue_tile_loads(t_begin, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int s = 0; s < n; s += 2) {  // unrolled by two: buffer indices are constants
@@ -432,42 +444,61 @@ __global__ __launch_bounds__(pf_threads<D>()) void prefill_causal_kernel(const u
         }
     }
 
-    // ---- merge splits 1..NSPLIT-1 into split 0 through LDS ----
-    float *xo = (float *)smem;                  // [split-1][rw][db][j][lane]
-    float *xml = (float *)(smem + L::MERGE_O);  // [split-1][rw][lane][max, sum]
-    if (split > 0) {
-        const int slot = (split - 1) * NRW + rw;
+    // ---- key chunks of a long row block: merge through the workspace ----
+    // Every chunk stores its partial with device-scope stores, waits for
+    // them, and takes a ticket; the chunk that arrives last merges all of
+    // them in chunk order (so the result does not depend on timing), writes
+    // the output and returns the counter to zero.  Counters sit in the
+    // workspace's flag region, partials after it, both indexed by the split
+    // row block (nc > 1 exactly for row blocks rb0 and later: the tile count
+    // grows with the row block).
+    if (nc > 1) {
+        const size_t split_rb = ((size_t)b * Hq + h) * (n_rb - items.rb0) + (rb - items.rb0);
+        unsigned *counter = (unsigned *)ws + split_rb;
+        unsigned char *slots = ws + kWsFlagBytes + split_rb * items.max_nc * SL::BYTES;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(slots, (size_t)nc * SL::BYTES);
+        auto o_off = [&](int c, int db, int j) { return c * SL::BYTES + (((rw * NDB + db) * 16 + j) * 64 + lane) * 4; };
+        auto ml_off = [&](int c) { return c * SL::BYTES + (SL::O_FLOATS + (rw * 64 + lane) * 2) * 4; };
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) xo[((slot * NDB + db) * 16 + j) * 64 + lane] = acc[db][j];
-        xml[(slot * 64 + lane) * 2 + 0] = m_run;
-        xml[(slot * 64 + lane) * 2 + 1] = l_part;
-    }
-    __syncthreads();
-    if (split > 0) return;
-    float m = m_run;
-#pragma unroll
-    for (int sp = 1; sp < NSPLIT; ++sp) m = fmaxf(m, xml[(((sp - 1) * NRW + rw) * 64 + lane) * 2 + 0]);
-    const float w0 = m_run == -kInf ? 0.0f : fast_exp2(aq * (m_run - m));
-    float l = w0 * l_part;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[db][j] *= w0;
-#pragma unroll
-    for (int sp = 1; sp < NSPLIT; ++sp) {
-        const int slot = (sp - 1) * NRW + rw;
-        const float ms = xml[(slot * 64 + lane) * 2 + 0];
-        const float ws = ms == -kInf ? 0.0f : fast_exp2(aq * (ms - m));
-        l += ws * xml[(slot * 64 + lane) * 2 + 1];
+            for (int j = 0; j < 16; ++j)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[db][j]), rs, o_off(chunk, db, j), 0, kSC1);
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, make_float2(m_run, l_part)), rs,
+            ml_off(chunk), 0, kSC1);
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
+        __syncthreads();                // ... and so have every other thread's
+        __shared__ int s_last;
+        if (tid == 0)
+            s_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == (unsigned)(nc - 1);
+        __syncthreads();
+        if (!s_last) return;
+        float m = -kInf;
+        for (int c = 0; c < nc; ++c) {
+            const float2 ml = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rs, ml_off(c), 0, kSC1));
+            m = fmaxf(m, ml.x);
+        }
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) acc[db][j] += ws * xo[((slot * NDB + db) * 16 + j) * 64 + lane];
+            for (int j = 0; j < 16; ++j) acc[db][j] = 0.0f;
+        l_part = 0.0f;
+        for (int c = 0; c < nc; ++c) {  // fixed order, own partial re-read like the others
+            const float2 ml = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rs, ml_off(c), 0, kSC1));
+            const float wc = ml.x == -kInf ? 0.0f : fast_exp2(aq * (ml.x - m));
+            l_part += wc * ml.y;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    acc[db][j] += wc * __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, o_off(c, db, j), 0, kSC1));
+        }
+        if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
+
     // ---- normalise and store: lane holds O^T[d][row] for d = 32db + 8i + 4lg + r ----
-    const float l_tot = l + __shfl_xor(l, 32, 64);
+    const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
     if (my_row < Tq) {
         const float inv = 1.0f / l_tot;
         uint16_t *orow = out + (((size_t)b * Hq + h) * (size_t)Tq + my_row) * D;
@@ -484,38 +515,128 @@ __global__ __launch_bounds__(pf_threads<D>()) void prefill_causal_kernel(const u
     }
 }
 
-template <typename T, int D>
-static hipError_t launch_pf(const void *q, const void *k, const void *v, void *out, int B, int Hq, int Hkv,
-                            int Tq, int Tk, int s_cap, float scale, hipStream_t s)
+// ---- work decomposition (host) ----
+// Key tiles of row block rb (the keys its valid rows can see).
+static int pf_row_tiles(int rb, int Tq, int Tk)
+{
+    const int row_hi = std::min((rb + 1) * kPfBM, Tq);
+    return (std::min(Tk, row_hi + Tk - Tq) + kPfBN - 1) / kPfBN;
+}
+
+// Chunking of the causal triangle.  The most key tiles per chunk, ch, is
+// the smallest value that gives about two workgroups' worth of tiles per
+// workgroup slot (4 per CU on 256 CUs), so that the scheduler can balance
+// the triangle, but at least 4 tiles (a chunk's partial costs a write and a
+// read), with the launch table's item count, the chunks per row block and
+// the split row blocks' counters within their limits.  Every limit is
+// monotone in ch and met once no row block is split.
+struct PfPlan {
+    int n_rb, ch, rb0, max_nc, n_items;
+};
+
+static PfPlan pf_plan_for(int Tq, int Tk, int ch)
+{
+    PfPlan p;
+    p.n_rb = (Tq + kPfBM - 1) / kPfBM;
+    p.ch = ch;
+    p.rb0 = p.n_rb;
+    p.max_nc = 1;
+    p.n_items = 0;
+    for (int rb = p.n_rb - 1; rb >= 0; --rb) {
+        const int nc = (pf_row_tiles(rb, Tq, Tk) + ch - 1) / ch;
+        if (nc > 1) p.rb0 = rb;
+        p.max_nc = std::max(p.max_nc, nc);
+        p.n_items += nc;
+    }
+    return p;
+}
+
+static bool pf_plan_fits(const PfPlan &p, int B, int Hq)
+{
+    return p.n_items <= kPfMaxItems && p.max_nc <= 63 &&
+           (size_t)B * Hq * (p.n_rb - p.rb0) * 4 <= kWsFlagBytes;
+}
+
+static PfPlan pf_plan(int B, int Hq, int Tq, int Tk)
 {
     const int n_rb = (Tq + kPfBM - 1) / kPfBM;
+    long total = 0;
+    for (int rb = 0; rb < n_rb; ++rb) total += pf_row_tiles(rb, Tq, Tk);
+    total *= (long)B * Hq;
+    int lo = (int)std::min<long>(std::max(4L, (total + 2 * 1024 - 1) / (2 * 1024)), 1 << 30);
+    int hi = std::max(lo, pf_row_tiles(n_rb - 1, Tq, Tk));  // no split: always fits
+    if (pf_plan_fits(pf_plan_for(Tq, Tk, lo), B, Hq)) return pf_plan_for(Tq, Tk, lo);
+    while (hi - lo > 1) {  // invariant: lo does not fit, hi does
+        const int mid = lo + (hi - lo) / 2;
+        if (pf_plan_fits(pf_plan_for(Tq, Tk, mid), B, Hq)) hi = mid; else lo = mid;
+    }
+    return pf_plan_for(Tq, Tk, hi);
+}
+
+// The (row block, chunk) items sorted longest first (ties: longer row block
+// first, so that the chunks that merge run early), as the launch table.
+static void pf_items(const PfPlan &p, int Tq, int Tk, PfItems *it)
+{
+    std::vector<std::pair<int, int>> v;  // (sort key, entry)
+    for (int rb = 0; rb < p.n_rb; ++rb) {
+        const int nt = pf_row_tiles(rb, Tq, Tk);
+        const int nc = (nt + p.ch - 1) / p.ch, per = (nt + nc - 1) / nc;
+        for (int c = 0; c < nc; ++c) {
+            const int t0 = std::min(nt, c * per), len = std::min(nt, t0 + per) - t0;
+            v.push_back({-(len * 1048576 + nt * 64 + (63 - c)), (rb << 6) | c});
+        }
+    }
+    std::sort(v.begin(), v.end());
+    it->n = (int)v.size();
+    it->ch = p.ch;
+    it->rb0 = p.rb0;
+    it->max_nc = p.max_nc;
+    for (int i = 0; i < it->n; ++i) it->e[i] = (unsigned short)v[i].second;
+}
+
+// Flag region, then one partial slot per chunk of every split row block.
+size_t prefill_workspace_bytes(int B, int Hq, int D, int Tq, int Tk)
+{
+    const PfPlan p = pf_plan(B, Hq, Tq, Tk);
+    const size_t slot = D == 64 ? PfSlot<64>::BYTES : PfSlot<128>::BYTES;
+    const size_t split_cols = (size_t)B * Hq * (p.n_rb - p.rb0);
+    return kWsFlagBytes + (p.max_nc > 1 ? split_cols * p.max_nc * slot : 0);
+}
+
+template <typename T, int D>
+static hipError_t launch_pf(const void *q, const void *k, const void *v, void *out, int B, int Hq, int Hkv,
+                            int Tq, int Tk, int s_cap, float scale, void *ws, hipStream_t s)
+{
+    const PfPlan plan = pf_plan(B, Hq, Tq, Tk);
+    PfItems items;
+    pf_items(plan, Tq, Tk, &items);
     // A zero scale (uniform weights over the visible keys) is run as the
     // smallest normal scale: every exponent is then below 2^-80 in
     // magnitude, exp2 of it rounds to exactly 1, and masked keys (-inf)
     // still give 0 rather than inf*0.
     float qscale = scale * 1.4426950408889634f;
     if (qscale == 0.0f) qscale = 1.17549435e-38f;
-    dim3 grid(n_rb * Hq, B);
+    dim3 grid((unsigned)(items.n * B * Hq));
     if (qscale < 0.0f)
-        hipLaunchKernelGGL((prefill_causal_kernel<T, D, true>), grid, dim3(pf_threads<D>()), 0, s, (const uint16_t *)q,
+        hipLaunchKernelGGL((prefill_causal_kernel<T, D, true>), grid, dim3(kPfThreads), 0, s, (const uint16_t *)q,
                            (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)out, Hq, Hkv, Tq, Tk, s_cap,
-                           qscale, n_rb);
+                           qscale, plan.n_rb, (unsigned char *)ws, B, items);
     else
-        hipLaunchKernelGGL((prefill_causal_kernel<T, D, false>), grid, dim3(pf_threads<D>()), 0, s, (const uint16_t *)q,
+        hipLaunchKernelGGL((prefill_causal_kernel<T, D, false>), grid, dim3(kPfThreads), 0, s, (const uint16_t *)q,
                            (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)out, Hq, Hkv, Tq, Tk, s_cap,
-                           qscale, n_rb);
+                           qscale, plan.n_rb, (unsigned char *)ws, B, items);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill(int dtype, int D, const void *q, const void *k, const void *v, void *out, int B,
-                          int Hq, int Hkv, int Tq, int Tk, int s_cap, float scale, hipStream_t s)
+                          int Hq, int Hkv, int Tq, int Tk, int s_cap, float scale, void *ws, hipStream_t s)
 {
     if (dtype == 1) {
-        if (D == 64) return launch_pf<bf16_t, 64>(q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, s);
-        if (D == 128) return launch_pf<bf16_t, 128>(q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, s);
+        if (D == 64) return launch_pf<bf16_t, 64>(q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, ws, s);
+        if (D == 128) return launch_pf<bf16_t, 128>(q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, ws, s);
     } else if (dtype == 2) {
-        if (D == 64) return launch_pf<f16_t, 64>(q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, s);
-        if (D == 128) return launch_pf<f16_t, 128>(q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, s);
+        if (D == 64) return launch_pf<f16_t, 64>(q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, ws, s);
+        if (D == 128) return launch_pf<f16_t, 128>(q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, ws, s);
     }
     return hipErrorInvalidValue;
 }

@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gqa.gqa_abi_version() == 1
+    assert gqa.gqa_abi_version() == 2
     for st in range(7):
         assert gqa.status_string(st)
     assert gqa.status_string(99) == "unknown status"
@@ -98,9 +98,12 @@ def test_batched_validation(lib):
 
 
 def test_prefill_validation(lib):
-    def call(q=FAKE, Hq=14, Hkv=2, D=64, Tq=8, Tk=8, s_cap=8, dtype=1, scale=0.125):
+    wsb = gqa.gqa_prefill_workspace_bytes(1, 14, 2, 64, 8, 8)
+    assert wsb > 0
+
+    def call(q=FAKE, Hq=14, Hkv=2, D=64, Tq=8, Tk=8, s_cap=8, dtype=1, scale=0.125, ws=FAKE, ws_bytes=wsb):
         return lib.gqa_prefill_causal(q, FAKE, FAKE, FAKE, 1, Hq, Hkv, D, Tq, Tk, s_cap, ctypes.c_float(scale),
-                                      dtype, NULL)
+                                      dtype, ws, ws_bytes, NULL)
 
     assert call(q=NULL) == gqa.GQA_ERR_NULL
     assert call(Tq=9) == gqa.GQA_ERR_SHAPE        # Tq > Tk
@@ -110,7 +113,47 @@ def test_prefill_validation(lib):
     assert call(scale=float("inf")) == gqa.GQA_ERR_SHAPE
     assert call(dtype=0) == gqa.GQA_ERR_UNSUPPORTED  # fp32 prefill is not provided
     assert call(D=80) == gqa.GQA_ERR_UNSUPPORTED
+    assert call(ws=NULL) == gqa.GQA_ERR_WORKSPACE
+    assert call(ws_bytes=wsb - 1) == gqa.GQA_ERR_WORKSPACE
     assert call(q=FAKE_ODD) == gqa.GQA_ERR_ALIGN
+    assert call(ws=FAKE_ODD) == gqa.GQA_ERR_ALIGN
+    assert call(Tq=131073, Tk=131073, s_cap=131073, ws_bytes=1 << 40) == gqa.GQA_ERR_SHAPE  # row-block index width
+
+
+MIB16 = 16 << 20  # fixed flag region at the front of every workspace
+
+
+def test_prefill_workspace_size():
+    # The flag region, then one partial slot per chunk of every split row
+    # block.  B=2, 14 heads, T=4097: row block rb (< 32) sees 2(rb+1) key
+    # tiles of 64, the last one 65, 1121 tiles a head, 31388 in all; about
+    # two workgroups per slot (2048) gives chunks of at most 16 tiles, so
+    # row blocks 8..32 (25 of them) are split, the last into 5 chunks.
+    slot64 = (4 * 2 * 16 * 64 + 4 * 64 * 2) * 4
+    assert gqa.gqa_prefill_workspace_bytes(2, 14, 2, 64, 4097, 4097) == MIB16 + 2 * 14 * 25 * 5 * slot64
+    # nothing is split: the flag region alone
+    assert gqa.gqa_prefill_workspace_bytes(1, 14, 2, 64, 8, 8) == MIB16
+    # Tq=200, Tk=300: row blocks of 4 and 5 tiles, chunks of at most 4
+    # tiles, so the second row block is split in two
+    slot128 = (4 * 4 * 16 * 64 + 4 * 64 * 2) * 4
+    assert gqa.gqa_prefill_workspace_bytes(1, 14, 2, 128, 200, 300) == MIB16 + 14 * 2 * slot128
+    # a large batch fills the GPU without splitting
+    assert gqa.gqa_prefill_workspace_bytes(64, 32, 8, 128, 2048, 2048) == MIB16
+    # invalid sizes give 0
+    assert gqa.gqa_prefill_workspace_bytes(1, 14, 2, 64, 9, 8) == 0
+    assert gqa.gqa_prefill_workspace_bytes(1, 14, 3, 64, 8, 8) == 0
+    assert gqa.gqa_prefill_workspace_bytes(1, 14, 2, 80, 8, 8) == 0
+
+
+def test_decode_workspace_layout():
+    # 28 query heads over 4 KV heads: 4 columns of 7 heads, 64 splits of 64
+    # keys at s_cap = 4096; one 128-float partial per (column, split, head)
+    # after the flag region
+    assert gqa.gqa_decode_workspace_bytes(1, 28, 4, 128, 4096) == MIB16 + 4 * 64 * 7 * 128 * 4
+    # the (max, sum) words, 8 bytes per partial, must fit the flag region:
+    # 28 * 64 * 8 bytes a request allow 1170 requests
+    assert gqa.gqa_decode_workspace_bytes(1170, 28, 4, 128, 4096) > 0
+    assert gqa.gqa_decode_workspace_bytes(1171, 28, 4, 128, 4096) == 0
 
 
 def test_q4_validation(lib):

@@ -99,6 +99,33 @@ def test_decode_deterministic_with_reused_workspace(gpu_lib):
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
+FLAG_BYTES = 16 << 20  # fixed flag region at the front of every workspace
+
+
+def test_decode_workspace_shared_across_batch_sizes(gpu_lib):
+    # One workspace serves calls of different batch sizes in any order: the
+    # (max, sum) flag words live in a region of their own, so the partial
+    # outputs a larger batch leaves behind are never read as flags by a
+    # smaller one.  Each call must match a run on a fresh workspace bit for
+    # bit and leave the flag region zero.
+    Hq, Hkv, D, S = 28, 4, 128, 1024
+    ws = gpu_lib.make_workspace(8, Hq, Hkv, D, S)
+    gen = torch.Generator().manual_seed(41)
+    for it, B in enumerate([8, 1, 5, 2, 8, 3]):
+        n = S - 37 * it
+        q = torch.randn(B, Hq, 1, D, generator=gen).cuda()
+        k = torch.randn(B, Hkv, S, D, generator=gen).cuda()
+        v = torch.randn(B, Hkv, S, D, generator=gen).cuda()
+        note("decode shared workspace it=%d B=%d kv_len=%d" % (it, B, n))
+        got = torch.empty_like(q)
+        gpu_lib.gqa_decode_attend(q, k, v, got, n, ws)
+        ref = torch.empty_like(q)
+        gpu_lib.gqa_decode_attend(q, k, v, ref, n, gpu_lib.make_workspace(B, Hq, Hkv, D, S))
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), "it=%d B=%d" % (it, B)
+        assert int((ws[:FLAG_BYTES] != 0).sum()) == 0, "flags not cleared, it=%d" % it
+
+
 def test_workspace_init_entry_point(gpu_lib):
     q = torch.randn(1, 8, 1, 64, device="cuda")
     k = torch.randn(1, 2, 300, 64, device="cuda")

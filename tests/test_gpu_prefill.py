@@ -23,9 +23,19 @@ from workloads import configs as W
 pytestmark = pytest.mark.gpu
 
 
+FLAG_BYTES = 16 << 20  # fixed flag region at the front of every workspace
+
+
+def prefill_ws(gqa, q, k, Tk=None):
+    B, Hq, Tq, D = q.shape
+    Tk = k.shape[2] if Tk is None else Tk
+    return gqa.make_prefill_workspace(B, Hq, k.shape[1], D, Tq, Tk)
+
+
 def run_prefill(gqa, q, k, v, Tk=None, scale=None):
     g = Guarded(q.shape, q.dtype)
-    gqa.gqa_prefill_causal(q.cuda(), k.cuda(), v.cuda(), g.t, Tk=Tk, scale=scale)
+    ws = prefill_ws(gqa, q, k, Tk)
+    gqa.gqa_prefill_causal(q.cuda(), k.cuda(), v.cuda(), g.t, ws, Tk=Tk, scale=scale)
     torch.cuda.synchronize()
     g.check()
     return g.t
@@ -71,6 +81,9 @@ CASES = [
     (2, 12, 2, 128, 65, 333, 400),
     (1, 16, 1, 128, 257, 257, 257),
     (1, 14, 2, 64, 64, 1000, 1000),
+    (1, 14, 2, 64, 64, 1100, 1100),   # 18 key tiles: two key chunks merged
+    (1, 4, 2, 64, 3, 2500, 2600),     # 40 key tiles: three key chunks merged
+    (2, 4, 1, 128, 130, 1300, 1300),  # D = 128, two row blocks, two chunks each
 ]
 
 
@@ -107,10 +120,65 @@ def test_prefill_deterministic(gpu_lib):
     q, k, v = (t.cuda() for t in W.prefill_inputs(w, 2049))
     a = torch.empty_like(q)
     b = torch.empty_like(q)
-    gpu_lib.gqa_prefill_causal(q, k, v, a)
-    gpu_lib.gqa_prefill_causal(q, k, v, b)
+    ws = prefill_ws(gpu_lib, q, k)
+    gpu_lib.gqa_prefill_causal(q, k, v, a, ws)
+    gpu_lib.gqa_prefill_causal(q, k, v, b, ws)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_prefill_workspace_reuse(gpu_lib):
+    # The key chunks of a long row block meet through the workspace: the last
+    # to arrive merges and returns the counter to zero.  Many calls in a row
+    # on one workspace, with changing inputs and lengths, must each match a
+    # fresh run, and leave every counter at zero.
+    w = W.by_name("prefill_0p5b")
+    q0, k0, v0 = (t.cuda() for t in W.prefill_inputs(w, 2049))
+    Hq, Hkv, D = q0.shape[1], k0.shape[1], q0.shape[3]
+    ws = gpu_lib.make_prefill_workspace(1, Hq, Hkv, D, 2049, 2049)
+    rng = np.random.default_rng(29)
+    for it in range(12):
+        Tq = int(rng.integers(1, 2049))
+        Tk = int(rng.integers(Tq, 2050))
+        q = (q0[:, :, :Tq] * (1 + 0.1 * it)).contiguous()
+        k = (k0 * (1 - 0.05 * it)).contiguous()
+        note("prefill reuse it=%d Tq=%d Tk=%d" % (it, Tq, Tk))
+        got = torch.empty_like(q)
+        gpu_lib.gqa_prefill_causal(q, k, v0, got, ws, Tk=Tk)
+        ref = torch.empty_like(q)
+        gpu_lib.gqa_prefill_causal(q, k, v0, ref, prefill_ws(gpu_lib, q, k, Tk), Tk=Tk)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), "it=%d" % it
+        assert int((ws[:FLAG_BYTES] != 0).sum()) == 0, "counters not reset, it=%d" % it
+
+
+def test_workspace_shared_by_decode_and_prefill(gpu_lib):
+    # Decode and prefill calls of changing sizes take turns on one
+    # workspace; each must match a run on a fresh workspace bit for bit.
+    w = W.by_name("prefill_0p5b")
+    q0, k0, v0 = (t.cuda() for t in W.prefill_inputs(w, 2049))
+    Hq, Hkv, D = q0.shape[1], k0.shape[1], q0.shape[3]
+    ws = torch.zeros(max(gpu_lib.gqa_prefill_workspace_bytes(1, Hq, Hkv, D, 2049, 2049),
+                         gpu_lib.gqa_decode_workspace_bytes(4, Hq, Hkv, D, 2049)), dtype=torch.uint8, device="cuda")
+    gen = torch.Generator().manual_seed(43)
+    for it, (Tq, Tk, B) in enumerate([(2049, 2049, 4), (300, 1900, 1), (1500, 1500, 3), (77, 2049, 2)]):
+        note("shared workspace it=%d prefill Tq=%d Tk=%d, decode B=%d" % (it, Tq, Tk, B))
+        q = q0[:, :, :Tq].contiguous()
+        got = torch.empty_like(q)
+        gpu_lib.gqa_prefill_causal(q, k0, v0, got, ws, Tk=Tk)
+        ref = torch.empty_like(q)
+        gpu_lib.gqa_prefill_causal(q, k0, v0, ref, prefill_ws(gpu_lib, q, k0, Tk), Tk=Tk)
+        qd = torch.randn(B, Hq, 1, D, generator=gen).to(torch.bfloat16).cuda()
+        kd = torch.randn(B, Hkv, 2049, D, generator=gen).to(torch.bfloat16).cuda()
+        vd = torch.randn(B, Hkv, 2049, D, generator=gen).to(torch.bfloat16).cuda()
+        got_d = torch.empty_like(qd)
+        gpu_lib.gqa_decode_attend(qd, kd, vd, got_d, Tk, ws)
+        ref_d = torch.empty_like(qd)
+        gpu_lib.gqa_decode_attend(qd, kd, vd, ref_d, Tk, gpu_lib.make_workspace(B, Hq, Hkv, D, 2049))
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), "prefill it=%d" % it
+        assert torch.equal(got_d, ref_d), "decode it=%d" % it
+        assert int((ws[:FLAG_BYTES] != 0).sum()) == 0, "flags not cleared, it=%d" % it
 
 
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 0.9])
