@@ -120,6 +120,8 @@ constexpr int kPfBM = 128;       // query rows per workgroup: 4 row-waves of 32 
 constexpr int kPfBN = 64;        // keys per tile
 constexpr int kPfThreads = 256;  // 4 waves
 constexpr int kPfMaxItems = 1024;     // (row block, key chunk) work items in the launch table
+constexpr int kPfSlots = 4 * 256;     // workgroup slots: 4 workgroups on each of the 256 CUs (D = 64)
+constexpr int kPfMinChunk = 8;        // fewest key tiles per chunk: a chunk's partial costs a write and a read
 
 // The launch's work items, longest first: entry r is (row block << 6) |
 // chunk; grid block x runs item x / (B * Hq) for request and head
@@ -144,10 +146,9 @@ template <int D> struct PfLds {
     static constexpr int TOTAL = 4 * TILE;
 };
 
-// Workspace of the key-chunk merge: one u32 arrival counter per (request,
-// head, row block), then one partial per (request, head, row block, chunk):
-// the 4 waves' fp32 O^T accumulators in register order ([wave][d-block][j]
-// [lane]) and each lane's (max, sum).
+// Partial result of one key chunk in the workspace: the 4 waves' fp32 O^T
+// accumulators, 16 bytes per lane and access ([wave][d-block][j/4][lane]
+// [j%4]), then each lane's (max, sum).
 template <int D> struct PfSlot {
     static constexpr int O_FLOATS = 4 * (D / 32) * 16 * 64;
     static constexpr int ML_FLOATS = 4 * 64 * 2;
@@ -237,7 +238,7 @@ __device__ __forceinline__ void softmax_inplace(f32x16_t (&st)[2], f32x16_t (&ac
 }
 
 template <typename T, int D, bool NEG>
-__global__ __launch_bounds__(kPfThreads) void prefill_causal_kernel(const uint16_t *__restrict__ q,
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2))) void prefill_causal_kernel(const uint16_t *__restrict__ q,
                                                                     const uint16_t *__restrict__ k,
                                                                     const uint16_t *__restrict__ v,
                                                                     uint16_t *__restrict__ out, int Hq, int Hkv,
@@ -457,16 +458,20 @@ __global__ __launch_bounds__(kPfThreads) void prefill_causal_kernel(const uint16
         unsigned *counter = (unsigned *)ws + split_rb;
         unsigned char *slots = ws + kWsFlagBytes + split_rb * items.max_nc * SL::BYTES;
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(slots, (size_t)nc * SL::BYTES);
-        auto o_off = [&](int c, int db, int j) { return c * SL::BYTES + (((rw * NDB + db) * 16 + j) * 64 + lane) * 4; };
+        typedef __attribute__((ext_vector_type(4))) unsigned u4;
+        typedef __attribute__((ext_vector_type(2))) unsigned u2;
+        auto o_off = [&](int c, int db, int qd) { return c * SL::BYTES + (((rw * NDB + db) * 4 + qd) * 64 + lane) * 16; };
         auto ml_off = [&](int c) { return c * SL::BYTES + (SL::O_FLOATS + (rw * 64 + lane) * 2) * 4; };
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[db][j]), rs, o_off(chunk, db, j), 0, kSC1);
-        __builtin_amdgcn_raw_buffer_store_b64(
-            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, make_float2(m_run, l_part)), rs,
-            ml_off(chunk), 0, kSC1);
+            for (int qd = 0; qd < 4; ++qd)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u4, make_float4(acc[db][4 * qd], acc[db][4 * qd + 1], acc[db][4 * qd + 2],
+                                                       acc[db][4 * qd + 3])),
+                    rs, o_off(chunk, db, qd), 0, kSC1);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, make_float2(m_run, l_part)), rs, ml_off(chunk), 0,
+                                              kSC1);
         __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
         __syncthreads();                // ... and so have every other thread's
         __shared__ int s_last;
@@ -474,26 +479,48 @@ __global__ __launch_bounds__(kPfThreads) void prefill_causal_kernel(const uint16
             s_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == (unsigned)(nc - 1);
         __syncthreads();
         if (!s_last) return;
-        float m = -kInf;
-        for (int c = 0; c < nc; ++c) {
-            const float2 ml = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rs, ml_off(c), 0, kSC1));
-            m = fmaxf(m, ml.x);
-        }
+        // Combine the chunks in chunk order with a running maximum, two
+        // partials per round trip (this workgroup's own re-read like the
+        // others: its stores have completed).
+        float M = -kInf, Lsum = 0.0f;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int j = 0; j < 16; ++j) acc[db][j] = 0.0f;
-        l_part = 0.0f;
-        for (int c = 0; c < nc; ++c) {  // fixed order, own partial re-read like the others
+        auto load_part = [&](int c, float &mc, float &lc, f32x16_t (&oc)[NDB]) {
             const float2 ml = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rs, ml_off(c), 0, kSC1));
-            const float wc = ml.x == -kInf ? 0.0f : fast_exp2(aq * (ml.x - m));
-            l_part += wc * ml.y;
+            mc = ml.x;
+            lc = ml.y;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    acc[db][j] += wc * __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, o_off(c, db, j), 0, kSC1));
+                for (int qd = 0; qd < 4; ++qd) {
+                    const float4 x =
+                        __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, o_off(c, db, qd), 0, kSC1));
+                    oc[db][4 * qd] = x.x; oc[db][4 * qd + 1] = x.y; oc[db][4 * qd + 2] = x.z; oc[db][4 * qd + 3] = x.w;
+                }
+        };
+        auto fold = [&](float mc, float lc, const f32x16_t (&oc)[NDB]) {
+            const float Mn = fmaxf(M, mc);
+            const float wa = M == -kInf ? 0.0f : fast_exp2(aq * (M - Mn));
+            const float wb = mc == -kInf ? 0.0f : fast_exp2(aq * (mc - Mn));
+            M = Mn;
+            Lsum = Lsum * wa + lc * wb;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) acc[db][j] = acc[db][j] * wa + oc[db][j] * wb;
+        };
+        for (int c = 0; c < nc; c += 2) {
+            float m0, l0, m1 = -kInf, l1 = 0.0f;
+            f32x16_t o0[NDB], o1[NDB];
+            load_part(c, m0, l0, o0);
+            if (c + 1 < nc) load_part(c + 1, m1, l1, o1);
+            fold(m0, l0, o0);
+            if (c + 1 < nc) fold(m1, l1, o1);
         }
+        m_run = M;
+        l_part = Lsum;
         if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
 
@@ -524,12 +551,11 @@ static int pf_row_tiles(int rb, int Tq, int Tk)
 }
 
 // Chunking of the causal triangle.  The most key tiles per chunk, ch, is
-// the smallest value that gives about two workgroups' worth of tiles per
-// workgroup slot (4 per CU on 256 CUs), so that the scheduler can balance
-// the triangle, but at least 4 tiles (a chunk's partial costs a write and a
-// read), with the launch table's item count, the chunks per row block and
-// the split row blocks' counters within their limits.  Every limit is
-// monotone in ch and met once no row block is split.
+// the smallest value that gives about one workgroup per workgroup slot (the
+// items, issued longest first, then finish close together), but at least
+// kPfMinChunk tiles, with the launch table's item count, the chunks per row
+// block and the split row blocks' counters within their limits.  Every
+// limit is monotone in ch and met once no row block is split.
 struct PfPlan {
     int n_rb, ch, rb0, max_nc, n_items;
 };
@@ -563,7 +589,7 @@ static PfPlan pf_plan(int B, int Hq, int Tq, int Tk)
     long total = 0;
     for (int rb = 0; rb < n_rb; ++rb) total += pf_row_tiles(rb, Tq, Tk);
     total *= (long)B * Hq;
-    int lo = (int)std::min<long>(std::max(4L, (total + 2 * 1024 - 1) / (2 * 1024)), 1 << 30);
+    int lo = (int)std::min<long>(std::max((long)kPfMinChunk, (total + kPfSlots - 1) / kPfSlots), 1 << 30);
     int hi = std::max(lo, pf_row_tiles(n_rb - 1, Tq, Tk));  // no split: always fits
     if (pf_plan_fits(pf_plan_for(Tq, Tk, lo), B, Hq)) return pf_plan_for(Tq, Tk, lo);
     while (hi - lo > 1) {  // invariant: lo does not fit, hi does

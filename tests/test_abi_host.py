@@ -124,19 +124,16 @@ MIB16 = 16 << 20  # fixed flag region at the front of every workspace
 
 
 def test_prefill_workspace_size():
-    # The flag region, then one partial slot per chunk of every split row
-    # block.  B=2, 14 heads, T=4097: row block rb (< 32) sees 2(rb+1) key
-    # tiles of 64, the last one 65, 1121 tiles a head, 31388 in all; about
-    # two workgroups per slot (2048) gives chunks of at most 16 tiles, so
-    # row blocks 8..32 (25 of them) are split, the last into 5 chunks.
+    # The flag region, then one partial slot per possible chunk of every
+    # split row block.  B=2, 14 heads, T=4097: row block rb (< 32) sees
+    # 2(rb+1) key tiles of 64, the last one 65, 1121 tiles a head, 31388 in
+    # all; about one workgroup per slot (1024) gives chunks of at most 31
+    # tiles, so row blocks 15..32 (18 of them) are split, at most 3 ways.
     slot64 = (4 * 2 * 16 * 64 + 4 * 64 * 2) * 4
-    assert gqa.gqa_prefill_workspace_bytes(2, 14, 2, 64, 4097, 4097) == MIB16 + 2 * 14 * 25 * 5 * slot64
-    # nothing is split: the flag region alone
+    assert gqa.gqa_prefill_workspace_bytes(2, 14, 2, 64, 4097, 4097) == MIB16 + 2 * 14 * 18 * 3 * slot64
+    # nothing is split: the flag region alone (chunks hold at least 8 tiles)
     assert gqa.gqa_prefill_workspace_bytes(1, 14, 2, 64, 8, 8) == MIB16
-    # Tq=200, Tk=300: row blocks of 4 and 5 tiles, chunks of at most 4
-    # tiles, so the second row block is split in two
-    slot128 = (4 * 4 * 16 * 64 + 4 * 64 * 2) * 4
-    assert gqa.gqa_prefill_workspace_bytes(1, 14, 2, 128, 200, 300) == MIB16 + 14 * 2 * slot128
+    assert gqa.gqa_prefill_workspace_bytes(1, 14, 2, 128, 200, 300) == MIB16
     # a large batch fills the GPU without splitting
     assert gqa.gqa_prefill_workspace_bytes(64, 32, 8, 128, 2048, 2048) == MIB16
     # invalid sizes give 0
