@@ -6,27 +6,28 @@
 // aligned to the end of the keys (row i sees keys j <= i + Tk - Tq), and never
 // stores the score matrix.
 //
-// Work decomposition.  A workgroup owns 128 query rows of one query head and
-// has 8 waves.  The visible key tiles (64 keys each) are cut into NSPLIT
-// contiguous ranges ("splits"); each split is walked by the row-waves that
-// together cover the 128 rows (D = 64: 4 splits x 2 waves of 64 rows;
-// D = 128: 2 splits x 4 waves of 32 rows).  At the end every split but the
-// first hands its running (output, max, sum) to the first through LDS, which
-// merges, normalises and stores.  Splitting the keys shortens the longest
-// chain of dependent tiles (the last row block sees every key).
+// Work decomposition.  A workgroup has 4 waves and owns 128 query rows of
+// one query head (32 rows per wave) and a contiguous range ("chunk") of the
+// 64-key tiles those rows can see.  Short row blocks are one chunk; the long
+// ones near the end of the causal triangle are cut into chunks of at most
+// ch tiles, ch chosen so that the launch has about one workgroup per
+// workgroup slot of the device (4 per CU).  The host sorts the (row block,
+// chunk) items longest first into a table passed with the launch, so the
+// long items start first and the short ones fill in behind them.  The
+// chunks of a split row block meet through the workspace: each stores its
+// partial (output, max, sum) and takes a ticket from a counter; the last
+// to arrive merges all partials in chunk order, normalises and stores.
 //
-// Per tile, on v_mfma_f32_32x32x16 (bf16 or f16 inputs, fp32 sums), for each
-// 32-row block of a wave:
+// Per tile, on v_mfma_f32_32x32x16 (bf16 or f16 inputs, fp32 sums), each
+// wave computes for its 32 rows:
 //   S^T[key][row] = K Q^T          (A = K rows from LDS, B = Q rows in registers)
 //   online softmax per row in fp32 (exp2 with scale*log2(e) folded in; the
 //   reference max is only raised when a score exceeds it by more than 2^8)
 //   O^T[d][row] += V^T P^T         (A = V^T fragments from LDS, B = P in registers)
 // Computing S transposed makes its accumulator layout (a lane holds keys of
 // one row) exactly the layout the second product wants for P, so P never
-// leaves registers.  A wave with 64 rows uses every K and V fragment it reads
-// from LDS twice: the LDS bytes per matrix instruction are what limits a
-// wave (one wave reads LDS at about 20 bytes per clock), and 64-row waves
-// halve them.
+// leaves registers.  With four workgroups per CU each SIMD runs four waves,
+// so one wave's matrix instructions overlap other waves' exponentials.
 //
 // Data movement.  K and V tiles go from HBM straight into LDS with buffer
 // loads that write LDS (no staging registers), row-major, each row's 16-byte
@@ -35,15 +36,9 @@
 // reads; V^T fragments come from the transposing LDS read
 // (ds_read_b64_tr_b16), which hands each lane four 16-bit values of one
 // column from four consecutive rows.  Rows past Tk load as zeros (buffer
-// range check).  K runs one tile ahead of V, each double-buffered.
-//
-// Schedule.  Each wave alternates a V phase (next tiles' loads issued;
-// softmax of the current tile in place) and an M phase (P to 16 bits; the
-// P V^T product; S^T of the next tile), one workgroup barrier after each
-// phase.  The splits of the second half of the workgroup run one phase
-// behind the first half, so on each SIMD one wave issues matrix instructions
-// while the other runs the exponentials.  Only tiles that cross the diagonal
-// are masked.  Workgroups are issued longest-row-block first.
+// range check).  K and V are double-buffered: the loads of tile t+1 run
+// while tile t is computed, and one barrier per tile hands the buffers
+// over.  Only tiles that cross the diagonal are masked.
 
 #include <algorithm>
 #include <type_traits>
@@ -120,7 +115,7 @@ constexpr int kPfBM = 128;       // query rows per workgroup: 4 row-waves of 32 
 constexpr int kPfBN = 64;        // keys per tile
 constexpr int kPfThreads = 256;  // 4 waves
 constexpr int kPfMaxItems = 1024;     // (row block, key chunk) work items in the launch table
-constexpr int kPfSlots = 4 * 256;     // workgroup slots: 4 workgroups on each of the 256 CUs (D = 64)
+constexpr int kPfCUs = 256;           // compute units of the gfx950 parts
 constexpr int kPfMinChunk = 8;        // fewest key tiles per chunk: a chunk's partial costs a write and a read
 
 // The launch's work items, longest first: entry r is (row block << 6) |
@@ -551,8 +546,9 @@ static int pf_row_tiles(int rb, int Tq, int Tk)
 }
 
 // Chunking of the causal triangle.  The most key tiles per chunk, ch, is
-// the smallest value that gives about one workgroup per workgroup slot (the
-// items, issued longest first, then finish close together), but at least
+// the smallest value that gives about one slot's share of the tiles per
+// chunk (4 workgroup slots per CU for D = 64, 2 for D = 128; the items,
+// issued longest first, then finish close together), but at least
 // kPfMinChunk tiles, with the launch table's item count, the chunks per row
 // block and the split row blocks' counters within their limits.  Every
 // limit is monotone in ch and met once no row block is split.
@@ -583,13 +579,14 @@ static bool pf_plan_fits(const PfPlan &p, int B, int Hq)
            (size_t)B * Hq * (p.n_rb - p.rb0) * 4 <= kWsFlagBytes;
 }
 
-static PfPlan pf_plan(int B, int Hq, int Tq, int Tk)
+static PfPlan pf_plan(int B, int Hq, int D, int Tq, int Tk)
 {
+    const long slots = (long)(D == 64 ? 4 : 2) * kPfCUs;  // resident workgroups (VGPR budget)
     const int n_rb = (Tq + kPfBM - 1) / kPfBM;
     long total = 0;
     for (int rb = 0; rb < n_rb; ++rb) total += pf_row_tiles(rb, Tq, Tk);
     total *= (long)B * Hq;
-    int lo = (int)std::min<long>(std::max((long)kPfMinChunk, (total + kPfSlots - 1) / kPfSlots), 1 << 30);
+    int lo = (int)std::min<long>(std::max((long)kPfMinChunk, (total + slots - 1) / slots), 1 << 30);
     int hi = std::max(lo, pf_row_tiles(n_rb - 1, Tq, Tk));  // no split: always fits
     if (pf_plan_fits(pf_plan_for(Tq, Tk, lo), B, Hq)) return pf_plan_for(Tq, Tk, lo);
     while (hi - lo > 1) {  // invariant: lo does not fit, hi does
@@ -623,7 +620,7 @@ static void pf_items(const PfPlan &p, int Tq, int Tk, PfItems *it)
 // Flag region, then one partial slot per chunk of every split row block.
 size_t prefill_workspace_bytes(int B, int Hq, int D, int Tq, int Tk)
 {
-    const PfPlan p = pf_plan(B, Hq, Tq, Tk);
+    const PfPlan p = pf_plan(B, Hq, D, Tq, Tk);
     const size_t slot = D == 64 ? PfSlot<64>::BYTES : PfSlot<128>::BYTES;
     const size_t split_cols = (size_t)B * Hq * (p.n_rb - p.rb0);
     return kWsFlagBytes + (p.max_nc > 1 ? split_cols * p.max_nc * slot : 0);
@@ -633,7 +630,7 @@ template <typename T, int D>
 static hipError_t launch_pf(const void *q, const void *k, const void *v, void *out, int B, int Hq, int Hkv,
                             int Tq, int Tk, int s_cap, float scale, void *ws, hipStream_t s)
 {
-    const PfPlan plan = pf_plan(B, Hq, Tq, Tk);
+    const PfPlan plan = pf_plan(B, Hq, D, Tq, Tk);
     PfItems items;
     pf_items(plan, Tq, Tk, &items);
     // A zero scale (uniform weights over the visible keys) is run as the
