@@ -42,6 +42,8 @@ BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 matrix peak (256 CU x 2.4 GHz
 PAGES_M2_US_PER_LAYER_7B_S4096 = 264.82  # Apple M2 fused Metal SDPA (context only)
 DECODE_SRCS = [os.path.join(ROOT, "prefill_split_gqa_amd", "csrc", f) for f in ("decode.hip", "common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_7b_s4096_traffic.txt")
+PREFILL_SRCS = [os.path.join(ROOT, "prefill_split_gqa_amd", "csrc", f) for f in ("prefill.hip", "common.h")]
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_0p5b_t4097_traffic.txt")
 
 
 def decode_bytes(S: int, Hq: int = 28, Hkv: int = 4, D: int = 128, elem: int = 4) -> int:
@@ -65,17 +67,17 @@ def source_digest(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per decode launch from the committed counter summary, or None
-    when it is missing or was taken on a different kernel source."""
+def read_traffic(path=TRAFFIC_FILE, key="decode_source_sha256_16", srcs=DECODE_SRCS):
+    """HBM bytes per launch from a committed counter summary, or None when it
+    is missing or was taken on a different kernel source."""
     try:
         kv = {}
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             for ln in f:
                 if ":" in ln and not ln.startswith("#"):
                     a, b = ln.split(":", 1)
                     kv[a.strip()] = b.strip()
-        if kv.get("decode_source_sha256_16") != source_digest(DECODE_SRCS):
+        if kv.get(key) != source_digest(srcs):
             return None
         return float(kv["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -283,7 +285,9 @@ def main():
                 "us": round(us, 2), "TFLOPs": round(tf, 2), "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
                 "roofline": {"bound": "mfma", "kernel": "prefill_causal_kernel<bf16_t,64,false>",
                              "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                             "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                             "traffic": read_traffic(PREFILL_TRAFFIC_FILE, "prefill_source_sha256_16",
+                                                     PREFILL_SRCS) if T == 4097 else None,
                              "algorithmic_flop_per_launch": p["flops"], "launch_duration_us": round(us, 2)},
                 "parity_ok": p["gate_ok"], "parity_max_abs": p["gate_max_abs"]}
     if secondary:
