@@ -117,6 +117,7 @@ constexpr int kPfThreads = 256;  // 4 waves
 constexpr int kPfMaxItems = 1024;     // (row block, key chunk) work items in the launch table
 constexpr int kPfCUs = 256;           // compute units of the gfx950 parts
 constexpr int kPfMinChunk = 8;        // fewest key tiles per chunk: a chunk's partial costs a write and a read
+constexpr float kPfSumLimit = 1024.0f;  // a lane's probability sum that needs the exact path
 
 // The launch's work items, longest first: entry r is (row block << 6) |
 // chunk; grid block x runs item x / (B * Hq) for request and head
@@ -190,19 +191,20 @@ template <int D> __device__ __forceinline__ int tile_off(int row, int chunk)
     return (row >> 3) * L::GROUP + (row & 7) * L::ROW + ((chunk ^ swz(row & 7)) << 4);
 }
 
-// Softmax part of one 64-key tile for one 32-row block, in place.
+// Reference maximum of one 64-key tile for one 32-row block.
 //
 // st holds S^T (raw q.k) in the accumulator layout: lane (ln, lg) has, for
 // sub-tile u and register j, key 32u + 8(j/4) + 4lg + (j%4) of the tile, row
 // ln.  Masked keys already hold sigma*(-inf), sigma the sign of the scale.
 // The running maximum m_run is kept over the oriented raw scores sigma*s, so
 // that one fused multiply-add per score gives the log2-domain exponent
-// exp2(s*qs - |qs|*m_run).  m_run is raised only when a tile's maximum
+// exp2(s*qs - |qs|*m_run).  m_run is raised only when the tile's maximum
 // exceeds it by more than thr (2^8 in the exponent); the running output and
-// sum are rescaled then.  On return st holds the probabilities (fp32).
+// sum are rescaled then.  Returns the exponent offset -|qs|*m_run (0 for a
+// row that has seen no visible key yet, whose probabilities are then 0).
 template <bool NEG, int NDB>
-__device__ __forceinline__ void softmax_inplace(f32x16_t (&st)[2], f32x16_t (&acc)[NDB], float &m_run,
-                                                float &l_part, float qs, float thr)
+__device__ __forceinline__ float softmax_max(const f32x16_t (&st)[2], f32x16_t (&acc)[NDB], float &m_run,
+                                             float &l_part, float qs, float thr)
 {
     constexpr float kInf = __builtin_huge_valf();
     float tmax = -kInf;
@@ -224,12 +226,7 @@ __device__ __forceinline__ void softmax_inplace(f32x16_t (&st)[2], f32x16_t (&ac
 #pragma unroll
             for (int j = 0; j < 16; ++j) acc[db][j] *= al;
     }
-    // a row that has seen no visible key yet (all -inf so far) gets p = 0
-    const float mq = m_run == -kInf ? 0.0f : -fabsf(qs) * m_run;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) st[u][j] = fast_exp2(__builtin_fmaf(st[u][j], qs, mq));
+    return m_run == -kInf ? 0.0f : -fabsf(qs) * m_run;
 }
 
 template <typename T, int D, bool NEG>
@@ -376,10 +373,9 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D ==
     // crossing the diagonal), online softmax, O^T += V^T P^T.  Fragments are
     // read from LDS as they are needed; the waves of the other workgroups on
     // the CU (four workgroups per CU for D = 64) hide the latency.
-    auto tile_step = [&](int kt, int buf) {
-        const unsigned char *Kt = smem + buf * L::TILE;
-        const unsigned char *Vt = smem + (2 + buf) * L::TILE;
-        f32x16_t st[2];
+    // S^T of tile kt from K buffer Kt, masked where the tile crosses the
+    // diagonal.
+    auto scores = [&](const unsigned char *Kt, int kt, f32x16_t (&st)[2]) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
 #pragma unroll
@@ -398,26 +394,60 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D ==
                 for (int j = 0; j < 16; ++j)
                     if (key0 + 32 * u + 8 * (j >> 2) + (j & 3) > my_lim) st[u][j] = NEG ? kInf : -kInf;
         }
-        softmax_inplace<NEG>(st, acc, m_run, l_part, qscale, thr);
-        // P to 16 bits (one vector conversion) and its row sums (independent
-        // partial sums); O^T += V^T P^T in four 16-key k-blocks
+    };
+    // Probabilities exp2(s*qs + mq), rounded to 16 bits in four 16-key
+    // blocks (one vector conversion each), and this lane's sum of the
+    // rounded values (independent partial sums).
+    auto probs = [&](f32x16_t (&st)[2], float mq, uint4 (&pb)[4]) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) st[u][j] = fast_exp2(__builtin_fmaf(st[u][j], qscale, mq));
         float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int u = t >> 1, hh = t & 1;
             f32x8_t x;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = st[u][8 * hh + i];
-            const uint4 pb = Ops::pack8(x);
-            lsum[0] = Ops::sum2(pb.x, lsum[0]);
-            lsum[1] = Ops::sum2(pb.y, lsum[1]);
-            lsum[2] = Ops::sum2(pb.z, lsum[2]);
-            lsum[3] = Ops::sum2(pb.w, lsum[3]);
+            for (int i = 0; i < 8; ++i) x[i] = st[t >> 1][8 * (t & 1) + i];
+            pb[t] = Ops::pack8(x);
+            lsum[0] = Ops::sum2(pb[t].x, lsum[0]);
+            lsum[1] = Ops::sum2(pb[t].y, lsum[1]);
+            lsum[2] = Ops::sum2(pb[t].z, lsum[2]);
+            lsum[3] = Ops::sum2(pb[t].w, lsum[3]);
+        }
+        return (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    };
+    // One tile of the wave's 32 rows from buffer buf.  Once every row has a
+    // reference maximum, the probabilities are taken against it directly,
+    // without the tile's maximum: the lane's sum of them bounds each one, so
+    // a sum at most kPfSumLimit proves none exceeds it.  Otherwise (the
+    // first tile, or scores that outgrew the reference) the tile's scores are
+    // formed again from LDS and go through the exact path: maximum, lazy
+    // rescale, probabilities.  P V is issued after the test.
+    auto tile_step = [&](int kt, int buf) {
+        const unsigned char *Kt = smem + buf * L::TILE;
+        const unsigned char *Vt = smem + (2 + buf) * L::TILE;
+        f32x16_t st[2];
+        scores(Kt, kt, st);
+        uint4 pb[4];
+        float lt = 0.0f;
+        bool exact = __any(m_run == -kInf);
+        if (!exact) {
+            lt = probs(st, -aq * m_run, pb);
+            exact = __any(lt > kPfSumLimit);
+            if (exact) scores(Kt, kt, st);
+        }
+        if (exact) {
+            const float mq = softmax_max<NEG>(st, acc, m_run, l_part, qscale, thr);
+            lt = probs(st, mq, pb);
+        }
+        l_part += lt;
+        // O^T += V^T P^T in four 16-key k-blocks
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
-                acc[db] = Ops::mfma(as_vec<vec>(v_frag(Vt, t, db)), as_vec<vec>(pb), acc[db]);
-        }
-        l_part += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+                acc[db] = Ops::mfma(as_vec<vec>(v_frag(Vt, t, db)), as_vec<vec>(pb[t]), acc[db]);
     };
 
     // Step s: the loads of tile t+1 go to the buffer that step s-1 read

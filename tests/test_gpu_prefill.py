@@ -102,12 +102,18 @@ def test_prefill_small_ragged(gpu_lib, dtype):
         assert_close(got, want, 2e-2, "Tq=%d Tk=%d" % (Tq, Tk))
 
 
-def test_prefill_large_scores(gpu_lib):
-    # scores spread far beyond the lazy-rescale threshold: the running max
-    # must be raised (rows with strongly increasing scores along the keys)
+@pytest.mark.parametrize("div", [20.0, 50.0, -20.0])
+def test_prefill_large_scores(gpu_lib, div):
+    # Scores that grow along the keys: at scale 1/8 they rise by 369/div
+    # log2 units per 64-key tile.  div=20: each tile outgrows the reference
+    # maximum by far more than 2^8, so it is raised every tile.  div=50: ~7.4
+    # units per tile, so a lane's probability sum passes the test limit
+    # (the tile is formed again) while the maximum is raised only every
+    # other tile.  div=-20: falling scores, the reference from the first
+    # tile serves every later one.
     T, D = 300, 64
     q = torch.ones(1, 2, T, D) * 0.5
-    k = (torch.arange(T, dtype=torch.float32)[:, None] / 20.0).expand(T, D).reshape(1, 1, T, D).contiguous()
+    k = (torch.arange(T, dtype=torch.float32)[:, None] / div).expand(T, D).reshape(1, 1, T, D).contiguous()
     v = torch.randn(1, 1, T, D)
     q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
     got = run_prefill(gpu_lib, q, k, v)
