@@ -11,7 +11,11 @@ value is microseconds per layer (lower is better).
 Secondary metric: causal prefill attention with Qwen2.5-0.5B heads (14 / 2,
 dim 64), bf16, T = 4097, one step = 24 layers (that model's depth) captured
 in a HIP graph, reported per layer as TFLOP/s and as a fraction of the bf16
-matrix-core peak.
+matrix-core peak.  The other configurations of the workload set (decode at
+KV length 128 with 0.5B heads, batched bf16 decode with Qwen3-4B heads at
+B = 1, 2, 4, 8, 4-bit decode at KV length 2048 and 16384, and the chunked
+prefill of 256 queries at offset 3841) are reported the same way, each
+behind its own parity gate (skip them with --no-extra).
 
 Protocol: inputs are generated on the host from fixed seeds and copied to
 HBM before anything is timed; a parity gate compares sampled outputs with
@@ -58,6 +62,12 @@ def prefill_flops(Tq: int, Tk: int, Hq: int = 14, D: int = 64) -> int:
     off = Tk - Tq
     pairs = sum(min(i + off + 1, Tk) for i in range(Tq))
     return 4 * D * Hq * pairs
+
+
+def decode_bytes_generic(B, Hq, Hkv, D, lens, elem):
+    """Algorithmic bytes of one decode launch: each request's valid K and V
+    rows read once, its queries read and outputs written once."""
+    return sum(2 * n * Hkv * D * elem for n in lens) + 2 * B * Hq * D * elem
 
 
 def source_digest(paths) -> str:
@@ -200,6 +210,162 @@ def bench_prefill(torch, gqa, oracle, W, T, steps, warmup, flush, layers=24, n_c
             "flops": prefill_flops(T, T)}
 
 
+def graph_of(torch, eager):
+    """Capture eager() (every launch of one step) once in a HIP graph."""
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        eager()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=st):
+            eager()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    return g
+
+
+def hbm_entry(us, nbytes, gate_ok, gate_max_abs, kernel, **extra):
+    """A secondary result for an HBM-bound configuration."""
+    gbs = nbytes / (us * 1e-6) / 1e9
+    d = {"us_layer": round(us, 3), "GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                      "algorithmic_bytes_per_launch": nbytes, "launch_duration_us": round(us, 3)},
+         "parity_ok": gate_ok, "parity_max_abs": gate_max_abs}
+    d.update(extra)
+    return d
+
+
+def bench_extra(torch, gqa, oracle, W, steps, warmup, flush):
+    """The other configurations of the workload set, each timed like the
+    headline (per-layer inputs of their own, cache flushed before each step,
+    one step captured in a HIP graph) after a parity gate on layer 0 against
+    the oracle; layers past the first are device copies of it, scaled (codes
+    permuted for the 4-bit cache), so that every layer reads its own memory."""
+    out = {}
+
+    # decode, Qwen2.5-0.5B heads, KV length 128, fp32; 28 layers per step
+    # (one launch alone would be mostly the graph's own launch cost)
+    w = W.by_name("decode_0p5b")
+    q, k, v = W.decode_inputs(w, 128, 0)
+    d0 = (q.cuda(), k.cuda(), v.cuda())
+    dev = [d0] + [tuple((x * (1.0 + l / 64.0)).contiguous() for x in d0) for l in range(1, 28)]
+    outs = [torch.empty_like(d0[0]) for _ in dev]
+    ws = gqa.make_workspace(1, w.Hq, w.Hkv, w.D, 128)
+
+    def eager_small():
+        for (qq, kk, vv), oo in zip(dev, outs):
+            gqa.gqa_decode_attend(qq, kk, vv, oo, 128, ws)
+
+    eager_small()
+    torch.cuda.synchronize()
+    err = float(np.abs(outs[0].cpu().double().numpy() - oracle.attend(q, k, v)).max())
+    ref = [t.clone() for t in outs]
+    g = graph_of(torch, eager_small)
+    us = float(np.median(time_steps(torch, g.replay, steps, warmup, flush))) * 1e3 / len(dev)
+    ok = err <= 2e-5 and all(torch.equal(a, b) for a, b in zip(outs, ref))
+    out["decode_0p5b_s128"] = hbm_entry(us, decode_bytes_generic(1, w.Hq, w.Hkv, w.D, [128], 4), ok, err,
+                                        "decode_splitk_kernel<DenseKV<float,64>,float,64,7>",
+                                        layers_per_step=len(dev))
+
+    # batched decode, Qwen3-4B heads, bf16, per-request lengths, 36 layers
+    w = W.by_name("batched_qwen3_4b")
+    for B in (1, 2, 4, 8):
+        q, k, v, lens = W.batched_inputs(w, B, 0)
+        d0 = (q.cuda(), k.cuda(), v.cuda())
+        dev = [d0] + [tuple((x * (1.0 + l / 64.0)).contiguous() for x in d0) for l in range(1, w.layers)]
+        outs = [torch.empty_like(d0[0]) for _ in dev]
+        lens_d = torch.as_tensor(lens.astype(np.int32)).cuda()
+        ws = gqa.make_workspace(B, w.Hq, w.Hkv, w.D, w.s_cap)
+
+        def eager(dev=dev, outs=outs, lens_d=lens_d, ws=ws):
+            for (qq, kk, vv), oo in zip(dev, outs):
+                gqa.gqa_decode_attend_batched(qq, kk, vv, oo, lens_d, ws)
+
+        eager()
+        torch.cuda.synchronize()
+        err = float(np.abs(outs[0].float().cpu().double().numpy() - oracle.attend(q, k, v, kv_lens=lens)).max())
+        ref = [x.clone() for x in outs]
+        g = graph_of(torch, eager)
+        us = float(np.median(time_steps(torch, g.replay, steps, warmup, flush))) * 1e3 / w.layers
+        ok = err <= 2e-2 and all(torch.equal(a, b) for a, b in zip(outs, ref))
+        out["batched_qwen3_4b_B%d" % B] = hbm_entry(
+            us, decode_bytes_generic(B, w.Hq, w.Hkv, w.D, [int(x) for x in lens], 2), ok, err,
+            "decode_splitk_kernel<DenseKV<bf16_t,128>,bf16_t,128,4>", layers_per_step=w.layers,
+            kv_lens=[int(x) for x in lens])
+        del dev, outs, ref, g
+        torch.cuda.empty_cache()
+
+    # 4-bit decode, 64 query / 8 KV heads, group 64, f16 queries, 80 layers
+    w = W.by_name("q4_decode")
+    names = ("k_codes", "k_scales", "k_biases", "v_codes", "v_scales", "v_biases")
+    for S in (2048, 16384):
+        x = W.q4_inputs(w, S, 0)
+        d0 = {n: t.cuda() for n, t in x.items()}
+        dev = [d0]
+        for l in range(1, w.layers):
+            dl = {"q": (d0["q"] * (1.0 + l / 64.0)).contiguous()}
+            for n in names:
+                t = d0[n]
+                dl[n] = (t ^ (l & 0xFF)) if t.dtype == torch.uint8 else (t * (1.0 + l / 64.0)).contiguous()
+            dev.append(dl)
+        outs = [torch.empty_like(d0["q"]) for _ in dev]
+        ws = gqa.make_workspace(1, w.Hq, w.Hkv, w.D, S)
+
+        def eager(dev=dev, outs=outs, ws=ws, S=S):
+            for dl, oo in zip(dev, outs):
+                gqa.gqa_decode_attend_q4(dl["q"], *(dl[n] for n in names), oo, w.group, S, ws)
+
+        eager()
+        torch.cuda.synchronize()
+        want = oracle.q4_attend(x["q"], *(x[n] for n in names), w.group)
+        err = float(np.abs(outs[0].float().cpu().double().numpy() - want).max())
+        ref = [t.clone() for t in outs]
+        g = graph_of(torch, eager)
+        us = float(np.median(time_steps(torch, g.replay, steps, warmup, flush))) * 1e3 / w.layers
+        ok = err <= 2e-2 and all(torch.equal(a, b) for a, b in zip(outs, ref))
+        nbytes = S * w.Hkv * 2 * (w.D // 2 + 2 * 2 * (w.D // w.group)) + 2 * w.Hq * w.D * 2
+        out["q4_decode_s%d" % S] = hbm_entry(us, nbytes, ok, err, "decode_splitk_kernel<Q4KV<128>,f16_t,128,8>",
+                                             layers_per_step=w.layers)
+        del dev, outs, ref, g
+        torch.cuda.empty_cache()
+
+    # chunked prefill: the last 256 queries of T=4097 against all 4097 keys, 24 layers
+    w = W.by_name("prefill_0p5b")
+    q, k, v = W.prefill_inputs(w, 4097)
+    qc = q[:, :, 4097 - 256:].contiguous()
+    d0 = (qc.cuda(), k.cuda(), v.cuda())
+    dev = [d0] + [tuple((x * (1.0 + l / 64.0)).contiguous() for x in d0) for l in range(1, 24)]
+    outs = [torch.empty_like(d0[0]) for _ in dev]
+    ws = gqa.make_prefill_workspace(1, w.Hq, w.Hkv, w.D, 256, 4097)
+
+    def eager_pf():
+        for (qq, kk, vv), oo in zip(dev, outs):
+            gqa.gqa_prefill_causal(qq, kk, vv, oo, ws)
+
+    eager_pf()
+    torch.cuda.synchronize()
+    rows = sorted(set([0, 1, 255] + list(np.random.default_rng(256).integers(0, 256, 13))))
+    err = 0.0
+    for i in rows:  # chunk row i sees keys 0 .. 3841 + i
+        want = oracle.attend(qc[:, :, i:i + 1], k[:, :, :3842 + i], v[:, :, :3842 + i], scale=w.scale())
+        err = max(err, float(np.abs(outs[0][:, :, i:i + 1].float().cpu().double().numpy() - want).max()))
+    ref = [t.clone() for t in outs]
+    g = graph_of(torch, eager_pf)
+    us = float(np.median(time_steps(torch, g.replay, steps, warmup, flush))) * 1e3 / len(dev)
+    flops = prefill_flops(256, 4097)
+    tf = flops / (us * 1e-6) / 1e12
+    out["prefill_0p5b_chunk256_at3841"] = {
+        "us": round(us, 2), "layers_per_step": len(dev), "TFLOPs": round(tf, 2),
+        "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": "prefill_causal_kernel<bf16_t,64,false>", "achieved": round(tf, 1),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flop_per_launch": flops, "launch_duration_us": round(us, 2)},
+        "parity_ok": err <= 2e-2 and all(torch.equal(a, b) for a, b in zip(outs, ref)), "parity_max_abs": err}
+    return out
+
+
 def cpu_baseline(oracle, host, scale, seconds):
     """Time the oracle, as it stands, on the host cores over whole layers of
     the headline workload until about `seconds` have elapsed."""
@@ -226,6 +392,8 @@ def main():
     ap.add_argument("--S", type=int, default=4096, help="KV length of the headline decode workload")
     ap.add_argument("--sweep", action="store_true", help="also time KV lengths 128..2048 and the other prefill sizes")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other configurations (decode S=128, batched, 4-bit, chunked prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
@@ -317,6 +485,8 @@ def main():
                                                      PREFILL_SRCS) if T == 4097 else None,
                              "algorithmic_flop_per_launch": p["flops"], "launch_duration_us": round(us, 2)},
                 "parity_ok": p["gate_ok"], "parity_max_abs": p["gate_max_abs"]}
+    if not args.no_extra:
+        secondary.update(bench_extra(torch, gqa, oracle, W, max(5, args.steps // 2), 2, flush))
     if secondary:
         result["secondary"] = secondary
 
