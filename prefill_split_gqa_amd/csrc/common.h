@@ -109,6 +109,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, si
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
 }
 
+// Buffer loads that write LDS (buffer_load_... lds): lane l's data at byte
+// offset voff goes to LDS address lds_base + 16*l (16-byte loads) or
+// lds_base + 4*l (16-bit loads, zero-extended to a dword); an offset outside
+// the descriptor's range writes zeros (the whole offset is in the vector
+// register, where the range check applies, per dword).  They are issued from
+// inline assembly so that the compiler does not treat them as pending LDS
+// stores (it would otherwise wait for every one of them at each workgroup
+// barrier); the kernels wait for them themselves (s_waitcnt vmcnt) before
+// the data is read.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+struct BufDesc { u32x4_t w; };
+
+__device__ __forceinline__ BufDesc buf_desc(const void *base, size_t bytes)
+{
+    const unsigned long long a = (unsigned long long)(uintptr_t)base;
+    BufDesc d;
+    d.w[0] = __builtin_amdgcn_readfirstlane((unsigned)a);
+    d.w[1] = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32)) & 0xFFFFu;  // stride 0
+    d.w[2] = __builtin_amdgcn_readfirstlane((unsigned)bytes);
+    d.w[3] = kRsrcWord3;
+    return d;
+}
+
+__device__ __forceinline__ void lds_load16(const BufDesc &d, unsigned lds_base, int voff)
+{
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(d.w), "{m0}"(lds_base) : "memory");
+}
+
+__device__ __forceinline__ void lds_load_u16(const BufDesc &d, unsigned lds_base, int voff)
+{
+    asm volatile("buffer_load_ushort %0, %1, 0 offen lds" ::"v"(voff), "s"(d.w), "{m0}"(lds_base) : "memory");
+}
+
 // ---------------------------------------------------------------------------
 // Decode split plan.  The host sizes the workspace and the grid from it and
 // the kernel derives every index from the same numbers, so a request's split

@@ -132,65 +132,6 @@ struct DenseKV {
     __device__ __forceinline__ static void unpack_q(const QRaw &r, float *x) { unpack(r, x); }
 };
 
-// 4-bit group-affine K/V rows: D/2 bytes of codes plus D/group f16 scales and
-// biases.  Lane lr owns the D/32 consecutive elements starting at lr*D/32.
-template <int D>
-struct Q4KV {
-    static constexpr int EPL = D / kDecodeLPR;
-    static constexpr int CB = EPL / 2;  // code bytes per lane (2 or 1)
-    struct Raw { uint32_t codes; uint32_t scale; uint32_t bias; };
-
-    __device__ __forceinline__ static int dim(int lr, int e) { return lr * EPL + e; }
-
-    struct Src {
-        __amdgpu_buffer_rsrc_t codes, scales, biases;  // rows [0, end)
-        int n_groups;      // D / group
-        int lane_group;    // group index of this lane's elements
-    };
-    __device__ __forceinline__ static Src make_src(const DecodeArgs &a, bool is_v, size_t head_row0, int end, int lr)
-    {
-        Src r;
-        r.n_groups = D / a.group;
-        r.lane_group = (lr * EPL) / a.group;
-        r.codes = make_rsrc((const uint8_t *)(is_v ? a.v : a.k) + head_row0 * (D / 2), (size_t)end * (D / 2));
-        r.scales = make_rsrc((const uint16_t *)(is_v ? a.v_scales : a.k_scales) + head_row0 * r.n_groups,
-                             (size_t)end * r.n_groups * 2);
-        r.biases = make_rsrc((const uint16_t *)(is_v ? a.v_biases : a.k_biases) + head_row0 * r.n_groups,
-                             (size_t)end * r.n_groups * 2);
-        return r;
-    }
-
-    __device__ __forceinline__ static void load(Raw &r, const Src &s, int row, int lr)
-    {
-        const int off = row * (D / 2) + lr * CB;
-        if constexpr (CB == 2) r.codes = __builtin_amdgcn_raw_buffer_load_b16(s.codes, off, 0, 0);
-        else r.codes = __builtin_amdgcn_raw_buffer_load_b8(s.codes, off, 0, 0);
-        const int goff = (row * s.n_groups + s.lane_group) * 2;
-        r.scale = __builtin_amdgcn_raw_buffer_load_b16(s.scales, goff, 0, 0);
-        r.bias = __builtin_amdgcn_raw_buffer_load_b16(s.biases, goff, 0, 0);
-    }
-    // f16 query: the lane's D/32 consecutive elements, from the staged rows
-    struct QRaw { uint32_t w[EPL / 2]; };
-    __device__ __forceinline__ static void load_q_lds(QRaw &r, const uint32_t *sq, int h, int lr)
-    {
-        const uint32_t *p = sq + (h * D + lr * EPL) / 2;
-#pragma unroll
-        for (int w = 0; w < EPL / 2; ++w) r.w[w] = p[w];
-    }
-    __device__ __forceinline__ static void unpack_q(const QRaw &r, float *x)
-    {
-#pragma unroll
-        for (int i = 0; i < EPL / 2; ++i) Unpack<f16_t>::run(r.w[i], x + 2 * i);
-    }
-    __device__ __forceinline__ static void unpack(const Raw &r, float *x)
-    {
-        const float sc = f16_bits_to_f32(r.scale & 0xFFFFu);
-        const float bi = f16_bits_to_f32(r.bias & 0xFFFFu);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) x[e] = q4_dequant_value(sc, bi, (r.codes >> (4 * e)) & 0xFu);
-    }
-};
-
 // Output stores of 4 consecutive elements.
 __device__ __forceinline__ void store4(float *p, float a, float b, float c, float d)
 {
@@ -253,6 +194,60 @@ struct DecodeGrid {
 
 template <typename TQ, int D, int GT>
 __device__ void merge_role(const DecodeArgs &a, int m);
+
+// End of a streaming workgroup.  so [waves][GT][D], sm and sl [waves][GT]
+// hold, per wave and query head, the unnormalised output row, its reference
+// maximum (log2 domain; -inf for a wave that saw no row) and its sum of
+// weights.  The waves are combined; with a single split the output is
+// written, otherwise the split's partial is published with device-scope
+// stores: outputs first, then (after they have completed) the (max, sum)
+// word that flags them.
+template <typename TQ, int D, int GT>
+__device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *so, const float *sm, const float *sl,
+                                             int col, int s, int n_split, TQ *out)
+{
+    constexpr int NW = kDecodeThreads / 64;
+    constexpr int NQ = GT * D / 4;  // 4-wide output items
+    const DecodePlan &P = a.plan;
+    const int tid = threadIdx.x;
+    const int qh = tid / (D / 4), qd = (tid % (D / 4)) * 4;
+    float Mw = kNegInf, Lw = 0.0f, O0 = 0.0f, O1 = 0.0f, O2 = 0.0f, O3 = 0.0f;
+    if (tid < NQ) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) Mw = fmaxf(Mw, sm[w * GT + qh]);
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float wt = rel_weight(sm[w * GT + qh], Mw);
+            const float4 x = *(const float4 *)&so[(w * GT + qh) * D + qd];
+            Lw += wt * sl[w * GT + qh];
+            O0 += wt * x.x; O1 += wt * x.y; O2 += wt * x.z; O3 += wt * x.w;
+        }
+    }
+    if (n_split == 1) {
+        if (tid < NQ) store4(out + (size_t)qh * D + qd, O0 / Lw, O1 / Lw, O2 / Lw, O3 / Lw);
+        return;
+    }
+    const __amdgpu_buffer_rsrc_t ws_o =
+        __builtin_amdgcn_make_buffer_rsrc(a.part_o, 0, (int)P.o_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t ws_ml =
+        __builtin_amdgcn_make_buffer_rsrc(a.part_ml, 0, (int)P.ml_bytes, kRsrcWord3);
+    const size_t colbase = (size_t)col * P.n_split_max;
+    if (tid < NQ) {
+        const int off_o = (int)((((colbase + s) * GT + qh) * D + qd) * 4);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, make_float4(O0, O1, O2, O3)), ws_o,
+            off_o, 0, kSC1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's output stores have completed
+    __syncthreads();                // ... and so have every other wave's
+    if (tid < NQ && qd == 0) {
+        const int off_ml = (int)(((colbase + s) * GT + qh) * 2 * 4);
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, make_float2(Mw, Lw)), ws_ml, off_ml, 0,
+            kSC1);
+    }
+}
 
 template <class KV, typename TQ, int D, int GT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArgs a, DecodeGrid grid)
@@ -440,48 +435,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
     }
     __syncthreads();
 
-    // ---- workgroup partial: 4 consecutive dims per item ----
-    const int col = b * P.HT + ht;
-    const int qh = tid / (D / 4), qd = (tid % (D / 4)) * 4;
-    float Mw = kNegInf, Lw = 0.0f, O0 = 0.0f, O1 = 0.0f, O2 = 0.0f, O3 = 0.0f;
-    if (tid < NQ) {
-#pragma unroll
-        for (int w = 0; w < NW; ++w) Mw = fmaxf(Mw, sm[w][qh]);
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const float wt = rel_weight(sm[w][qh], Mw);
-            const float4 x = *(const float4 *)&so[w][qh][qd];
-            Lw += wt * sl[w][qh];
-            O0 += wt * x.x; O1 += wt * x.y; O2 += wt * x.z; O3 += wt * x.w;
-        }
-    }
-    if (n_split == 1) {
-        if (tid < NQ) store4(out + (size_t)qh * D + qd, O0 / Lw, O1 / Lw, O2 / Lw, O3 / Lw);
-        return;
-    }
-
-    // ---- publish the partial with device-scope stores: outputs first, then
-    //      (after they have completed) the (max, sum) word that flags them ----
-    const __amdgpu_buffer_rsrc_t ws_o =
-        __builtin_amdgcn_make_buffer_rsrc(a.part_o, 0, (int)P.o_bytes, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t ws_ml =
-        __builtin_amdgcn_make_buffer_rsrc(a.part_ml, 0, (int)P.ml_bytes, kRsrcWord3);
-    const size_t colbase = (size_t)col * P.n_split_max;
-    if (tid < NQ) {
-        const int off_o = (int)((((colbase + s) * GT + qh) * D + qd) * 4);
-        __builtin_amdgcn_raw_buffer_store_b128(
-            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, make_float4(O0, O1, O2, O3)), ws_o,
-            off_o, 0, kSC1);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's output stores have completed
-    __syncthreads();                // ... and so have every other wave's
-    if (tid < NQ && qd == 0) {
-        const int off_ml = (int)(((colbase + s) * GT + qh) * 2 * 4);
-        __builtin_amdgcn_raw_buffer_store_b64(
-            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, make_float2(Mw, Lw)), ws_ml, off_ml, 0,
-            kSC1);
-    }
+    finish_split<TQ, D, GT>(a, &so[0][0][0], &sm[0][0], &sl[0][0], b * P.HT + ht, s, n_split, out);
 }
 
 // Merge workgroup m: request b, query head h0 + hh of head tile ht.
@@ -580,6 +534,372 @@ __device__ void merge_role(const DecodeArgs &a, int m)
             (tid * GT + hh) * 8, 0, kSC1);
 }
 
+// ===========================================================================
+// 4-bit group-affine cache on the matrix cores
+// ===========================================================================
+//
+// With codes c, and scale s and bias b per group of G elements of a row,
+// both products of the attention factor per group:
+//     q . k          = s * sum_e q_e c_e + b * sum_e q_e
+//     sum_r p_r v_r  = sum_r (p_r s_r) c_r + sum_r p_r b_r
+// so the matrix cores multiply the codes themselves, and the scales and
+// biases are applied per row and group in fp32 around them (the products
+// equal those with dequantized K and V, up to rounding).
+//
+// Codes as f16 operands.  A 4-bit code c in bits 0..3 of a 16-bit lane is
+// the f16 subnormal c * 2^-24, which v_mfma_f32_16x16x32_f16 multiplies
+// exactly; a code in bits 4..7 is 16c * 2^-24, and the matching entry of
+// the other operand is divided by 16 instead.  A word of 8 codes (nibble n
+// = element n) thus becomes a full 8-slot operand with four masks and one
+// shift, in the slot order (n0, n4, 16 n1, 16 n5, n2, n6, 16 n3, 16 n7), and
+// the factor 2^24 is restored in fp32.
+//
+// Work.  One workgroup per (request, head tile, split), as the dense
+// kernel; each wave takes 32-row steps of the split in turn (wave w: steps
+// w, w + 8, ...), each staged into the wave's own LDS buffer (two per
+// wave) by buffer loads that write LDS: codes of K and V in 16-byte pieces,
+// scales and biases one 16-bit value per lane.  Per step, with lane l
+// (l % 16 = j, l / 16 = qg):
+//   S^T[row][head] = K Q^T per group: A = the K codes of row j of a 16-row
+//     block (the lane's G/8 bytes of each group), B = the queries of head j
+//     in the same slot order (zero for j >= GT);
+//   scores in the log2 domain, scale * log2(e) folded in; the lane holds
+//     head j and rows 4qg..4qg+3 of both 16-row blocks; online softmax with
+//     an exact running maximum (so every p <= 1 and p * s fits f16);
+//   O^T[d][head] += V^T (p s)^T: A = V codes of column d = 16n + j for the
+//     lane's 8 rows, which ds_read_b64_tr_b4 delivers directly (lane i of a
+//     16-lane group receives nibble i of the 8 bytes each of the group's 16
+//     lanes names: here 8 rows at two 16-column blocks), B = p * s of the
+//     same 8 rows in f16, one operand per group.
+// The lane's rows of the second product (4qg + r of each block) are exactly
+// the rows its scores hold, so P never leaves registers.  At the end each
+// wave holds, per head, O = 2^24 O^T + sum_r p_r b_r, its maximum and its sum.
+
+typedef _Float16 q4f16x8_t __attribute__((ext_vector_type(8)));
+typedef float q4f32x4_t __attribute__((ext_vector_type(4)));
+typedef int q4i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) q4i32x2_t lds_q4i32x2_t;
+typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
+
+constexpr int kQ4Rows = 32;                     // rows per wave step (two 16-row blocks)
+constexpr int kQ4Waves = kDecodeThreads / 64;   // waves per workgroup
+
+// LDS staging of one step: offsets in bytes within one buffer.
+template <int D, int G>
+struct Q4Stage {
+    static constexpr int NG = D / G;                        // groups per row
+    static constexpr int ROWB = D / 2;                      // code bytes per row
+    static constexpr int CDMA = kQ4Rows * ROWB / 1024;      // 16-byte loads per step and code array
+    // V rows 16..31 start VHALF bytes after rows 0..15 (D = 128: 32 bytes of
+    // padding, so the transposing reads of the two blocks use other banks)
+    static constexpr int VHALF = D == 128 ? 16 * ROWB + 32 : 16 * ROWB;
+    static constexpr int SDMA = (kQ4Rows * NG + 63) / 64;   // 16-bit loads per step and scale/bias array
+    static constexpr int SB = SDMA * 256;                   // bytes per scale/bias array (a dword per value)
+    static constexpr int K = 0;
+    static constexpr int V = kQ4Rows * ROWB;
+    static constexpr int KS = V + VHALF + 16 * ROWB;
+    static constexpr int KB = KS + SB;
+    static constexpr int VS = KB + SB;
+    static constexpr int VB = VS + SB;
+    static constexpr int BYTES = VB + SB;
+    static constexpr int NL = 2 * CDMA + 4 * SDMA;          // loads per step
+    static_assert(CDMA * 1024 == kQ4Rows * ROWB, "code block");
+};
+
+// 8 codes (one word, nibble n = element n) as an f16 MFMA operand, slots
+// (n0, n4, 16 n1, 16 n5, n2, n6, 16 n3, 16 n7) times 2^-24.
+__device__ __forceinline__ q4f16x8_t q4_operand(uint32_t w)
+{
+    const uint32_t h = w >> 8;
+    const u32x4_t x = {w & 0x000F000Fu, w & 0x00F000F0u, h & 0x000F000Fu, h & 0x00F000F0u};
+    return __builtin_bit_cast(q4f16x8_t, x);
+}
+
+// max / sum over the 4 lanes l % 16 == j (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float max4q(float x)
+{
+    float a, b;
+    swap16(x, x, a, b);
+    x = fmaxf(a, b);
+    swap32(x, x, a, b);
+    return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum4q(float x)
+{
+    float a, b;
+    swap16(x, x, a, b);
+    x = a + b;
+    swap32(x, x, a, b);
+    return a + b;
+}
+
+template <int D, int G, int GT>
+__global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a, DecodeGrid grid)
+{
+    typedef Q4Stage<D, G> S;
+    constexpr int NG = S::NG;
+    constexpr int TPG = G / 32;      // code words per lane, group and row
+    constexpr int NT = D / 32;       // code words per lane and row (= k-blocks of the first product)
+    constexpr int NDB = D / 16;      // 16-column blocks of the output
+    static_assert(GT <= 16 && G % 32 == 0 && D % G == 0, "tile shape");
+
+    if ((int)blockIdx.x >= grid.n_stream) {
+        merge_role<f16_t, D, GT>(a, (int)blockIdx.x - grid.n_stream);
+        return;
+    }
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, j = lane & 15, qg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const DecodePlan &P = a.plan;
+    const int s = (int)blockIdx.x % grid.gx;
+    const int ht = ((int)blockIdx.x / grid.gx) % P.HT;
+    const int b = (int)blockIdx.x / (grid.gx * P.HT);
+
+    int n = a.kv_len;
+    if (a.kv_lens) {
+        n = a.kv_lens[b];
+        n = n < 0 ? 0 : (n > a.s_cap ? a.s_cap : n);
+    }
+    const int n_split = (n + P.L - 1) / P.L;
+    const int g = ht / P.ht_per_kv;
+    const int h0 = g * P.G + (ht % P.ht_per_kv) * GT;
+    f16_t *out = (f16_t *)a.out + ((size_t)b * a.Hq + h0) * D;
+
+    if (n == 0) {  // empty request: defined as an all-zero output
+        if (s == 0)
+            for (int idx = tid; idx < GT * D; idx += kDecodeThreads) store_elem(out + idx, 0.0f);
+        return;
+    }
+    if (s >= n_split) return;
+    const int start = s * P.L;
+    const int end = min(start + P.L, n);
+    const int nst = (end - start + kQ4Rows - 1) / kQ4Rows;
+
+    // sources bounded to rows [0, end) of this (request, KV head): rows past
+    // the split's end stage as zeros (and are masked below)
+    const size_t head_row0 = ((size_t)b * a.Hkv + g) * (size_t)a.s_cap;
+    const BufDesc dk = buf_desc((const uint8_t *)a.k + head_row0 * S::ROWB, (size_t)end * S::ROWB);
+    const BufDesc dv = buf_desc((const uint8_t *)a.v + head_row0 * S::ROWB, (size_t)end * S::ROWB);
+    const BufDesc dks = buf_desc((const uint16_t *)a.k_scales + head_row0 * NG, (size_t)end * NG * 2);
+    const BufDesc dkb = buf_desc((const uint16_t *)a.k_biases + head_row0 * NG, (size_t)end * NG * 2);
+    const BufDesc dvs = buf_desc((const uint16_t *)a.v_scales + head_row0 * NG, (size_t)end * NG * 2);
+    const BufDesc dvb = buf_desc((const uint16_t *)a.v_biases + head_row0 * NG, (size_t)end * NG * 2);
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kQ4Waves * 2 * S::BYTES];
+    static_assert(kQ4Waves * 2 * S::BYTES >= kQ4Waves * GT * D * 4, "wave outputs alias the staging buffers");
+    const unsigned lds0 = (unsigned)(uintptr_t)(lds_u8_t *)smem;
+    const int wbuf = wave * 2 * S::BYTES;  // this wave's two buffers
+
+    auto issue = [&](int st, int buf) {
+        const int r0 = start + st * kQ4Rows;
+        const unsigned base = lds0 + (unsigned)(wbuf + buf * S::BYTES);
+#pragma unroll
+        for (int i = 0; i < S::CDMA; ++i) lds_load16(dk, base + S::K + 1024 * i, r0 * S::ROWB + 1024 * i + 16 * lane);
+#pragma unroll
+        for (int i = 0; i < S::CDMA; ++i)
+            lds_load16(dv, base + S::V + S::VHALF * i, r0 * S::ROWB + 1024 * i + 16 * lane);
+#pragma unroll
+        for (int i = 0; i < S::SDMA; ++i) {
+            const int off = (r0 * NG + 64 * i + lane) * 2;
+            lds_load_u16(dks, base + S::KS + 256 * i, off);
+            lds_load_u16(dkb, base + S::KB + 256 * i, off);
+            lds_load_u16(dvs, base + S::VS + 256 * i, off);
+            lds_load_u16(dvb, base + S::VB + 256 * i, off);
+        }
+    };
+
+    // The first two steps of this wave go out first, then the query rows
+    // (16 bytes per thread, staged in LDS for the whole workgroup).
+    if (wave < nst) issue(wave, 0);
+    if (wave + kQ4Waves < nst) issue(wave + kQ4Waves, 1);
+    constexpr int QB = GT * D * 2;
+    __shared__ __attribute__((aligned(16))) uint16_t sq[GT * D];
+    const bool q_loader = tid < QB / 16;
+    const uint4 qv = *((const uint4 *)((const char *)a.q + ((size_t)b * a.Hq + h0) * D * 2) + (q_loader ? tid : 0));
+    if (q_loader) *((uint4 *)sq + tid) = qv;
+    __syncthreads();
+
+    // B operands of the first product: head j, slot order of q4_operand,
+    // entries facing a 16c slot divided by 16; and per group the sum of the
+    // head's query elements (times scale * log2(e)) for the bias term.
+    q4f16x8_t qop[NT];
+    float qs[NG];
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) qs[gg] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int gg = t / TPG;
+        const int d0 = gg * G + qg * (G / 4) + 8 * (t % TPG);
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            x[e] = j < GT ? f16_bits_to_f32(sq[(j < GT ? j : 0) * D + d0 + e]) : 0.0f;
+            qs[gg] += x[e];
+        }
+        const float r = 0.0625f;
+        const q4f16x8_t op = {(_Float16)x[0], (_Float16)x[4], (_Float16)(x[1] * r), (_Float16)(x[5] * r),
+                              (_Float16)x[2], (_Float16)x[6], (_Float16)(x[3] * r), (_Float16)(x[7] * r)};
+        qop[t] = op;
+    }
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) qs[gg] = sum4q(qs[gg]) * a.qscale;
+    const float C = a.qscale * 16777216.0f;  // scale * log2(e) * 2^24
+
+    // transposing-read address of this lane: row R(j % 8) of the step
+    // (4qg + 0..3 in block 0, then in block 1), 8-byte column chunk j / 8
+    int voff;
+    {
+        const int rr = j & 7;
+        const int row = rr < 4 ? 4 * qg + rr : 16 + 4 * qg + (rr - 4);
+        voff = S::V + (row < 16 ? row * S::ROWB : S::VHALF + (row - 16) * S::ROWB) + 8 * (j >> 3);
+    }
+
+    q4f32x4_t o[NDB];
+#pragma unroll
+    for (int nb = 0; nb < NDB; ++nb) o[nb] = q4f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run = kNegInf, l_run = 0.0f, bsum[NG];
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) bsum[gg] = 0.0f;
+
+    auto step = [&](int boff, int r0) {
+        const unsigned char *bp = smem + boff;
+        // ---- S^T = K Q^T, one accumulator per 16-row block and group ----
+        q4f32x4_t acc[2][NG];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int gg = 0; gg < NG; ++gg) {
+                const unsigned char *kp = bp + S::K + (16 * u + j) * S::ROWB + gg * (G / 2) + qg * (G / 8);
+                uint32_t w[TPG];
+                if constexpr (TPG == 4) {
+                    const uint4 x = *(const uint4 *)kp;
+                    w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+                } else if constexpr (TPG == 2) {
+                    const uint2 x = *(const uint2 *)kp;
+                    w[0] = x.x; w[1] = x.y;
+                } else {
+                    w[0] = *(const uint32_t *)kp;
+                }
+                q4f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int tt = 0; tt < TPG; ++tt)
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(q4_operand(w[tt]), qop[gg * TPG + tt], c, 0, 0, 0);
+                acc[u][gg] = c;
+            }
+        }
+        // ---- scores (log2 domain); rows past the split's end masked ----
+        float sc[2][4];
+        float mx = kNegInf;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const uint32_t *ks = (const uint32_t *)(bp + S::KS) + (16 * u + 4 * qg) * NG;
+            const uint32_t *kb = (const uint32_t *)(bp + S::KB) + (16 * u + 4 * qg) * NG;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float x = 0.0f, y = 0.0f;
+#pragma unroll
+                for (int gg = 0; gg < NG; ++gg) {
+                    x = __builtin_fmaf(f16_bits_to_f32(ks[r * NG + gg]), acc[u][gg][r], x);
+                    y = __builtin_fmaf(f16_bits_to_f32(kb[r * NG + gg]), qs[gg], y);
+                }
+                const float v = __builtin_fmaf(C, x, y);
+                sc[u][r] = r0 + 16 * u + 4 * qg + r < end ? v : kNegInf;
+                mx = fmaxf(mx, sc[u][r]);
+            }
+        }
+        mx = max4q(mx);  // finite: the step's first row is valid
+        if (__any(mx > m_run)) {
+            const float mn = fmaxf(m_run, mx);
+            const float al = fast_exp2(m_run - mn);  // 0 on the first step, 1 where unchanged
+            m_run = mn;
+            l_run *= al;
+#pragma unroll
+            for (int gg = 0; gg < NG; ++gg) bsum[gg] *= al;
+#pragma unroll
+            for (int nb = 0; nb < NDB; ++nb) o[nb] *= al;
+        }
+        // ---- probabilities, V-bias sums, and p * s as f16 operands ----
+        float pr[2][4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const uint32_t *vb = (const uint32_t *)(bp + S::VB) + (16 * u + 4 * qg) * NG;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pr[u][r] = fast_exp2(sc[u][r] - m_run);
+                l_run += pr[u][r];
+#pragma unroll
+                for (int gg = 0; gg < NG; ++gg)
+                    bsum[gg] = __builtin_fmaf(pr[u][r], f16_bits_to_f32(vb[r * NG + gg]), bsum[gg]);
+            }
+        }
+        q4f16x8_t pop[NG];
+        {
+            const uint32_t *vs0 = (const uint32_t *)(bp + S::VS) + (4 * qg) * NG;
+            const uint32_t *vs1 = (const uint32_t *)(bp + S::VS) + (16 + 4 * qg) * NG;
+#pragma unroll
+            for (int gg = 0; gg < NG; ++gg) {
+                _Float16 e[8];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float f = (r & 1) ? 0.0625f : 1.0f;
+                    e[2 * r] = (_Float16)(pr[0][r] * f16_bits_to_f32(vs0[r * NG + gg]) * f);
+                    e[2 * r + 1] = (_Float16)(pr[1][r] * f16_bits_to_f32(vs1[r * NG + gg]) * f);
+                }
+                const q4f16x8_t op = {e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]};
+                pop[gg] = op;
+            }
+        }
+        // ---- O^T += V^T (p s)^T ----
+#pragma unroll
+        for (int pp = 0; pp < D / 32; ++pp) {
+            const q4i32x2_t w2 =
+                __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_q4i32x2_t *)((lds_u8_t *)smem + boff + voff + 16 * pp));
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int nb = 2 * pp + hh;
+                o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(q4_operand((uint32_t)w2[hh]), pop[(16 * nb) / G], o[nb],
+                                                               0, 0, 0);
+            }
+        }
+    };
+
+    // Steps of this wave, two buffers: step st + 8 is in flight while st is
+    // computed; the buffer of st is refilled with st + 16 afterwards.
+    int it = 0;
+    for (int st = wave; st < nst; st += kQ4Waves, ++it) {
+        const int buf = it & 1;
+        if (st + kQ4Waves < nst)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(S::NL) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        step(wbuf + buf * S::BYTES, start + st * kQ4Rows);
+        if (st + 2 * kQ4Waves < nst) issue(st + 2 * kQ4Waves, buf);
+    }
+
+    // ---- wave totals, then the workgroup's combination ----
+    l_run = sum4q(l_run);
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) bsum[gg] = sum4q(bsum[gg]);
+    __shared__ float sm[kQ4Waves * GT], sl[kQ4Waves * GT];
+    __syncthreads();  // every wave is done with its staging buffers
+    float *so = (float *)smem;  // [waves][GT][D]
+    if (j < GT) {
+#pragma unroll
+        for (int nb = 0; nb < NDB; ++nb) {
+            const float bb = bsum[(16 * nb) / G];
+            *(float4 *)&so[(wave * GT + j) * D + 16 * nb + 4 * qg] =
+                make_float4(16777216.0f * o[nb][0] + bb, 16777216.0f * o[nb][1] + bb, 16777216.0f * o[nb][2] + bb,
+                            16777216.0f * o[nb][3] + bb);
+        }
+        if (qg == 0) {
+            sm[wave * GT + j] = m_run;
+            sl[wave * GT + j] = l_run;
+        }
+    }
+    __syncthreads();
+    finish_split<f16_t, D, GT>(a, so, sm, sl, b * P.HT + ht, s, n_split, out);
+}
+
 // ---------------------------------------------------------------------------
 // Launch helpers
 // ---------------------------------------------------------------------------
@@ -632,11 +952,41 @@ hipError_t launch_decode(int dtype, int D, int B, const DecodeArgs &a, hipStream
     return hipErrorInvalidValue;
 }
 
+template <int D, int G, int GT>
+static hipError_t launch_q4(int B, const DecodeArgs &a, hipStream_t stream)
+{
+    DecodeGrid g;
+    g.gx = a.kv_lens ? a.plan.n_split_max : (a.kv_len + a.plan.L - 1) / a.plan.L;
+    g.n_stream = g.gx * a.plan.HT * B;
+    const int n_merge = a.plan.n_split_max > 1 && g.gx > 1 ? B * a.plan.HT * GT : 0;
+    hipLaunchKernelGGL((decode_q4_kernel<D, G, GT>), dim3(g.n_stream + n_merge), dim3(kDecodeThreads), 0, stream, a, g);
+    return hipGetLastError();
+}
+
+template <int D, int G>
+static hipError_t dispatch_q4(int B, const DecodeArgs &a, hipStream_t s)
+{
+    switch (a.plan.GT) {
+    case 1: return launch_q4<D, G, 1>(B, a, s);
+    case 2: return launch_q4<D, G, 2>(B, a, s);
+    case 3: return launch_q4<D, G, 3>(B, a, s);
+    case 4: return launch_q4<D, G, 4>(B, a, s);
+    case 5: return launch_q4<D, G, 5>(B, a, s);
+    case 6: return launch_q4<D, G, 6>(B, a, s);
+    case 7: return launch_q4<D, G, 7>(B, a, s);
+    case 8: return launch_q4<D, G, 8>(B, a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_decode_q4(int D, int group, int B, const DecodeArgs &a, hipStream_t s)
 {
     if (group != a.group) return hipErrorInvalidValue;
-    if (D == 128) return dispatch_gt<Q4KV<128>, f16_t, 128>(B, a, s);
-    if (D == 64) return dispatch_gt<Q4KV<64>, f16_t, 64>(B, a, s);
+    if (D == 128 && group == 32) return dispatch_q4<128, 32>(B, a, s);
+    if (D == 128 && group == 64) return dispatch_q4<128, 64>(B, a, s);
+    if (D == 128 && group == 128) return dispatch_q4<128, 128>(B, a, s);
+    if (D == 64 && group == 32) return dispatch_q4<64, 32>(B, a, s);
+    if (D == 64 && group == 64) return dispatch_q4<64, 64>(B, a, s);
     return hipErrorInvalidValue;
 }
 

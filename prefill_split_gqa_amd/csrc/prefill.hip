@@ -158,33 +158,6 @@ template <int D> struct PfSlot {
 // V reads: 4 rows, an aligned pair of chunks each).
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
-// Buffer loads that write LDS (buffer_load_dwordx4 ... lds): lane l's 16
-// bytes at byte offset voff go to LDS address lds_base + 16*l; an offset
-// outside the descriptor's range writes zeros (the whole offset is in the
-// vector register, where the range check applies).  They are issued from inline
-// assembly so that the compiler does not treat them as pending LDS stores
-// (it would otherwise wait for every one of them at each workgroup barrier);
-// the kernel waits for them itself (s_waitcnt vmcnt) before the barrier
-// that precedes their readers.
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-struct BufDesc { u32x4_t w; };
-
-__device__ __forceinline__ BufDesc buf_desc(const void *base, size_t bytes)
-{
-    const unsigned long long a = (unsigned long long)(uintptr_t)base;
-    BufDesc d;
-    d.w[0] = __builtin_amdgcn_readfirstlane((unsigned)a);
-    d.w[1] = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32)) & 0xFFFFu;  // stride 0
-    d.w[2] = __builtin_amdgcn_readfirstlane((unsigned)bytes);
-    d.w[3] = kRsrcWord3;
-    return d;
-}
-
-__device__ __forceinline__ void lds_load16(const BufDesc &d, unsigned lds_base, int voff)
-{
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(d.w), "{m0}"(lds_base) : "memory");
-}
-
 template <int D> __device__ __forceinline__ int tile_off(int row, int chunk)
 {
     typedef PfLds<D> L;

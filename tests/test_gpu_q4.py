@@ -80,7 +80,7 @@ def test_q4_dequant_of_workload_cache(gpu_lib):
     assert np.array_equal(out.cpu().numpy().view(np.uint32), want.view(np.uint32))
 
 
-@pytest.mark.parametrize("D,group", [(128, 64), (128, 32), (64, 64), (128, 128)])
+@pytest.mark.parametrize("D,group", [(128, 64), (128, 32), (64, 64), (64, 32), (128, 128)])
 def test_q4_small_ragged(gpu_lib, D, group):
     rng = np.random.default_rng(D + group)
     for Hq, Hkv, n, s_cap in [(8, 8, 1, 4), (64, 8, 33, 70), (16, 2, 100, 100), (12, 4, 777, 800)]:
