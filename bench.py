@@ -244,8 +244,15 @@ def bench_extra(torch, gqa, oracle, W, steps, warmup, flush):
     the oracle; layers past the first are device copies of it, scaled (codes
     permuted for the 4-bit cache), so that every layer reads its own memory."""
     out = {}
+    for part in (extra_decode_small, extra_batched, extra_q4, extra_chunked_prefill):
+        out.update(part(torch, gqa, oracle, W, steps, warmup, flush))
+    return out
 
-    # decode, Qwen2.5-0.5B heads, KV length 128, fp32; 28 layers per step
+
+def extra_decode_small(torch, gqa, oracle, W, steps, warmup, flush):
+    """Decode, Qwen2.5-0.5B heads, KV length 128, fp32; 28 layers per step
+    (one launch alone would be mostly the graph's own launch cost)."""
+    out = {}
     # (one launch alone would be mostly the graph's own launch cost)
     w = W.by_name("decode_0p5b")
     q, k, v = W.decode_inputs(w, 128, 0)
@@ -268,8 +275,12 @@ def bench_extra(torch, gqa, oracle, W, steps, warmup, flush):
     out["decode_0p5b_s128"] = hbm_entry(us, decode_bytes_generic(1, w.Hq, w.Hkv, w.D, [128], 4), ok, err,
                                         "decode_splitk_kernel<DenseKV<float,64>,float,64,7>",
                                         layers_per_step=len(dev))
+    return out
 
-    # batched decode, Qwen3-4B heads, bf16, per-request lengths, 36 layers
+
+def extra_batched(torch, gqa, oracle, W, steps, warmup, flush):
+    """Batched decode, Qwen3-4B heads, bf16, per-request lengths, 36 layers."""
+    out = {}
     w = W.by_name("batched_qwen3_4b")
     for B in (1, 2, 4, 8):
         q, k, v, lens = W.batched_inputs(w, B, 0)
@@ -296,11 +307,15 @@ def bench_extra(torch, gqa, oracle, W, steps, warmup, flush):
             kv_lens=[int(x) for x in lens])
         del dev, outs, ref, g
         torch.cuda.empty_cache()
+    return out
 
-    # 4-bit decode, 64 query / 8 KV heads, group 64, f16 queries, 80 layers
+
+def extra_q4(torch, gqa, oracle, W, steps, warmup, flush, sizes=(2048, 16384)):
+    """4-bit decode, 64 query / 8 KV heads, group 64, f16 queries, 80 layers."""
+    out = {}
     w = W.by_name("q4_decode")
     names = ("k_codes", "k_scales", "k_biases", "v_codes", "v_scales", "v_biases")
-    for S in (2048, 16384):
+    for S in sizes:
         x = W.q4_inputs(w, S, 0)
         d0 = {n: t.cuda() for n, t in x.items()}
         dev = [d0]
@@ -326,12 +341,17 @@ def bench_extra(torch, gqa, oracle, W, steps, warmup, flush):
         us = float(np.median(time_steps(torch, g.replay, steps, warmup, flush))) * 1e3 / w.layers
         ok = err <= 2e-2 and all(torch.equal(a, b) for a, b in zip(outs, ref))
         nbytes = S * w.Hkv * 2 * (w.D // 2 + 2 * 2 * (w.D // w.group)) + 2 * w.Hq * w.D * 2
-        out["q4_decode_s%d" % S] = hbm_entry(us, nbytes, ok, err, "decode_splitk_kernel<Q4KV<128>,f16_t,128,8>",
+        out["q4_decode_s%d" % S] = hbm_entry(us, nbytes, ok, err, "decode_q4_kernel<128,64,8>",
                                              layers_per_step=w.layers)
         del dev, outs, ref, g
         torch.cuda.empty_cache()
+    return out
 
-    # chunked prefill: the last 256 queries of T=4097 against all 4097 keys, 24 layers
+
+def extra_chunked_prefill(torch, gqa, oracle, W, steps, warmup, flush):
+    """Chunked prefill: the last 256 queries of T=4097 against all 4097 keys,
+    24 layers."""
+    out = {}
     w = W.by_name("prefill_0p5b")
     q, k, v = W.prefill_inputs(w, 4097)
     qc = q[:, :, 4097 - 256:].contiguous()

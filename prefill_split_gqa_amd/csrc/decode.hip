@@ -708,15 +708,29 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
         }
     };
 
-    // The first two steps of this wave go out first, then the query rows
-    // (16 bytes per thread, staged in LDS for the whole workgroup).
-    if (wave < nst) issue(wave, 0);
-    if (wave + kQ4Waves < nst) issue(wave + kQ4Waves, 1);
+    // The workgroup's query rows go to LDS by the same kind of load (the
+    // first QDMA waves, 1 KB each), ahead of each wave's first two steps;
+    // those waves wait for their query piece only, then the workgroup meets.
+    // (With every load issued this way, the only waits are the explicit
+    // ones: the first step is computed while the second is still arriving.)
     constexpr int QB = GT * D * 2;
-    __shared__ __attribute__((aligned(16))) uint16_t sq[GT * D];
-    const bool q_loader = tid < QB / 16;
-    const uint4 qv = *((const uint4 *)((const char *)a.q + ((size_t)b * a.Hq + h0) * D * 2) + (q_loader ? tid : 0));
-    if (q_loader) *((uint4 *)sq + tid) = qv;
+    constexpr int QDMA = (QB + 1023) / 1024;
+    __shared__ __attribute__((aligned(16))) uint16_t sq[QDMA * 512];
+    if (wave < QDMA) {
+        const BufDesc dq = buf_desc((const char *)a.q + ((size_t)b * a.Hq + h0) * D * 2, QB);
+        lds_load16(dq, (unsigned)(uintptr_t)(lds_u8_t *)sq + 1024 * wave, 1024 * wave + 16 * lane);
+    }
+    const bool two = wave + kQ4Waves < nst;
+    if (wave < nst) issue(wave, 0);
+    if (two) issue(wave + kQ4Waves, 1);
+    if (wave < QDMA) {
+        if (two)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * S::NL) : "memory");
+        else if (wave < nst)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(S::NL) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     __syncthreads();
 
     // B operands of the first product: head j, slot order of q4_operand,
@@ -730,10 +744,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
     for (int t = 0; t < NT; ++t) {
         const int gg = t / TPG;
         const int d0 = gg * G + qg * (G / 4) + 8 * (t % TPG);
+        // one 16-byte read of a valid row (lanes of padding heads read row 0
+        // and zero the values), not eight predicated 16-bit reads
+        const uint4 raw = *(const uint4 *)&sq[(j < GT ? j : 0) * D + d0];
+        const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            x[e] = j < GT ? f16_bits_to_f32(sq[(j < GT ? j : 0) * D + d0 + e]) : 0.0f;
+            x[e] = j < GT ? f16_bits_to_f32(rw[e / 2] >> (16 * (e & 1))) : 0.0f;
             qs[gg] += x[e];
         }
         const float r = 0.0625f;
@@ -808,9 +826,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
             }
         }
         mx = max4q(mx);  // finite: the step's first row is valid
-        if (__any(mx > m_run)) {
+        if (m_run == kNegInf) {  // first step of this wave: nothing to rescale
+            m_run = mx;
+        } else if (__any(mx > m_run)) {
             const float mn = fmaxf(m_run, mx);
-            const float al = fast_exp2(m_run - mn);  // 0 on the first step, 1 where unchanged
+            const float al = fast_exp2(m_run - mn);  // 1 where unchanged
             m_run = mn;
             l_run *= al;
 #pragma unroll
