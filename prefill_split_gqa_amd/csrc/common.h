@@ -218,6 +218,7 @@ struct DecodeArgs {
     DecodePlan plan;
     float *part_o, *part_ml; // per split: [GT][D] outputs, [GT][2] (max, sum)
     size_t ws_bytes;
+    int n_cus;               // compute units of the device (launch shape)
 };
 
 // Launchers (defined in the .hip files; return a hipError_t).

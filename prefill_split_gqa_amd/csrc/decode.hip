@@ -24,21 +24,26 @@
 // LDS, giving one (max, sum, output) partial per split.
 //
 // Cross-split merge: one CU can pull only ~70 GB/s, so a single workgroup
-// reading every split's partial would be the tail of the launch.  Instead the
-// grid carries, after all streaming workgroups, one merge workgroup per
-// (request, query head).  It waits until every split of its (request, head
-// tile) has published its partial for that head, reads only that head's
-// slice and merges it with the log-sum-exp rule in a fixed order (results do
-// not depend on timing).  A split publishes its outputs, waits for them to
+// reading every split's partial would be the tail of the launch.  Instead
+// each (request, query head) is merged by a whole workgroup that waits until
+// every split of its (request, head tile) has published its partial for that
+// head, reads only that head's slice and merges it with the log-sum-exp rule
+// in a fixed order (results do not depend on timing).  When all splits of
+// the launch are resident at once, split s merges heads s, s + n_split, ...
+// of its tile right after publishing its own partial (it is resident
+// already, so the merge starts as soon as the last partial lands);
+// otherwise the grid carries, after all splits, one merge workgroup per
+// (request, query head).  A split publishes its outputs, waits for them to
 // complete, then writes its (max, sum) pair: the sum is >= 1 (the split's
 // maximum row contributes exp2(0)) and never 0, so a non-zero sum word means
-// "published".  The merge workgroup zeroes the words it consumed, leaving the
+// "published".  The merge zeroes the words it consumed, leaving the
 // workspace ready for the next call; no counters or atomics are involved.
-// The wait always ends: workgroups are dispatched in linear-id order on every
-// XCD, so all streaming workgroups are dispatched before any merge workgroup
-// that waits for them, and they never wait on anything; the wait is also
-// bounded, and a merge workgroup that gives up writes NaN so that the failure
-// cannot pass silently.
+// The wait always ends: splits that wait have published already and wait
+// only for splits of their own tile, which never wait before publishing and
+// are either resident (every split is, in the first mode) or dispatched
+// before any merge workgroup (workgroups are dispatched in linear-id order).
+// The wait is also bounded, and a merge that gives up writes NaN so that
+// the failure cannot pass silently.
 
 // Cross-workgroup exchange without cache maintenance: on gfx950 each XCD has
 // its own L2, and a device-scope fence writes back / invalidates that L2
@@ -46,13 +51,13 @@
 // crosses workgroups is written and read with device-scope (sc1) accesses,
 // which are coherent at device scope by themselves; a split waits for its
 // output stores to complete (s_waitcnt) before it writes its (max, sum)
-// word, and the merge workgroup reads the outputs only after it has seen
+// word, and the merging workgroup reads the outputs only after it has seen
 // every split's word.
 //
 // The 4-bit cache variant (VeloxQuant-MLX "attention" posts, Part 4: codes,
-// scales, biases and the group size go to the kernel, which dequantizes in
-// registers) replaces the row loads by code/scale/bias loads and the
-// unpacking by the group-affine dequant below; everything else is shared.
+// scales, biases and the group size go to the kernel, which dequantizes
+// inside it) has a kernel of its own on the matrix cores (below); the split
+// plan, the partials and the merge are shared.
 
 #include "common.h"
 
@@ -189,11 +194,12 @@ constexpr unsigned kMergeSpinLimit = 1u << 22;  // polls before a merge workgrou
 // merge workgroups (one per request and query head).
 struct DecodeGrid {
     int gx;        // splits per (request, head tile) in the grid
-    int n_stream;  // gx * HT * B
+    int n_stream;  // gx * HT * B splits; merge workgroups (if any) follow
+    int inplace;   // 1: the splits merge themselves (no merge workgroups)
 };
 
 template <typename TQ, int D, int GT>
-__device__ void merge_role(const DecodeArgs &a, int m);
+__device__ void merge_head(const DecodeArgs &a, int m);
 
 // End of a streaming workgroup.  so [waves][GT][D], sm and sl [waves][GT]
 // hold, per wave and query head, the unnormalised output row, its reference
@@ -262,9 +268,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
     static_assert(NF % 2 == 0 && NQ <= kDecodeThreads && kDecodeLPR == 32, "tile shape");
 
     if ((int)blockIdx.x >= grid.n_stream) {
-        merge_role<TQ, D, GT>(a, (int)blockIdx.x - grid.n_stream);
+        merge_head<TQ, D, GT>(a, (int)blockIdx.x - grid.n_stream);
         return;
     }
+
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, rgq = lane >> 5, lr = lane & 31;
     const int rg = wave * 2 + rgq;  // row-group (half wave) within the workgroup
@@ -436,13 +443,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
     __syncthreads();
 
     finish_split<TQ, D, GT>(a, &so[0][0][0], &sm[0][0], &sl[0][0], b * P.HT + ht, s, n_split, out);
+    // split s then merges query heads s, s + n_split, ... of its head tile
+    if (grid.inplace && n_split > 1)
+        for (int hh = s; hh < GT; hh += n_split) merge_head<TQ, D, GT>(a, (b * P.HT + ht) * GT + hh);
 }
 
-// Merge workgroup m: request b, query head h0 + hh of head tile ht.
-// Thread t handles 4 dims (t % (D/4)) of the splits j = t / (D/4) + k * NG;
-// the NG strided groups are then added in group order.
+// Merge of item m = (request b, head tile ht) * GT + hh: the partials of
+// every split for query head h0 + hh, combined by a whole workgroup (one
+// that has published its own split).  Thread t handles 4 dims (t % (D/4)) of
+// the splits j = t / (D/4) + k * NG; the NG strided groups are then added in
+// group order.
 template <typename TQ, int D, int GT>
-__device__ void merge_role(const DecodeArgs &a, int m)
+__device__ void merge_head(const DecodeArgs &a, int m)
 {
     constexpr int D4 = D / 4;
     constexpr int NG = kDecodeThreads / D4;              // split groups
@@ -453,6 +465,7 @@ __device__ void merge_role(const DecodeArgs &a, int m)
     __shared__ int s_go;
     const DecodePlan &P = a.plan;
     const int tid = threadIdx.x;
+    __syncthreads();  // a previous merge in this workgroup is done with the shared arrays
     const int hh = m % GT;
     const int col = m / GT;
     const int ht = col % P.HT;
@@ -644,9 +657,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
     static_assert(GT <= 16 && G % 32 == 0 && D % G == 0, "tile shape");
 
     if ((int)blockIdx.x >= grid.n_stream) {
-        merge_role<f16_t, D, GT>(a, (int)blockIdx.x - grid.n_stream);
+        merge_head<f16_t, D, GT>(a, (int)blockIdx.x - grid.n_stream);
         return;
     }
+
     const int tid = threadIdx.x;
     const int lane = tid & 63, j = lane & 15, qg = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -918,19 +932,34 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
     }
     __syncthreads();
     finish_split<f16_t, D, GT>(a, so, sm, sl, b * P.HT + ht, s, n_split, out);
+    // split s then merges query heads s, s + n_split, ... of its head tile
+    if (grid.inplace && n_split > 1)
+        for (int hh = s; hh < GT; hh += n_split) merge_head<f16_t, D, GT>(a, (b * P.HT + ht) * GT + hh);
 }
 
 // ---------------------------------------------------------------------------
 // Launch helpers
 // ---------------------------------------------------------------------------
+// Grid of a decode launch; returns the number of merge workgroups.  When
+// every split can be resident at once (no more splits than compute units;
+// each kernel holds at least one workgroup per CU), the splits merge the
+// heads themselves right after publishing.  Otherwise a split that waited
+// would hold a CU that later splits need, so dedicated merge workgroups
+// follow every split in the grid instead.
+static int decode_grid(int B, int GT, const DecodeArgs &a, DecodeGrid *g)
+{
+    g->gx = a.kv_lens ? a.plan.n_split_max : (a.kv_len + a.plan.L - 1) / a.plan.L;
+    g->n_stream = g->gx * a.plan.HT * B;
+    const bool several = a.plan.n_split_max > 1 && g->gx > 1;
+    g->inplace = g->n_stream <= a.n_cus ? 1 : 0;
+    return several && !g->inplace ? B * a.plan.HT * GT : 0;
+}
+
 template <class KV, typename TQ, int D, int GT>
 static hipError_t launch_one(int B, const DecodeArgs &a, hipStream_t stream)
 {
     DecodeGrid g;
-    g.gx = a.kv_lens ? a.plan.n_split_max : (a.kv_len + a.plan.L - 1) / a.plan.L;
-    g.n_stream = g.gx * a.plan.HT * B;
-    // merge workgroups are needed only when a request can have several splits
-    const int n_merge = a.plan.n_split_max > 1 && g.gx > 1 ? B * a.plan.HT * GT : 0;
+    const int n_merge = decode_grid(B, GT, a, &g);
     hipLaunchKernelGGL((decode_splitk_kernel<KV, TQ, D, GT>), dim3(g.n_stream + n_merge), dim3(kDecodeThreads), 0,
                        stream, a, g);
     return hipGetLastError();
@@ -976,10 +1005,9 @@ template <int D, int G, int GT>
 static hipError_t launch_q4(int B, const DecodeArgs &a, hipStream_t stream)
 {
     DecodeGrid g;
-    g.gx = a.kv_lens ? a.plan.n_split_max : (a.kv_len + a.plan.L - 1) / a.plan.L;
-    g.n_stream = g.gx * a.plan.HT * B;
-    const int n_merge = a.plan.n_split_max > 1 && g.gx > 1 ? B * a.plan.HT * GT : 0;
-    hipLaunchKernelGGL((decode_q4_kernel<D, G, GT>), dim3(g.n_stream + n_merge), dim3(kDecodeThreads), 0, stream, a, g);
+    const int n_merge = decode_grid(B, GT, a, &g);
+    hipLaunchKernelGGL((decode_q4_kernel<D, G, GT>), dim3(g.n_stream + n_merge), dim3(kDecodeThreads), 0, stream, a,
+                       g);
     return hipGetLastError();
 }
 

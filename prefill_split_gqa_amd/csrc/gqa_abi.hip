@@ -50,11 +50,12 @@ bool plan_decode(int B, int Hq, int Hkv, int D, int s_cap, DecodePlan *p)
     return p->HT <= 65535 && p->n_split_max <= 65535 && p->bytes < ((size_t)1 << 31);
 }
 
-// 1 = gfx950, 0 = other device, -1 = HIP error.  Cached per device ordinal.
-int device_supported()
+// 1 = gfx950, 0 = other device, -1 = HIP error; *cus = the device's compute
+// units.  Cached per device ordinal.
+int device_supported(int *cus = nullptr)
 {
     static std::mutex mu;
-    static int cache[64];
+    static int cache[64], n_cus[64];
     static bool init = false;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return -1;
@@ -67,14 +68,16 @@ int device_supported()
     if (cache[dev] == 2) {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return -1;
+        n_cus[dev] = prop.multiProcessorCount;
         cache[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
     }
+    if (cus) *cus = n_cus[dev];
     return cache[dev];
 }
 
-int check_device()
+int check_device(int *cus = nullptr)
 {
-    const int d = device_supported();
+    const int d = device_supported(cus);
     if (d < 0) return GQA_ERR_HIP;
     if (d == 0) return GQA_ERR_UNSUPPORTED;
     return GQA_OK;
@@ -152,8 +155,10 @@ int gqa_decode_attend(const void *q, const void *k, const void *v, void *out, in
         return st;
     if (kv_len < 1 || kv_len > s_cap) return GQA_ERR_SHAPE;
     if (!dense_dtype(dtype)) return GQA_ERR_UNSUPPORTED;
-    if (int st = check_device()) return st;
+    int cus = 0;
+    if (int st = check_device(&cus)) return st;
     DecodeArgs a{};
+    a.n_cus = cus;
     a.q = q; a.k = k; a.v = v; a.out = out;
     a.kv_lens = nullptr; a.kv_len = kv_len;
     a.Hq = Hq; a.Hkv = Hkv; a.s_cap = s_cap; a.group = 0;
@@ -173,8 +178,10 @@ int gqa_decode_attend_batched(const void *q, const void *k, const void *v, void 
         return st;
     if (!aligned16(kv_lens)) return GQA_ERR_ALIGN;
     if (!dense_dtype(dtype)) return GQA_ERR_UNSUPPORTED;
-    if (int st = check_device()) return st;
+    int cus = 0;
+    if (int st = check_device(&cus)) return st;
     DecodeArgs a{};
+    a.n_cus = cus;
     a.q = q; a.k = k; a.v = v; a.out = out;
     a.kv_lens = kv_lens; a.kv_len = 0;
     a.Hq = Hq; a.Hkv = Hkv; a.s_cap = s_cap; a.group = 0;
@@ -231,8 +238,10 @@ int gqa_decode_attend_q4(const void *q, const uint8_t *k_codes, const void *k_sc
     if (D % group_size != 0) return GQA_ERR_SHAPE;
     if (!aligned16(k_scales) || !aligned16(k_biases) || !aligned16(v_scales) || !aligned16(v_biases))
         return GQA_ERR_ALIGN;
-    if (int st = check_device()) return st;
+    int cus = 0;
+    if (int st = check_device(&cus)) return st;
     DecodeArgs a{};
+    a.n_cus = cus;
     a.q = q; a.k = k_codes; a.v = v_codes; a.out = out;
     a.k_scales = k_scales; a.k_biases = k_biases; a.v_scales = v_scales; a.v_biases = v_biases;
     a.kv_lens = nullptr; a.kv_len = kv_len;

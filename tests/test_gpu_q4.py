@@ -103,3 +103,21 @@ def test_q4_small_ragged(gpu_lib, D, group):
         note("q4 D=%d group=%d Hq=%d Hkv=%d n=%d" % (D, group, Hq, Hkv, n))
         got = run_q4(gpu_lib, inp, wg, n)
         assert_close(got, oracle_q4(inp, wg, n), 2e-2, "q4 n=%d" % n)
+
+
+def test_q4_two_requests_merge_workgroups(gpu_lib):
+    """Two requests of the 4-bit workload geometry (64 query / 8 KV heads,
+    KV length 4096): 512 splits, more than the device has compute units, so
+    the launch merges the splits with merge workgroups placed after them
+    instead of in place; both requests match the oracle, and the first one
+    is bit-identical to the same request decoded alone (the split of the KV
+    length does not depend on the batch)."""
+    w = W.by_name("q4_decode")
+    S = 4096
+    parts = [W.q4_inputs(w, S, layer) for layer in (3, 4)]
+    inp = {k: torch.cat([p[k] for p in parts], dim=0) for k in parts[0]}
+    note("q4 B=2 S=%d" % S)
+    got = run_q4(gpu_lib, inp, w, S)
+    assert_close(got, oracle_q4(inp, w, S), 2e-2, "q4 B=2")
+    alone = run_q4(gpu_lib, parts[0], w, S)
+    assert torch.equal(got[:1], alone)
