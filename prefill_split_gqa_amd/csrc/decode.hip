@@ -201,14 +201,14 @@ struct DecodeGrid {
 template <typename TQ, int D, int GT>
 __device__ void merge_head(const DecodeArgs &a, int m);
 
-// End of a streaming workgroup.  so [waves][GT][D], sm and sl [waves][GT]
-// hold, per wave and query head, the unnormalised output row, its reference
-// maximum (log2 domain; -inf for a wave that saw no row) and its sum of
-// weights.  The waves are combined; with a single split the output is
-// written, otherwise the split's partial is published with device-scope
-// stores: outputs first, then (after they have completed) the (max, sum)
-// word that flags them.
-template <typename TQ, int D, int GT>
+// End of a streaming workgroup.  so [waves][GT][SOD] (rows of D floats at
+// a stride of SOD), sm and sl [waves][GT] hold, per wave and query head, the
+// unnormalised output row, its reference maximum (log2 domain; -inf for a
+// wave that saw no row) and its sum of weights.  The waves are combined;
+// with a single split the output is written, otherwise the split's partial
+// is published with device-scope stores: outputs first, then (after they
+// have completed) the (max, sum) word that flags them.
+template <typename TQ, int D, int GT, int SOD = D>
 __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *so, const float *sm, const float *sl,
                                              int col, int s, int n_split, TQ *out)
 {
@@ -219,14 +219,22 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *s
     const int qh = tid / (D / 4), qd = (tid % (D / 4)) * 4;
     float Mw = kNegInf, Lw = 0.0f, O0 = 0.0f, O1 = 0.0f, O2 = 0.0f, O3 = 0.0f;
     if (tid < NQ) {
-#pragma unroll
-        for (int w = 0; w < NW; ++w) Mw = fmaxf(Mw, sm[w * GT + qh]);
+        // every read first, then the arithmetic
+        float mw[NW], lw[NW];
+        float4 xw[NW];
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            const float wt = rel_weight(sm[w * GT + qh], Mw);
-            const float4 x = *(const float4 *)&so[(w * GT + qh) * D + qd];
-            Lw += wt * sl[w * GT + qh];
-            O0 += wt * x.x; O1 += wt * x.y; O2 += wt * x.z; O3 += wt * x.w;
+            mw[w] = sm[w * GT + qh];
+            lw[w] = sl[w * GT + qh];
+            xw[w] = *(const float4 *)&so[(w * GT + qh) * SOD + qd];
+        }
+#pragma unroll
+        for (int w = 0; w < NW; ++w) Mw = fmaxf(Mw, mw[w]);
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float wt = rel_weight(mw[w], Mw);
+            Lw += wt * lw[w];
+            O0 += wt * xw[w].x; O1 += wt * xw[w].y; O2 += wt * xw[w].z; O3 += wt * xw[w].w;
         }
     }
     if (n_split == 1) {
@@ -700,7 +708,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
     const BufDesc dvb = buf_desc((const uint16_t *)a.v_biases + head_row0 * NG, (size_t)end * NG * 2);
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[kQ4Waves * 2 * S::BYTES];
-    static_assert(kQ4Waves * 2 * S::BYTES >= kQ4Waves * GT * D * 4, "wave outputs alias the staging buffers");
+    constexpr int SOD = D + 4;  // wave-output row stride (floats): the 16 heads' rows start in distinct banks
+    static_assert(kQ4Waves * 2 * S::BYTES >= kQ4Waves * GT * SOD * 4, "wave outputs alias the staging buffers");
     const unsigned lds0 = (unsigned)(uintptr_t)(lds_u8_t *)smem;
     const int wbuf = wave * 2 * S::BYTES;  // this wave's two buffers
 
@@ -834,11 +843,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
                     x = __builtin_fmaf(f16_bits_to_f32(ks[r * NG + gg]), acc[u][gg][r], x);
                     y = __builtin_fmaf(f16_bits_to_f32(kb[r * NG + gg]), qs[gg], y);
                 }
-                const float v = __builtin_fmaf(C, x, y);
-                sc[u][r] = r0 + 16 * u + 4 * qg + r < end ? v : kNegInf;
-                mx = fmaxf(mx, sc[u][r]);
+                sc[u][r] = __builtin_fmaf(C, x, y);
             }
         }
+        if (r0 + kQ4Rows > end) {  // the split's last step: rows past its end
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (r0 + 16 * u + 4 * qg + r >= end) sc[u][r] = kNegInf;
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[u][r]);
         mx = max4q(mx);  // finite: the step's first row is valid
         if (m_run == kNegInf) {  // first step of this wave: nothing to rescale
             m_run = mx;
@@ -870,14 +888,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
         {
             const uint32_t *vs0 = (const uint32_t *)(bp + S::VS) + (4 * qg) * NG;
             const uint32_t *vs1 = (const uint32_t *)(bp + S::VS) + (16 + 4 * qg) * NG;
+            float pf[2][4];  // p, divided by 16 for the rows that face 16c slots
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pf[u][r] = (r & 1) ? pr[u][r] * 0.0625f : pr[u][r];
 #pragma unroll
             for (int gg = 0; gg < NG; ++gg) {
                 _Float16 e[8];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float f = (r & 1) ? 0.0625f : 1.0f;
-                    e[2 * r] = (_Float16)(pr[0][r] * f16_bits_to_f32(vs0[r * NG + gg]) * f);
-                    e[2 * r + 1] = (_Float16)(pr[1][r] * f16_bits_to_f32(vs1[r * NG + gg]) * f);
+                    e[2 * r] = (_Float16)__builtin_fmaf(pf[0][r], f16_bits_to_f32(vs0[r * NG + gg]), 0.0f);
+                    e[2 * r + 1] = (_Float16)__builtin_fmaf(pf[1][r], f16_bits_to_f32(vs1[r * NG + gg]), 0.0f);
                 }
                 const q4f16x8_t op = {e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]};
                 pop[gg] = op;
@@ -916,12 +938,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
     for (int gg = 0; gg < NG; ++gg) bsum[gg] = sum4q(bsum[gg]);
     __shared__ float sm[kQ4Waves * GT], sl[kQ4Waves * GT];
     __syncthreads();  // every wave is done with its staging buffers
-    float *so = (float *)smem;  // [waves][GT][D]
+    float *so = (float *)smem;  // [waves][GT][SOD]
     if (j < GT) {
 #pragma unroll
         for (int nb = 0; nb < NDB; ++nb) {
             const float bb = bsum[(16 * nb) / G];
-            *(float4 *)&so[(wave * GT + j) * D + 16 * nb + 4 * qg] =
+            *(float4 *)&so[(wave * GT + j) * SOD + 16 * nb + 4 * qg] =
                 make_float4(16777216.0f * o[nb][0] + bb, 16777216.0f * o[nb][1] + bb, 16777216.0f * o[nb][2] + bb,
                             16777216.0f * o[nb][3] + bb);
         }
@@ -931,7 +953,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
         }
     }
     __syncthreads();
-    finish_split<f16_t, D, GT>(a, so, sm, sl, b * P.HT + ht, s, n_split, out);
+    finish_split<f16_t, D, GT, SOD>(a, so, sm, sl, b * P.HT + ht, s, n_split, out);
     // split s then merges query heads s, s + n_split, ... of its head tile
     if (grid.inplace && n_split > 1)
         for (int hh = s; hh < GT; hh += n_split) merge_head<f16_t, D, GT>(a, (b * P.HT + ht) * GT + hh);
