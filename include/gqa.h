@@ -80,27 +80,30 @@ int gqa_abi_version(void);
 const char *gqa_status_string(int status);
 
 /*
- * Workspaces.  Every workspace starts with a flag region of 16 MiB: the
- * words through which workgroups of one call meet (decode (max, sum) words,
- * a non-zero sum marking a published partial; prefill arrival counters)
- * live only there, and every call leaves the ones it used at zero.  Partial
- * results follow the region.  Since the region's place and size never
- * depend on a call's sizes, one workspace may serve any sequence of decode
- * and prefill calls of any sizes, as long as it is large enough for each
- * call and their work does not overlap in time.
+ * Workspaces.  A workspace must be zero-filled before its first use.  It
+ * begins with a region of 16 MiB that holds the decode (max, sum) pairs and
+ * the prefill arrival counters; the other partial results follow it.  Every
+ * call leaves, once its work has completed, the 16 MiB region zero-filled
+ * and every 32-bit word after it with its lowest bit clear: decode
+ * publishes its partial results with that bit set in every word (which is
+ * how they are recognised) and the workgroup that consumes them zeroes them;
+ * prefill writes its partial results with that bit clear and returns its
+ * counters to zero.  One workspace may therefore serve any sequence of
+ * decode and prefill calls of any sizes, as long as it is large enough for
+ * each call and their work does not overlap in time.
  *
  * Bytes of device workspace the decode entry points need for these sizes:
- * the flag region plus one fp32 partial output per (request, query head,
+ * the 16 MiB region plus one fp32 partial output per (request, query head,
  * split).  Returns 0 when the sizes are invalid, which includes (max, sum)
- * words that would not fit the flag region (8 bytes per request, query head
- * and split; at most 64 splits).  The value depends only on the arguments.
+ * pairs that would not fit the region (8 bytes per request, query head and
+ * split; at most 64 splits).  The value depends only on the arguments.
  */
 size_t gqa_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int s_cap);
 
 /*
  * Prepare a workspace for its first use: zero-fills `bytes` bytes at
- * `workspace` with a kernel on `stream`.  Every entry point leaves the flag
- * region at zero when its work completes, so this is needed once per
+ * `workspace` with a kernel on `stream`.  Every entry point leaves the
+ * workspace ready for the next call (see above), so this is needed once per
  * allocation (a zero-filled allocation needs no call).  Two calls whose work
  * may overlap in time must not share a workspace.
  */
@@ -141,9 +144,9 @@ int gqa_decode_attend_batched(const void *q, const void *k, const void *v, void 
 
 /*
  * Bytes of device workspace gqa_prefill_causal needs for these sizes: the
- * flag region (one u32 arrival counter per request, query head and 128-row
+ * 16 MiB region (one u32 arrival counter per request, query head and 128-row
  * block that is split into key chunks) plus the fp32 partial results of
- * those chunks; when no row block is split, the flag region alone.  Returns
+ * those chunks; when no row block is split, the region alone.  Returns
  * 0 when the sizes are invalid.  The value depends only on the arguments.
  * Like the decode workspace it must start zero-filled (torch.zeros, or
  * gqa_workspace_init once per allocation).

@@ -33,11 +33,13 @@
 // of its tile right after publishing its own partial (it is resident
 // already, so the merge starts as soon as the last partial lands);
 // otherwise the grid carries, after all splits, one merge workgroup per
-// (request, query head).  A split publishes its outputs, waits for them to
-// complete, then writes its (max, sum) pair: the sum is >= 1 (the split's
-// maximum row contributes exp2(0)) and never 0, so a non-zero sum word means
-// "published".  The merge zeroes the words it consumed, leaving the
-// workspace ready for the next call; no counters or atomics are involved.
+// (request, query head).  A split publishes its outputs and its (max, sum)
+// pair with one store each and no wait: every fp32 word is written with its
+// lowest mantissa bit set, so in the zero-filled workspace a word with that
+// bit set has been published.  The merge polls the words it needs (one
+// round trip once they have landed) and zeroes them after reading, leaving
+// the workspace ready for the next call; no counters or atomics are
+// involved.
 // The wait always ends: splits that wait have published already and wait
 // only for splits of their own tile, which never wait before publishing and
 // are either resident (every split is, in the first mode) or dispatched
@@ -49,10 +51,8 @@
 // its own L2, and a device-scope fence writes back / invalidates that L2
 // (tens of microseconds across a full launch).  Instead, every value that
 // crosses workgroups is written and read with device-scope (sc1) accesses,
-// which are coherent at device scope by themselves; a split waits for its
-// output stores to complete (s_waitcnt) before it writes its (max, sum)
-// word, and the merging workgroup reads the outputs only after it has seen
-// every split's word.
+// which are coherent at device scope by themselves; each 32-bit word is
+// written whole, and the merge accepts a word only once its tag bit is set.
 //
 // The 4-bit cache variant (VeloxQuant-MLX "attention" posts, Part 4: codes,
 // scales, biases and the group size go to the kernel, which dequantizes
@@ -188,6 +188,24 @@ __device__ __forceinline__ float rowgroup_sum(float x)
     return a + b;
 }
 
+// max / sum over the 4 lanes l % 16 == j (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float max4q(float x)
+{
+    float a, b;
+    swap16(x, x, a, b);
+    x = fmaxf(a, b);
+    swap32(x, x, a, b);
+    return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum4q(float x)
+{
+    float a, b;
+    swap16(x, x, a, b);
+    x = a + b;
+    swap32(x, x, a, b);
+    return a + b;
+}
+
 constexpr unsigned kMergeSpinLimit = 1u << 22;  // polls before a merge workgroup gives up
 
 // Kernel launch shape of the decode grid: streaming workgroups first, then
@@ -201,13 +219,25 @@ struct DecodeGrid {
 template <typename TQ, int D, int GT>
 __device__ void merge_head(const DecodeArgs &a, int m);
 
+// Published partials carry a tag: every fp32 word is written with its
+// lowest mantissa bit set, so a published word can be told from a word of
+// the zero-filled workspace without a separate flag, and a publisher never
+// waits for its stores.  The tag moves a value by at most one unit in the
+// last place; the reference maximum is tagged before the weights relative
+// to it are taken, so it costs nothing there.
+typedef __attribute__((ext_vector_type(4))) unsigned tag_u4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned tag_u2_t;
+__device__ __forceinline__ float tagged_f32(float x) { return __uint_as_float(__float_as_uint(x) | 1u); }
+__device__ __forceinline__ bool is_tagged4(tag_u4_t w) { return (w[0] & w[1] & w[2] & w[3] & 1u) != 0u; }
+__device__ __forceinline__ bool is_tagged2(tag_u2_t w) { return (w[0] & w[1] & 1u) != 0u; }
+
 // End of a streaming workgroup.  so [waves][GT][SOD] (rows of D floats at
 // a stride of SOD), sm and sl [waves][GT] hold, per wave and query head, the
 // unnormalised output row, its reference maximum (log2 domain; -inf for a
 // wave that saw no row) and its sum of weights.  The waves are combined;
 // with a single split the output is written, otherwise the split's partial
-// is published with device-scope stores: outputs first, then (after they
-// have completed) the (max, sum) word that flags them.
+// is published with tagged device-scope stores (its outputs and its (max,
+// sum) pair), with no wait.
 template <typename TQ, int D, int GT, int SOD = D>
 __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *so, const float *sm, const float *sl,
                                              int col, int s, int n_split, TQ *out)
@@ -230,6 +260,7 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *s
         }
 #pragma unroll
         for (int w = 0; w < NW; ++w) Mw = fmaxf(Mw, mw[w]);
+        if (n_split > 1) Mw = tagged_f32(Mw);  // finite: every split has a row
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             const float wt = rel_weight(mw[w], Mw);
@@ -248,18 +279,14 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *s
     const size_t colbase = (size_t)col * P.n_split_max;
     if (tid < NQ) {
         const int off_o = (int)((((colbase + s) * GT + qh) * D + qd) * 4);
-        __builtin_amdgcn_raw_buffer_store_b128(
-            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, make_float4(O0, O1, O2, O3)), ws_o,
-            off_o, 0, kSC1);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's output stores have completed
-    __syncthreads();                // ... and so have every other wave's
-    if (tid < NQ && qd == 0) {
-        const int off_ml = (int)(((colbase + s) * GT + qh) * 2 * 4);
-        __builtin_amdgcn_raw_buffer_store_b64(
-            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, make_float2(Mw, Lw)), ws_ml, off_ml, 0,
-            kSC1);
+        const tag_u4_t w = {__float_as_uint(O0) | 1u, __float_as_uint(O1) | 1u, __float_as_uint(O2) | 1u,
+                            __float_as_uint(O3) | 1u};
+        __builtin_amdgcn_raw_buffer_store_b128(w, ws_o, off_o, 0, kSC1);
+        if (qd == 0) {
+            const int off_ml = (int)(((colbase + s) * GT + qh) * 2 * 4);
+            const tag_u2_t wm = {__float_as_uint(Mw), __float_as_uint(Lw) | 1u};
+            __builtin_amdgcn_raw_buffer_store_b64(wm, ws_ml, off_ml, 0, kSC1);
+        }
     }
 }
 
@@ -467,10 +494,12 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     constexpr int D4 = D / 4;
     constexpr int NG = kDecodeThreads / D4;              // split groups
     constexpr int PER = (kDecodeMaxSplits + NG - 1) / NG; // splits per group
+    static_assert(kDecodeMaxSplits <= 64, "every split's (max, sum) pair is polled by a lane of wave 0");
     __shared__ float2 sml[kDecodeMaxSplits];
     __shared__ float4 sacc[NG][D4];
     __shared__ float sls[NG][D4];
     __shared__ int s_go;
+    __shared__ float s_M;
     const DecodePlan &P = a.plan;
     const int tid = threadIdx.x;
     __syncthreads();  // a previous merge in this workgroup is done with the shared arrays
@@ -489,40 +518,66 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     const int h = g * P.G + (ht % P.ht_per_kv) * GT + hh;
     TQ *out = (TQ *)a.out + ((size_t)b * a.Hq + h) * D;
 
-    // wait until every split has published this head's partial: thread j
-    // polls split j's (max, sum) word (the sum is never 0 once written)
+    // Wait until every split has published this head's partial: each thread
+    // polls the tagged words it needs -- the (max, sum) pair of split tid
+    // (tid < n_split) and its output slices of splits grp + k * NG -- and
+    // zeroes them once read, leaving the workspace as it found it.
     const size_t colbase = (size_t)col * P.n_split_max;
     const __amdgpu_buffer_rsrc_t ws_ml = make_rsrc(a.part_ml + colbase * GT * 2, (size_t)n_split * GT * 8);
+    const __amdgpu_buffer_rsrc_t ws_o = make_rsrc(a.part_o + colbase * GT * D, (size_t)n_split * GT * D * 4);
+    const int d4 = tid % D4, grp = tid / D4;
+    auto o_off = [&](int k) { return (int)(((((size_t)grp + (size_t)k * NG) * GT + hh) * D + d4 * 4) * 4); };
     if (tid == 0) s_go = 1;
     __syncthreads();
-    if (tid < n_split) {
-        unsigned it = 0;
-        float2 ml = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(ws_ml, (tid * GT + hh) * 8, 0, kSC1));
-        while (__float_as_uint(ml.y) == 0u && ++it < kMergeSpinLimit) {
-            __builtin_amdgcn_s_sleep(2);
-            ml = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(ws_ml, (tid * GT + hh) * 8, 0, kSC1));
-        }
-        sml[tid] = ml;
-        if (__float_as_uint(ml.y) == 0u) s_go = 0;
+    tag_u4_t po[PER];
+    tag_u2_t mlw = {0u, 0u};
+    unsigned need = tid < n_split ? 1u << PER : 0u;  // bit k: slice k, bit PER: the pair
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+        if (grp + k * NG < n_split) need |= 1u << k;
+    // Every poll issues all of this thread's loads before looking at any of
+    // them (one round trip per poll).  Loads of splits past n_split fall
+    // outside the resources' ranges: they read zero and touch no memory.
+    unsigned pend = need;
+    for (unsigned it = 0;; ++it) {
+#pragma unroll
+        for (int k = 0; k < PER; ++k)
+            po[k] = __builtin_bit_cast(tag_u4_t, __builtin_amdgcn_raw_buffer_load_b128(ws_o, o_off(k), 0, kSC1));
+        mlw = __builtin_bit_cast(tag_u2_t, __builtin_amdgcn_raw_buffer_load_b64(ws_ml, (tid * GT + hh) * 8, 0, kSC1));
+        unsigned ok = is_tagged2(mlw) ? 1u << PER : 0u;
+#pragma unroll
+        for (int k = 0; k < PER; ++k)
+            if (is_tagged4(po[k])) ok |= 1u << k;
+        pend = need & ~ok;
+        if (pend == 0u || it + 1 >= kMergeSpinLimit) break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    if (pend != 0u) {
+        s_go = 0;
+    } else {
+        // consume: every word read goes back to zero
+#pragma unroll
+        for (int k = 0; k < PER; ++k)
+            if (grp + k * NG < n_split)
+                __builtin_amdgcn_raw_buffer_store_b128(tag_u4_t{0u, 0u, 0u, 0u}, ws_o, o_off(k), 0, kSC1);
+        if (tid < n_split) __builtin_amdgcn_raw_buffer_store_b64(tag_u2_t{0u, 0u}, ws_ml, (tid * GT + hh) * 8, 0, kSC1);
+    }
+    if (tid < n_split) sml[tid] = __builtin_bit_cast(float2, mlw);
+    if (tid < 64) {  // the maximum over the splits, reduced within wave 0
+        float mx = tid < n_split ? __builtin_bit_cast(float2, mlw).x : kNegInf;
+        mx = fmaxf(mx, dpp_f32<0xB1>(mx));
+        mx = fmaxf(mx, dpp_f32<0x4E>(mx));
+        mx = fmaxf(mx, dpp_f32<0x141>(mx));
+        mx = fmaxf(mx, dpp_f32<0x140>(mx));
+        mx = max4q(mx);
+        if (tid == 0) s_M = mx;
     }
     __syncthreads();
-    const int d4 = tid % D4, grp = tid / D4;
-    if (!s_go) {  // not reachable with in-order dispatch; never pass silently
+    if (!s_go) {  // not reachable: every split publishes; never pass silently
         if (grp == 0) store4(out + d4 * 4, __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
         return;
     }
-
-    const __amdgpu_buffer_rsrc_t ws_o =
-        make_rsrc(a.part_o + colbase * GT * D, (size_t)n_split * GT * D * 4);  // splits past n_split read 0
-    float4 po[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int j = grp + k * NG;
-        const int off = (int)((((size_t)j * GT + hh) * D + d4 * 4) * 4);
-        po[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ws_o, off, 0, kSC1));
-    }
-    float M = kNegInf;
-    for (int j = 0; j < n_split; ++j) M = fmaxf(M, sml[j].x);
+    const float M = s_M;
     float Ls = 0.0f;
     float4 R = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
@@ -531,8 +586,9 @@ __device__ void merge_head(const DecodeArgs &a, int m)
         if (j < n_split) {
             const float2 ml = sml[j];
             const float w = rel_weight(ml.x, M);
+            const float4 x = __builtin_bit_cast(float4, po[k]);
             Ls += w * ml.y;
-            R.x += w * po[k].x; R.y += w * po[k].y; R.z += w * po[k].z; R.w += w * po[k].w;
+            R.x += w * x.x; R.y += w * x.y; R.z += w * x.z; R.w += w * x.w;
         }
     }
     sacc[grp][d4] = R;
@@ -547,12 +603,6 @@ __device__ void merge_head(const DecodeArgs &a, int m)
         }
         store4(out + d4 * 4, R.x / Ls, R.y / Ls, R.z / Ls, R.w / Ls);
     }
-    // consume the flags: this head's (max, sum) words go back to zero (the
-    // reads above have completed: their values were used)
-    if (tid < n_split)
-        __builtin_amdgcn_raw_buffer_store_b64(
-            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, make_float2(0.0f, 0.0f)), ws_ml,
-            (tid * GT + hh) * 8, 0, kSC1);
 }
 
 // ===========================================================================
@@ -634,24 +684,6 @@ __device__ __forceinline__ q4f16x8_t q4_operand(uint32_t w)
     const uint32_t h = w >> 8;
     const u32x4_t x = {w & 0x000F000Fu, w & 0x00F000F0u, h & 0x000F000Fu, h & 0x00F000F0u};
     return __builtin_bit_cast(q4f16x8_t, x);
-}
-
-// max / sum over the 4 lanes l % 16 == j (lanes l, l^16, l^32, l^48)
-__device__ __forceinline__ float max4q(float x)
-{
-    float a, b;
-    swap16(x, x, a, b);
-    x = fmaxf(a, b);
-    swap32(x, x, a, b);
-    return fmaxf(a, b);
-}
-__device__ __forceinline__ float sum4q(float x)
-{
-    float a, b;
-    swap16(x, x, a, b);
-    x = a + b;
-    swap32(x, x, a, b);
-    return a + b;
 }
 
 template <int D, int G, int GT>

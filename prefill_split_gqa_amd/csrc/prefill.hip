@@ -447,7 +447,9 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D ==
     // Every chunk stores its partial with device-scope stores, waits for
     // them, and takes a ticket; the chunk that arrives last merges all of
     // them in chunk order (so the result does not depend on timing), writes
-    // the output and returns the counter to zero.  Counters sit in the
+    // the output and returns the counter to zero.  Partial words are written
+    // with their lowest bit clear (at most one unit in the last place), so
+    // what they leave behind never looks like a published decode word.  Counters sit in the
     // workspace's flag region, partials after it, both indexed by the split
     // row block (nc > 1 exactly for row blocks rb0 and later: the tile count
     // grows with the row block).
@@ -460,16 +462,17 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D ==
         typedef __attribute__((ext_vector_type(2))) unsigned u2;
         auto o_off = [&](int c, int db, int qd) { return c * SL::BYTES + (((rw * NDB + db) * 4 + qd) * 64 + lane) * 16; };
         auto ml_off = [&](int c) { return c * SL::BYTES + (SL::O_FLOATS + (rw * 64 + lane) * 2) * 4; };
+        const unsigned clr = ~1u;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd)
                 __builtin_amdgcn_raw_buffer_store_b128(
                     __builtin_bit_cast(u4, make_float4(acc[db][4 * qd], acc[db][4 * qd + 1], acc[db][4 * qd + 2],
-                                                       acc[db][4 * qd + 3])),
+                                                       acc[db][4 * qd + 3])) & clr,
                     rs, o_off(chunk, db, qd), 0, kSC1);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, make_float2(m_run, l_part)), rs, ml_off(chunk), 0,
-                                              kSC1);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, make_float2(m_run, l_part)) & clr, rs,
+                                              ml_off(chunk), 0, kSC1);
         __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
         __syncthreads();                // ... and so have every other thread's
         __shared__ int s_last;

@@ -49,3 +49,19 @@ class Guarded:
         b = self.buf.float().cpu()
         s = torch.tensor(self.sentinel, dtype=self.buf.dtype).float()
         assert (b[:self.PAD] == s).all() and (b[self.PAD + self.n:] == s).all(), "write outside the output"
+
+
+REGION_BYTES = 16 << 20  # region at the front of every workspace
+
+
+def assert_workspace_ready(ws: torch.Tensor, what: str) -> None:
+    """A workspace between calls: the 16 MiB region zero-filled, and every
+    32-bit word after it with its lowest bit clear (decode recognises its
+    published partial words by that bit)."""
+    torch.cuda.synchronize()
+    head = ws[:REGION_BYTES]
+    assert int((head != 0).sum()) == 0, "region not zero-filled: " + what
+    rest = ws[REGION_BYTES:]
+    n = rest.numel() // 4 * 4
+    words = rest[:n].view(torch.int32)
+    assert int((words & 1).sum()) == 0, "a word past the region has its lowest bit set: " + what

@@ -17,13 +17,12 @@ import pytest
 import torch
 
 import oracle
-from tests.helpers import Guarded, assert_close, note
+from tests.helpers import Guarded, assert_close, assert_workspace_ready, note
 from workloads import configs as W
 
 pytestmark = pytest.mark.gpu
 
 
-FLAG_BYTES = 16 << 20  # fixed flag region at the front of every workspace
 
 
 def prefill_ws(gqa, q, k, Tk=None):
@@ -135,9 +134,9 @@ def test_prefill_deterministic(gpu_lib):
 
 def test_prefill_workspace_reuse(gpu_lib):
     # The key chunks of a long row block meet through the workspace: the last
-    # to arrive merges and returns the counter to zero.  Many calls in a row
-    # on one workspace, with changing inputs and lengths, must each match a
-    # fresh run, and leave every counter at zero.
+    # to arrive merges and returns the slots and the counter to zero.  Many
+    # calls in a row on one workspace, with changing inputs and lengths, must
+    # each match a fresh run, and leave the workspace ready for the next call.
     w = W.by_name("prefill_0p5b")
     q0, k0, v0 = (t.cuda() for t in W.prefill_inputs(w, 2049))
     Hq, Hkv, D = q0.shape[1], k0.shape[1], q0.shape[3]
@@ -155,7 +154,7 @@ def test_prefill_workspace_reuse(gpu_lib):
         gpu_lib.gqa_prefill_causal(q, k, v0, ref, prefill_ws(gpu_lib, q, k, Tk), Tk=Tk)
         torch.cuda.synchronize()
         assert torch.equal(got, ref), "it=%d" % it
-        assert int((ws[:FLAG_BYTES] != 0).sum()) == 0, "counters not reset, it=%d" % it
+        assert_workspace_ready(ws, "it=%d" % it)
 
 
 def test_workspace_shared_by_decode_and_prefill(gpu_lib):
@@ -184,7 +183,7 @@ def test_workspace_shared_by_decode_and_prefill(gpu_lib):
         torch.cuda.synchronize()
         assert torch.equal(got, ref), "prefill it=%d" % it
         assert torch.equal(got_d, ref_d), "decode it=%d" % it
-        assert int((ws[:FLAG_BYTES] != 0).sum()) == 0, "flags not cleared, it=%d" % it
+        assert_workspace_ready(ws, "it=%d" % it)
 
 
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 0.9])
