@@ -580,14 +580,15 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     const float M = s_M;
     float Ls = 0.0f;
     float4 R = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float2 mlk[PER];  // all (max, sum) reads first (clamped to a valid split)
+#pragma unroll
+    for (int k = 0; k < PER; ++k) mlk[k] = sml[min(grp + k * NG, n_split - 1)];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-        const int j = grp + k * NG;
-        if (j < n_split) {
-            const float2 ml = sml[j];
-            const float w = rel_weight(ml.x, M);
+        if (grp + k * NG < n_split) {
+            const float w = rel_weight(mlk[k].x, M);
             const float4 x = __builtin_bit_cast(float4, po[k]);
-            Ls += w * ml.y;
+            Ls += w * mlk[k].y;
             R.x += w * x.x; R.y += w * x.y; R.z += w * x.z; R.w += w * x.w;
         }
     }
@@ -595,11 +596,17 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     sls[grp][d4] = Ls;
     __syncthreads();
     if (grp == 0) {
+        float4 xs[NG];  // all reads first, then the sums in group order
+        float ls[NG];
 #pragma unroll
         for (int q = 1; q < NG; ++q) {
-            const float4 x = sacc[q][d4];
-            Ls += sls[q][d4];
-            R.x += x.x; R.y += x.y; R.z += x.z; R.w += x.w;
+            xs[q] = sacc[q][d4];
+            ls[q] = sls[q][d4];
+        }
+#pragma unroll
+        for (int q = 1; q < NG; ++q) {
+            Ls += ls[q];
+            R.x += xs[q].x; R.y += xs[q].y; R.z += xs[q].z; R.w += xs[q].w;
         }
         store4(out + d4 * 4, R.x / Ls, R.y / Ls, R.z / Ls, R.w / Ls);
     }
