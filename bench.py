@@ -49,6 +49,7 @@ DECODE_SRCS = [os.path.join(ROOT, "prefill_split_gqa_amd", "csrc", f) for f in (
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_7b_s4096_traffic.txt")
 PREFILL_SRCS = [os.path.join(ROOT, "prefill_split_gqa_amd", "csrc", f) for f in ("prefill.hip", "common.h")]
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_0p5b_t4097_traffic.txt")
+Q4_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4_decode_s16384_traffic.txt")
 
 
 def decode_bytes(S: int, Hq: int = 28, Hkv: int = 4, D: int = 128, elem: int = 4) -> int:
@@ -225,27 +226,39 @@ def graph_of(torch, eager):
     return g
 
 
-def hbm_entry(us, nbytes, gate_ok, gate_max_abs, kernel, **extra):
+def hbm_entry(us, nbytes, gate_ok, gate_max_abs, kernel, traffic=None, **extra):
     """A secondary result for an HBM-bound configuration."""
     gbs = nbytes / (us * 1e-6) / 1e9
     d = {"us_layer": round(us, 3), "GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
          "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                       "algorithmic_bytes_per_launch": nbytes, "launch_duration_us": round(us, 3)},
          "parity_ok": gate_ok, "parity_max_abs": gate_max_abs}
     d.update(extra)
     return d
 
 
-def bench_extra(torch, gqa, oracle, W, steps, warmup, flush):
-    """The other configurations of the workload set, each timed like the
-    headline (per-layer inputs of their own, cache flushed before each step,
-    one step captured in a HIP graph) after a parity gate on layer 0 against
-    the oracle; layers past the first are device copies of it, scaled (codes
-    permuted for the 4-bit cache), so that every layer reads its own memory."""
+EXTRAS = ("decode_0p5b_s128", "batched_qwen3_4b", "q4_decode_s2048", "q4_decode_s16384",
+          "prefill_0p5b_chunk256_at3841")
+
+
+def bench_extra(torch, gqa, oracle, W, steps, warmup, flush, names=EXTRAS):
+    """The other configurations of the workload set (those named), each timed
+    like the headline (per-layer inputs of their own, cache flushed before
+    each step, one step captured in a HIP graph) after a parity gate on layer
+    0 against the oracle; layers past the first are device copies of it,
+    scaled (codes permuted for the 4-bit cache), so that every layer reads its
+    own memory."""
     out = {}
-    for part in (extra_decode_small, extra_batched, extra_q4, extra_chunked_prefill):
-        out.update(part(torch, gqa, oracle, W, steps, warmup, flush))
+    if "decode_0p5b_s128" in names:
+        out.update(extra_decode_small(torch, gqa, oracle, W, steps, warmup, flush))
+    if "batched_qwen3_4b" in names:
+        out.update(extra_batched(torch, gqa, oracle, W, steps, warmup, flush))
+    sizes = tuple(S for S in (2048, 16384) if "q4_decode_s%d" % S in names)
+    if sizes:
+        out.update(extra_q4(torch, gqa, oracle, W, steps, warmup, flush, sizes=sizes))
+    if "prefill_0p5b_chunk256_at3841" in names:
+        out.update(extra_chunked_prefill(torch, gqa, oracle, W, steps, warmup, flush))
     return out
 
 
@@ -341,7 +354,8 @@ def extra_q4(torch, gqa, oracle, W, steps, warmup, flush, sizes=(2048, 16384)):
         us = float(np.median(time_steps(torch, g.replay, steps, warmup, flush))) * 1e3 / w.layers
         ok = err <= 2e-2 and all(torch.equal(a, b) for a, b in zip(outs, ref))
         nbytes = S * w.Hkv * 2 * (w.D // 2 + 2 * 2 * (w.D // w.group)) + 2 * w.Hq * w.D * 2
-        out["q4_decode_s%d" % S] = hbm_entry(us, nbytes, ok, err, "decode_q4_kernel<128,64,8>",
+        traffic = read_traffic(Q4_TRAFFIC_FILE, "decode_source_sha256_16", DECODE_SRCS) if S == 16384 else None
+        out["q4_decode_s%d" % S] = hbm_entry(us, nbytes, ok, err, "decode_q4_kernel<128,64,8>", traffic=traffic,
                                              layers_per_step=w.layers)
         del dev, outs, ref, g
         torch.cuda.empty_cache()
@@ -412,6 +426,8 @@ def main():
     ap.add_argument("--S", type=int, default=4096, help="KV length of the headline decode workload")
     ap.add_argument("--sweep", action="store_true", help="also time KV lengths 128..2048 and the other prefill sizes")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--extras", default=",".join(EXTRAS),
+                    help="comma-separated extra configurations to time (default: all of " + ", ".join(EXTRAS) + ")")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other configurations (decode S=128, batched, 4-bit, chunked prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -506,7 +522,11 @@ def main():
                              "algorithmic_flop_per_launch": p["flops"], "launch_duration_us": round(us, 2)},
                 "parity_ok": p["gate_ok"], "parity_max_abs": p["gate_max_abs"]}
     if not args.no_extra:
-        secondary.update(bench_extra(torch, gqa, oracle, W, max(5, args.steps // 2), 2, flush))
+        names = tuple(x for x in args.extras.split(",") if x)
+        unknown = [x for x in names if x not in EXTRAS]
+        if unknown:
+            sys.exit("bench.py: unknown --extras %s (known: %s)" % (",".join(unknown), ",".join(EXTRAS)))
+        secondary.update(bench_extra(torch, gqa, oracle, W, max(5, args.steps // 2), 2, flush, names))
     if secondary:
         result["secondary"] = secondary
 

@@ -368,15 +368,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
     if (q_loader) *((uint4 *)sq + tid) = qv;
     __syncthreads();
 
-    // Queries of the GT heads, pre-multiplied by scale*log2(e).
+    // Queries of the GT heads, pre-multiplied by scale*log2(e) (every LDS
+    // read issued before the first is used).
     float qf[GT][EPL];
+    {
+        typename KV::QRaw qraw[GT];
 #pragma unroll
-    for (int h = 0; h < GT; ++h) {
-        typename KV::QRaw qraw;
-        KV::load_q_lds(qraw, sq, h, lr);
-        KV::unpack_q(qraw, qf[h]);
+        for (int h = 0; h < GT; ++h) KV::load_q_lds(qraw[h], sq, h, lr);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) qf[h][e] *= a.qscale;
+        for (int h = 0; h < GT; ++h) {
+            KV::unpack_q(qraw[h], qf[h]);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) qf[h][e] *= a.qscale;
+        }
     }
 
     float m[GT], l[GT], o[GT][EPL];
