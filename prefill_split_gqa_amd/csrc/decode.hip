@@ -487,25 +487,44 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
         for (int hh = s; hh < GT; hh += n_split) merge_head<TQ, D, GT>(a, (b * P.HT + ht) * GT + hh);
 }
 
+// Sum over the lanes of a wave that share lane % CPW (CPW a power of two
+// below 16): rotations by CPW, 2 CPW, ... inside each 16-lane row, then the
+// two row swaps.  Every lane of the group ends with the same value.
+template <int CPW> __device__ __forceinline__ float colgroup_sum(float x)
+{
+    if constexpr (CPW <= 1) x += dpp_f32<0x121>(x);  // row_ror:1
+    if constexpr (CPW <= 2) x += dpp_f32<0x122>(x);  // row_ror:2
+    if constexpr (CPW <= 4) x += dpp_f32<0x124>(x);  // row_ror:4
+    if constexpr (CPW <= 8) x += dpp_f32<0x128>(x);  // row_ror:8
+    return sum4q(x);
+}
+
 // Merge of item m = (request b, head tile ht) * GT + hh: the partials of
 // every split for query head h0 + hh, combined by a whole workgroup (one
-// that has published its own split).  Thread t handles 4 dims (t % (D/4)) of
-// the splits j = t / (D/4) + k * NG; the NG strided groups are then added in
-// group order.
+// that has published its own split, or a merge workgroup).  Wave w owns the
+// 4-wide output columns w*CPW .. w*CPW + CPW - 1; lane (c = lane % CPW,
+// sg = lane / CPW) handles column c of the splits sg + k*LPC and polls
+// those output slices itself.  Wave 0 polls the (max, sum) pairs (lane j:
+// split j) and leaves them and their maximum in LDS; after one barrier each
+// wave forms its weights and sums its lanes with cross-lane steps.
 template <typename TQ, int D, int GT>
 __device__ void merge_head(const DecodeArgs &a, int m)
 {
-    constexpr int D4 = D / 4;
-    constexpr int NG = kDecodeThreads / D4;              // split groups
-    constexpr int PER = (kDecodeMaxSplits + NG - 1) / NG; // splits per group
+    constexpr int D4 = D / 4;                     // 4-wide output columns
+    constexpr int NW = kDecodeThreads / 64;       // waves
+    constexpr int CPW = D4 / NW;                  // columns per wave
+    constexpr int LPC = 64 / CPW;                 // lanes per column
+    constexpr int PER = kDecodeMaxSplits / LPC;   // splits per lane
+    static_assert(CPW * NW == D4 && CPW < 16 && LPC * PER == kDecodeMaxSplits, "merge layout");
     static_assert(kDecodeMaxSplits <= 64, "every split's (max, sum) pair is polled by a lane of wave 0");
     __shared__ float2 sml[kDecodeMaxSplits];
-    __shared__ float4 sacc[NG][D4];
-    __shared__ float sls[NG][D4];
     __shared__ int s_go;
     __shared__ float s_M;
     const DecodePlan &P = a.plan;
     const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int c = lane % CPW, sg = lane / CPW;
+    const int d4 = wave * CPW + c;
     __syncthreads();  // a previous merge in this workgroup is done with the shared arrays
     const int hh = m % GT;
     const int col = m / GT;
@@ -524,13 +543,12 @@ __device__ void merge_head(const DecodeArgs &a, int m)
 
     // Wait until every split has published this head's partial: each thread
     // polls the tagged words it needs -- the (max, sum) pair of split tid
-    // (tid < n_split) and its output slices of splits grp + k * NG -- and
+    // (tid < n_split) and its output slices of splits sg + k * LPC -- and
     // zeroes them once read, leaving the workspace as it found it.
     const size_t colbase = (size_t)col * P.n_split_max;
     const __amdgpu_buffer_rsrc_t ws_ml = make_rsrc(a.part_ml + colbase * GT * 2, (size_t)n_split * GT * 8);
     const __amdgpu_buffer_rsrc_t ws_o = make_rsrc(a.part_o + colbase * GT * D, (size_t)n_split * GT * D * 4);
-    const int d4 = tid % D4, grp = tid / D4;
-    auto o_off = [&](int k) { return (int)(((((size_t)grp + (size_t)k * NG) * GT + hh) * D + d4 * 4) * 4); };
+    auto o_off = [&](int k) { return (int)(((((size_t)sg + (size_t)k * LPC) * GT + hh) * D + d4 * 4) * 4); };
     if (tid == 0) s_go = 1;
     __syncthreads();
     tag_u4_t po[PER];
@@ -538,7 +556,7 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     unsigned need = tid < n_split ? 1u << PER : 0u;  // bit k: slice k, bit PER: the pair
 #pragma unroll
     for (int k = 0; k < PER; ++k)
-        if (grp + k * NG < n_split) need |= 1u << k;
+        if (sg + k * LPC < n_split) need |= 1u << k;
     // Every poll issues all of this thread's loads before looking at any of
     // them (one round trip per poll).  Loads of splits past n_split fall
     // outside the resources' ranges: they read zero and touch no memory.
@@ -562,7 +580,7 @@ __device__ void merge_head(const DecodeArgs &a, int m)
         // consume: every word read goes back to zero
 #pragma unroll
         for (int k = 0; k < PER; ++k)
-            if (grp + k * NG < n_split)
+            if (sg + k * LPC < n_split)
                 __builtin_amdgcn_raw_buffer_store_b128(tag_u4_t{0u, 0u, 0u, 0u}, ws_o, o_off(k), 0, kSC1);
         if (tid < n_split) __builtin_amdgcn_raw_buffer_store_b64(tag_u2_t{0u, 0u}, ws_ml, (tid * GT + hh) * 8, 0, kSC1);
     }
@@ -578,7 +596,7 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     }
     __syncthreads();
     if (!s_go) {  // not reachable: every split publishes; never pass silently
-        if (grp == 0) store4(out + d4 * 4, __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
+        if (sg == 0) store4(out + d4 * 4, __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
         return;
     }
     const float M = s_M;
@@ -586,34 +604,22 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     float4 R = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     float2 mlk[PER];  // all (max, sum) reads first (clamped to a valid split)
 #pragma unroll
-    for (int k = 0; k < PER; ++k) mlk[k] = sml[min(grp + k * NG, n_split - 1)];
+    for (int k = 0; k < PER; ++k) mlk[k] = sml[min(sg + k * LPC, n_split - 1)];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-        if (grp + k * NG < n_split) {
+        if (sg + k * LPC < n_split) {
             const float w = rel_weight(mlk[k].x, M);
             const float4 x = __builtin_bit_cast(float4, po[k]);
             Ls += w * mlk[k].y;
             R.x += w * x.x; R.y += w * x.y; R.z += w * x.z; R.w += w * x.w;
         }
     }
-    sacc[grp][d4] = R;
-    sls[grp][d4] = Ls;
-    __syncthreads();
-    if (grp == 0) {
-        float4 xs[NG];  // all reads first, then the sums in group order
-        float ls[NG];
-#pragma unroll
-        for (int q = 1; q < NG; ++q) {
-            xs[q] = sacc[q][d4];
-            ls[q] = sls[q][d4];
-        }
-#pragma unroll
-        for (int q = 1; q < NG; ++q) {
-            Ls += ls[q];
-            R.x += xs[q].x; R.y += xs[q].y; R.z += xs[q].z; R.w += xs[q].w;
-        }
-        store4(out + d4 * 4, R.x / Ls, R.y / Ls, R.z / Ls, R.w / Ls);
-    }
+    Ls = colgroup_sum<CPW>(Ls);
+    R.x = colgroup_sum<CPW>(R.x);
+    R.y = colgroup_sum<CPW>(R.y);
+    R.z = colgroup_sum<CPW>(R.z);
+    R.w = colgroup_sum<CPW>(R.w);
+    if (sg == 0) store4(out + d4 * 4, R.x / Ls, R.y / Ls, R.z / Ls, R.w / Ls);
 }
 
 // ===========================================================================
