@@ -83,7 +83,9 @@ def test_q4_dequant_of_workload_cache(gpu_lib):
 @pytest.mark.parametrize("D,group", [(128, 64), (128, 32), (64, 64), (64, 32), (128, 128)])
 def test_q4_small_ragged(gpu_lib, D, group):
     rng = np.random.default_rng(D + group)
-    for Hq, Hkv, n, s_cap in [(8, 8, 1, 4), (64, 8, 33, 70), (16, 2, 100, 100), (12, 4, 777, 800)]:
+    # (32, 2): 16 query heads per KV head, two head tiles of 8 reading the same KV head
+    for Hq, Hkv, n, s_cap in [(8, 8, 1, 4), (64, 8, 33, 70), (16, 2, 100, 100), (12, 4, 777, 800),
+                              (32, 2, 300, 320), (10, 2, 64, 64)]:
         x_k = rng.standard_normal((1, Hkv, s_cap, D)).astype(np.float32)
         x_v = rng.standard_normal((1, Hkv, s_cap, D)).astype(np.float32)
         kc, ks, kb = gen.q4_encode(x_k, group)
