@@ -214,7 +214,51 @@ struct DecodeGrid {
     int gx;        // splits per (request, head tile) in the grid
     int n_stream;  // gx * HT * B splits; merge workgroups (if any) follow
     int inplace;   // 1: the splits merge themselves (no merge workgroups)
+    int B;         // requests
 };
+
+// With per-request lengths and at most kDecodePackMaxB requests, the
+// working splits are packed at the front of the grid: request b's
+// HT * max(1, n_split(b)) items (head tile major, split minor) follow those
+// of requests 0 .. b-1, so no workgroup slot goes to a split past its
+// request's length (a request of length 0 keeps one item per head tile,
+// which writes its zero output).  Every wave derives the same mapping:
+// lane r reads request r's length, the items are prefix-summed across the
+// lanes, and a ballot finds the request holding item i.  The split
+// boundaries, and so the results, are those of the strided mapping.
+constexpr int kDecodePackMaxB = 64;
+struct SplitItem {
+    int b, ht, s, n;  // request, head tile, split, clamped length
+};
+__device__ __forceinline__ bool packed_item(const DecodeArgs &a, int B, int i, SplitItem *it)
+{
+    const DecodePlan &P = a.plan;
+    const int lane = threadIdx.x & 63;
+    int n = 0;
+    if (lane < B) {
+        n = a.kv_lens[lane];
+        n = n < 0 ? 0 : (n > a.s_cap ? a.s_cap : n);
+    }
+    const int ns = (n + P.L - 1) / P.L;
+    const int items = lane < B ? P.HT * (ns > 1 ? ns : 1) : 0;
+    int incl = items;  // inclusive prefix sum over the lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += y;
+    }
+    const int b = __popcll(__ballot(incl <= i));  // requests whose items all precede item i
+    if (b >= B) return false;                      // past the working items
+    const int start = __shfl(incl - items, b, 64);
+    const int nb = __shfl(n, b, 64);
+    const int local = i - start;
+    const int nsb = (nb + P.L - 1) / P.L > 1 ? (nb + P.L - 1) / P.L : 1;
+    it->b = __builtin_amdgcn_readfirstlane(b);
+    it->n = __builtin_amdgcn_readfirstlane(nb);
+    it->ht = __builtin_amdgcn_readfirstlane(local / nsb);
+    it->s = __builtin_amdgcn_readfirstlane(local % nsb);
+    return true;
+}
 
 template <typename TQ, int D, int GT>
 __device__ void merge_head(const DecodeArgs &a, int m);
@@ -311,14 +355,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
     const int wave = tid >> 6, lane = tid & 63, rgq = lane >> 5, lr = lane & 31;
     const int rg = wave * 2 + rgq;  // row-group (half wave) within the workgroup
     const DecodePlan &P = a.plan;
-    const int s = (int)blockIdx.x % grid.gx;
-    const int ht = ((int)blockIdx.x / grid.gx) % P.HT;
-    const int b = (int)blockIdx.x / (grid.gx * P.HT);
-
-    int n = a.kv_len;
-    if (a.kv_lens) {
-        n = a.kv_lens[b];
-        n = n < 0 ? 0 : (n > a.s_cap ? a.s_cap : n);
+    int s, ht, b, n;
+    if (a.kv_lens && grid.B <= kDecodePackMaxB) {
+        SplitItem it;
+        if (!packed_item(a, grid.B, (int)blockIdx.x, &it)) return;
+        s = it.s; ht = it.ht; b = it.b; n = it.n;
+    } else {
+        s = (int)blockIdx.x % grid.gx;
+        ht = ((int)blockIdx.x / grid.gx) % P.HT;
+        b = (int)blockIdx.x / (grid.gx * P.HT);
+        n = a.kv_len;
+        if (a.kv_lens) {
+            n = a.kv_lens[b];
+            n = n < 0 ? 0 : (n > a.s_cap ? a.s_cap : n);
+        }
     }
     const int n_split = (n + P.L - 1) / P.L;
     const int g = ht / P.ht_per_kv;
@@ -1021,6 +1071,7 @@ static int decode_grid(int B, int GT, const DecodeArgs &a, DecodeGrid *g)
 {
     g->gx = a.kv_lens ? a.plan.n_split_max : (a.kv_len + a.plan.L - 1) / a.plan.L;
     g->n_stream = g->gx * a.plan.HT * B;
+    g->B = B;
     const bool several = a.plan.n_split_max > 1 && g->gx > 1;
     g->inplace = g->n_stream <= a.n_cus ? 1 : 0;
     return several && !g->inplace ? B * a.plan.HT * GT : 0;

@@ -183,6 +183,35 @@ def test_batched_lengths_zero_clamped_and_ragged(gpu_lib):
     assert (got[0] == 0).all() and (got[5] == 0).all()
 
 
+@pytest.mark.parametrize("B", [64, 70])
+def test_batched_many_requests(gpu_lib, B):
+    # Up to 64 requests, the splits that have rows are packed at the front of
+    # the grid (each workgroup derives its request, head tile and split from
+    # all the lengths); past 64 the grid is strided over (request, head tile,
+    # split).  Both must match the oracle, with empty and full requests mixed
+    # in, and each request must equal its own single-request call.
+    Hq, Hkv, D, s_cap = 8, 2, 64, 96
+    rng = np.random.default_rng(B)
+    q = torch.from_numpy(rng.standard_normal((B, Hq, 1, D), dtype=np.float32)).to(torch.bfloat16)
+    k = torch.from_numpy(rng.standard_normal((B, Hkv, s_cap, D), dtype=np.float32)).to(torch.bfloat16)
+    v = torch.from_numpy(rng.standard_normal((B, Hkv, s_cap, D), dtype=np.float32)).to(torch.bfloat16)
+    lens = rng.integers(0, s_cap + 1, size=B).astype(np.int32)
+    lens[0], lens[1], lens[B - 1] = 0, s_cap, 1
+    note("batched many requests B=%d" % B)
+    got = run_batched(gpu_lib, q, k, v, lens)
+    assert_close(got, oracle.attend(q, k, v, kv_lens=lens), 2e-2, "B=%d" % B)
+    assert (got[0].cpu() == 0).all()
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    for b in (1, 2, B // 2, B - 1):
+        if lens[b] == 0:  # (a single-request call needs a length of at least 1)
+            continue
+        ws = gpu_lib.make_workspace(1, Hq, Hkv, D, s_cap)
+        o1 = torch.empty_like(qd[b:b + 1])
+        gpu_lib.gqa_decode_attend(qd[b:b + 1], kd[b:b + 1], vd[b:b + 1], o1, int(lens[b]), ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, got[b:b + 1]), "request %d differs from its single call" % b
+
+
 def test_workspace_reuse_with_changing_inputs(gpu_lib):
     """Back-to-back calls on one workspace with different inputs: a merge that
     read a previous call's partials (or a counter left non-zero) would show up
