@@ -38,7 +38,9 @@
 // column from four consecutive rows.  Rows past Tk load as zeros (buffer
 // range check).  K and V are double-buffered: the loads of tile t+1 run
 // while tile t is computed, and one barrier per tile hands the buffers
-// over.  Only tiles that cross the diagonal are masked.
+// over.  Only tiles that cross a wave's diagonal are masked, and a wave
+// skips the arithmetic of tiles it cannot see at all (the end of a row
+// block's diagonal, or a last row block with fewer than 128 valid rows).
 
 #include <algorithm>
 #include <type_traits>
@@ -250,7 +252,12 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D ==
     const int per = (n_tiles + nc - 1) / nc;        // tiles per chunk
     const int t_begin = min(n_tiles, chunk * per);
     const int n = min(n_tiles, t_begin + per) - t_begin;
-    const int n_full = min(n_tiles, max(0, (r0 + off + 1) / kPfBN));  // tiles every row sees in full
+    // Per wave (wave-uniform): tiles below n_full are visible in full to
+    // every row of the wave, so they need no mask; tiles from w_end on are
+    // masked for every row of the wave (or the wave has no valid row), so it
+    // skips their arithmetic and only takes part in the loads and barriers.
+    const int n_full = min(n_tiles, (rw0 + off + 1) / kPfBN);
+    const int w_end = rw0 < row_hi ? min(n_tiles, (min(rw0 + 31, row_hi - 1) + off) / kPfBN + 1) : 0;
     const int my_row = rw0 + ln;
     const int my_lim = my_row + off;  // last visible key of this lane's row
 
@@ -432,12 +439,12 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D ==
     __syncthreads();
     for (int s = 0; s < n; s += 2) {  // unrolled by two: buffer indices are constants
         issue_tile_loads(t_begin + s + 1, 1);
-        tile_step(t_begin + s, 0);
+        if (t_begin + s < w_end) tile_step(t_begin + s, 0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (s + 1 < n) {
             issue_tile_loads(t_begin + s + 2, 0);
-            tile_step(t_begin + s + 1, 1);
+            if (t_begin + s + 1 < w_end) tile_step(t_begin + s + 1, 1);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }

@@ -83,6 +83,8 @@ CASES = [
     (1, 14, 2, 64, 64, 1100, 1100),   # 18 key tiles: two key chunks merged
     (1, 4, 2, 64, 3, 2500, 2600),     # 40 key tiles: three key chunks merged
     (2, 4, 1, 128, 130, 1300, 1300),  # D = 128, two row blocks, two chunks each
+    (1, 4, 2, 64, 1057, 1057, 1057),  # last row block of 33 rows (waves with 32, 1, 0, 0 rows), 3 key chunks
+    (1, 4, 1, 128, 1057, 1057, 1057),  # the same at D = 128
 ]
 
 
