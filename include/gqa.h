@@ -206,6 +206,9 @@ int gqa_decode_attend_q4(const void *q,
  *
  *   codes [n_rows, D/2] uint8, scales/biases [n_rows, D/group_size] f16,
  *   out [n_rows, D] float32.
+ *
+ * Requires D in {64, 128}, group_size in {32, 64, 128} dividing D and
+ * n_rows >= 0 (0 enqueues nothing).
  */
 int gqa_dequant_q4(const uint8_t *codes, const void *scales, const void *biases, float *out,
                    int n_rows, int D, int group_size, void *stream);

@@ -1166,14 +1166,14 @@ hipError_t launch_decode_q4(int D, int group, int B, const DecodeArgs &a, hipStr
 __global__ void dequant_q4_kernel(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
                                   float *out, long n_elems, int D, int group)
 {
-    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n_elems) return;
-    const long row = i / D;
-    const int e = (int)(i % D);
-    const uint32_t byte = codes[row * (D / 2) + e / 2];
-    const uint32_t code = (e & 1) ? (byte >> 4) : (byte & 0xFu);
-    const long gi = row * (D / group) + e / group;
-    out[i] = q4_dequant_value(f16_bits_to_f32(scales[gi]), f16_bits_to_f32(biases[gi]), code);
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n_elems; i += (long)gridDim.x * blockDim.x) {
+        const long row = i / D;
+        const int e = (int)(i % D);
+        const uint32_t byte = codes[row * (D / 2) + e / 2];
+        const uint32_t code = (e & 1) ? (byte >> 4) : (byte & 0xFu);
+        const long gi = row * (D / group) + e / group;
+        out[i] = q4_dequant_value(f16_bits_to_f32(scales[gi]), f16_bits_to_f32(biases[gi]), code);
+    }
 }
 
 hipError_t launch_dequant_q4(const uint8_t *codes, const void *scales, const void *biases, float *out,
@@ -1182,7 +1182,8 @@ hipError_t launch_dequant_q4(const uint8_t *codes, const void *scales, const voi
     const long n = (long)n_rows * D;
     if (n == 0) return hipSuccess;
     const int threads = 256;
-    const long blocks = (n + threads - 1) / threads;
+    long blocks = (n + threads - 1) / threads;
+    if (blocks > 65536) blocks = 65536;  // grid-stride beyond this
     hipLaunchKernelGGL(dequant_q4_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, codes,
                        (const uint16_t *)scales, (const uint16_t *)biases, out, n, D, group);
     return hipGetLastError();
@@ -1190,19 +1191,21 @@ hipError_t launch_dequant_q4(const uint8_t *codes, const void *scales, const voi
 
 // Zero-fill with a kernel (kept out of hipMemsetAsync so that callers may
 // capture it in a graph).
-__global__ void fill_zero_kernel(uint32_t *p, size_t n_words)
+__global__ void fill_zero_kernel(uint32_t *p, size_t bytes)
 {
+    const size_t n_words = bytes / 4;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words; i += (size_t)gridDim.x * blockDim.x)
         p[i] = 0u;
+    if (blockIdx.x == 0 && threadIdx.x < (bytes & 3u)) ((uint8_t *)p)[n_words * 4 + threadIdx.x] = 0u;  // 1-3 tail bytes
 }
 
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s)
 {
-    const size_t words = bytes / 4;
-    if (words == 0) return hipSuccess;
-    size_t blocks = (words + 255) / 256;
+    if (bytes == 0) return hipSuccess;
+    size_t blocks = (bytes / 4 + 255) / 256;
+    if (blocks < 1) blocks = 1;
     if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t *)p, words);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t *)p, bytes);
     return hipGetLastError();
 }
 

@@ -257,7 +257,7 @@ int gqa_dequant_q4(const uint8_t *codes, const void *scales, const void *biases,
 {
     if (!codes || !scales || !biases || !out) return GQA_ERR_NULL;
     if (n_rows < 0) return GQA_ERR_SHAPE;
-    if (D < 2 || D % 2) return GQA_ERR_SHAPE;
+    if (D != 64 && D != 128) return GQA_ERR_UNSUPPORTED;
     if (group_size != 32 && group_size != 64 && group_size != 128) return GQA_ERR_UNSUPPORTED;
     if (D % group_size != 0) return GQA_ERR_SHAPE;
     if (int st = check_device()) return st;

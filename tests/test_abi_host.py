@@ -169,6 +169,8 @@ def test_q4_validation(lib):
     assert lib.gqa_dequant_q4(NULL, FAKE, FAKE, FAKE, 4, 128, 64, NULL) == gqa.GQA_ERR_NULL
     assert lib.gqa_dequant_q4(FAKE, FAKE, FAKE, FAKE, 4, 128, 48, NULL) == gqa.GQA_ERR_UNSUPPORTED
     assert lib.gqa_dequant_q4(FAKE, FAKE, FAKE, FAKE, -1, 128, 64, NULL) == gqa.GQA_ERR_SHAPE
+    assert lib.gqa_dequant_q4(FAKE, FAKE, FAKE, FAKE, 4, 96, 32, NULL) == gqa.GQA_ERR_UNSUPPORTED
+    assert lib.gqa_dequant_q4(FAKE, FAKE, FAKE, FAKE, 4, 64, 128, NULL) == gqa.GQA_ERR_SHAPE
 
 
 def test_workspace_init_validation(lib):

@@ -122,6 +122,15 @@ def test_decode_workspace_shared_across_batch_sizes(gpu_lib):
         assert_workspace_ready(ws, "it=%d" % it)
 
 
+def test_workspace_init_odd_size(gpu_lib):
+    # every byte is cleared, including a tail shorter than a 32-bit word
+    for n in (1, 3, 1027, 4096 * 1024 + 2):
+        ws = torch.full((n,), 7, dtype=torch.uint8, device="cuda")
+        gpu_lib.gqa_workspace_init(ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0, n
+
+
 def test_workspace_init_entry_point(gpu_lib):
     q = torch.randn(1, 8, 1, 64, device="cuda")
     k = torch.randn(1, 2, 300, 64, device="cuda")

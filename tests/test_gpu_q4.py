@@ -41,6 +41,23 @@ def test_dequant_hook_bit_exact(gpu_lib, group):
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
 
+@pytest.mark.parametrize("D,group", [(128, 64), (64, 32)])
+def test_dequant_hook_many_rows(gpu_lib, D, group):
+    # more elements than one pass of the launch grid covers (grid-stride loop)
+    rng = np.random.default_rng(D + group)
+    n_rows = 150000 if D == 128 else 300000
+    codes = rng.integers(0, 16, size=(n_rows, D), dtype=np.uint8)
+    scales = (rng.random((n_rows, D // group)) * 0.5).astype(np.float16)
+    biases = rng.standard_normal((n_rows, D // group)).astype(np.float16)
+    packed = gen.q4_pack_codes(codes)
+    out = torch.empty((n_rows, D), dtype=torch.float32, device="cuda")
+    gpu_lib.gqa_dequant_q4(torch.from_numpy(packed).cuda(), torch.from_numpy(scales).cuda(),
+                           torch.from_numpy(biases).cuda(), out, group)
+    torch.cuda.synchronize()
+    want = oracle.q4_dequant(packed, scales, biases, group)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
 def run_q4(gqa, inp, w, kv_len):
     dev = {k: t.cuda() for k, t in inp.items()}
     q = dev["q"]
