@@ -43,6 +43,7 @@
 // block's diagonal, or a last row block with fewer than 128 valid rows).
 
 #include <algorithm>
+#include <cstdlib>
 #include <type_traits>
 #include <utility>
 #include <vector>
@@ -118,7 +119,7 @@ constexpr int kPfBN = 64;        // keys per tile
 constexpr int kPfThreads = 256;  // 4 waves
 constexpr int kPfMaxItems = 1024;     // (row block, key chunk) work items in the launch table
 constexpr int kPfCUs = 256;           // compute units of the gfx950 parts
-constexpr int kPfMinChunk = 8;        // fewest key tiles per chunk: a chunk's partial costs a write and a read
+constexpr int kPfMinChunk = 10;       // fewest key tiles per chunk: a chunk's partial costs a write and a read
 constexpr float kPfSumLimit = 1024.0f;  // a lane's probability sum that needs the exact path
 
 // The launch's work items, longest first: entry r is (row block << 6) |
@@ -592,14 +593,24 @@ static bool pf_plan_fits(const PfPlan &p, int B, int Hq)
            (size_t)B * Hq * (p.n_rb - p.rb0) * 4 <= kWsFlagBytes;
 }
 
+// Tuning overrides of the chunking (environment, read once; for sweeps).
+static int pf_env(const char *name, int dflt)
+{
+    const char *s = std::getenv(name);
+    const int x = s ? std::atoi(s) : 0;
+    return x > 0 ? x : dflt;
+}
+
 static PfPlan pf_plan(int B, int Hq, int D, int Tq, int Tk)
 {
-    const long slots = (long)(D == 64 ? 4 : 2) * kPfCUs;  // resident workgroups (VGPR budget)
+    static const int slot_factor = pf_env("GQA_PREFILL_SLOT_PERCENT", 100);  // percent of the resident slots
+    static const int min_chunk = pf_env("GQA_PREFILL_MIN_CHUNK", kPfMinChunk);
+    const long slots = (long)(D == 64 ? 4 : 2) * kPfCUs * slot_factor / 100;  // resident workgroups (VGPR budget)
     const int n_rb = (Tq + kPfBM - 1) / kPfBM;
     long total = 0;
     for (int rb = 0; rb < n_rb; ++rb) total += pf_row_tiles(rb, Tq, Tk);
     total *= (long)B * Hq;
-    int lo = (int)std::min<long>(std::max((long)kPfMinChunk, (total + slots - 1) / slots), 1 << 30);
+    int lo = (int)std::min<long>(std::max((long)min_chunk, (total + slots - 1) / std::max(slots, 1L)), 1 << 30);
     int hi = std::max(lo, pf_row_tiles(n_rb - 1, Tq, Tk));  // no split: always fits
     if (pf_plan_fits(pf_plan_for(Tq, Tk, lo), B, Hq)) return pf_plan_for(Tq, Tk, lo);
     while (hi - lo > 1) {  // invariant: lo does not fit, hi does

@@ -80,10 +80,10 @@ CASES = [
     (2, 12, 2, 128, 65, 333, 400),
     (1, 16, 1, 128, 257, 257, 257),
     (1, 14, 2, 64, 64, 1000, 1000),
-    (1, 14, 2, 64, 64, 1100, 1100),   # 18 key tiles: two key chunks merged
-    (1, 4, 2, 64, 3, 2500, 2600),     # 40 key tiles: three key chunks merged
-    (2, 4, 1, 128, 130, 1300, 1300),  # D = 128, two row blocks, two chunks each
-    (1, 4, 2, 64, 1057, 1057, 1057),  # last row block of 33 rows (waves with 32, 1, 0, 0 rows), 3 key chunks
+    (1, 14, 2, 64, 64, 1100, 1100),   # 18 key tiles: split into key chunks and merged
+    (1, 4, 2, 64, 3, 2500, 2600),     # 40 key tiles: four key chunks merged
+    (2, 4, 1, 128, 130, 1300, 1300),  # D = 128, two row blocks of 21 key tiles, each split into chunks
+    (1, 4, 2, 64, 1057, 1057, 1057),  # last row block: 33 rows (waves with 32, 1, 0, 0 rows), 17 key tiles in chunks
     (1, 4, 1, 128, 1057, 1057, 1057),  # the same at D = 128
 ]
 
