@@ -226,6 +226,48 @@ def graph_of(torch, eager):
     return g
 
 
+def calibration(torch, gqa, steps, warmup, flush, nbytes=16805888, layers=28, n=8192):
+    """Self-calibrated ceilings, measured in the same run as the kernels.
+    read_floor: the library's plain streaming-read helper over the decode
+    step's bytes, launched like the decode step (a HIP graph of 28 launches,
+    each reading its own 16.8 MB buffer, after the cache flush), so launch
+    cost and cold-cache latency are included exactly as for decode.
+    gemm_bf16: a dense n x n x n bf16 product through torch (the vendor GEMM)
+    on contiguous operands, the matrix-core rate a tuned library reaches."""
+    bufs = [torch.full((nbytes // 4,), l, dtype=torch.int32, device="cuda") for l in range(layers)]
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def eager():
+        for b in bufs:
+            gqa.gqa_read_probe(b, sink)
+
+    g = graph_of(torch, eager)
+    us = float(np.median(time_steps(torch, g.replay, steps, warmup, flush))) * 1e3 / layers
+    del g, bufs
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.mm(a, b, out=c)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        torch.mm(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_s = e0.elapsed_time(e1) * 1e-3 / reps
+    tf = 2.0 * n ** 3 / gemm_s / 1e12
+    del a, b, c
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"read_floor": {"kernel": "read_probe_kernel", "us_per_launch": round(us, 3), "GBps": round(gbps, 1),
+                           "frac_hbm_peak": round(gbps / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes,
+                           "launches_per_step": layers},
+            "gemm_bf16": {"n": n, "TFLOPs": round(tf, 1), "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}}
+
+
 def hbm_entry(us, nbytes, gate_ok, gate_max_abs, kernel, traffic=None, **extra):
     """A secondary result for an HBM-bound configuration."""
     gbs = nbytes / (us * 1e-6) / 1e9
@@ -431,6 +473,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other configurations (decode S=128, batched, 4-bit, chunked prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip the self-calibrated read floor and GEMM rate")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of MIB MiB (reference for memory counters)")
@@ -496,6 +540,11 @@ def main():
                           "parity_max_abs": d["gate_max_abs"]},
     })
 
+    if not args.no_calibration:
+        cal = calibration(torch, gqa, args.steps, args.warmup, flush)
+        result["calibration"] = cal
+        result["decode_detail"]["frac_of_read_floor"] = round(achieved / cal["read_floor"]["GBps"], 4)
+
     secondary = {}
     if args.sweep:
         sweep = {}
@@ -521,6 +570,9 @@ def main():
                                                      PREFILL_SRCS) if T == 4097 else None,
                              "algorithmic_flop_per_launch": p["flops"], "launch_duration_us": round(us, 2)},
                 "parity_ok": p["gate_ok"], "parity_max_abs": p["gate_max_abs"]}
+            if "calibration" in result:
+                secondary["prefill_0p5b_T%d" % T]["frac_of_gemm_bf16"] = round(
+                    tf / result["calibration"]["gemm_bf16"]["TFLOPs"], 4)
     if not args.no_extra:
         names = tuple(x for x in args.extras.split(",") if x)
         unknown = [x for x in names if x not in EXTRAS]

@@ -213,6 +213,17 @@ int gqa_decode_attend_q4(const void *q,
 int gqa_dequant_q4(const uint8_t *codes, const void *scales, const void *biases, float *out,
                    int n_rows, int D, int group_size, void *stream);
 
+/*
+ * Measurement helper, not part of the attention path: reads `bytes` bytes at
+ * `src` once with coalesced 16-byte loads (the plain streaming read that
+ * bounds any HBM-bound kernel), so that a benchmark can time the achievable
+ * read rate exactly as it times the decode kernels.  Stores nothing in
+ * practice: one 32-bit word at `sink` (device memory) is written only if the
+ * data fold to one fixed value.  Requires bytes > 0 and a multiple of 16,
+ * src and sink 16-byte aligned.
+ */
+int gqa_read_probe(const void *src, size_t bytes, void *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,6 +36,7 @@ EXPORTED = (
     "gqa_prefill_causal",
     "gqa_decode_attend_q4",
     "gqa_dequant_q4",
+    "gqa_read_probe",
 )
 
 
@@ -76,6 +77,8 @@ def load() -> ctypes.CDLL:
     lib.gqa_decode_attend_q4.restype = i
     lib.gqa_dequant_q4.argtypes = [vp, vp, vp, vp, i, i, i, vp]
     lib.gqa_dequant_q4.restype = i
+    lib.gqa_read_probe.argtypes = [vp, sz, vp, vp]
+    lib.gqa_read_probe.restype = i
     _lib = lib
     return lib
 
@@ -241,3 +244,14 @@ def gqa_dequant_q4(codes, scales, biases, out, group_size: int) -> torch.Tensor:
     _check(load().gqa_dequant_q4(_ptr(codes), _ptr(scales), _ptr(biases), _ptr(out), n_rows, D,
                                  int(group_size), _stream(codes)), "gqa_dequant_q4")
     return out
+
+
+def gqa_read_probe(src: torch.Tensor, sink: torch.Tensor) -> None:
+    """Stream every byte of `src` once (measurement helper; see gqa.h)."""
+    for n, t in (("src", src), ("sink", sink)):
+        if t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous GPU tensor" % n)
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink must hold at least 4 bytes")
+    _check(load().gqa_read_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(src)),
+           "gqa_read_probe")

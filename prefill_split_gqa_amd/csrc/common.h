@@ -230,5 +230,6 @@ hipError_t launch_prefill(int dtype, int D, const void *q, const void *k, const 
                           int B, int Hq, int Hkv, int Tq, int Tk, int s_cap, float scale, void *ws, hipStream_t s);
 size_t prefill_workspace_bytes(int B, int Hq, int D, int Tq, int Tk);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+hipError_t launch_read_probe(const void *src, size_t bytes, void *sink, hipStream_t s);
 
 }  // namespace gqa

@@ -1161,7 +1161,7 @@ hipError_t launch_decode_q4(int D, int group, int B, const DecodeArgs &a, hipStr
 }
 
 // ---------------------------------------------------------------------------
-// Dequant check hook: one thread per element, same dequant function.
+// Dequant check hook: a grid-stride loop over the elements, same dequant function.
 // ---------------------------------------------------------------------------
 __global__ void dequant_q4_kernel(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
                                   float *out, long n_elems, int D, int group)
@@ -1186,26 +1186,6 @@ hipError_t launch_dequant_q4(const uint8_t *codes, const void *scales, const voi
     if (blocks > 65536) blocks = 65536;  // grid-stride beyond this
     hipLaunchKernelGGL(dequant_q4_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, codes,
                        (const uint16_t *)scales, (const uint16_t *)biases, out, n, D, group);
-    return hipGetLastError();
-}
-
-// Zero-fill with a kernel (kept out of hipMemsetAsync so that callers may
-// capture it in a graph).
-__global__ void fill_zero_kernel(uint32_t *p, size_t bytes)
-{
-    const size_t n_words = bytes / 4;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words; i += (size_t)gridDim.x * blockDim.x)
-        p[i] = 0u;
-    if (blockIdx.x == 0 && threadIdx.x < (bytes & 3u)) ((uint8_t *)p)[n_words * 4 + threadIdx.x] = 0u;  // 1-3 tail bytes
-}
-
-hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s)
-{
-    if (bytes == 0) return hipSuccess;
-    size_t blocks = (bytes / 4 + 255) / 256;
-    if (blocks < 1) blocks = 1;
-    if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t *)p, bytes);
     return hipGetLastError();
 }
 

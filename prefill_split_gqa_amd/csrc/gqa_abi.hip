@@ -264,4 +264,13 @@ int gqa_dequant_q4(const uint8_t *codes, const void *scales, const void *biases,
     return hip_status(launch_dequant_q4(codes, scales, biases, out, n_rows, D, group_size, (hipStream_t)stream));
 }
 
+int gqa_read_probe(const void *src, size_t bytes, void *sink, void *stream)
+{
+    if (!src || !sink) return GQA_ERR_NULL;
+    if (bytes == 0 || bytes % 16 != 0 || bytes / 16 / 1024 >= ((size_t)1 << 32)) return GQA_ERR_SHAPE;
+    if (!aligned16(src) || !aligned16(sink)) return GQA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return hip_status(launch_read_probe(src, bytes, sink, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -178,6 +178,15 @@ def test_workspace_init_validation(lib):
     assert lib.gqa_workspace_init(FAKE_ODD, 256, NULL) == gqa.GQA_ERR_ALIGN
 
 
+def test_read_probe_validation(lib):
+    assert lib.gqa_read_probe(NULL, 256, FAKE, NULL) == gqa.GQA_ERR_NULL
+    assert lib.gqa_read_probe(FAKE, 256, NULL, NULL) == gqa.GQA_ERR_NULL
+    assert lib.gqa_read_probe(FAKE, 0, FAKE, NULL) == gqa.GQA_ERR_SHAPE
+    assert lib.gqa_read_probe(FAKE, 100, FAKE, NULL) == gqa.GQA_ERR_SHAPE
+    assert lib.gqa_read_probe(FAKE_ODD, 256, FAKE, NULL) == gqa.GQA_ERR_ALIGN
+    assert lib.gqa_read_probe(FAKE, 256, FAKE_ODD, NULL) == gqa.GQA_ERR_ALIGN
+
+
 def test_library_does_not_link_the_oracle():
     # the product library and the oracle share nothing
     with open(gqa.LIB_PATH, "rb") as f:

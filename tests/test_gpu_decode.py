@@ -131,6 +131,16 @@ def test_workspace_init_odd_size(gpu_lib):
         assert int(ws.count_nonzero()) == 0, n
 
 
+def test_read_probe_reads_and_writes_nothing(gpu_lib):
+    # the measurement helper streams its input and leaves the sink alone
+    for n in (16, 4096 + 16, 16805888):
+        src = torch.arange(n // 4, dtype=torch.int32, device="cuda")
+        sink = torch.full((4,), 5, dtype=torch.int32, device="cuda")
+        gpu_lib.gqa_read_probe(src, sink)
+        torch.cuda.synchronize()
+        assert sink.tolist() == [5, 5, 5, 5], n
+
+
 def test_workspace_init_entry_point(gpu_lib):
     q = torch.randn(1, 8, 1, 64, device="cuda")
     k = torch.randn(1, 2, 300, 64, device="cuda")
