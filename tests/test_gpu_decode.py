@@ -77,6 +77,21 @@ def test_decode_small_ragged(gpu_lib, dtype, D):
             assert_close(got, want, tol_for(DT[dtype]), "n=%d Hq=%d Hkv=%d" % (n, Hq, Hkv))
 
 
+def test_decode_long_context(gpu_lib):
+    # 65537 keys: the split plan's cap on splits makes every split stream
+    # many chunks; the length is one past a multiple of every chunk size
+    rng = np.random.default_rng(65537)
+    Hq, Hkv, D, n, s_cap = 16, 4, 128, 65537, 65600
+    q = torch.from_numpy(rng.standard_normal((1, Hq, 1, D), dtype=np.float32)).to(torch.bfloat16)
+    k = torch.from_numpy(rng.standard_normal((1, Hkv, s_cap, D), dtype=np.float32)).to(torch.bfloat16)
+    v = torch.from_numpy(rng.standard_normal((1, Hkv, s_cap, D), dtype=np.float32)).to(torch.bfloat16)
+    k[:, :, n:] = float("nan")
+    v[:, :, n:] = float("nan")
+    note("decode bf16 long context n=%d" % n)
+    got = run_decode(gpu_lib, q, k, v, n)
+    assert_close(got, oracle.attend(q, k, v, kv_lens=n), 2e-2, "long context")
+
+
 def test_decode_single_key_is_value_row(gpu_lib):
     q = torch.randn(1, 28, 1, 128)
     k = torch.randn(1, 4, 64, 128)
@@ -187,6 +202,24 @@ def test_batched_qwen3_4b(gpu_lib, B):
         # requests carry distinct data: no output is another's copy
         for b in range(1, B):
             assert not torch.equal(got[b], got[0])
+
+
+def test_batched_long_and_short_requests(gpu_lib):
+    # one request near the cache's end next to short and empty ones
+    rng = np.random.default_rng(4)
+    B, Hq, Hkv, D, s_cap = 4, 8, 2, 128, 65600
+    q = torch.from_numpy(rng.standard_normal((B, Hq, 1, D), dtype=np.float32)).to(torch.bfloat16)
+    k = torch.from_numpy(rng.standard_normal((B, Hkv, s_cap, D), dtype=np.float32)).to(torch.bfloat16)
+    v = torch.from_numpy(rng.standard_normal((B, Hkv, s_cap, D), dtype=np.float32)).to(torch.bfloat16)
+    lens = np.array([65537, 1, 30000, 0], np.int32)
+    for b, n in enumerate(lens):
+        k[b, :, n:] = float("nan")
+        v[b, :, n:] = float("nan")
+    note("batched long and short lens=%s" % list(lens))
+    got = run_batched(gpu_lib, q, k, v, lens).cpu()
+    want = oracle.attend(q, k, v, kv_lens=lens)
+    assert_close(got, want, 2e-2, "long and short")
+    assert torch.count_nonzero(got[3]) == 0
 
 
 def test_batched_lengths_zero_clamped_and_ragged(gpu_lib):

@@ -53,6 +53,19 @@ def test_prefill_0p5b(gpu_lib, T):
     assert torch.equal(g[0, :, 0], v[0, :, 0].repeat_interleave(w.G, dim=0))
 
 
+def test_prefill_long_d128(gpu_lib):
+    # T = 8193 at D = 128: 65 row blocks, the longest split into more key
+    # chunks than any benchmark size, and a one-row last block
+    rng = np.random.default_rng(8193)
+    T, Hq, Hkv, D = 8193, 2, 1, 128
+    q = torch.from_numpy(rng.standard_normal((1, Hq, T, D), dtype=np.float32)).to(torch.bfloat16)
+    k = torch.from_numpy(rng.standard_normal((1, Hkv, T, D), dtype=np.float32)).to(torch.bfloat16)
+    v = torch.from_numpy(rng.standard_normal((1, Hkv, T, D), dtype=np.float32)).to(torch.bfloat16)
+    note("prefill long T=%d D=%d" % (T, D))
+    got = run_prefill(gpu_lib, q, k, v)
+    assert_close(got, oracle.attend(q, k, v, causal=True), 2e-2, "prefill T=%d" % T)
+
+
 def test_prefill_chunk_at_offset(gpu_lib):
     w = W.by_name("prefill_0p5b")
     c = W.PREFILL_CHUNK
