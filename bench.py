@@ -71,6 +71,18 @@ def decode_bytes_generic(B, Hq, Hkv, D, lens, elem):
     return sum(2 * n * Hkv * D * elem for n in lens) + 2 * B * Hq * D * elem
 
 
+def expanded_kv_bytes(S: int, Hq: int = 28, D: int = 128, elem: int = 4) -> int:
+    """Bytes of the K and V copies an unfused decode writes per layer when it
+    repeats every KV head once per query head (what this path never does)."""
+    return 2 * Hq * S * D * elem
+
+
+def score_matrix_bytes(T: int, Hq: int = 14, elem: int = 2) -> int:
+    """Bytes of the [Hq, T, T] score matrix an unfused prefill writes per
+    layer (what this path never does)."""
+    return Hq * T * T * elem
+
+
 def source_digest(paths) -> str:
     h = hashlib.sha256()
     for p in paths:
@@ -534,7 +546,8 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,
                      "launch_duration_us": round(us_layer, 3)},
-        "decode_detail": {"p10_us_layer": round(float(np.percentile(d["graph_ms"], 10)) * 1e3 / layers, 3),
+        "decode_detail": {"expanded_kv_bytes_avoided": expanded_kv_bytes(args.S),
+                          "p10_us_layer": round(float(np.percentile(d["graph_ms"], 10)) * 1e3 / layers, 3),
                           "p90_us_layer": round(float(np.percentile(d["graph_ms"], 90)) * 1e3 / layers, 3),
                           "eager_us_layer": round(float(np.median(d["eager_ms"])) * 1e3 / layers, 3),
                           "parity_max_abs": d["gate_max_abs"]},
@@ -562,6 +575,7 @@ def main():
             tf = p["flops"] / (us * 1e-6) / 1e12
             secondary["prefill_0p5b_T%d" % T] = {
                 "us": round(us, 2), "layers_per_step": p["layers"], "TFLOPs": round(tf, 2),
+                "score_matrix_bytes_avoided": score_matrix_bytes(T),
                 "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
                 "roofline": {"bound": "mfma", "kernel": "prefill_causal_kernel<bf16_t,64,false>",
                              "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
