@@ -107,6 +107,19 @@ def _dense(name: str, t: torch.Tensor, ndim: int) -> None:
         raise ValueError("%s must be a contiguous %d-d tensor" % (name, ndim))
 
 
+def _same_device(ref: torch.Tensor, **named) -> None:
+    for n, t in named.items():
+        if t.device != ref.device:
+            raise ValueError("%s is on %s, expected %s" % (n, t.device, ref.device))
+
+
+def _workspace(ws: torch.Tensor, ref: torch.Tensor):
+    """Device pointer and size in bytes of a workspace tensor on ref's device."""
+    if not isinstance(ws, torch.Tensor) or ws.device != ref.device or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on %s" % ref.device)
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
 def default_scale(D: int) -> float:
     """1/sqrt(D) rounded to float32 (the value the kernels receive)."""
     return float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32))
@@ -129,6 +142,8 @@ def make_workspace(B: int, Hq: int, Hkv: int, D: int, s_cap: int, device="cuda")
 
 
 def gqa_workspace_init(workspace: torch.Tensor) -> None:
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
     _check(load().gqa_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
                                      _stream(workspace)), "gqa_workspace_init")
 
@@ -144,9 +159,11 @@ def gqa_decode_attend(q, k, v, out, kv_len: int, workspace, scale: Optional[floa
     dt = _DTYPE_CODE.get(q.dtype, -1)
     if not (q.dtype == k.dtype == v.dtype == out.dtype):
         raise ValueError("q, k, v and out must share one dtype")
+    _same_device(q, k=k, v=v, out=out)
+    ws, ws_bytes = _workspace(workspace, q)
     scale = default_scale(D) if scale is None else scale
     _check(load().gqa_decode_attend(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, D, int(kv_len), s_cap,
-                                    float(scale), dt, _ptr(workspace), workspace.numel(), _stream(q)),
+                                    float(scale), dt, ws, ws_bytes, _stream(q)),
            "gqa_decode_attend")
     return out
 
@@ -165,9 +182,11 @@ def gqa_decode_attend_batched(q, k, v, out, kv_lens, workspace, scale: Optional[
     if not (q.dtype == k.dtype == v.dtype == out.dtype):
         raise ValueError("q, k, v and out must share one dtype")
     dt = _DTYPE_CODE.get(q.dtype, -1)
+    _same_device(q, k=k, v=v, out=out, kv_lens=kv_lens)
+    ws, ws_bytes = _workspace(workspace, q)
     scale = default_scale(D) if scale is None else scale
     _check(load().gqa_decode_attend_batched(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(kv_lens), B, Hq, Hkv, D,
-                                            s_cap, float(scale), dt, _ptr(workspace), workspace.numel(),
+                                            s_cap, float(scale), dt, ws, ws_bytes,
                                             _stream(q)), "gqa_decode_attend_batched")
     return out
 
@@ -190,7 +209,6 @@ def gqa_prefill_causal(q, k, v, out, workspace, Tk: Optional[int] = None,
     workspace: uint8 device tensor of gqa_prefill_workspace_bytes(...) bytes, zero-filled once."""
     for n, t in (("q", q), ("k", k), ("v", v), ("out", out)):
         _dense(n, t, 4)
-    _dense("workspace", workspace, 1)
     B, Hq, Tq, D = q.shape
     _, Hkv, s_cap, _ = k.shape
     if out.shape != q.shape or k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
@@ -199,9 +217,11 @@ def gqa_prefill_causal(q, k, v, out, workspace, Tk: Optional[int] = None,
         raise ValueError("q, k, v and out must share one dtype")
     Tk = s_cap if Tk is None else int(Tk)
     dt = _DTYPE_CODE.get(q.dtype, -1)
+    _same_device(q, k=k, v=v, out=out)
+    ws, ws_bytes = _workspace(workspace, q)
     scale = default_scale(D) if scale is None else scale
     _check(load().gqa_prefill_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, D, Tq, Tk, s_cap,
-                                     float(scale), dt, _ptr(workspace), workspace.numel(), _stream(q)),
+                                     float(scale), dt, ws, ws_bytes, _stream(q)),
            "gqa_prefill_causal")
     return out
 
@@ -224,10 +244,13 @@ def gqa_decode_attend_q4(q, k_codes, k_scales, k_biases, v_codes, v_scales, v_bi
     for n, t in (("k_scales", k_scales), ("k_biases", k_biases), ("v_scales", v_scales), ("v_biases", v_biases)):
         if t.dtype != torch.float16 or tuple(t.shape) != gshape:
             raise ValueError("%s must be float16 %s" % (n, gshape))
+    _same_device(q, out=out, k_codes=k_codes, v_codes=v_codes, k_scales=k_scales, k_biases=k_biases,
+                 v_scales=v_scales, v_biases=v_biases)
+    ws, ws_bytes = _workspace(workspace, q)
     scale = default_scale(D) if scale is None else scale
     _check(load().gqa_decode_attend_q4(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(k_biases), _ptr(v_codes),
                                        _ptr(v_scales), _ptr(v_biases), _ptr(out), B, Hq, Hkv, D, int(group_size),
-                                       int(kv_len), s_cap, float(scale), _ptr(workspace), workspace.numel(),
+                                       int(kv_len), s_cap, float(scale), ws, ws_bytes,
                                        _stream(q)), "gqa_decode_attend_q4")
     return out
 
@@ -239,8 +262,15 @@ def gqa_dequant_q4(codes, scales, biases, out, group_size: int) -> torch.Tensor:
             raise ValueError("%s must be a contiguous GPU tensor" % n)
     D = codes.shape[-1] * 2
     n_rows = codes.numel() // max(codes.shape[-1], 1)
+    if codes.dtype != torch.uint8:
+        raise ValueError("codes must be uint8")
     if out.dtype != torch.float32 or out.numel() != n_rows * D:
         raise ValueError("out must be float32 with D elements per row")
+    group_size = int(group_size)
+    for n, t in (("scales", scales), ("biases", biases)):
+        if t.dtype != torch.float16 or group_size <= 0 or t.numel() != n_rows * (D // group_size):
+            raise ValueError("%s must be float16 with D/group_size elements per row" % n)
+    _same_device(codes, scales=scales, biases=biases, out=out)
     _check(load().gqa_dequant_q4(_ptr(codes), _ptr(scales), _ptr(biases), _ptr(out), n_rows, D,
                                  int(group_size), _stream(codes)), "gqa_dequant_q4")
     return out
@@ -253,5 +283,6 @@ def gqa_read_probe(src: torch.Tensor, sink: torch.Tensor) -> None:
             raise ValueError("%s must be a contiguous GPU tensor" % n)
     if sink.numel() * sink.element_size() < 4:
         raise ValueError("sink must hold at least 4 bytes")
+    _same_device(src, sink=sink)
     _check(load().gqa_read_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(src)),
            "gqa_read_probe")

@@ -137,6 +137,24 @@ def test_decode_workspace_shared_across_batch_sizes(gpu_lib):
         assert_workspace_ready(ws, "it=%d" % it)
 
 
+def test_binding_checks_workspace_and_devices(gpu_lib):
+    # a host workspace or a host tensor is refused before anything is launched;
+    # a workspace of another element type is measured in bytes
+    q = torch.randn(1, 8, 1, 64, device="cuda")
+    k = torch.randn(1, 2, 300, 64, device="cuda")
+    v = torch.randn(1, 2, 300, 64, device="cuda")
+    o = torch.empty_like(q)
+    n = gpu_lib.gqa_decode_workspace_bytes(1, 8, 2, 64, 300)
+    with pytest.raises(ValueError):
+        gpu_lib.gqa_decode_attend(q, k, v, o, 300, torch.zeros(n, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        gpu_lib.gqa_decode_attend(q, k.cpu(), v, o, 300, gpu_lib.make_workspace(1, 8, 2, 64, 300))
+    ws32 = torch.zeros((n + 3) // 4, dtype=torch.float32, device="cuda")
+    gpu_lib.gqa_decode_attend(q, k, v, o, 300, ws32)
+    torch.cuda.synchronize()
+    assert_close(o, oracle.attend(q.cpu(), k.cpu(), v.cpu()), 2e-5, "float32 workspace")
+
+
 def test_workspace_init_odd_size(gpu_lib):
     # every byte is cleared, including a tail shorter than a 32-bit word
     for n in (1, 3, 1027, 4096 * 1024 + 2):
