@@ -49,6 +49,7 @@ DECODE_SRCS = [os.path.join(ROOT, "prefill_split_gqa_amd", "csrc", f) for f in (
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_7b_s4096_traffic.txt")
 PREFILL_SRCS = [os.path.join(ROOT, "prefill_split_gqa_amd", "csrc", f) for f in ("prefill.hip", "common.h")]
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_0p5b_t4097_traffic.txt")
+PREFILL_COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_0p5b_t4097_counters.txt")
 Q4_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4_decode_s16384_traffic.txt")
 
 
@@ -91,21 +92,27 @@ def source_digest(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(path=TRAFFIC_FILE, key="decode_source_sha256_16", srcs=DECODE_SRCS):
-    """HBM bytes per launch from a committed counter summary, or None when it
-    is missing or was taken on a different kernel source."""
+def read_summary_value(path, key, srcs, field):
+    """A value from a committed rocprofv3 counter summary, or None when the
+    summary is missing or was taken on a different kernel source."""
     try:
         kv = {}
         with open(path) as f:
             for ln in f:
                 if ":" in ln and not ln.startswith("#"):
                     a, b = ln.split(":", 1)
-                    kv[a.strip()] = b.strip()
+                    kv[a.strip()] = b.split("#", 1)[0].strip()
         if kv.get(key) != source_digest(srcs):
             return None
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv[field])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def read_traffic(path=TRAFFIC_FILE, key="decode_source_sha256_16", srcs=DECODE_SRCS):
+    """HBM bytes per launch from a committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, calibrated), or None when it does not match the source."""
+    return read_summary_value(path, key, srcs, "hbm_bytes_per_launch")
 
 
 class Flusher:
@@ -584,6 +591,10 @@ def main():
                                                      PREFILL_SRCS) if T == 4097 else None,
                              "algorithmic_flop_per_launch": p["flops"], "launch_duration_us": round(us, 2)},
                 "parity_ok": p["gate_ok"], "parity_max_abs": p["gate_max_abs"]}
+            if T == 4097:
+                # matrix-core busy cycles over all SIMD-cycles, from the committed counter pass
+                secondary["prefill_0p5b_T%d" % T]["roofline"]["mfma_busy_counter_frac"] = read_summary_value(
+                    PREFILL_COUNTERS_FILE, "prefill_source_sha256_16", PREFILL_SRCS, "mfma_busy_over_simd_cycles")
             if "calibration" in result:
                 secondary["prefill_0p5b_T%d" % T]["frac_of_gemm_bf16"] = round(
                     tf / result["calibration"]["gemm_bf16"]["TFLOPs"], 4)
