@@ -461,9 +461,10 @@ def extra_chunked_prefill(torch, gqa, oracle, W, steps, warmup, flush):
     return out
 
 
-def cpu_baseline(oracle, host, scale, seconds):
-    """Time the oracle, as it stands, on the host cores over whole layers of
-    the headline workload until about `seconds` have elapsed."""
+def cpu_baseline(oracle, host, scale, seconds, nthreads=0):
+    """Time the oracle, as it stands, on the host cores (all of them, or
+    `nthreads`) over whole layers of the headline workload until about
+    `seconds` have elapsed."""
     import torch
 
     layers_f64 = [tuple(t.to(torch.float64).numpy() for t in x) for x in host]
@@ -471,12 +472,23 @@ def cpu_baseline(oracle, host, scale, seconds):
     t0 = time.perf_counter()
     while True:
         q, k, v = layers_f64[n_done % len(layers_f64)]
-        oracle.attend(q, k, v, scale=scale)
+        oracle.attend(q, k, v, scale=scale, nthreads=nthreads)
         n_done += 1
         el = time.perf_counter() - t0
         if el >= seconds and n_done >= 1:
             break
     return el / n_done * 1e6, n_done
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -609,10 +621,13 @@ def main():
 
     if not args.no_cpu_baseline:
         us_cpu, n = cpu_baseline(oracle, d["host"], d["scale"], args.cpu_seconds)
+        us_1, n_1 = cpu_baseline(oracle, d["host"], d["scale"], max(1.0, args.cpu_seconds / 4), nthreads=1)
         result["cpu_baseline"] = {"value": round(us_cpu, 1), "unit": "us/layer", "cores": oracle.max_threads(),
                                   "kind": "oracle",
                                   "sample": "%d whole layers of the same workload (S=%d), fp64 oracle, "
-                                            "inputs widened before timing" % (n, args.S)}
+                                            "inputs widened before timing" % (n, args.S),
+                                  "one_thread": {"value": round(us_1, 1), "layers": n_1},
+                                  "cpu": cpu_model()}
     print(json.dumps(result), flush=True)
 
 
