@@ -92,6 +92,22 @@ def test_decode_long_context(gpu_lib):
     assert_close(got, oracle.attend(q, k, v, kv_lens=n), 2e-2, "long context")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 2.0])
+def test_decode_scale_sign(gpu_lib, dtype, scale):
+    # negative: the maximum is the smallest raw score; zero: the plain mean of
+    # the value rows; 2.0: exponents far apart, so the reference maximum is
+    # raised often along the keys
+    rng = np.random.default_rng(31)
+    B, Hq, Hkv, D, n = 2, 14, 2, 128, 1000
+    q = torch.from_numpy(rng.standard_normal((B, Hq, 1, D), dtype=np.float32)).to(DT[dtype])
+    k = torch.from_numpy(rng.standard_normal((B, Hkv, n, D), dtype=np.float32)).to(DT[dtype])
+    v = torch.from_numpy(rng.standard_normal((B, Hkv, n, D), dtype=np.float32)).to(DT[dtype])
+    note("decode %s scale=%g" % (dtype, scale))
+    got = run_decode(gpu_lib, q, k, v, n, scale=scale)
+    assert_close(got, oracle.attend(q, k, v, kv_lens=n, scale=scale), tol_for(DT[dtype]), "scale=%g" % scale)
+
+
 def test_decode_single_key_is_value_row(gpu_lib):
     q = torch.randn(1, 28, 1, 128)
     k = torch.randn(1, 4, 64, 128)

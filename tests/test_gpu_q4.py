@@ -66,7 +66,7 @@ def run_q4(gqa, inp, w, kv_len):
     ws = gqa.make_workspace(B, Hq, Hkv, D, s_cap)
     g = Guarded(q.shape, q.dtype)
     gqa.gqa_decode_attend_q4(q, dev["k_codes"], dev["k_scales"], dev["k_biases"], dev["v_codes"],
-                             dev["v_scales"], dev["v_biases"], g.t, w.group, kv_len, ws)
+                             dev["v_scales"], dev["v_biases"], g.t, w.group, kv_len, ws, scale=w.scale())
     torch.cuda.synchronize()
     g.check()
     return g.t
@@ -122,6 +122,24 @@ def test_q4_small_ragged(gpu_lib, D, group):
         note("q4 D=%d group=%d Hq=%d Hkv=%d n=%d" % (D, group, Hq, Hkv, n))
         got = run_q4(gpu_lib, inp, wg, n)
         assert_close(got, oracle_q4(inp, wg, n), 2e-2, "q4 n=%d" % n)
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 2.0])
+def test_q4_scale_sign(gpu_lib, scale):
+    # the running maximum is exact in this kernel: a negative scale, a zero
+    # scale (plain mean of the dequantized value rows) and a large one
+    w = W.by_name("q4_decode")
+    inp = W.q4_inputs(w, 2048, 7)
+
+    class Wg:
+        pass
+
+    wg = Wg()
+    wg.group = w.group
+    wg.scale = lambda: scale
+    note("q4 scale=%g" % scale)
+    got = run_q4(gpu_lib, inp, wg, 1500)
+    assert_close(got, oracle_q4(inp, wg, 1500), 2e-2, "q4 scale=%g" % scale)
 
 
 def test_q4_two_requests_merge_workgroups(gpu_lib):
