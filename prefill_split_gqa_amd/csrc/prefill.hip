@@ -488,9 +488,23 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D ==
             s_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == (unsigned)(nc - 1);
         __syncthreads();
         if (!s_last) return;
-        // Combine the chunks in chunk order with a running maximum, two
-        // partials per round trip (this workgroup's own re-read like the
-        // others: its stores have completed).
+        // Combine the chunks in chunk order with a running maximum.  This
+        // workgroup's own partial is not re-read from the workspace: it is
+        // parked in the (now idle) tile buffers exactly as it was stored
+        // (lowest bits clear), so the result does not depend on which chunk
+        // merges, and folded from there in its turn; the others are loaded
+        // two per round trip.  Each lane parks and reads back only its own
+        // words ([wave][d-block][register][lane]; 4 KB per d-block and wave).
+        static_assert(4 * NDB * 16 * 64 * 4 <= L::TOTAL, "own partial fits the tile buffers");
+        float *own_lds = (float *)smem + (rw * NDB * 16) * 64 + lane;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                own_lds[(db * 16 + j) * 64] = __uint_as_float(__float_as_uint(acc[db][j]) & clr);
+        asm volatile("" ::: "memory");  // read them back from LDS, not kept live in registers
+        const float own_m = __uint_as_float(__float_as_uint(m_run) & clr);
+        const float own_l = __uint_as_float(__float_as_uint(l_part) & clr);
         float M = -kInf, Lsum = 0.0f;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -514,20 +528,48 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D ==
             const float wa = M == -kInf ? 0.0f : fast_exp2(aq * (M - Mn));
             const float wb = mc == -kInf ? 0.0f : fast_exp2(aq * (mc - Mn));
             M = Mn;
-            Lsum = Lsum * wa + lc * wb;
+            // one rounded product and one fused multiply-add, spelled out, so
+            // that every call site rounds alike (which site folds a chunk
+            // depends on which chunk merges)
+            Lsum = __builtin_fmaf(lc, wb, __fmul_rn(Lsum, wa));
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) acc[db][j] = acc[db][j] * wa + oc[db][j] * wb;
+                for (int j = 0; j < 16; ++j) acc[db][j] = __builtin_fmaf(oc[db][j], wb, __fmul_rn(acc[db][j], wa));
         };
-        for (int c = 0; c < nc; c += 2) {
+        auto fold_own = [&]() {
+            f32x16_t oc[NDB];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) oc[db][j] = own_lds[(db * 16 + j) * 64];
+            fold(own_m, own_l, oc);
+            asm volatile("" ::: "memory");
+        };
+        // the i-th other chunk is i below this one's index, i + 1 from it on
+        bool own_done = false;
+        for (int i = 0; i < nc - 1; i += 2) {
+            const int c0 = i < chunk ? i : i + 1;
+            const int c1 = i + 1 < chunk ? i + 1 : i + 2;
+            const bool two = i + 1 < nc - 1;
+            if (!own_done && chunk < c0) {  // before the loads: fewer registers live
+                fold_own();
+                own_done = true;
+            }
             float m0, l0, m1 = -kInf, l1 = 0.0f;
             f32x16_t o0[NDB], o1[NDB];
-            load_part(c, m0, l0, o0);
-            if (c + 1 < nc) load_part(c + 1, m1, l1, o1);
+            load_part(c0, m0, l0, o0);
+            if (two) load_part(c1, m1, l1, o1);
             fold(m0, l0, o0);
-            if (c + 1 < nc) fold(m1, l1, o1);
+            if (two) {
+                if (!own_done && chunk < c1) {
+                    fold_own();
+                    own_done = true;
+                }
+                fold(m1, l1, o1);
+            }
         }
+        if (!own_done) fold_own();
         m_run = M;
         l_part = Lsum;
         if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
