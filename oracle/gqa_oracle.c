@@ -23,8 +23,9 @@
  *    repeat_kv (query heads a multiple of KV heads) and, with the causal flag,
  *    the queries are aligned to the end of the keys so that a chunk at an
  *    offset sees every earlier key.
- *  - same page, "Cause": the unfused path is repeat_kv, a matmul, scale, mask,
- *    softmax and a second matmul -- the plain definition written out below.
+ *  - same page, section "Cause and workaround", its opening paragraph on the
+ *    cause: the unfused path is repeat_kv, a matmul, scale, mask, softmax and
+ *    a second matmul -- the plain definition written out below.
  *
  * A row whose visible set J is empty (possible only for a zero-length request)
  * gets an all-zero output.
