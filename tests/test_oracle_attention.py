@@ -4,7 +4,8 @@ The oracle (oracle/gqa_oracle.c) is checked against things other than itself:
 
 * a numpy brute force that expands the KV heads with ``np.repeat`` (the
   repeat_kv step of the unfused path in "Fused attention makes a 4,096-token
-  Qwen2 prefill on Metal 4.5x faster", section "Cause"), builds the full
+  Qwen2 prefill on Metal 4.5x faster", section "Cause and workaround", its
+  paragraph on the cause), builds the full
   score matrix, adds a -inf mask and applies scipy's softmax;
 * torch's CPU ``scaled_dot_product_attention`` in float64 on repeated K/V
   with an explicit bottom-right boolean mask (the end-alignment of the same
