@@ -511,6 +511,10 @@ def main():
                     help="also run one plain device copy of MIB MiB (reference for memory counters)")
     args = ap.parse_args()
 
+    extra_names = tuple(x for x in args.extras.split(",") if x)
+    unknown = [x for x in extra_names if x not in EXTRAS]
+    if unknown:
+        sys.exit("bench.py: unknown --extras %s (known: %s)" % (",".join(unknown), ",".join(EXTRAS)))
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         sys.stderr.write("bench.py measures one GPU: this build has no multi-GPU path "
                          "(--gpus %d requested)\n" % args.gpus)
@@ -614,11 +618,7 @@ def main():
                 secondary["prefill_0p5b_T%d" % T]["frac_of_gemm_bf16"] = round(
                     tf / result["calibration"]["gemm_bf16"]["TFLOPs"], 4)
     if not args.no_extra:
-        names = tuple(x for x in args.extras.split(",") if x)
-        unknown = [x for x in names if x not in EXTRAS]
-        if unknown:
-            sys.exit("bench.py: unknown --extras %s (known: %s)" % (",".join(unknown), ",".join(EXTRAS)))
-        secondary.update(bench_extra(torch, gqa, oracle, W, max(5, args.steps // 2), 2, flush, names))
+        secondary.update(bench_extra(torch, gqa, oracle, W, max(5, args.steps // 2), 2, flush, extra_names))
     if secondary:
         result["secondary"] = secondary
 
