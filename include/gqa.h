@@ -19,7 +19,7 @@
  *    stride instead of materialising one K/V copy per query head.
  *  - "Fused attention makes a 4,096-token Qwen2 prefill on Metal 4.5x
  *    faster...", section "Cause and workaround", points 1-3: K/V are passed
- *    before repeat_kv with the query heads a multiple of the KV heads; with
+ *    before repeat_kv, with Hq divisible by Hkv; with
  *    more than one query the causal mask is applied in-kernel with the
  *    queries aligned to the end of the keys; the single-query kernel reads K
  *    and V through the head stride and needs each head's rows to be

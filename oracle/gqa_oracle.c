@@ -21,8 +21,8 @@
  *  - "Fused attention makes a 4,096-token Qwen2 prefill on Metal 4.5x faster",
  *    section "Cause and workaround", points 1 and 2: K/V are given before
  *    repeat_kv (query heads a multiple of KV heads) and, with the causal flag,
- *    the queries are aligned to the end of the keys so that a chunk at an
- *    offset sees every earlier key.
+ *    the queries are aligned to the end of the keys, so query i of a chunk
+ *    that starts at key offset Tk - Tq attends to every key up to i + Tk - Tq.
  *  - same page, section "Cause and workaround", its opening paragraph on the
  *    cause: the unfused path is repeat_kv, a matmul, scale, mask, softmax and
  *    a second matmul -- the plain definition written out below.

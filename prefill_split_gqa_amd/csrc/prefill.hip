@@ -1,10 +1,10 @@
 // prefill.hip -- causal grouped-query prefill on the gfx950 matrix cores.
 //
 // "Fused attention makes a 4,096-token Qwen2 prefill on Metal 4.5x faster",
-// section "Cause and workaround": one pass reads the grouped KV heads
-// directly, applies the causal mask inside the kernel with the queries
-// aligned to the end of the keys (row i sees keys j <= i + Tk - Tq), and never
-// stores the score matrix.
+// section "Cause and workaround": a single kernel takes K and V with their
+// original (grouped) heads, applies the causal mask inside the kernel with
+// the queries aligned to the end of the keys (row i sees keys
+// j <= i + Tk - Tq), and never stores the score matrix.
 //
 // Work decomposition.  A workgroup has 4 waves and owns 128 query rows of
 // one query head (32 rows per wave) and a contiguous range ("chunk") of the

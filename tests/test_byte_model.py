@@ -2,9 +2,9 @@
 (no GPU needed).
 
 * "2x faster Qwen2 decode on Metal in Candle", section "Why It Matters: 7x KV
-  Expansion on Every Decode Step": at 7B geometry, fp32, 2048 tokens, one
-  layer's unexpanded KV cache is 8 MiB, and repeating the KV heads up to the
-  28 query heads writes 56 MiB per layer, 1.53 GiB over 28 layers.
+  Expansion on Every Decode Step": at 7B geometry, fp32 and 2048 tokens, K
+  and V of one layer take 8 MiB as stored; copied up to the 28 query heads
+  they take 56 MiB per layer, 1.53 GiB for the 28 layers.
 * "Fused attention makes a 4,096-token Qwen2 prefill on Metal 4.5x
   faster...", section "Why it matters": the unfused prefill writes a
   [14, T, T] score matrix of 470 MB at T = 4096.
