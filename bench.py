@@ -51,6 +51,7 @@ PREFILL_SRCS = [os.path.join(ROOT, "prefill_split_gqa_amd", "csrc", f) for f in 
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_0p5b_t4097_traffic.txt")
 PREFILL_COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_0p5b_t4097_counters.txt")
 Q4_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4_decode_s16384_traffic.txt")
+BATCHED_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "batched_qwen3_4b_traffic.txt")
 
 
 def decode_bytes(S: int, Hq: int = 28, Hkv: int = 4, D: int = 128, elem: int = 4) -> int:
@@ -377,8 +378,10 @@ def extra_batched(torch, gqa, oracle, W, steps, warmup, flush):
         ok = err <= 2e-2 and all(torch.equal(a, b) for a, b in zip(outs, ref))
         out["batched_qwen3_4b_B%d" % B] = hbm_entry(
             us, decode_bytes_generic(B, w.Hq, w.Hkv, w.D, [int(x) for x in lens], 2), ok, err,
-            "decode_splitk_kernel<DenseKV<bf16_t,128>,bf16_t,128,4>", layers_per_step=w.layers,
-            kv_lens=[int(x) for x in lens])
+            "decode_splitk_kernel<DenseKV<bf16_t,128>,bf16_t,128,4>",
+            traffic=read_summary_value(BATCHED_TRAFFIC_FILE, "decode_source_sha256_16", DECODE_SRCS,
+                                       "hbm_bytes_per_launch_B%d" % B),
+            layers_per_step=w.layers, kv_lens=[int(x) for x in lens])
         del dev, outs, ref, g
         torch.cuda.empty_cache()
     return out
