@@ -12,23 +12,19 @@
  * K and V are read unexpanded, straight from a preallocated cache, and no
  * score matrix is ever written to memory.
  *
- * Sources (web pages; section names as printed there):
- *  - "2x faster Qwen2 decode on Metal in Candle", sections "Why Qwen2 Was
- *    Running at Half Speed" and "Why It Matters: 7x KV Expansion": the fused
- *    single-token kernel attends over the original KV heads through a GQA
- *    stride instead of materialising one K/V copy per query head.
+ * Each entry point below cites the web page passage that defines it (page
+ * title and section as printed there).  The pages:
+ *  - "2x faster Qwen2 decode on Metal in Candle" (the Candle decode page);
  *  - "Fused attention makes a 4,096-token Qwen2 prefill on Metal 4.5x
- *    faster...", section "Cause and workaround", points 1-3: K/V are passed
- *    before repeat_kv, with Hq divisible by Hkv; with
- *    more than one query the causal mask is applied in-kernel with the
- *    queries aligned to the end of the keys; the single-query kernel reads K
- *    and V through the head stride and needs each head's rows to be
- *    contiguous.  Same page, end of "Cause and workaround": a device the
- *    kernel does not support gets an explicit error, not a fallback.
- *  - VeloxQuant-MLX "attention" posts, Result 4 and Part 4: the decode
- *    kernel's grid carries a request (B) axis; the quantized path takes the
- *    queries, the cache's codes, scales and biases, the group size and the
- *    scale, and dequantizes inside the kernel.
+ *    faster and lowers its peak from 3,403 MiB to 1,470 MiB" (the Fornace
+ *    prefill page);
+ *  - the VeloxQuant-MLX blog posts tagged "attention": "Batching Decode
+ *    Attention Across Requests Got Us 3.83x Real Throughput..." and
+ *    "Batching Decode Attention Across Layers Sounded Great -- Until the
+ *    Residual Stream Said No" (the VeloxQuant posts).
+ * A device other than gfx950 gets GQA_ERR_UNSUPPORTED rather than a
+ * fallback, as the Fornace page's engine refuses to load its fused path
+ * where the kernel does not exist ("Cause and workaround", last paragraph).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -92,6 +88,16 @@ const char *gqa_status_string(int status);
  * decode and prefill calls of any sizes, as long as it is large enough for
  * each call and their work does not overlap in time.
  *
+ * Decode merges never depend on every workgroup of a launch being resident
+ * at once: a workgroup waits for others only after all of them have
+ * started, so calls on other streams, other processes or a CU mask cannot
+ * stall one.  The waits are bounded all the same; should one ever give up
+ * (the protocol makes that unreachable), that merge writes NaN and marks
+ * the workspace poisoned (a word in the last 64 bytes of the 16 MiB
+ * region), and every later decode merge on it writes NaN too, rather than
+ * reading what the abandoned call left behind, until the workspace is
+ * zero-filled again (gqa_workspace_init).
+ *
  * Bytes of device workspace the decode entry points need for these sizes:
  * the 16 MiB region plus one fp32 partial output per (request, query head,
  * split).  Returns 0 when the sizes are invalid, which includes (max, sum)
@@ -113,6 +119,13 @@ int gqa_workspace_init(void *workspace, size_t bytes, void *stream);
  * Single-token decode over a preallocated KV cache, every request with the
  * same length.
  *
+ * Defined by the Candle decode page, "Why It Matters: 7x KV Expansion on
+ * Every Decode Step" (the fused kernel attends over the original KV heads
+ * through a GQA stride instead of a copy per query head), and the Fornace
+ * prefill page, "Cause and workaround", points 1 and 3 (K/V given before
+ * repeat_kv; the one-token kernel reads each KV head's rows contiguously
+ * through the head stride).
+ *
  *   q, out  [B, Hq, 1, D]        dtype
  *   k, v    [B, Hkv, s_cap, D]   dtype, rows 0..kv_len-1 valid (others never read)
  *   visible keys J = { j : j < kv_len }   (no mask: one query token)
@@ -132,7 +145,10 @@ int gqa_decode_attend(const void *q, const void *k, const void *v, void *out,
 
 /*
  * Batched decode: as gqa_decode_attend, but request b attends over its own
- * first kv_lens[b] cache rows.  kv_lens is a DEVICE array of B int32 values;
+ * first kv_lens[b] cache rows.  Defined by the VeloxQuant posts ("Part 4:
+ * the other half of the lever actually works": the decode kernel's grid
+ * carries a request axis, B x H_kv x S_q threadgroups; "Where this leaves
+ * things": variable-length concurrent requests).  kv_lens is a DEVICE array of B int32 values;
  * the host cannot check it, so the kernel clamps each value to [0, s_cap].
  * A request with length 0 gets an all-zero output row.
  */
@@ -147,7 +163,10 @@ int gqa_decode_attend_batched(const void *q, const void *k, const void *v, void 
  * 16 MiB region (one u32 arrival counter per request, query head and 128-row
  * block that is split into key chunks) plus the fp32 partial results of
  * those chunks; when no row block is split, the region alone.  Returns
- * 0 when the sizes are invalid.  The value depends only on the arguments.
+ * 0 when the sizes are invalid.  The value depends on the arguments and on
+ * the compute-unit count of the current HIP device (the chunking sizes the
+ * launch to the device; 256 when no device can be queried), so size the
+ * workspace with the device current that the call will run on.
  * Like the decode workspace it must start zero-filled (torch.zeros, or
  * gqa_workspace_init once per allocation).
  */
@@ -155,6 +174,12 @@ size_t gqa_prefill_workspace_bytes(int B, int Hq, int Hkv, int D, int Tq, int Tk
 
 /*
  * Causal prefill with the queries aligned to the end of the keys.
+ *
+ * Defined by the Fornace prefill page, "Cause and workaround": one kernel
+ * reads the grouped KV heads directly (point 1), applies the causal mask
+ * inside the kernel with the queries aligned to the end of the keys so that
+ * a chunk at an offset sees every earlier key (point 2), and never stores
+ * the [Hq, T, T] score matrix ("Why it matters").
  *
  *   q, out  [B, Hq, Tq, D]       dtype
  *   k, v    [B, Hkv, s_cap, D]   dtype, rows 0..Tk-1 valid (others never read)
@@ -185,9 +210,24 @@ int gqa_prefill_causal(const void *q, const void *k, const void *v, void *out,
  *   k_scales, k_biases,
  *   v_scales, v_biases     [B, Hkv, s_cap, D/group_size] f16
  *
+ * Defined by the VeloxQuant posts ("Part 4": the fused decode call takes
+ * the queries, the cache's codes, scales and biases, the group size and the
+ * scale, and dequantizes inside the kernel; "The setup": the fused
+ * group-affine decode+attention kernel behind the KIVI-style cache).
+ *
  * Element e of a row with code c has the value s*c + b (s, b of group
- * e / group_size), rounded once to float32, exactly as gqa_dequant_q4
- * returns it; attention then proceeds as in gqa_decode_attend.
+ * e / group_size); the result is attention over those values, as in
+ * gqa_decode_attend.  The kernel does not form s*c + b per element: per
+ * group it uses
+ *     q . k         = s * sum_e q_e c_e + b * sum_e q_e
+ *     sum_r p_r v_r = sum_r (p_r s_r) c_r + sum_r p_r b_r
+ * with the code products on the matrix cores (fp32 sums), and it rounds two
+ * kinds of intermediate values to f16: the query elements that face a high
+ * nibble (divided by 16; exact unless |q| < 2^-10) and each probability
+ * times its row's scale, p_r s_r (and p_r s_r / 16 for high nibbles).  With
+ * one visible key (kv_len = 1) the output is that key's dequantized value
+ * row, s*c + b rounded once to float32 (as gqa_dequant_q4 returns it), then
+ * rounded to f16: bit for bit.
  * Requires D in {64, 128}, group_size in {32, 64, 128} dividing D,
  * 1 <= kv_len <= s_cap, and a workspace as for gqa_decode_attend (same size
  * function).
@@ -200,9 +240,11 @@ int gqa_decode_attend_q4(const void *q,
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Dequantize n_rows cache rows to float32 with the device routine that
- * gqa_decode_attend_q4 applies to every element (a check hook: its output
- * can be compared bit for bit with the definition above).
+ * Dequantize n_rows cache rows to float32: s*c + b per element, rounded once
+ * (a check hook for the encoding the 4-bit entry points share; its output
+ * can be compared bit for bit with that definition).  The attention kernel
+ * does not call it: it applies scales and biases around the code products
+ * (see gqa_decode_attend_q4).
  *
  *   codes [n_rows, D/2] uint8, scales/biases [n_rows, D/group_size] f16,
  *   out [n_rows, D] float32.
@@ -212,17 +254,6 @@ int gqa_decode_attend_q4(const void *q,
  */
 int gqa_dequant_q4(const uint8_t *codes, const void *scales, const void *biases, float *out,
                    int n_rows, int D, int group_size, void *stream);
-
-/*
- * Measurement helper, not part of the attention path: reads `bytes` bytes at
- * `src` once with coalesced 16-byte loads (the plain streaming read that
- * bounds any HBM-bound kernel), so that a benchmark can time the achievable
- * read rate exactly as it times the decode kernels.  Stores nothing in
- * practice: one 32-bit word at `sink` (device memory) is written only if the
- * data fold to one fixed value.  Requires bytes > 0 and a multiple of 16,
- * src and sink 16-byte aligned.
- */
-int gqa_read_probe(const void *src, size_t bytes, void *sink, void *stream);
 
 #ifdef __cplusplus
 }

@@ -57,6 +57,11 @@ def _load():
     lib.gqa_oracle_f16_to_f32.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long]
     lib.gqa_oracle_f16_to_f32.restype = ctypes.c_int
     lib.gqa_oracle_max_threads.restype = ctypes.c_int
+    lib.gqa_oracle_f32_to_f16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long]
+    lib.gqa_oracle_f32_to_f16.restype = ctypes.c_int
+    lib.gqa_oracle_q4_quantize.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.gqa_oracle_q4_quantize.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -178,3 +183,53 @@ def q4_attend(q, k_codes, k_scales, k_biases, v_codes, v_scales, v_biases, group
     k = q4_dequant(k_codes, k_scales, k_biases, group)
     v = q4_dequant(v_codes, v_scales, v_biases, group)
     return attend(q, k, v, kv_lens=kv_lens, causal=False, scale=scale, nthreads=nthreads)
+
+
+def f32_to_f16(x) -> np.ndarray:
+    """float32 values -> float16 (round to nearest, ties to even), as bit patterns viewed as float16."""
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    out = np.empty(a.shape, dtype=np.uint16)
+    rc = _load().gqa_oracle_f32_to_f16(a.ctypes.data, out.ctypes.data, a.size)
+    if rc != 0:
+        raise ValueError("bad arguments")
+    return out.view(np.float16)
+
+
+def q4_quantize(x, group: int):
+    """Min-max group-affine 4-bit encoding of x [..., D] (widened exactly to
+    float32): (packed codes uint8 [..., D/2], scales f16 [..., D/group],
+    biases f16 [..., D/group]).  See gqa_oracle_q4_quantize for the steps."""
+    if hasattr(x, "detach"):
+        import torch
+
+        x = x.detach().cpu().to(torch.float32).numpy()
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    D = a.shape[-1]
+    n_rows = a.size // max(D, 1)
+    packed = np.empty(a.shape[:-1] + (D // 2,), dtype=np.uint8)
+    sc = np.empty(a.shape[:-1] + (D // group,), dtype=np.uint16)
+    bi = np.empty(a.shape[:-1] + (D // group,), dtype=np.uint16)
+    rc = _load().gqa_oracle_q4_quantize(a.ctypes.data, n_rows, D, int(group), packed.ctypes.data, sc.ctypes.data,
+                                        bi.ctypes.data)
+    if rc != 0:
+        raise ValueError("bad arguments")
+    return packed, sc.view(np.float16), bi.view(np.float16)
+
+
+def kv_append(cache, new, kv_lens):
+    """A preallocated cache after appending new rows: cache [B, H, s_cap, ...]
+    (any dtype), new [B, H, T_new, ...].  Request b's rows go to positions
+    p_b .. p_b + T_new - 1, p_b = kv_lens[b] clamped to [0, s_cap]; rows that
+    would land at or past s_cap are dropped.  Returns (updated copy of cache,
+    new lengths min(p_b + T_new, s_cap))."""
+    c = np.array(cache, copy=True)
+    n = np.asarray(new)
+    s_cap = c.shape[2]
+    t_new = n.shape[2]
+    out_lens = np.empty(c.shape[0], dtype=np.int32)
+    for b in range(c.shape[0]):
+        p = min(max(int(kv_lens[b]), 0), s_cap)
+        m = min(t_new, s_cap - p)
+        c[b, :, p:p + m] = n[b, :, :m]
+        out_lens[b] = p + m
+    return c, out_lens

@@ -209,6 +209,48 @@ static float half_bits_to_float(uint16_t hbits)
     return (float)(sign ? -mag : mag);
 }
 
+/*
+ * IEEE 754 binary32 -> binary16 bits, rounded to nearest, ties to even, from
+ * the format's definition: a finite magnitude below 2^-14 is a multiple of
+ * 2^-24 (subnormal; 1024 * 2^-24 is the smallest normal, whose encoding
+ * 0x0400 the same integer gives); otherwise 1.f * 2^e with 10 fraction bits
+ * and e + 15 in 1..30; magnitudes that round past 65504 become infinity.
+ * Every step is exact in double except the one rint (ties to even).
+ */
+static uint16_t float_to_half_bits(float f)
+{
+    const uint16_t sign = signbit(f) ? 0x8000 : 0;
+    const double a = fabs((double)f);
+    if (isnan(f))
+        return (uint16_t)(sign | 0x7E00);
+    if (isinf(f))
+        return (uint16_t)(sign | 0x7C00);
+    if (a < ldexp(1.0, -14)) {
+        const double n = rint(a * ldexp(1.0, 24));   /* 0 .. 1024 */
+        return (uint16_t)(sign | (uint16_t)n);
+    }
+    int e;
+    const double m = frexp(a, &e);                   /* a = m * 2^e, m in [0.5, 1) */
+    double n = rint(m * 2048.0);                     /* 1024 .. 2048: 11 significant bits */
+    e -= 1;                                          /* a = (n / 1024) * 2^e */
+    if (n == 2048.0) {
+        n = 1024.0;
+        e += 1;
+    }
+    if (e + 15 >= 31)
+        return (uint16_t)(sign | 0x7C00);            /* rounds past 65504 */
+    return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)(n - 1024.0));
+}
+
+int gqa_oracle_f32_to_f16(const float *in, uint16_t *out, long n)
+{
+    if (!in || !out || n < 0)
+        return ORACLE_ERR_ARG;
+    for (long i = 0; i < n; ++i)
+        out[i] = float_to_half_bits(in[i]);
+    return ORACLE_OK;
+}
+
 int gqa_oracle_f16_to_f32(const uint16_t *in, float *out, long n)
 {
     if (!in || !out || n < 0)
@@ -254,5 +296,69 @@ int gqa_oracle_q4_dequant(const uint8_t *packed, const uint16_t *scales, const u
         }
     }
     free(codes);
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Min-max group-affine 4-bit quantizer: what the incremental cache append
+ * computes for each new row (VeloxQuant-MLX "attention" posts, "Part 4":
+ * re-quantizing the whole K/V history every decode step cost ~25 ms/step,
+ * fixed by quantizing only the newly aged rows; the encoding is the one the
+ * fused decode reads: codes, and an f16 scale and bias per group).
+ *
+ * The pages do not print the quantizer; the reading taken is the plain
+ * min-max affine map onto the 16 codes, in float32 on the input values
+ * (f16, bf16 and f32 inputs all widen exactly), for each group of `group`
+ * consecutive elements of a row:
+ *   lo = min x, hi = max x                        (exact)
+ *   s16 = f16(fl32(fl32(hi - lo) / 15)),  b16 = f16(lo)     (ties to even)
+ *   s = f32(s16), b = f32(b16)
+ *   c  = 0                                        if s == 0
+ *        clamp(rint(fl32(fl32(x - b) / s)), 0, 15) otherwise (rint: ties to even)
+ * Inputs must be finite, with lo and (hi - lo) / 15 inside the f16 range.
+ * ------------------------------------------------------------------------- */
+
+/* x [n_rows, D] float32 -> packed codes [n_rows, D/2], scale and bias bits
+   [n_rows, D/group] (IEEE binary16) */
+int gqa_oracle_q4_quantize(const float *x, long n_rows, int D, int group, uint8_t *packed,
+                           uint16_t *scales, uint16_t *biases)
+{
+    if (!x || !packed || !scales || !biases || n_rows < 0 || D < 2 || D % 2 || group < 1 || D % group)
+        return ORACLE_ERR_ARG;
+    const int n_groups = D / group;
+    for (long r = 0; r < n_rows; ++r) {
+        const float *xr = x + (size_t)r * D;
+        uint8_t *pr = packed + (size_t)r * (D / 2);
+        memset(pr, 0, (size_t)(D / 2));
+        for (int g = 0; g < n_groups; ++g) {
+            const float *xg = xr + (size_t)g * group;
+            float lo = xg[0], hi = xg[0];
+            for (int e = 1; e < group; ++e) {
+                if (xg[e] < lo)
+                    lo = xg[e];
+                if (xg[e] > hi)
+                    hi = xg[e];
+            }
+            const float range = hi - lo;
+            const float step = range / 15.0f;
+            const uint16_t sh = float_to_half_bits(step);
+            const uint16_t bh = float_to_half_bits(lo);
+            scales[(size_t)r * n_groups + g] = sh;
+            biases[(size_t)r * n_groups + g] = bh;
+            const float sv = half_bits_to_float(sh);
+            const float bv = half_bits_to_float(bh);
+            for (int e = 0; e < group; ++e) {
+                int c = 0;
+                if (sv != 0.0f) {
+                    const float t = xg[e] - bv;
+                    const float u = t / sv;
+                    const float k = rintf(u);
+                    c = k < 0.0f ? 0 : (k > 15.0f ? 15 : (int)k);
+                }
+                const int idx = g * group + e;
+                pr[idx / 2] |= (uint8_t)((idx % 2 == 0) ? c : (c << 4));
+            }
+        }
+    }
     return ORACLE_OK;
 }

@@ -161,6 +161,13 @@ constexpr int kDecodeTargetWGs = 256;   // one workgroup per CU at full length
 // and size never depend on a call's sizes, the partial results of one call
 // can never land where another call, of any sizes, looks for its flags.
 constexpr size_t kWsFlagBytes = (size_t)16 << 20;
+// The last kWsTailBytes of the region are never used for per-call words:
+// they hold the poison word (offset kWsPoisonOff), set only if a decode
+// merge ever had to give up waiting (then every later decode merge on that
+// workspace writes NaN instead of trusting what it reads, until the
+// workspace is zero-filled again).
+constexpr size_t kWsTailBytes = 64;
+constexpr size_t kWsPoisonOff = kWsFlagBytes - 16;
 
 struct DecodePlan {
     int G;            // query heads per KV head
@@ -169,10 +176,21 @@ struct DecodePlan {
     int HT;           // Hkv * ht_per_kv: workgroup columns per request
     int L;            // keys per split (multiple of kDecodeRowGroups)
     int n_split_max;  // ceil(s_cap / L)
-    // workspace layout: (max, sum) words at offset 0 (flag region), partial
-    // outputs from kWsFlagBytes on
-    size_t ml_bytes, off_o, o_bytes, bytes;
+    // workspace layout: (max, sum) words at offset 0 (flag region), then
+    // kCtrlWords control words per (request, head tile) at off_ctrl (also in
+    // the flag region), partial outputs from kWsFlagBytes on
+    size_t ml_bytes, off_ctrl, ctrl_bytes, off_o, o_bytes, bytes;
 };
+
+// Control words of one (request, head tile): a tile word, then one word per
+// group of kSplitGroup splits (at most kDecodeMaxSplits / kSplitGroup),
+// each on a 128-byte line of its own: many workgroups adding to one word at
+// once queue behind each other in the memory system (measured: 64 adds on
+// one word at the start of the launch cost 2.4 us of a 11.4 us decode, on
+// separate lines nothing).
+constexpr int kSplitGroup = 8;
+constexpr int kCtrlStride = 32;  // words
+constexpr int kCtrlWords = 1 + kDecodeMaxSplits / kSplitGroup;
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -202,11 +220,14 @@ inline bool make_decode_plan(int B, int Hq, int Hkv, int D, int s_cap, int targe
     p->n_split_max = (int)((s_cap + p->L - 1) / p->L);
     const size_t parts = (size_t)B * p->HT * p->n_split_max * p->GT;  // (request, query head, split)
     p->ml_bytes = parts * 2 * 4;
+    p->off_ctrl = align_up(p->ml_bytes, 128);
+    p->ctrl_bytes = (size_t)B * p->HT * kCtrlWords * kCtrlStride * 4;
     p->off_o = kWsFlagBytes;
     p->o_bytes = parts * (size_t)D * 4;
     p->bytes = align_up(p->off_o + p->o_bytes, 256);
-    // the flags must fit their region; partials are addressed with 32-bit offsets
-    return p->ml_bytes <= kWsFlagBytes && p->o_bytes < ((size_t)1 << 31);
+    // the flags and control words must fit their region (its tail is
+    // reserved); partials are addressed with 32-bit offsets
+    return p->off_ctrl + p->ctrl_bytes <= kWsFlagBytes - kWsTailBytes && p->o_bytes < ((size_t)1 << 31);
 }
 
 // Arguments of the split-K decode kernels (passed by value).
@@ -223,6 +244,8 @@ struct DecodeArgs {
     float qscale;            // scale * log2(e)
     DecodePlan plan;
     float *part_o, *part_ml; // per split: [GT][D] outputs, [GT][2] (max, sum)
+    unsigned *ctrl;          // kCtrlWords control words per (request, head tile)
+    unsigned *poison;        // the workspace's poison word
     size_t ws_bytes;
     int n_cus;               // compute units of the device (launch shape)
 };
@@ -233,8 +256,9 @@ hipError_t launch_decode_q4(int D, int group, int B, const DecodeArgs &a, hipStr
 hipError_t launch_dequant_q4(const uint8_t *codes, const void *scales, const void *biases, float *out,
                              int n_rows, int D, int group, hipStream_t s);
 hipError_t launch_prefill(int dtype, int D, const void *q, const void *k, const void *v, void *out,
-                          int B, int Hq, int Hkv, int Tq, int Tk, int s_cap, float scale, void *ws, hipStream_t s);
-size_t prefill_workspace_bytes(int B, int Hq, int D, int Tq, int Tk);
+                          int B, int Hq, int Hkv, int Tq, int Tk, int s_cap, float scale, void *ws, int n_cus,
+                          hipStream_t s);
+size_t prefill_workspace_bytes(int B, int Hq, int D, int Tq, int Tk, int n_cus);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_read_probe(const void *src, size_t bytes, void *sink, hipStream_t s);
 

@@ -28,24 +28,41 @@
 // each (request, query head) is merged by a whole workgroup that waits until
 // every split of its (request, head tile) has published its partial for that
 // head, reads only that head's slice and merges it with the log-sum-exp rule
-// in a fixed order (results do not depend on timing).  When all splits of
-// the launch are resident at once, split s merges heads s, s + n_split, ...
-// of its tile right after publishing its own partial (it is resident
-// already, so the merge starts as soon as the last partial lands);
-// otherwise the grid carries, after all splits, one merge workgroup per
-// (request, query head).  A split publishes its outputs and its (max, sum)
-// pair with one store each and no wait: every fp32 word is written with its
-// lowest mantissa bit set, so in the zero-filled workspace a word with that
-// bit set has been published.  The merge polls the words it needs (one
-// round trip once they have landed) and zeroes them after reading, leaving
-// the workspace ready for the next call; no counters or atomics are
-// involved.
-// The wait always ends: splits that wait have published already and wait
-// only for splits of their own tile, which never wait before publishing and
-// are either resident (every split is, in the first mode) or dispatched
-// before any merge workgroup (workgroups are dispatched in linear-id order).
-// The wait is also bounded, and a merge that gives up writes NaN so that
-// the failure cannot pass silently.
+// in a fixed order (results do not depend on timing).  The designated merger
+// of query head hh is split hh mod n_split when the whole grid can be
+// resident (it merges right after publishing its own partial), otherwise a
+// merge workgroup placed after every split in the grid.  A split publishes
+// its outputs and its (max, sum) pair with one store each and no wait: every
+// fp32 word is written with its lowest mantissa bit set, so in the
+// zero-filled workspace a word with that bit set has been published.  The
+// merge polls the words it needs (one round trip once they have landed) and
+// zeroes them after reading, leaving the workspace ready for the next call.
+//
+// Waiting without co-residency.  A workgroup may wait without bound for
+// other workgroups only once it has proof that all of them have started: a
+// started split is resident (or done) and never waits before publishing, so
+// its partial always lands, whatever else shares the device (other kernels,
+// other streams, a CU mask).  The splits count themselves in groups of
+// kSplitGroup, one word per group (an atomic add first thing); the split
+// that completes its group adds one to the (request, head tile)'s tile word:
+//   bits 0..3   groups whose splits have all started;
+//   bits 4..7   heads whose designated merger has decided;
+//   bits 8+hh   set by head hh's designated merger when it decides.
+// A designated merger decides with exactly one add, (1 << 4) | (1 << (8 +
+// hh)) (a split merging in place makes it when its streaming is done, for
+// all of its heads at once): if the add finds every group counted, it has
+// its proof and merges; otherwise it leaves the head, and the split that
+// completed the last group -- whose add comes after in the word's order, and
+// so finds the head's bit set -- merges it after its own split, with proof.
+// The adds to one word are totally ordered, so each head is merged exactly
+// once and no workgroup waits without proof.  Every group and every head
+// adds exactly once, so the add that leaves the word at its final value
+// (all groups, all heads, every bit) returns it to zero; each group
+// completer zeroes its group word.  The waits are still bounded: a merge
+// that gives up (not reachable by the argument above) writes NaN and sets
+// the workspace's poison word, and every later merge on that workspace
+// writes NaN instead of trusting stale words, until the workspace is
+// zero-filled again.
 
 // Cross-workgroup exchange without cache maintenance: on gfx950 each XCD has
 // its own L2, and a device-scope fence writes back / invalidates that L2
@@ -207,6 +224,7 @@ __device__ __forceinline__ float sum4q(float x)
 }
 
 constexpr unsigned kMergeSpinLimit = 1u << 22;  // polls before a merge workgroup gives up
+constexpr unsigned kStartPolls = 256;           // tile word reads of a merge workgroup before it decides
 
 // Kernel launch shape of the decode grid: streaming workgroups first, then
 // merge workgroups (one per request and query head).
@@ -262,6 +280,76 @@ __device__ __forceinline__ bool packed_item(const DecodeArgs &a, int B, int i, S
 
 template <typename TQ, int D, int GT>
 __device__ void merge_head(const DecodeArgs &a, int m);
+template <typename TQ, int D, int GT>
+__device__ void merge_tile(const DecodeArgs &a, int col, int n_split, unsigned own_heads, unsigned decision,
+                           int ticket_tid, unsigned ticket);
+template <typename TQ, int D, int GT>
+__device__ void merge_workgroup(const DecodeArgs &a, int m);
+
+// Control words (see the file header): the tile word of (request, head
+// tile) col, and the word of its split group g.
+constexpr unsigned kTwGroups = 0xFu;    // bits 0..3
+constexpr int kTwDecidedShift = 4;      // bits 4..7
+constexpr int kTwHeadShift = 8;         // bits 8..15
+constexpr unsigned kNoTicket = ~0u;
+__device__ __forceinline__ unsigned *tile_word(const DecodeArgs &a, int col)
+{
+    return a.ctrl + (size_t)col * kCtrlWords * kCtrlStride;
+}
+__device__ __forceinline__ unsigned *group_word(const DecodeArgs &a, int col, int g)
+{
+    return tile_word(a, col) + (1 + g) * kCtrlStride;
+}
+__device__ __forceinline__ unsigned split_groups(int n_split)
+{
+    return (unsigned)(n_split + kSplitGroup - 1) / kSplitGroup;
+}
+
+// First thing a split of a multi-split (request, head tile) does: count
+// itself in its group.
+__device__ __forceinline__ unsigned group_add(const DecodeArgs &a, int col, int s)
+{
+    return __hip_atomic_fetch_add(group_word(a, col, s / kSplitGroup), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Given its group add's result t: the split that completed its group zeroes
+// the group word and counts the group in the tile word, returning that add's
+// result (awaited at the end); kNoTicket for the others.
+__device__ __forceinline__ unsigned group_done(const DecodeArgs &a, int col, int s, int n_split, unsigned t)
+{
+    const int g = s / kSplitGroup;
+    const int gs = min(kSplitGroup, n_split - g * kSplitGroup);
+    if (t != (unsigned)gs - 1u) return kNoTicket;
+    __hip_atomic_store(group_word(a, col, g), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_fetch_add(tile_word(a, col), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// A designated merger's one add for the heads in `heads`; the result shows
+// whether every group had started when it landed.
+__device__ __forceinline__ unsigned tile_decision_add(unsigned heads)
+{
+    return ((unsigned)__popc(heads) << kTwDecidedShift) | (heads << kTwHeadShift);
+}
+__device__ __forceinline__ unsigned decide(const DecodeArgs &a, int col, unsigned heads)
+{
+    return __hip_atomic_fetch_add(tile_word(a, col), tile_decision_add(heads), __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+}
+// After an add to the tile word that left it at `after`: the last add
+// (every group, every head counted) returns it to zero.
+template <int GT>
+__device__ __forceinline__ void tile_word_last(const DecodeArgs &a, int col, int n_split, unsigned after)
+{
+    const unsigned all = (1u << GT) - 1u;
+    if ((after & 0xFFFFu) == (split_groups(n_split) | ((unsigned)GT << kTwDecidedShift) | (all << kTwHeadShift)))
+        __hip_atomic_store(tile_word(a, col), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Heads a split designates itself merger of when the splits merge in place.
+template <int GT> __device__ __forceinline__ unsigned inplace_heads(int s, int n_split)
+{
+    unsigned h = 0u;
+    for (int hh = s; hh < GT; hh += n_split) h |= 1u << hh;
+    return h;
+}
 
 // Published partials carry a tag: every fp32 word is written with its
 // lowest mantissa bit set, so a published word can be told from a word of
@@ -347,7 +435,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
     static_assert(NF % 2 == 0 && NQ <= kDecodeThreads && kDecodeLPR == 32, "tile shape");
 
     if ((int)blockIdx.x >= grid.n_stream) {
-        merge_head<TQ, D, GT>(a, (int)blockIdx.x - grid.n_stream);
+        merge_workgroup<TQ, D, GT>(a, (int)blockIdx.x - grid.n_stream);
         return;
     }
 
@@ -412,11 +500,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
     const bool q_loader = tid < QB / 16;
     const uint4 qv = *((const uint4 *)((const char *)a.q + ((size_t)b * a.Hq + h0) * D * sizeof(TQ)) +
                        (q_loader ? tid : 0));
+    // this split counts itself in its group right after the query load
+    // (its result is awaited after the queries, before any K/V wait)
+    const int col = b * P.HT + ht;
+    unsigned gticket = 0u;
+    if (n_split > 1 && tid == 0) gticket = group_add(a, col, s);
     asm volatile("" ::: "memory");  // keep the query load ahead of the K/V loads
     load_chunk(0, start);
     load_chunk(1, start + CHUNK);
     if (q_loader) *((uint4 *)sq + tid) = qv;
     __syncthreads();
+    unsigned ticket = kNoTicket;  // a group completer's tile word add (awaited at the end)
+    if (n_split > 1 && tid == 0) ticket = group_done(a, col, s, n_split, gticket);
 
     // Queries of the GT heads, pre-multiplied by scale*log2(e) (every LDS
     // read issued before the first is used).
@@ -505,6 +600,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
         if (more) load_chunk(1, c1 + 2 * CHUNK);
     }
 
+    // in place, split s is the designated merger of heads s, s + n_split, ...,
+    // and decides for them now (the add's result is first needed after the
+    // split has published)
+    const unsigned own = n_split > 1 && grid.inplace ? inplace_heads<GT>(s, n_split) : 0u;
+    unsigned decision = 0u;
+    if (tid == 0 && own != 0u) decision = decide(a, col, own);
+
     // ---- merge the 2 row-groups of each wave ----
     __shared__ __attribute__((aligned(16))) float so[NW][GT][D];
     __shared__ float sm[NW][GT], sl[NW][GT];
@@ -531,10 +633,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
     }
     __syncthreads();
 
-    finish_split<TQ, D, GT>(a, &so[0][0][0], &sm[0][0], &sl[0][0], b * P.HT + ht, s, n_split, out);
-    // split s then merges query heads s, s + n_split, ... of its head tile
-    if (grid.inplace && n_split > 1)
-        for (int hh = s; hh < GT; hh += n_split) merge_head<TQ, D, GT>(a, (b * P.HT + ht) * GT + hh);
+    finish_split<TQ, D, GT>(a, &so[0][0][0], &sm[0][0], &sl[0][0], col, s, n_split, out);
+    if (n_split > 1) merge_tile<TQ, D, GT>(a, col, n_split, own, decision, 0, ticket);
 }
 
 // Sum over the lanes of a wave that share lane % CPW (CPW a power of two
@@ -555,8 +655,9 @@ template <int CPW> __device__ __forceinline__ float colgroup_sum(float x)
 // 4-wide output columns w*CPW .. w*CPW + CPW - 1; lane (c = lane % CPW,
 // sg = lane / CPW) handles column c of the splits sg + k*LPC and polls
 // those output slices itself.  Wave 0 polls the (max, sum) pairs (lane j:
-// split j) and leaves them and their maximum in LDS; after one barrier each
-// wave forms its weights and sums its lanes with cross-lane steps.
+// split j) and leaves them and their maximum in LDS; each wave then forms
+// its weights and sums its lanes with cross-lane steps.
+//
 template <typename TQ, int D, int GT>
 __device__ void merge_head(const DecodeArgs &a, int m)
 {
@@ -591,16 +692,19 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     const int h = g * P.G + (ht % P.ht_per_kv) * GT + hh;
     TQ *out = (TQ *)a.out + ((size_t)b * a.Hq + h) * D;
 
-    // Wait until every split has published this head's partial: each thread
-    // polls the tagged words it needs -- the (max, sum) pair of split tid
-    // (tid < n_split) and its output slices of splits sg + k * LPC -- and
-    // zeroes them once read, leaving the workspace as it found it.
+    // Wait until every split has published this head's partial (the caller
+    // holds the proof that every split has started): each thread polls the
+    // tagged words it needs -- the (max, sum) pair of split tid (tid <
+    // n_split) and its output slices of splits sg + k * LPC -- and zeroes
+    // them once read, leaving the workspace as it found it.
     const size_t colbase = (size_t)col * P.n_split_max;
     const __amdgpu_buffer_rsrc_t ws_ml = make_rsrc(a.part_ml + colbase * GT * 2, (size_t)n_split * GT * 8);
     const __amdgpu_buffer_rsrc_t ws_o = make_rsrc(a.part_o + colbase * GT * D, (size_t)n_split * GT * D * 4);
     auto o_off = [&](int k) { return (int)(((((size_t)sg + (size_t)k * LPC) * GT + hh) * D + d4 * 4) * 4); };
     if (tid == 0) s_go = 1;
     __syncthreads();
+    // a poisoned workspace (an earlier merge gave up) is not trusted
+    const unsigned poisoned = tid == 0 ? __hip_atomic_load(a.poison, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
     tag_u4_t po[PER];
     tag_u2_t mlw = {0u, 0u};
     unsigned need = tid < n_split ? 1u << PER : 0u;  // bit k: slice k, bit PER: the pair
@@ -626,6 +730,9 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     }
     if (pend != 0u) {
         s_go = 0;
+        __hip_atomic_store(a.poison, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (poisoned != 0u) {
+        s_go = 0;
     } else {
         // consume: every word read goes back to zero
 #pragma unroll
@@ -645,7 +752,7 @@ __device__ void merge_head(const DecodeArgs &a, int m)
         if (tid == 0) s_M = mx;
     }
     __syncthreads();
-    if (!s_go) {  // not reachable: every split publishes; never pass silently
+    if (!s_go) {  // not reachable (see the file header); never pass silently
         if (sg == 0) store4(out + d4 * 4, __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
         return;
     }
@@ -670,6 +777,75 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     R.z = colgroup_sum<CPW>(R.z);
     R.w = colgroup_sum<CPW>(R.w);
     if (sg == 0) store4(out + d4 * 4, R.x / Ls, R.y / Ls, R.z / Ls, R.w / Ls);
+}
+
+// The merges a split performs for (request, head tile) col once its own
+// partial is published (see the file header): the heads it is the
+// designated merger of (own_heads, in place), if its decision add (result
+// `decision`, thread 0) found every group counted; and, if its tile word
+// add (thread ticket_tid holds the result; kNoTicket if it completed no
+// group) counted the last group, the heads whose designated mergers
+// decided before that.
+template <typename TQ, int D, int GT>
+__device__ void merge_tile(const DecodeArgs &a, int col, int n_split, unsigned own_heads, unsigned decision,
+                           int ticket_tid, unsigned ticket)
+{
+    __shared__ unsigned s_ticket, s_heads;
+    if ((int)threadIdx.x == ticket_tid) s_ticket = ticket;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned all = (1u << GT) - 1u;
+        const unsigned n_groups = split_groups(n_split);
+        unsigned heads = 0u;
+        const unsigned t = ticket_tid >= 0 ? s_ticket : kNoTicket;
+        if (t != kNoTicket) {
+            const unsigned after = t + 1u;
+            if ((after & kTwGroups) == n_groups) heads |= (t >> kTwHeadShift) & all;  // left to this split
+            tile_word_last<GT>(a, col, n_split, after);
+        }
+        if (own_heads != 0u) {
+            if ((decision & kTwGroups) == n_groups) heads |= own_heads;
+            tile_word_last<GT>(a, col, n_split, decision + tile_decision_add(own_heads));
+        }
+        s_heads = heads;
+    }
+    __syncthreads();
+    const unsigned heads = s_heads;
+    for (int hh = 0; hh < GT; ++hh)
+        if (heads & (1u << hh)) merge_head<TQ, D, GT>(a, col * GT + hh);
+}
+
+// A merge workgroup (placed after every split in the grid): the designated
+// merger of item m = (request, head tile) * GT + head.  Thread 0 waits a
+// bounded time for the tile word to count every group (it waits for starts
+// only that long), then decides with its one add.
+template <typename TQ, int D, int GT>
+__device__ void merge_workgroup(const DecodeArgs &a, int m)
+{
+    __shared__ int s_go;
+    const int col = m / GT, hh = m % GT;
+    const int b = col / a.plan.HT;
+    int n = a.kv_len;
+    if (a.kv_lens) {
+        n = a.kv_lens[b];
+        n = n < 0 ? 0 : (n > a.s_cap ? a.s_cap : n);
+    }
+    const int n_split = (n + a.plan.L - 1) / a.plan.L;
+    if (n_split <= 1) return;  // written directly by the streaming workgroup
+    if (threadIdx.x == 0) {
+        const unsigned n_groups = split_groups(n_split);
+        for (unsigned it = 0; it < kStartPolls; ++it) {
+            if ((__hip_atomic_load(tile_word(a, col), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kTwGroups) ==
+                n_groups)
+                break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+        const unsigned old = decide(a, col, 1u << hh);
+        tile_word_last<GT>(a, col, n_split, old + tile_decision_add(1u << hh));
+        s_go = (old & kTwGroups) == n_groups ? 1 : 0;
+    }
+    __syncthreads();
+    if (s_go) merge_head<TQ, D, GT>(a, m);
 }
 
 // ===========================================================================
@@ -764,7 +940,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
     static_assert(GT <= 16 && G % 32 == 0 && D % G == 0, "tile shape");
 
     if ((int)blockIdx.x >= grid.n_stream) {
-        merge_head<f16_t, D, GT>(a, (int)blockIdx.x - grid.n_stream);
+        merge_workgroup<f16_t, D, GT>(a, (int)blockIdx.x - grid.n_stream);
         return;
     }
 
@@ -845,6 +1021,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
     const bool two = wave + kQ4Waves < nst;
     if (wave < nst) issue(wave, 0);
     if (two) issue(wave + kQ4Waves, 1);
+    // The group add comes from the last wave (not one that stages queries)
+    // after its loads: the explicit waits below then at most also wait for
+    // it, never miss a load they count on.  Its result is looked at once
+    // the wave's steps are done.
+    const int col = b * P.HT + ht;
+    constexpr int kTicketTid = kDecodeThreads - 64;
+    unsigned gticket = 0u;
+    if (n_split > 1 && tid == kTicketTid) gticket = group_add(a, col, s);
     if (wave < QDMA) {
         if (two)
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * S::NL) : "memory");
@@ -1031,6 +1215,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
         if (st + 2 * kQ4Waves < nst) issue(st + 2 * kQ4Waves, buf);
     }
 
+    const unsigned own = n_split > 1 && grid.inplace ? inplace_heads<GT>(s, n_split) : 0u;
+    unsigned decision = 0u;
+    if (tid == 0 && own != 0u) decision = decide(a, col, own);
+
     // ---- wave totals, then the workgroup's combination ----
     l_run = sum4q(l_run);
 #pragma unroll
@@ -1051,11 +1239,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
             sl[wave * GT + j] = l_run;
         }
     }
+    unsigned ticket = kNoTicket;  // a group completer's tile word add (awaited at the end)
+    if (n_split > 1 && tid == kTicketTid) ticket = group_done(a, col, s, n_split, gticket);
     __syncthreads();
-    finish_split<f16_t, D, GT, SOD>(a, so, sm, sl, b * P.HT + ht, s, n_split, out);
-    // split s then merges query heads s, s + n_split, ... of its head tile
-    if (grid.inplace && n_split > 1)
-        for (int hh = s; hh < GT; hh += n_split) merge_head<f16_t, D, GT>(a, (b * P.HT + ht) * GT + hh);
+    finish_split<f16_t, D, GT, SOD>(a, so, sm, sl, col, s, n_split, out);
+    if (n_split > 1) merge_tile<f16_t, D, GT>(a, col, n_split, own, decision, kTicketTid, ticket);
 }
 
 // ---------------------------------------------------------------------------

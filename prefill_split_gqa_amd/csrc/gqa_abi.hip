@@ -8,11 +8,11 @@
 // kernels are enqueued on the caller's stream.
 
 #include <cmath>
-#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
 #include "../../include/gqa.h"
+#include "../../include/gqa_bench.h"
 #include "common.h"
 
 using namespace gqa;
@@ -23,29 +23,9 @@ constexpr int kAbiVersion = 2;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-int env_int(const char *name, int dflt)
-{
-    const char *s = std::getenv(name);
-    const int x = s ? std::atoi(s) : 0;
-    return x > 0 ? x : dflt;
-}
-
-// Launch-shape knobs (defaults fill the chip once at full length); the
-// environment overrides exist for tuning sweeps only.
-int decode_target_wgs()
-{
-    static const int v = env_int("GQA_DECODE_TARGET_WGS", kDecodeTargetWGs);
-    return v;
-}
-int decode_max_splits()
-{
-    static const int v = env_int("GQA_DECODE_MAX_SPLITS", kDecodeMaxSplits);
-    return v < kDecodeMaxSplits ? v : kDecodeMaxSplits;  // the merge holds at most this many
-}
-
 bool plan_decode(int B, int Hq, int Hkv, int D, int s_cap, DecodePlan *p)
 {
-    if (!make_decode_plan(B, Hq, Hkv, D, s_cap, decode_target_wgs(), decode_max_splits(), p)) return false;
+    if (!make_decode_plan(B, Hq, Hkv, D, s_cap, kDecodeTargetWGs, kDecodeMaxSplits, p)) return false;
     // grid limits, and buffer-resource ranges of the partial arrays
     return p->HT <= 65535 && p->n_split_max <= 65535 && p->bytes < ((size_t)1 << 31);
 }
@@ -73,6 +53,15 @@ int device_supported(int *cus = nullptr)
     }
     if (cus) *cus = n_cus[dev];
     return cache[dev];
+}
+
+// Compute units of the current device, for launch plans whose sizes the
+// host needs before it can launch (workspace sizes); 256 (the gfx950 parts)
+// when no device can be queried.
+int plan_cus()
+{
+    int cus = 0;
+    return device_supported(&cus) == 1 && cus > 0 ? cus : 256;
 }
 
 int check_device(int *cus = nullptr)
@@ -107,6 +96,8 @@ void fill_ws(DecodeArgs &a, void *ws)
     char *base = (char *)ws;
     a.part_o = (float *)(base + a.plan.off_o);
     a.part_ml = (float *)base;  // the flag region
+    a.ctrl = (unsigned *)(base + a.plan.off_ctrl);
+    a.poison = (unsigned *)(base + kWsPoisonOff);
     a.ws_bytes = a.plan.bytes;
 }
 
@@ -195,7 +186,7 @@ size_t gqa_prefill_workspace_bytes(int B, int Hq, int Hkv, int D, int Tq, int Tk
 {
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Tq < 1 || Tq > Tk) return 0;
     if (D != 64 && D != 128) return 0;
-    return prefill_workspace_bytes(B, Hq, D, Tq, Tk);
+    return prefill_workspace_bytes(B, Hq, D, Tq, Tk, plan_cus());
 }
 
 int gqa_prefill_causal(const void *q, const void *k, const void *v, void *out, int B, int Hq, int Hkv, int D,
@@ -214,13 +205,14 @@ int gqa_prefill_causal(const void *q, const void *k, const void *v, void *out, i
     // a head's rows (plus the tile past the end that a prefetch names) are
     // addressed with 32-bit byte offsets
     if ((size_t)(s_cap + 512) * D * 2 >= ((size_t)1 << 31)) return GQA_ERR_SHAPE;
-    const size_t need = prefill_workspace_bytes(B, Hq, D, Tq, Tk);
+    const int cus = plan_cus();
+    const size_t need = prefill_workspace_bytes(B, Hq, D, Tq, Tk, cus);
     if (!workspace || workspace_bytes < need) return GQA_ERR_WORKSPACE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace))
         return GQA_ERR_ALIGN;
     if (int st = check_device()) return st;
-    return hip_status(
-        launch_prefill(dtype, D, q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, workspace, (hipStream_t)stream));
+    return hip_status(launch_prefill(dtype, D, q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, workspace, cus,
+                                     (hipStream_t)stream));
 }
 
 int gqa_decode_attend_q4(const void *q, const uint8_t *k_codes, const void *k_scales, const void *k_biases,

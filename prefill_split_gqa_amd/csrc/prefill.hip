@@ -43,7 +43,6 @@
 // block's diagonal, or a last row block with fewer than 128 valid rows).
 
 #include <algorithm>
-#include <cstdlib>
 #include <type_traits>
 #include <utility>
 #include <vector>
@@ -118,7 +117,6 @@ constexpr int kPfBM = 128;       // query rows per workgroup: 4 row-waves of 32 
 constexpr int kPfBN = 64;        // keys per tile
 constexpr int kPfThreads = 256;  // 4 waves
 constexpr int kPfMaxItems = 1024;     // (row block, key chunk) work items in the launch table
-constexpr int kPfCUs = 256;           // compute units of the gfx950 parts
 constexpr int kPfMinChunk = 10;       // fewest key tiles per chunk: a chunk's partial costs a write and a read
 constexpr float kPfSumLimit = 1024.0f;  // a lane's probability sum that needs the exact path
 
@@ -632,22 +630,14 @@ static PfPlan pf_plan_for(int Tq, int Tk, int ch)
 static bool pf_plan_fits(const PfPlan &p, int B, int Hq)
 {
     return p.n_items <= kPfMaxItems && p.max_nc <= 63 &&
-           (size_t)B * Hq * (p.n_rb - p.rb0) * 4 <= kWsFlagBytes;
+           (size_t)B * Hq * (p.n_rb - p.rb0) * 4 <= kWsFlagBytes - kWsTailBytes;
 }
 
-// Tuning overrides of the chunking (environment, read once; for sweeps).
-static int pf_env(const char *name, int dflt)
+// n_cus: compute units of the device the launch runs on.
+static PfPlan pf_plan(int B, int Hq, int D, int Tq, int Tk, int n_cus)
 {
-    const char *s = std::getenv(name);
-    const int x = s ? std::atoi(s) : 0;
-    return x > 0 ? x : dflt;
-}
-
-static PfPlan pf_plan(int B, int Hq, int D, int Tq, int Tk)
-{
-    static const int slot_factor = pf_env("GQA_PREFILL_SLOT_PERCENT", 100);  // percent of the resident slots
-    static const int min_chunk = pf_env("GQA_PREFILL_MIN_CHUNK", kPfMinChunk);
-    const long slots = (long)(D == 64 ? 4 : 2) * kPfCUs * slot_factor / 100;  // resident workgroups (VGPR budget)
+    const int min_chunk = kPfMinChunk;
+    const long slots = (long)(D == 64 ? 4 : 2) * n_cus;  // resident workgroups (VGPR budget)
     const int n_rb = (Tq + kPfBM - 1) / kPfBM;
     long total = 0;
     for (int rb = 0; rb < n_rb; ++rb) total += pf_row_tiles(rb, Tq, Tk);
@@ -684,9 +674,9 @@ static void pf_items(const PfPlan &p, int Tq, int Tk, PfItems *it)
 }
 
 // Flag region, then one partial slot per chunk of every split row block.
-size_t prefill_workspace_bytes(int B, int Hq, int D, int Tq, int Tk)
+size_t prefill_workspace_bytes(int B, int Hq, int D, int Tq, int Tk, int n_cus)
 {
-    const PfPlan p = pf_plan(B, Hq, D, Tq, Tk);
+    const PfPlan p = pf_plan(B, Hq, D, Tq, Tk, n_cus);
     const size_t slot = D == 64 ? PfSlot<64>::BYTES : PfSlot<128>::BYTES;
     const size_t split_cols = (size_t)B * Hq * (p.n_rb - p.rb0);
     return kWsFlagBytes + (p.max_nc > 1 ? split_cols * p.max_nc * slot : 0);
@@ -694,9 +684,9 @@ size_t prefill_workspace_bytes(int B, int Hq, int D, int Tq, int Tk)
 
 template <typename T, int D>
 static hipError_t launch_pf(const void *q, const void *k, const void *v, void *out, int B, int Hq, int Hkv,
-                            int Tq, int Tk, int s_cap, float scale, void *ws, hipStream_t s)
+                            int Tq, int Tk, int s_cap, float scale, void *ws, int n_cus, hipStream_t s)
 {
-    const PfPlan plan = pf_plan(B, Hq, D, Tq, Tk);
+    const PfPlan plan = pf_plan(B, Hq, D, Tq, Tk, n_cus);
     PfItems items;
     pf_items(plan, Tq, Tk, &items);
     // A zero scale (uniform weights over the visible keys) is run as the
@@ -718,14 +708,14 @@ static hipError_t launch_pf(const void *q, const void *k, const void *v, void *o
 }
 
 hipError_t launch_prefill(int dtype, int D, const void *q, const void *k, const void *v, void *out, int B,
-                          int Hq, int Hkv, int Tq, int Tk, int s_cap, float scale, void *ws, hipStream_t s)
+                          int Hq, int Hkv, int Tq, int Tk, int s_cap, float scale, void *ws, int n_cus, hipStream_t s)
 {
     if (dtype == 1) {
-        if (D == 64) return launch_pf<bf16_t, 64>(q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, ws, s);
-        if (D == 128) return launch_pf<bf16_t, 128>(q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, ws, s);
+        if (D == 64) return launch_pf<bf16_t, 64>(q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, ws, n_cus, s);
+        if (D == 128) return launch_pf<bf16_t, 128>(q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, ws, n_cus, s);
     } else if (dtype == 2) {
-        if (D == 64) return launch_pf<f16_t, 64>(q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, ws, s);
-        if (D == 128) return launch_pf<f16_t, 128>(q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, ws, s);
+        if (D == 64) return launch_pf<f16_t, 64>(q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, ws, n_cus, s);
+        if (D == 128) return launch_pf<f16_t, 128>(q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, ws, n_cus, s);
     }
     return hipErrorInvalidValue;
 }

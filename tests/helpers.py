@@ -26,9 +26,28 @@ def max_abs_err(got: torch.Tensor, want: np.ndarray) -> float:
     return float(np.abs(g - want).max()) if g.size else 0.0
 
 
-def assert_close(got: torch.Tensor, want: np.ndarray, tol: float, what: str) -> float:
+def row_ulps(got: torch.Tensor, want: np.ndarray) -> np.ndarray:
+    """Per output row (last axis), the max-abs error in units in the last
+    place of the output dtype at the row's largest |oracle value|
+    (bf16: 8 significant bits, f16: 11, fp32: 24)."""
+    bits = {torch.bfloat16: 8, torch.float16: 11, torch.float32: 24}[got.dtype]
+    g = got.detach().float().cpu().double().numpy()
+    err = np.abs(g - want).max(axis=-1)
+    top = np.maximum(np.abs(want).max(axis=-1), 2.0 ** -126)
+    ulp = np.exp2(np.floor(np.log2(top)) - (bits - 1))
+    return err / ulp
+
+
+def assert_close(got: torch.Tensor, want: np.ndarray, tol: float, what: str, max_ulps=None) -> float:
     err = max_abs_err(got, want)
-    note("  %s: max-abs error %.3e (bound %.1e)" % (what, err, tol))
+    if got.dtype in (torch.bfloat16, torch.float16) and got.numel():
+        u = row_ulps(got, want)
+        note("  %s: max-abs error %.3e (bound %.1e); per-row error up to %.2f ulps of the row max%s"
+             % (what, err, tol, float(u.max()), "" if max_ulps is None else " (bound %g)" % max_ulps))
+        if max_ulps is not None:
+            assert float(u.max()) <= max_ulps, "%s: %.2f ulps > %g" % (what, float(u.max()), max_ulps)
+    else:
+        note("  %s: max-abs error %.3e (bound %.1e)" % (what, err, tol))
     assert err <= tol, "%s: max-abs error %.3e > %.1e" % (what, err, tol)
     return err
 

@@ -1,6 +1,7 @@
 """The C ABI is usable from plain C (no GPU needed).
 
-A C99 program that includes include/gqa.h is compiled with gcc (-Wall
+A C99 program that includes include/gqa.h (and the benchmark helper's
+include/gqa_bench.h) is compiled with gcc (-Wall
 -Werror, strict prototypes), linked against libgqa.so and run: it checks the
 version, every status string, the workspace-size functions, and that invalid
 calls return their status codes before touching a device.  The header is also
@@ -23,6 +24,7 @@ C_PROGRAM = r"""
 #include <stdio.h>
 #include <string.h>
 #include "gqa.h"
+#include "gqa_bench.h"
 
 static int fails = 0;
 #define CHECK(c) do { if (!(c)) { printf("FAIL line %d: %s\n", __LINE__, #c); ++fails; } } while (0)

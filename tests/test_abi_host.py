@@ -16,7 +16,7 @@ import pytest
 import prefill_split_gqa_amd as gqa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gqa.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("gqa.h", "gqa_bench.h")]
 
 FAKE = ctypes.c_void_p(0x10000)      # 16-byte aligned, never dereferenced
 FAKE_ODD = ctypes.c_void_p(0x10004)  # misaligned
@@ -24,9 +24,11 @@ NULL = ctypes.c_void_p(0)
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gqa_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(gqa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -147,10 +149,11 @@ def test_decode_workspace_layout():
     # keys at s_cap = 4096; one 128-float partial per (column, split, head)
     # after the flag region
     assert gqa.gqa_decode_workspace_bytes(1, 28, 4, 128, 4096) == MIB16 + 4 * 64 * 7 * 128 * 4
-    # the (max, sum) words, 8 bytes per partial, must fit the flag region:
-    # 28 * 64 * 8 bytes a request allow 1170 requests
-    assert gqa.gqa_decode_workspace_bytes(1170, 28, 4, 128, 4096) > 0
-    assert gqa.gqa_decode_workspace_bytes(1171, 28, 4, 128, 4096) == 0
+    # the (max, sum) words, 8 bytes per partial, and one 4-byte control word
+    # per (request, head tile) must fit the flag region less its 64-byte
+    # tail: 28 * 64 * 8 + 4 * 4 bytes a request allow 1168 requests
+    assert gqa.gqa_decode_workspace_bytes(1168, 28, 4, 128, 4096) > 0
+    assert gqa.gqa_decode_workspace_bytes(1169, 28, 4, 128, 4096) == 0
 
 
 def test_q4_validation(lib):

@@ -317,3 +317,42 @@ def test_workspace_reuse_with_changing_inputs(gpu_lib):
     torch.cuda.synchronize()
     for q, k, v, n, o in cases:
         assert_close(o, oracle.attend(q, k, v, kv_lens=n), 2e-5, "reuse n=%d" % n)
+
+
+def test_decode_concurrent_streams_separate_workspaces(gpu_lib):
+    """The 7B-geometry fp32 decode at KV length 4096 and the 4-bit decode at
+    KV length 16384 run concurrently on two streams (default priority), each
+    with its own workspace, four calls per stream and round, ten rounds.  Each
+    launch fills the device, so their workgroups compete for compute units:
+    the merges must not rely on a whole launch being resident.  Every output
+    is checked against the oracle; the first failure stops the test."""
+    w7 = W.by_name("decode_7b")
+    q7, k7, v7 = W.decode_inputs(w7, 4096, 0)
+    want7 = oracle.attend(q7, k7, v7, scale=w7.scale())
+    w4 = W.by_name("q4_decode")
+    x4 = W.q4_inputs(w4, 16384, 0)
+    names = ("k_codes", "k_scales", "k_biases", "v_codes", "v_scales", "v_biases")
+    want4 = oracle.q4_attend(x4["q"], *(x4[n] for n in names), w4.group, scale=w4.scale())
+    d7 = [t.cuda() for t in (q7, k7, v7)]
+    d4 = {n: t.cuda() for n, t in x4.items()}
+    ws7 = gpu_lib.make_workspace(1, w7.Hq, w7.Hkv, w7.D, 4096)
+    ws4 = gpu_lib.make_workspace(1, w4.Hq, w4.Hkv, w4.D, 16384)
+    outs7 = [torch.empty_like(d7[0]) for _ in range(4)]
+    outs4 = [torch.empty_like(d4["q"]) for _ in range(4)]
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for r in range(10):
+        note("concurrent decode round %d" % r)
+        with torch.cuda.stream(s1):
+            for o in outs7:
+                gpu_lib.gqa_decode_attend(d7[0], d7[1], d7[2], o, 4096, ws7)
+        with torch.cuda.stream(s2):
+            for o in outs4:
+                gpu_lib.gqa_decode_attend_q4(d4["q"], *(d4[n] for n in names), o, w4.group, 16384, ws4)
+        torch.cuda.synchronize()
+        for i, o in enumerate(outs7):
+            assert_close(o, want7, 2e-5, "round %d fp32 call %d" % (r, i))
+        for i, o in enumerate(outs4):
+            assert_close(o, want4, 2e-2, "round %d 4-bit call %d" % (r, i))
+    assert_workspace_ready(ws7, "fp32 decode workspace after the concurrent rounds")
+    assert_workspace_ready(ws4, "4-bit decode workspace after the concurrent rounds")

@@ -7,9 +7,19 @@ workaround" point 2 of the Fornace prefill page).  T = 513 and 2049 and the
 chunk are compared on every output; T = 4097 on every output too (the oracle
 takes a few seconds on all cores).  Small shapes cover ragged tiles, Tq < Tk,
 D = 128, f16, several group sizes and B > 1.  Bound: max-abs 2e-2 (bf16/f16
-outputs).  Row 0 of a square prefill sees one key and must equal that key's
-value row exactly; the chunk must match the tail of the full prefill within
-the bound.
+outputs); every 16-bit comparison also reports the per-row error in units
+in the last place at the row's largest |output|.  Row 0 of a square prefill
+sees one key and must equal that key's value row exactly; the chunk must
+match the tail of the full prefill within the bound.
+
+Seam cases: long rows are split into chunks of 64-key tiles merged through
+the workspace, and on plain N(0,1) inputs one key more or less at a chunk
+seam moves long rows by under the bound.  The seam cases plant, on each
+side of every tile boundary, a key that dominates one (row, head) pair
+(workloads.gen.seam_planted), so a key lost or doubled at any boundary
+fails the bound (tests/test_check_power.py shows the check rejecting
+exactly those mistakes on the oracle's output); their per-row error must
+also stay within 2 ulps.
 """
 
 import numpy as np
@@ -19,6 +29,7 @@ import torch
 import oracle
 from tests.helpers import Guarded, assert_close, assert_workspace_ready, note
 from workloads import configs as W
+from workloads import gen
 
 pytestmark = pytest.mark.gpu
 
@@ -221,3 +232,25 @@ def test_prefill_scale_sign(gpu_lib, scale):
     got = run_prefill(gpu_lib, q, k, v, scale=scale)
     want = oracle.attend(q, k, v, causal=True, scale=scale)
     assert_close(got, want, 2e-2, "scale=%g" % scale)
+
+
+SEAM_CASES = [
+    # B, Hq, Hkv, D, Tq, Tk, s_cap, dtype
+    (1, 14, 2, 64, 4097, 4097, 4097, torch.bfloat16),   # the T=4097 workload geometry
+    (1, 14, 2, 64, 256, 4097, 4097, torch.bfloat16),    # the 256-query chunk at offset 3841
+    (1, 4, 2, 64, 3, 2500, 2600, torch.bfloat16),       # three rows, 40 key tiles in chunks
+    (2, 4, 1, 128, 130, 1300, 1300, torch.float16),     # D = 128
+    (1, 4, 2, 64, 1057, 1057, 1057, torch.float16),     # ragged last row block
+]
+
+
+@pytest.mark.parametrize("case", range(len(SEAM_CASES)))
+def test_prefill_seams_planted(gpu_lib, case):
+    B, Hq, Hkv, D, Tq, Tk, s_cap, dtype = SEAM_CASES[case]
+    dt = "bf16" if dtype == torch.bfloat16 else "f16"
+    q, k, v, keys = gen.seam_planted(B, Hq, Hkv, D, Tq, Tk, dt, seed=case, s_cap=s_cap)
+    note("prefill seams planted B=%d Hq=%d Hkv=%d D=%d Tq=%d Tk=%d (%d planted keys)" % (B, Hq, Hkv, D, Tq, Tk,
+                                                                                       len(keys)))
+    got = run_prefill(gpu_lib, q, k, v, Tk=Tk)
+    want = oracle.attend(q, k, v, kv_lens=Tk, causal=True)
+    assert_close(got, want, 2e-2, "seams Tq=%d Tk=%d" % (Tq, Tk), max_ulps=2.0)

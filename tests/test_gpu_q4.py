@@ -1,9 +1,17 @@
 """GPU parity of the 4-bit quantized decode path.
 
-* The dequant hook (the device routine the attention kernel applies to every
-  element) is bit-identical to the oracle's unpack + dequant, on random
-  codes with the edge codes 0 and 15 and zero scales, and on the encoded
-  workload cache.
+* The dequant hook (s*c + b per element, rounded once: the values the 4-bit
+  attention is defined over) is bit-identical to the oracle's unpack +
+  dequant, on random codes with the edge codes 0 and 15 and zero scales, and
+  on the encoded workload cache.  The attention kernel does not call it.
+* The attention kernel's own unpack and dequant, bit for bit: with one
+  visible key the output is the oracle's dequantized value row 0 rounded to
+  f16; with one key whose weight is exactly 1 (every other weight
+  underflows to 0; single split, so no partial is merged) the output is
+  that key's dequantized value row rounded to f16.  The dominant key is
+  picked by one K code per row, so a wrong K nibble slot picks another row;
+  the V rows carry random codes, so a wrong V nibble or row slot changes the
+  output.  Every (head dim, group) pair, several head geometries.
 * Decode over the quantized cache (64 query / 8 KV heads, dim 128, group 64,
   f16 queries; KV length 2048 and 16384) matches the oracle's attention over
   the dequantized cache within 2e-2 (f16 outputs).
@@ -158,3 +166,110 @@ def test_q4_two_requests_merge_workgroups(gpu_lib):
     assert_close(got, oracle_q4(inp, w, S), 2e-2, "q4 B=2")
     alone = run_q4(gpu_lib, parts[0], w, S)
     assert torch.equal(got[:1], alone)
+
+
+# ---------------------------------------------------------------------------
+# The kernel's own unpack and dequant, bit for bit
+# ---------------------------------------------------------------------------
+Q4_PAIRS = [(128, 64), (128, 32), (128, 128), (64, 64), (64, 32)]
+
+
+def _f16(x):
+    return torch.from_numpy(np.ascontiguousarray(x))
+
+
+def _q4_random_v(rng, Hkv, s_cap, D, group):
+    """V codes with every code value, scales in [2^-9, 2) (so s/16 is an exact
+    f16 for the rows facing high nibbles) and biases of both signs."""
+    codes = rng.integers(0, 16, size=(1, Hkv, s_cap, D), dtype=np.uint8)
+    codes[..., 0] = 0
+    codes[..., 1] = 15
+    scales = np.exp2(rng.uniform(-9, 1, size=(1, Hkv, s_cap, D // group))).astype(np.float16)
+    biases = (rng.standard_normal((1, Hkv, s_cap, D // group)) * 2).astype(np.float16)
+    return gen.q4_pack_codes(codes), scales, biases
+
+
+def _run_q4_raw(gqa, q, kc, ks, kb, vc, vs, vb, group, kv_len, scale):
+    B, Hq, _, D = q.shape
+    Hkv, s_cap = kc.shape[1], kc.shape[2]
+    ws = gqa.make_workspace(B, Hq, Hkv, D, s_cap)
+    g = Guarded(q.shape, torch.float16)
+    d = lambda a: _f16(a).cuda()  # noqa: E731
+    gqa.gqa_decode_attend_q4(q.cuda(), d(kc), d(ks), d(kb), d(vc), d(vs), d(vb), g.t, group, kv_len, ws, scale=scale)
+    torch.cuda.synchronize()
+    g.check()
+    return g.t.cpu()
+
+
+@pytest.mark.parametrize("D,group", Q4_PAIRS)
+@pytest.mark.parametrize("Hq,Hkv", [(64, 8), (14, 2), (256, 256)])
+def test_q4_kernel_one_key_bit_exact(gpu_lib, D, group, Hq, Hkv):
+    """kv_len = 1: the output is V row 0 dequantized (s*c + b, one fp32
+    rounding) and rounded to f16, bit for bit, for every query head."""
+    rng = np.random.default_rng(D * 1000 + group + Hq)
+    s_cap = 40
+    kc = rng.integers(0, 256, size=(1, Hkv, s_cap, D // 2), dtype=np.uint8)
+    ks = rng.standard_normal((1, Hkv, s_cap, D // group)).astype(np.float16)
+    kb = rng.standard_normal((1, Hkv, s_cap, D // group)).astype(np.float16)
+    vc, vs, vb = _q4_random_v(rng, Hkv, s_cap, D, group)
+    # rows past the valid one hold NaN scales and biases: never read
+    for a in (ks, kb, vs, vb):
+        a[:, :, 1:] = np.nan
+    q = torch.from_numpy(rng.standard_normal((1, Hq, 1, D)).astype(np.float16))
+    note("q4 one key D=%d group=%d Hq=%d Hkv=%d" % (D, group, Hq, Hkv))
+    got = _run_q4_raw(gpu_lib, q, kc, ks, kb, vc, vs, vb, group, 1, 1.0 / np.sqrt(D))
+    v0 = oracle.q4_dequant(vc[:, :, :1], vs[:, :, :1], vb[:, :, :1], group)  # [1,Hkv,1,D] float32
+    want = np.repeat(v0, Hq // Hkv, axis=1).astype(np.float16)
+    assert np.array_equal(got.numpy().view(np.uint16), want.view(np.uint16))
+
+
+def _dominant_case(rng, Hq, Hkv, D, group, s_cap, kv_len):
+    """K codes: row r has code 15 in dimension owner[r] (at most one row owns
+    a dimension) and 0 elsewhere, scale 1, bias 0.  Query head h is 4.0 in
+    one dimension d(h) and 0 elsewhere, so with scale 4 its score is 240 for
+    the row owning d(h) and 0 for every other row: a log2 gap of ~346, so
+    that row's weight is exactly 1 and every other weight is exactly 0."""
+    G = Hq // Hkv
+    kcodes = np.zeros((1, Hkv, s_cap, D), np.uint8)
+    dims = np.zeros((Hkv, G), np.int64)
+    rows = np.zeros((Hkv, G), np.int64)
+    for g in range(Hkv):
+        n_own = min(kv_len, D)
+        own_rows = rng.choice(kv_len, size=n_own, replace=False)
+        own_dims = rng.choice(D, size=n_own, replace=False)
+        kcodes[0, g, own_rows, own_dims] = 15
+        pick = rng.integers(0, n_own, size=G)
+        dims[g] = own_dims[pick]
+        rows[g] = own_rows[pick]
+    q = np.zeros((1, Hq, 1, D), np.float16)
+    for h in range(Hq):
+        q[0, h, 0, dims[h // G, h % G]] = 4.0
+    ks = np.ones((1, Hkv, s_cap, D // group), np.float16)
+    kb = np.zeros((1, Hkv, s_cap, D // group), np.float16)
+    ks[:, :, kv_len:] = np.nan
+    return q, gen.q4_pack_codes(kcodes), ks, kb, rows
+
+
+@pytest.mark.parametrize("D,group", Q4_PAIRS)
+@pytest.mark.parametrize("Hq,Hkv,s_cap", [(64, 8, 16), (14, 2, 16), (256, 256, 300), (2048, 256, 97)])
+def test_q4_kernel_dominant_key_bit_exact(gpu_lib, D, group, Hq, Hkv, s_cap):
+    """One key per query head has weight exactly 1: the output is that key's
+    dequantized value row rounded to f16, bit for bit.  Every case runs as a
+    single split (no partial merged); the last two geometries span several
+    32-row steps over several waves."""
+    if Hq == 2048 and D == 64:
+        pytest.skip("one head dim suffices for the widest geometry")
+    rng = np.random.default_rng(D * 7 + group + Hq + s_cap)
+    kv_len = s_cap if s_cap <= 16 else s_cap - 3
+    q, kc, ks, kb, rows = _dominant_case(rng, Hq, Hkv, D, group, s_cap, kv_len)
+    vc, vs, vb = _q4_random_v(rng, Hkv, s_cap, D, group)
+    qt = torch.from_numpy(q)
+    note("q4 dominant key D=%d group=%d Hq=%d Hkv=%d s_cap=%d kv_len=%d" % (D, group, Hq, Hkv, s_cap, kv_len))
+    got = _run_q4_raw(gpu_lib, qt, kc, ks, kb, vc, vs, vb, group, kv_len, 4.0)
+    vdq = oracle.q4_dequant(vc, vs, vb, group)  # [1,Hkv,s_cap,D]
+    G = Hq // Hkv
+    want = np.stack([vdq[0, h // G, rows[h // G, h % G]] for h in range(Hq)])[None, :, None, :].astype(np.float16)
+    # the premise holds in the oracle: attention equals that row (other weights < 1e-100)
+    ref = oracle.q4_attend(qt, kc, ks, kb, vc, vs, vb, group, kv_lens=kv_len, scale=4.0)
+    assert np.abs(ref - want.astype(np.float64)).max() <= np.abs(want.astype(np.float64)).max() * 2.0 ** -10
+    assert np.array_equal(got.numpy().view(np.uint16), want.view(np.uint16))

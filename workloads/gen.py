@@ -84,3 +84,43 @@ def q4_encode(x: np.ndarray, group: int):
     c = np.where(s32 == 0, 0.0, c)
     c = np.clip(c, 0, 15).astype(np.uint8).reshape(x.shape)
     return q4_pack_codes(c), scale16, bias16
+
+
+def seam_planted(B: int, Hq: int, Hkv: int, D: int, Tq: int, Tk: int, dtype: str, seed: int,
+                 tile: int = 64, gain: float = 3.0, s_cap=None):
+    """Causal-prefill inputs whose every key-tile boundary is visible in the output.
+
+    Q, K, V are seeded N(0,1) float32.  Then, for every request and KV head,
+    each key j on either side of a boundary between ``tile``-key tiles (j a
+    multiple of ``tile``, and j - 1) is replaced by ``gain`` times the query
+    row of one (row, query head of the group) pair that can see it (row
+    i >= j - (Tk - Tq)), drawn from the same generator.  At the usual scale
+    1/sqrt(D) that key's score for that pair is about gain * sqrt(D) above
+    the typical one, so its weight there is close to 1 and leaving the key
+    out, or counting it twice, moves that output row by O(1).  Rows past Tk
+    up to ``s_cap`` are NaN.  Returns CPU tensors (q, k, v) cast to ``dtype``
+    and the sorted list of planted keys.
+    """
+    s_cap = Tk if s_cap is None else s_cap
+    rng = np.random.default_rng(np.random.SeedSequence([97, int(seed), Tq, Tk]))
+    q = rng.standard_normal((B, Hq, Tq, D), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, Tk, D), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, Tk, D), dtype=np.float32)
+    off = Tk - Tq
+    G = Hq // Hkv
+    keys = sorted({j for t in range(1, (Tk + tile - 1) // tile) for j in (t * tile - 1, t * tile) if j < Tk})
+    for b in range(B):
+        for g in range(Hkv):
+            for j in keys:
+                lo = max(0, j - off)
+                if lo >= Tq:
+                    continue
+                i = int(rng.integers(lo, Tq))
+                h = g * G + int(rng.integers(0, G))
+                k[b, g, j] = np.float32(gain) * q[b, h, i]
+    if s_cap > Tk:
+        pad = np.full((B, Hkv, s_cap - Tk, D), np.nan, np.float32)
+        k = np.concatenate([k, pad], axis=2)
+        v = np.concatenate([v, pad], axis=2)
+    t = _TORCH_DTYPES[dtype]
+    return torch.from_numpy(q).to(t), torch.from_numpy(k).to(t), torch.from_numpy(v).to(t), keys
