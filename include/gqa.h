@@ -240,6 +240,54 @@ int gqa_decode_attend_q4(const void *q,
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Append new tokens' K and V rows to a preallocated dense cache (the step
+ * before each decode call).  The Fornace prefill page runs decode over a
+ * preallocated KV cache ("What was measured and how"; "What it means if you
+ * run models on your own hardware": use the fused kernel with a preallocated
+ * cache), into which each new token's rows are written in place.
+ *
+ *   k_new, v_new      [B, Hkv, T_new, D]   dtype
+ *   k_cache, v_cache  [B, Hkv, s_cap, D]   dtype
+ *   kv_lens           [B] int32 (DEVICE): rows already in request b's cache
+ *   new_lens          [B] int32 (DEVICE) or NULL: receives
+ *                     min(p_b + T_new, s_cap)
+ *
+ * Request b's new row t goes to cache row p_b + t, p_b = kv_lens[b] clamped
+ * to [0, s_cap]; rows that would land at or past s_cap are dropped.  Nothing
+ * else in the caches changes; the copy is exact.  new_lens must not be
+ * kv_lens (every workgroup reads the old lengths).  Requires D in {64, 128},
+ * dtype in {GQA_F32, GQA_BF16, GQA_F16}, T_new >= 1, 16-byte aligned
+ * pointers.
+ */
+int gqa_kv_append(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                  const int32_t *kv_lens, int32_t *new_lens,
+                  int B, int Hkv, int D, int T_new, int s_cap, int dtype, void *stream);
+
+/*
+ * Append new tokens' K and V rows to a 4-bit cache, quantizing only the new
+ * rows (the VeloxQuant posts, "Part 4": re-quantizing the whole K/V history
+ * every decode step cost ~25 ms/step against a ~12 ms/step kernel; the fix
+ * quantizes only the newly aged rows).  Layouts as in gqa_decode_attend_q4;
+ * k_new, v_new [B, Hkv, T_new, D] in `dtype` (GQA_F32, GQA_BF16 or GQA_F16);
+ * kv_lens, new_lens and the placement of rows as in gqa_kv_append.
+ *
+ * Each group of group_size elements of a new row is encoded with the
+ * min-max group-affine map, in float32 on the exactly widened inputs:
+ *   scale = f16((max - min) / 15), bias = f16(min)   (round to nearest even;
+ *           a zero minimum or step is stored as +0)
+ *   code  = clamp(rint((x - bias) / scale), 0, 15)   (ties to even; 0 when
+ *           the scale is 0)
+ * Inputs must be finite, with the minimum and (max - min) / 15 within the
+ * f16 range.  Requires D in {64, 128}, group_size in {32, 64, 128} dividing
+ * D, T_new >= 1, 16-byte aligned pointers.
+ */
+int gqa_kv_append_q4(const void *k_new, const void *v_new, int dtype,
+                     uint8_t *k_codes, void *k_scales, void *k_biases,
+                     uint8_t *v_codes, void *v_scales, void *v_biases,
+                     const int32_t *kv_lens, int32_t *new_lens,
+                     int B, int Hkv, int D, int group_size, int T_new, int s_cap, void *stream);
+
+/*
  * Dequantize n_rows cache rows to float32: s*c + b per element, rounded once
  * (a check hook for the encoding the 4-bit entry points share; its output
  * can be compared bit for bit with that definition).  The attention kernel

@@ -311,7 +311,9 @@ int gqa_oracle_q4_dequant(const uint8_t *packed, const uint16_t *scales, const u
  * (f16, bf16 and f32 inputs all widen exactly), for each group of `group`
  * consecutive elements of a row:
  *   lo = min x, hi = max x                        (exact)
- *   s16 = f16(fl32(fl32(hi - lo) / 15)),  b16 = f16(lo)     (ties to even)
+ *   s16 = f16(fl32(fl32(hi - lo) / 15)),  b16 = f16(lo)     (ties to even;
+ *         a zero minimum or step is taken as +0, so that a group holding
+ *         both -0 and +0 has one encoding)
  *   s = f32(s16), b = f32(b16)
  *   c  = 0                                        if s == 0
  *        clamp(rint(fl32(fl32(x - b) / s)), 0, 15) otherwise (rint: ties to even)
@@ -339,8 +341,12 @@ int gqa_oracle_q4_quantize(const float *x, long n_rows, int D, int group, uint8_
                 if (xg[e] > hi)
                     hi = xg[e];
             }
+            if (lo == 0.0f)
+                lo = 0.0f;                               /* +0 */
             const float range = hi - lo;
-            const float step = range / 15.0f;
+            float step = range / 15.0f;
+            if (step == 0.0f)
+                step = 0.0f;                             /* +0 */
             const uint16_t sh = float_to_half_bits(step);
             const uint16_t bh = float_to_half_bits(lo);
             scales[(size_t)r * n_groups + g] = sh;

@@ -36,6 +36,8 @@ EXPORTED = (
     "gqa_prefill_causal",
     "gqa_decode_attend_q4",
     "gqa_dequant_q4",
+    "gqa_kv_append",
+    "gqa_kv_append_q4",
     "gqa_read_probe",
 )
 
@@ -77,6 +79,10 @@ def load() -> ctypes.CDLL:
     lib.gqa_decode_attend_q4.restype = i
     lib.gqa_dequant_q4.argtypes = [vp, vp, vp, vp, i, i, i, vp]
     lib.gqa_dequant_q4.restype = i
+    lib.gqa_kv_append.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    lib.gqa_kv_append.restype = i
+    lib.gqa_kv_append_q4.argtypes = [vp, vp, i, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    lib.gqa_kv_append_q4.restype = i
     lib.gqa_read_probe.argtypes = [vp, sz, vp, vp]
     lib.gqa_read_probe.restype = i
     _lib = lib
@@ -274,6 +280,64 @@ def gqa_dequant_q4(codes, scales, biases, out, group_size: int) -> torch.Tensor:
     _check(load().gqa_dequant_q4(_ptr(codes), _ptr(scales), _ptr(biases), _ptr(out), n_rows, D,
                                  int(group_size), _stream(codes)), "gqa_dequant_q4")
     return out
+
+
+def gqa_kv_append(k_new, v_new, k_cache, v_cache, kv_lens, new_lens=None) -> None:
+    """k_new, v_new [B,Hkv,T_new,D]; caches [B,Hkv,s_cap,D] (same dtype); kv_lens, new_lens int32 [B] (device)."""
+    for n, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dense(n, t, 4)
+    _dense("kv_lens", kv_lens, 1)
+    B, Hkv, T_new, D = k_new.shape
+    s_cap = k_cache.shape[2]
+    if v_new.shape != k_new.shape or k_cache.shape != v_cache.shape or k_cache.shape[:2] != (B, Hkv) \
+            or k_cache.shape[3] != D:
+        raise ValueError("shape mismatch")
+    if not (k_new.dtype == v_new.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("new rows and caches must share one dtype")
+    if kv_lens.dtype != torch.int32 or kv_lens.numel() != B:
+        raise ValueError("kv_lens must be int32 [B]")
+    if new_lens is not None:
+        _dense("new_lens", new_lens, 1)
+        if new_lens.dtype != torch.int32 or new_lens.numel() != B:
+            raise ValueError("new_lens must be int32 [B]")
+        _same_device(k_new, new_lens=new_lens)
+    _same_device(k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, kv_lens=kv_lens)
+    _check(load().gqa_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(kv_lens),
+                                _ptr(new_lens), B, Hkv, D, T_new, s_cap, _DTYPE_CODE.get(k_new.dtype, -1),
+                                _stream(k_new)), "gqa_kv_append")
+
+
+def gqa_kv_append_q4(k_new, v_new, k_codes, k_scales, k_biases, v_codes, v_scales, v_biases, group_size: int,
+                     kv_lens, new_lens=None) -> None:
+    """k_new, v_new [B,Hkv,T_new,D] (f32/bf16/f16); 4-bit caches as in gqa_decode_attend_q4; lengths int32 [B]."""
+    for n, t in (("k_new", k_new), ("v_new", v_new), ("k_codes", k_codes), ("v_codes", v_codes),
+                 ("k_scales", k_scales), ("k_biases", k_biases), ("v_scales", v_scales), ("v_biases", v_biases)):
+        _dense(n, t, 4)
+    _dense("kv_lens", kv_lens, 1)
+    B, Hkv, T_new, D = k_new.shape
+    s_cap = k_codes.shape[2]
+    group_size = int(group_size)
+    if v_new.shape != k_new.shape or k_codes.shape != (B, Hkv, s_cap, D // 2) or v_codes.shape != k_codes.shape:
+        raise ValueError("shape mismatch")
+    if k_new.dtype != v_new.dtype or k_codes.dtype != torch.uint8 or v_codes.dtype != torch.uint8:
+        raise ValueError("dtype mismatch")
+    gshape = (B, Hkv, s_cap, D // max(group_size, 1))
+    for n, t in (("k_scales", k_scales), ("k_biases", k_biases), ("v_scales", v_scales), ("v_biases", v_biases)):
+        if t.dtype != torch.float16 or tuple(t.shape) != gshape:
+            raise ValueError("%s must be float16 %s" % (n, gshape))
+    if kv_lens.dtype != torch.int32 or kv_lens.numel() != B:
+        raise ValueError("kv_lens must be int32 [B]")
+    if new_lens is not None:
+        _dense("new_lens", new_lens, 1)
+        if new_lens.dtype != torch.int32 or new_lens.numel() != B:
+            raise ValueError("new_lens must be int32 [B]")
+        _same_device(k_new, new_lens=new_lens)
+    _same_device(k_new, v_new=v_new, k_codes=k_codes, v_codes=v_codes, k_scales=k_scales, k_biases=k_biases,
+                 v_scales=v_scales, v_biases=v_biases, kv_lens=kv_lens)
+    _check(load().gqa_kv_append_q4(_ptr(k_new), _ptr(v_new), _DTYPE_CODE.get(k_new.dtype, -1), _ptr(k_codes),
+                                   _ptr(k_scales), _ptr(k_biases), _ptr(v_codes), _ptr(v_scales), _ptr(v_biases),
+                                   _ptr(kv_lens), _ptr(new_lens), B, Hkv, D, group_size, T_new, s_cap,
+                                   _stream(k_new)), "gqa_kv_append_q4")
 
 
 def gqa_read_probe(src: torch.Tensor, sink: torch.Tensor) -> None:

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgqa.so")
-SOURCES = ["decode.hip", "prefill.hip", "util.hip", "gqa_abi.hip"]
+SOURCES = ["decode.hip", "prefill.hip", "append.hip", "util.hip", "gqa_abi.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -259,6 +259,13 @@ hipError_t launch_prefill(int dtype, int D, const void *q, const void *k, const 
                           int B, int Hq, int Hkv, int Tq, int Tk, int s_cap, float scale, void *ws, int n_cus,
                           hipStream_t s);
 size_t prefill_workspace_bytes(int B, int Hq, int D, int Tq, int Tk, int n_cus);
+hipError_t launch_kv_append(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                            const int32_t *kv_lens, int32_t *new_lens, int B, int Hkv, int D, int T_new, int s_cap,
+                            int elem_bytes, hipStream_t s);
+hipError_t launch_kv_append_q4(int dtype, const void *k_new, const void *v_new, uint8_t *k_codes, void *k_scales,
+                               void *k_biases, uint8_t *v_codes, void *v_scales, void *v_biases,
+                               const int32_t *kv_lens, int32_t *new_lens, int B, int Hkv, int D, int group, int T_new,
+                               int s_cap, hipStream_t s);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_read_probe(const void *src, size_t bytes, void *sink, hipStream_t s);
 

@@ -244,6 +244,47 @@ int gqa_decode_attend_q4(const void *q, const uint8_t *k_codes, const void *k_sc
     return hip_status(launch_decode_q4(D, group_size, B, a, (hipStream_t)stream));
 }
 
+int gqa_kv_append(const void *k_new, const void *v_new, void *k_cache, void *v_cache, const int32_t *kv_lens,
+                  int32_t *new_lens, int B, int Hkv, int D, int T_new, int s_cap, int dtype, void *stream)
+{
+    if (!k_new || !v_new || !k_cache || !v_cache || !kv_lens) return GQA_ERR_NULL;
+    if (B < 1 || Hkv < 1 || T_new < 1 || s_cap < 1) return GQA_ERR_SHAPE;
+    if ((const void *)new_lens == (const void *)kv_lens) return GQA_ERR_SHAPE;  // every lane reads kv_lens
+    if (D != 64 && D != 128) return GQA_ERR_UNSUPPORTED;
+    if (!dense_dtype(dtype)) return GQA_ERR_UNSUPPORTED;
+    const int elem = dtype == GQA_F32 ? 4 : 2;
+    if ((long)B * Hkv * (long)(s_cap > T_new ? s_cap : T_new) * D * elem >= (1L << 46)) return GQA_ERR_SHAPE;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(kv_lens) ||
+        !aligned16(new_lens))
+        return GQA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return hip_status(launch_kv_append(k_new, v_new, k_cache, v_cache, kv_lens, new_lens, B, Hkv, D, T_new, s_cap,
+                                       elem, (hipStream_t)stream));
+}
+
+int gqa_kv_append_q4(const void *k_new, const void *v_new, int dtype, uint8_t *k_codes, void *k_scales,
+                     void *k_biases, uint8_t *v_codes, void *v_scales, void *v_biases, const int32_t *kv_lens,
+                     int32_t *new_lens, int B, int Hkv, int D, int group_size, int T_new, int s_cap, void *stream)
+{
+    if (!k_new || !v_new || !k_codes || !k_scales || !k_biases || !v_codes || !v_scales || !v_biases || !kv_lens)
+        return GQA_ERR_NULL;
+    if (B < 1 || Hkv < 1 || T_new < 1 || s_cap < 1) return GQA_ERR_SHAPE;
+    if ((const void *)new_lens == (const void *)kv_lens) return GQA_ERR_SHAPE;
+    if (D != 64 && D != 128) return GQA_ERR_UNSUPPORTED;
+    if (group_size != 32 && group_size != 64 && group_size != 128) return GQA_ERR_UNSUPPORTED;
+    if (D % group_size != 0) return GQA_ERR_SHAPE;
+    if (!dense_dtype(dtype)) return GQA_ERR_UNSUPPORTED;
+    if ((long)B * Hkv * (long)(s_cap > T_new ? s_cap : T_new) * D * 4 >= (1L << 46)) return GQA_ERR_SHAPE;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_codes) || !aligned16(v_codes) ||
+        !aligned16(k_scales) || !aligned16(k_biases) || !aligned16(v_scales) || !aligned16(v_biases) ||
+        !aligned16(kv_lens) || !aligned16(new_lens))
+        return GQA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return hip_status(launch_kv_append_q4(dtype, k_new, v_new, k_codes, k_scales, k_biases, v_codes, v_scales,
+                                          v_biases, kv_lens, new_lens, B, Hkv, D, group_size, T_new, s_cap,
+                                          (hipStream_t)stream));
+}
+
 int gqa_dequant_q4(const uint8_t *codes, const void *scales, const void *biases, float *out, int n_rows, int D,
                    int group_size, void *stream)
 {

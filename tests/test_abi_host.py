@@ -149,11 +149,12 @@ def test_decode_workspace_layout():
     # keys at s_cap = 4096; one 128-float partial per (column, split, head)
     # after the flag region
     assert gqa.gqa_decode_workspace_bytes(1, 28, 4, 128, 4096) == MIB16 + 4 * 64 * 7 * 128 * 4
-    # the (max, sum) words, 8 bytes per partial, and one 4-byte control word
-    # per (request, head tile) must fit the flag region less its 64-byte
-    # tail: 28 * 64 * 8 + 4 * 4 bytes a request allow 1168 requests
-    assert gqa.gqa_decode_workspace_bytes(1168, 28, 4, 128, 4096) > 0
-    assert gqa.gqa_decode_workspace_bytes(1169, 28, 4, 128, 4096) == 0
+    # the (max, sum) words, 8 bytes per partial, and nine control words on
+    # lines of their own (1152 bytes) per (request, head tile) must fit the
+    # flag region less its 64-byte tail: 28 * 64 * 8 + 4 * 1152 bytes a
+    # request allow 885 requests
+    assert gqa.gqa_decode_workspace_bytes(885, 28, 4, 128, 4096) > 0
+    assert gqa.gqa_decode_workspace_bytes(886, 28, 4, 128, 4096) == 0
 
 
 def test_q4_validation(lib):
@@ -195,3 +196,29 @@ def test_library_does_not_link_the_oracle():
     with open(gqa.LIB_PATH, "rb") as f:
         blob = f.read()
     assert b"gqa_oracle" not in blob
+
+
+def test_append_validation(lib):
+    def dense(kn=FAKE, lens=FAKE, new=NULL, B=2, D=128, T=1, s_cap=64, dtype=1):
+        return lib.gqa_kv_append(kn, FAKE, FAKE, FAKE, lens, new, B, 8, D, T, s_cap, dtype, NULL)
+
+    assert dense(kn=NULL) == gqa.GQA_ERR_NULL
+    assert dense(lens=NULL) == gqa.GQA_ERR_NULL
+    assert dense(T=0) == gqa.GQA_ERR_SHAPE
+    assert dense(B=0) == gqa.GQA_ERR_SHAPE
+    assert dense(new=FAKE, lens=FAKE) == gqa.GQA_ERR_SHAPE            # new_lens may not be kv_lens
+    assert dense(D=96) == gqa.GQA_ERR_UNSUPPORTED
+    assert dense(dtype=7) == gqa.GQA_ERR_UNSUPPORTED
+    assert dense(kn=FAKE_ODD) == gqa.GQA_ERR_ALIGN
+
+    def q4(kn=FAKE, lens=FAKE, new=NULL, D=128, group=64, T=1, dtype=2):
+        return lib.gqa_kv_append_q4(kn, FAKE, dtype, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, lens, new, 1, 8, D, group,
+                                    T, 64, NULL)
+
+    assert q4(kn=NULL) == gqa.GQA_ERR_NULL
+    assert q4(T=0) == gqa.GQA_ERR_SHAPE
+    assert q4(new=FAKE) == gqa.GQA_ERR_SHAPE                          # same pointer as kv_lens
+    assert q4(group=48) == gqa.GQA_ERR_UNSUPPORTED
+    assert q4(group=128, D=64) == gqa.GQA_ERR_SHAPE
+    assert q4(dtype=9) == gqa.GQA_ERR_UNSUPPORTED
+    assert q4(kn=FAKE_ODD) == gqa.GQA_ERR_ALIGN

@@ -126,3 +126,16 @@ def test_kv_append_definition():
     assert np.array_equal(out[1, :, :4], cache[1, :, :4])
     out2, lens2 = oracle.kv_append(cache, new, [-3, 99])   # lengths clamp to [0, capacity]
     assert lens2.tolist() == [4, 6] and np.array_equal(out2[0, :, :4], new[0]) and np.array_equal(out2[1], cache[1])
+
+
+def test_signed_zeros_have_one_encoding():
+    # a group of zeros of both signs: scale and bias are +0, codes 0; a group
+    # whose minimum is -0 stores its bias as +0
+    x = np.zeros((2, 16), np.float32)
+    x[0, ::2] = -0.0
+    x[1] = np.arange(16, dtype=np.float32)
+    x[1, 0] = -0.0
+    packed, s, b = oracle.q4_quantize(x, 16)
+    assert s.view(np.uint16).tolist() == [[0], [np.float16(1.0).view(np.uint16)]]
+    assert b.view(np.uint16).tolist() == [[0], [0]]
+    assert oracle.q4_unpack(packed).tolist() == [[0] * 16, list(range(16))]
