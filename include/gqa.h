@@ -60,7 +60,8 @@ typedef enum gqa_status {
     GQA_ERR_UNSUPPORTED = 3, /* dtype, head dim or device not supported */
     GQA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
     GQA_ERR_HIP = 5,         /* the HIP runtime reported an error */
-    GQA_ERR_ALIGN = 6        /* a pointer is not 16-byte aligned */
+    GQA_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned */
+    GQA_ERR_SCRATCH = 7      /* sizes exceed the allocation-free entry point's scratch */
 } gqa_status_t;
 
 typedef enum gqa_dtype {
@@ -142,6 +143,27 @@ int gqa_decode_attend(const void *q, const void *k, const void *v, void *out,
                       int B, int Hq, int Hkv, int D, int kv_len, int s_cap,
                       float scale, int dtype,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gqa_decode_attend without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  It allocates nothing and calls
+ * no allocating routine: its partial results live in a scratch array of
+ * 8 MiB built into the library (one per GPU, held until the process ends):
+ * 512 KiB for the (max, sum) and control words (which must fit 512 KiB less
+ * 64 bytes) and 7.5 MiB for the fp32 partial outputs (B * Hq * splits * D * 4
+ * bytes; e.g. the 28/4-head, D = 128 geometry up to B = 8 at s_cap = 4096).
+ * Larger sizes return GQA_ERR_SCRATCH.  Same kernels and split plan as
+ * gqa_decode_attend, so the output is bit-identical to it.  The first call
+ * on a device also zero-fills the array with a kernel on `stream` (make that
+ * first call outside any graph capture).  Every call on one GPU shares that
+ * GPU's array: calls that may overlap in time on one GPU race and must not
+ * be issued (serialize them on one stream); each call leaves the array
+ * ready for the next.
+ */
+int gqa_decode_attend_noalloc(const void *q, const void *k, const void *v, void *out,
+                              int B, int Hq, int Hkv, int D, int kv_len, int s_cap,
+                              float scale, int dtype, void *stream);
 
 /*
  * Batched decode: as gqa_decode_attend, but request b attends over its own

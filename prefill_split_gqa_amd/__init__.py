@@ -21,7 +21,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgqa.so")
 
-GQA_OK, GQA_ERR_NULL, GQA_ERR_SHAPE, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP, GQA_ERR_ALIGN = range(7)
+(GQA_OK, GQA_ERR_NULL, GQA_ERR_SHAPE, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP, GQA_ERR_ALIGN,
+ GQA_ERR_SCRATCH) = range(8)
 GQA_F32, GQA_BF16, GQA_F16 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: GQA_F32, torch.bfloat16: GQA_BF16, torch.float16: GQA_F16}
 
@@ -32,6 +33,7 @@ EXPORTED = (
     "gqa_prefill_workspace_bytes",
     "gqa_workspace_init",
     "gqa_decode_attend",
+    "gqa_decode_attend_noalloc",
     "gqa_decode_attend_batched",
     "gqa_prefill_causal",
     "gqa_decode_attend_q4",
@@ -71,6 +73,8 @@ def load() -> ctypes.CDLL:
     lib.gqa_workspace_init.restype = i
     lib.gqa_decode_attend.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
     lib.gqa_decode_attend.restype = i
+    lib.gqa_decode_attend_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    lib.gqa_decode_attend_noalloc.restype = i
     lib.gqa_decode_attend_batched.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.gqa_decode_attend_batched.restype = i
     lib.gqa_prefill_causal.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
@@ -171,6 +175,24 @@ def gqa_decode_attend(q, k, v, out, kv_len: int, workspace, scale: Optional[floa
     _check(load().gqa_decode_attend(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, D, int(kv_len), s_cap,
                                     float(scale), dt, ws, ws_bytes, _stream(q)),
            "gqa_decode_attend")
+    return out
+
+
+def gqa_decode_attend_noalloc(q, k, v, out, kv_len: int, scale: Optional[float] = None) -> torch.Tensor:
+    """As gqa_decode_attend, with the library's built-in scratch instead of a workspace (allocates nothing)."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _dense(n, t, 4)
+    B, Hq, Tq, D = q.shape
+    _, Hkv, s_cap, _ = k.shape
+    if Tq != 1 or out.shape != q.shape or k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("shape mismatch")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype):
+        raise ValueError("q, k, v and out must share one dtype")
+    _same_device(q, k=k, v=v, out=out)
+    scale = default_scale(D) if scale is None else scale
+    _check(load().gqa_decode_attend_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, D, int(kv_len), s_cap,
+                                            float(scale), _DTYPE_CODE.get(q.dtype, -1), _stream(q)),
+           "gqa_decode_attend_noalloc")
     return out
 
 

@@ -19,7 +19,7 @@ using namespace gqa;
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -91,6 +91,42 @@ int check_decode_common(const void *q, const void *k, const void *v, void *out, 
     return GQA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free decode entry point: a file-scope device
+// array (one per GPU), laid out like a workspace with a smaller flag
+// region: (max, sum) words and control words at the front, the poison word
+// at the end of that region, partial outputs after it.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+constexpr size_t kScratchFlagBytes = (size_t)512 << 10;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+bool scratch_fits(const DecodePlan &p)
+{
+    return p.off_ctrl + p.ctrl_bytes <= kScratchFlagBytes - kWsTailBytes && p.o_bytes <= kScratchBytes - kScratchFlagBytes;
+}
+
+// Device address of `scratch` on the current device: taken with
+// hipGetSymbolAddress once per device (with that device current) and kept;
+// the first call on a device also zero-fills the array on `stream` (a
+// kernel, not a memset).  The array's host-side name is never used as an
+// address.  nullptr on a HIP error.
+unsigned char *scratch_address(hipStream_t stream)
+{
+    static std::mutex mu;
+    static unsigned char *addr[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        if (launch_fill_zero(ptr, kScratchBytes, stream) != hipSuccess) return nullptr;
+        addr[dev] = (unsigned char *)ptr;
+    }
+    return addr[dev];
+}
+
 void fill_ws(DecodeArgs &a, void *ws)
 {
     char *base = (char *)ws;
@@ -117,6 +153,7 @@ const char *gqa_status_string(int status)
     case GQA_ERR_WORKSPACE: return "workspace missing or too small";
     case GQA_ERR_HIP: return "HIP runtime error";
     case GQA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case GQA_ERR_SCRATCH: return "sizes exceed the built-in scratch of the allocation-free entry point";
     default: return "unknown status";
     }
 }
@@ -156,6 +193,39 @@ int gqa_decode_attend(const void *q, const void *k, const void *v, void *out, in
     a.qscale = scale * 1.4426950408889634f;
     a.plan = plan;
     fill_ws(a, workspace);
+    return hip_status(launch_decode(dtype, D, B, a, (hipStream_t)stream));
+}
+
+int gqa_decode_attend_noalloc(const void *q, const void *k, const void *v, void *out, int B, int Hq, int Hkv,
+                              int D, int kv_len, int s_cap, float scale, int dtype, void *stream)
+{
+    if (!q || !k || !v || !out) return GQA_ERR_NULL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || s_cap < 1) return GQA_ERR_SHAPE;
+    if (!std::isfinite(scale)) return GQA_ERR_SHAPE;
+    if (D != 64 && D != 128) return GQA_ERR_UNSUPPORTED;
+    if (B > 65535 || (size_t)s_cap * D * 4 >= ((size_t)1 << 31)) return GQA_ERR_SHAPE;
+    DecodePlan plan;
+    if (!plan_decode(B, Hq, Hkv, D, s_cap, &plan)) return GQA_ERR_SHAPE;
+    if (!scratch_fits(plan)) return GQA_ERR_SCRATCH;
+    if (kv_len < 1 || kv_len > s_cap) return GQA_ERR_SHAPE;
+    if (!dense_dtype(dtype)) return GQA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_ERR_ALIGN;
+    int cus = 0;
+    if (int st = check_device(&cus)) return st;
+    unsigned char *base = scratch_address((hipStream_t)stream);
+    if (!base) return GQA_ERR_HIP;
+    DecodeArgs a{};
+    a.n_cus = cus;
+    a.q = q; a.k = k; a.v = v; a.out = out;
+    a.kv_lens = nullptr; a.kv_len = kv_len;
+    a.Hq = Hq; a.Hkv = Hkv; a.s_cap = s_cap; a.group = 0;
+    a.qscale = scale * 1.4426950408889634f;
+    a.plan = plan;
+    a.part_ml = (float *)base;
+    a.ctrl = (unsigned *)(base + plan.off_ctrl);
+    a.poison = (unsigned *)(base + kScratchFlagBytes - 16);
+    a.part_o = (float *)(base + kScratchFlagBytes);
+    a.ws_bytes = kScratchBytes;
     return hip_status(launch_decode(dtype, D, B, a, (hipStream_t)stream));
 }
 

@@ -34,7 +34,7 @@ int main(void)
     int s;
     void *fake = (void *)0x10000; /* aligned, never dereferenced */
     CHECK(gqa_abi_version() >= 1);
-    for (s = GQA_OK; s <= GQA_ERR_ALIGN; ++s) CHECK(strlen(gqa_status_string(s)) > 0);
+    for (s = GQA_OK; s <= GQA_ERR_SCRATCH; ++s) CHECK(strlen(gqa_status_string(s)) > 0);
     CHECK(gqa_status_string(12345) != NULL);
     CHECK(gqa_decode_workspace_bytes(1, 28, 4, 128, 4096) > ((size_t)16 << 20));
     CHECK(gqa_decode_workspace_bytes(1, 28, 5, 128, 4096) == 0); /* Hq not a multiple of Hkv */

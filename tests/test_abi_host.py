@@ -45,8 +45,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gqa.gqa_abi_version() == 2
-    for st in range(7):
+    assert gqa.gqa_abi_version() == 3
+    for st in range(8):
         assert gqa.status_string(st)
     assert gqa.status_string(99) == "unknown status"
 
