@@ -49,6 +49,11 @@ def _load():
                                       ctypes.POINTER(ctypes.c_int32), ctypes.c_int, ctypes.c_double,
                                       dp, ctypes.c_int]
     lib.gqa_oracle_attend.restype = ctypes.c_int
+    lib.gqa_oracle_attend_ex.argtypes = [dp, dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.POINTER(ctypes.c_int32), ctypes.c_int, ctypes.c_double,
+                                         ctypes.c_int, dp, dp, ctypes.c_int]
+    lib.gqa_oracle_attend_ex.restype = ctypes.c_int
     lib.gqa_oracle_q4_unpack.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_int, ctypes.c_void_p]
     lib.gqa_oracle_q4_unpack.restype = ctypes.c_int
     lib.gqa_oracle_q4_dequant.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -100,14 +105,16 @@ def _f16bits(x) -> np.ndarray:
 
 
 def attend(q, k, v, kv_lens=None, causal: bool = False, scale: Optional[float] = None,
-           return_probs: bool = False, nthreads: int = 0):
+           return_probs: bool = False, nthreads: int = 0, window: int = 0, sinks=None):
     """Grouped-query attention in fp64.
 
     q [B,Hq,Tq,D]; k, v [B,Hkv,s_cap,D]; kv_lens: None (= s_cap), an int, or a
     length-B sequence of valid key counts.  ``causal`` aligns the Tq queries
     to the end of each request's keys.  ``scale`` defaults to the float32
-    value of 1/sqrt(D).  Returns O [B,Hq,Tq,D] (and the softmax weights
-    [B,Hq,Tq,s_cap] when ``return_probs``).
+    value of 1/sqrt(D).  ``window`` (> 0) keeps only the last ``window`` keys
+    up to each row's own position; ``sinks`` ([Hq] logits) join each softmax's
+    normaliser without a value.  Returns O [B,Hq,Tq,D] (and the softmax
+    weights [B,Hq,Tq,s_cap] when ``return_probs``).
     """
     q = _f64(q)
     k = _f64(k)
@@ -129,10 +136,13 @@ def attend(q, k, v, kv_lens=None, causal: bool = False, scale: Optional[float] =
     out = np.empty((B, Hq, Tq, D), dtype=np.float64)
     probs = np.empty((B, Hq, Tq, s_cap), dtype=np.float64) if return_probs else None
     dp = ctypes.POINTER(ctypes.c_double)
-    rc = _load().gqa_oracle_attend(
+    sk = None
+    if sinks is not None:
+        sk = _f64(sinks).reshape(Hq)
+    rc = _load().gqa_oracle_attend_ex(
         q.ctypes.data_as(dp), k.ctypes.data_as(dp), v.ctypes.data_as(dp), out.ctypes.data_as(dp),
         B, Hq, Hkv, Tq, D, s_cap, lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-        1 if causal else 0, float(scale),
+        1 if causal else 0, float(scale), int(window), sk.ctypes.data_as(dp) if sk is not None else None,
         probs.ctypes.data_as(dp) if probs is not None else None, int(nthreads))
     if rc != 0:
         raise ValueError("gqa_oracle_attend rejected its arguments (code %d)" % rc)

@@ -30,6 +30,18 @@
  * A row whose visible set J is empty (possible only for a zero-length request)
  * gets an all-zero output.
  *
+ * Two options (gqa_oracle_attend_ex), from the pages' remarks on what the
+ * fused kernels leave out -- the Fornace prefill page, "What this does not
+ * prove" (no sliding window is applied; Qwen2.5's window never masks, other
+ * models can differ) and the VeloxQuant-MLX "attention" posts, "Part 4" (the
+ * SDPA signature the fused decode path intercepts carries `sinks`):
+ *  - window W >= 1: only the W most recent keys up to the row's own position
+ *    are visible, J = { j in J : j > i + (n_b - Tq) - W } (for decode, the
+ *    last W keys);
+ *  - sinks: one logit sink_h per query head (in the units of the scaled
+ *    scores) that joins the softmax's normaliser and carries no value:
+ *      O = sum_j e^{s_j} V_j / (e^{sink_h} + sum_j e^{s_j}).
+ *
  * Arithmetic: every stored element is widened exactly to double by the
  * caller; dot products, exp (libm) and sums run in double in ascending index
  * order; the result is returned unrounded.
@@ -72,10 +84,25 @@ int gqa_oracle_max_threads(void)
  *       zero where a key is not visible.
  * nthreads <= 0 means the OpenMP default.
  */
+int gqa_oracle_attend_ex(const double *q, const double *k, const double *v, double *out,
+                         int B, int Hq, int Hkv, int Tq, int D, int s_cap,
+                         const int32_t *kv_lens, int causal, double scale, int window,
+                         const double *sinks, double *probs, int nthreads);
+
 int gqa_oracle_attend(const double *q, const double *k, const double *v, double *out,
                       int B, int Hq, int Hkv, int Tq, int D, int s_cap,
                       const int32_t *kv_lens, int causal, double scale,
                       double *probs, int nthreads)
+{
+    return gqa_oracle_attend_ex(q, k, v, out, B, Hq, Hkv, Tq, D, s_cap, kv_lens, causal, scale, 0, NULL,
+                                probs, nthreads);
+}
+
+/* window <= 0: no window; sinks: NULL or [Hq] logits. */
+int gqa_oracle_attend_ex(const double *q, const double *k, const double *v, double *out,
+                         int B, int Hq, int Hkv, int Tq, int D, int s_cap,
+                         const int32_t *kv_lens, int causal, double scale, int window,
+                         const double *sinks, double *probs, int nthreads)
 {
     if (!q || !k || !v || !out || !kv_lens)
         return ORACLE_ERR_ARG;
@@ -115,7 +142,8 @@ int gqa_oracle_attend(const double *q, const double *k, const double *v, double 
             const int g = h / G;
             const int n = kv_lens[b];
 
-            /* visible keys: j < n, and j <= i + (n - Tq) when causal */
+            /* visible keys: first <= j < limit; j < n, and j <= i + (n - Tq)
+               when causal; with a window, j > (last visible key) - window */
             long limit = n;
             if (causal) {
                 long last = (long)i + ((long)n - Tq);
@@ -124,6 +152,9 @@ int gqa_oracle_attend(const double *q, const double *k, const double *v, double 
                 if (limit < 0)
                     limit = 0;
             }
+            long first = 0;
+            if (window > 0 && limit - window > 0)
+                first = limit - window;
 
             const double *qi = q + (size_t)r * D;
             const double *kb = k + ((size_t)b * Hkv + g) * (size_t)s_cap * D;
@@ -143,7 +174,7 @@ int gqa_oracle_attend(const double *q, const double *k, const double *v, double 
 
             /* scores */
             double m = -INFINITY;
-            for (long j = 0; j < limit; ++j) {
+            for (long j = first; j < limit; ++j) {
                 const double *kj = kb + (size_t)j * D;
                 double dot = 0.0;
                 for (int d = 0; d < D; ++d)
@@ -153,17 +184,23 @@ int gqa_oracle_attend(const double *q, const double *k, const double *v, double 
                     m = s[j];
             }
 
-            /* softmax weights (shifted by the row maximum) and their sum */
+            /* softmax weights (shifted by the row maximum, the sink
+               included) and their sum; the sink adds to the sum only */
+            const double sink = sinks ? sinks[h] : -INFINITY;
+            if (sink > m)
+                m = sink;
             double l = 0.0;
-            for (long j = 0; j < limit; ++j) {
+            for (long j = first; j < limit; ++j) {
                 s[j] = exp(s[j] - m);
                 l += s[j];
             }
+            if (sinks)
+                l += exp(sink - m);
 
             /* weighted sum of value rows */
             for (int d = 0; d < D; ++d)
                 oi[d] = 0.0;
-            for (long j = 0; j < limit; ++j) {
+            for (long j = first; j < limit; ++j) {
                 const double *vj = vb + (size_t)j * D;
                 for (int d = 0; d < D; ++d)
                     oi[d] += s[j] * vj[d];
@@ -172,7 +209,7 @@ int gqa_oracle_attend(const double *q, const double *k, const double *v, double 
                 oi[d] /= l;
 
             if (pi)
-                for (long j = 0; j < limit; ++j)
+                for (long j = first; j < limit; ++j)
                     pi[j] = s[j] / l;
         }
         free(s);
