@@ -223,6 +223,42 @@ int gqa_prefill_causal(const void *q, const void *k, const void *v, void *out,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Decode and causal prefill with a sliding window and attention sinks.  The
+ * pages' fused kernels leave both out -- the Fornace prefill page, "What
+ * this does not prove": no sliding window is applied (Qwen2.5's window never
+ * masks a position, other models can differ); the VeloxQuant posts, "Part
+ * 4": the SDPA call the fused decode path intercepts carries `sinks` -- and
+ * models that use them need them in the same fused pass:
+ *
+ *   window > 0   only the `window` most recent keys up to a query's own
+ *                position are visible: key j is visible to row i iff
+ *                last - window < j <= last, last = i + (Tk - Tq) for
+ *                prefill and kv_lens[b] - 1 for decode (0: no window);
+ *   sinks        NULL, or a DEVICE float array [Hq]: one logit per query
+ *                head, in the units of scale * <q, k>, that joins the
+ *                softmax normaliser and carries no value:
+ *                out = sum_j e^{s_j} v_j / (e^{sinks[h]} + sum_j e^{s_j}).
+ *
+ * gqa_decode_attend_ex is gqa_decode_attend_batched with these options (its
+ * split plan covers min(window, s_cap) rows, so a call's workspace is at
+ * most gqa_decode_workspace_bytes(B, Hq, Hkv, D, s_cap)); with window = 0
+ * and sinks = NULL its output is bit-identical to the batched entry point.
+ * gqa_prefill_causal_ex is gqa_prefill_causal with these options and needs
+ * gqa_prefill_workspace_bytes_ex(..., window) bytes of workspace.  Errors,
+ * layouts and workspaces as for the entry points they extend;
+ * GQA_ERR_SHAPE for window < 0.
+ */
+int gqa_decode_attend_ex(const void *q, const void *k, const void *v, void *out,
+                         const int32_t *kv_lens, int B, int Hq, int Hkv, int D, int s_cap,
+                         float scale, int dtype, int window, const float *sinks,
+                         void *workspace, size_t workspace_bytes, void *stream);
+size_t gqa_prefill_workspace_bytes_ex(int B, int Hq, int Hkv, int D, int Tq, int Tk, int window);
+int gqa_prefill_causal_ex(const void *q, const void *k, const void *v, void *out,
+                          int B, int Hq, int Hkv, int D, int Tq, int Tk, int s_cap,
+                          float scale, int dtype, int window, const float *sinks,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Decode over a 4-bit group-affine quantized KV cache.
  *
  *   q, out                 [B, Hq, 1, D]                 f16

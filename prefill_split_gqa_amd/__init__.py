@@ -35,6 +35,9 @@ EXPORTED = (
     "gqa_decode_attend",
     "gqa_decode_attend_noalloc",
     "gqa_decode_attend_batched",
+    "gqa_decode_attend_ex",
+    "gqa_prefill_workspace_bytes_ex",
+    "gqa_prefill_causal_ex",
     "gqa_prefill_causal",
     "gqa_decode_attend_q4",
     "gqa_dequant_q4",
@@ -79,6 +82,12 @@ def load() -> ctypes.CDLL:
     lib.gqa_decode_attend_batched.restype = i
     lib.gqa_prefill_causal.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     lib.gqa_prefill_causal.restype = i
+    lib.gqa_decode_attend_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, vp, sz, vp]
+    lib.gqa_decode_attend_ex.restype = i
+    lib.gqa_prefill_workspace_bytes_ex.argtypes = [i, i, i, i, i, i, i]
+    lib.gqa_prefill_workspace_bytes_ex.restype = sz
+    lib.gqa_prefill_causal_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp, vp, sz, vp]
+    lib.gqa_prefill_causal_ex.restype = i
     lib.gqa_decode_attend_q4.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
     lib.gqa_decode_attend_q4.restype = i
     lib.gqa_dequant_q4.argtypes = [vp, vp, vp, vp, i, i, i, vp]
@@ -251,6 +260,64 @@ def gqa_prefill_causal(q, k, v, out, workspace, Tk: Optional[int] = None,
     _check(load().gqa_prefill_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, D, Tq, Tk, s_cap,
                                      float(scale), dt, ws, ws_bytes, _stream(q)),
            "gqa_prefill_causal")
+    return out
+
+
+def _sinks(sinks, ref, Hq):
+    if sinks is None:
+        return ctypes.c_void_p(0)
+    _dense("sinks", sinks, 1)
+    if sinks.dtype != torch.float32 or sinks.numel() != Hq:
+        raise ValueError("sinks must be float32 [Hq]")
+    _same_device(ref, sinks=sinks)
+    return _ptr(sinks)
+
+
+def gqa_decode_attend_ex(q, k, v, out, kv_lens, workspace, window: int = 0, sinks=None,
+                         scale: Optional[float] = None) -> torch.Tensor:
+    """Batched decode with a sliding window (last `window` keys; 0 = none) and per-head sink logits [Hq]."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _dense(n, t, 4)
+    _dense("kv_lens", kv_lens, 1)
+    B, Hq, Tq, D = q.shape
+    _, Hkv, s_cap, _ = k.shape
+    if Tq != 1 or out.shape != q.shape or k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("shape mismatch")
+    if kv_lens.dtype != torch.int32 or kv_lens.numel() != B:
+        raise ValueError("kv_lens must be int32 [B]")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype):
+        raise ValueError("q, k, v and out must share one dtype")
+    _same_device(q, k=k, v=v, out=out, kv_lens=kv_lens)
+    ws, ws_bytes = _workspace(workspace, q)
+    scale = default_scale(D) if scale is None else scale
+    _check(load().gqa_decode_attend_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(kv_lens), B, Hq, Hkv, D, s_cap,
+                                       float(scale), _DTYPE_CODE.get(q.dtype, -1), int(window), _sinks(sinks, q, Hq),
+                                       ws, ws_bytes, _stream(q)), "gqa_decode_attend_ex")
+    return out
+
+
+def gqa_prefill_workspace_bytes_ex(B: int, Hq: int, Hkv: int, D: int, Tq: int, Tk: int, window: int) -> int:
+    return int(load().gqa_prefill_workspace_bytes_ex(B, Hq, Hkv, D, Tq, Tk, window))
+
+
+def gqa_prefill_causal_ex(q, k, v, out, workspace, Tk: Optional[int] = None, window: int = 0, sinks=None,
+                          scale: Optional[float] = None) -> torch.Tensor:
+    """Causal prefill with a sliding window (0 = none) and per-head sink logits [Hq]."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _dense(n, t, 4)
+    B, Hq, Tq, D = q.shape
+    _, Hkv, s_cap, _ = k.shape
+    if out.shape != q.shape or k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("shape mismatch")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype):
+        raise ValueError("q, k, v and out must share one dtype")
+    Tk = s_cap if Tk is None else int(Tk)
+    _same_device(q, k=k, v=v, out=out)
+    ws, ws_bytes = _workspace(workspace, q)
+    scale = default_scale(D) if scale is None else scale
+    _check(load().gqa_prefill_causal_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, D, Tq, Tk, s_cap,
+                                        float(scale), _DTYPE_CODE.get(q.dtype, -1), int(window),
+                                        _sinks(sinks, q, Hq), ws, ws_bytes, _stream(q)), "gqa_prefill_causal_ex")
     return out
 
 

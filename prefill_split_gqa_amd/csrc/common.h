@@ -241,6 +241,8 @@ struct DecodeArgs {
     int kv_len;              // uniform length when kv_lens == nullptr
     int Hq, Hkv, s_cap;
     int group;               // 4-bit cache group size (0 for dense caches)
+    int window;              // > 0: only the last `window` rows of each request are visible
+    const float *sinks;      // per query head softmax sink logits, or nullptr
     float qscale;            // scale * log2(e)
     DecodePlan plan;
     float *part_o, *part_ml; // per split: [GT][D] outputs, [GT][2] (max, sum)
@@ -256,9 +258,9 @@ hipError_t launch_decode_q4(int D, int group, int B, const DecodeArgs &a, hipStr
 hipError_t launch_dequant_q4(const uint8_t *codes, const void *scales, const void *biases, float *out,
                              int n_rows, int D, int group, hipStream_t s);
 hipError_t launch_prefill(int dtype, int D, const void *q, const void *k, const void *v, void *out,
-                          int B, int Hq, int Hkv, int Tq, int Tk, int s_cap, float scale, void *ws, int n_cus,
-                          hipStream_t s);
-size_t prefill_workspace_bytes(int B, int Hq, int D, int Tq, int Tk, int n_cus);
+                          int B, int Hq, int Hkv, int Tq, int Tk, int s_cap, float scale, void *ws, int window,
+                          const float *sinks, int n_cus, hipStream_t s);
+size_t prefill_workspace_bytes(int B, int Hq, int D, int Tq, int Tk, int window, int n_cus);
 hipError_t launch_kv_append(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                             const int32_t *kv_lens, int32_t *new_lens, int B, int Hkv, int D, int T_new, int s_cap,
                             int elem_bytes, hipStream_t s);

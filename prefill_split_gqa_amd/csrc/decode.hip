@@ -235,6 +235,24 @@ struct DecodeGrid {
     int B;         // requests
 };
 
+// Rows of request b that its query sees: its length (device lengths are
+// clamped to [0, s_cap]); with a window, only the last `window` of them,
+// which start at row *lo.
+__device__ __forceinline__ int request_len(const DecodeArgs &a, int b)
+{
+    int n = a.kv_len;
+    if (a.kv_lens) {
+        n = a.kv_lens[b];
+        n = n < 0 ? 0 : (n > a.s_cap ? a.s_cap : n);
+    }
+    return n;
+}
+__device__ __forceinline__ int windowed(const DecodeArgs &a, int n, int *lo)
+{
+    *lo = a.window > 0 && n > a.window ? n - a.window : 0;
+    return n - *lo;
+}
+
 // With per-request lengths and at most kDecodePackMaxB requests, the
 // working splits are packed at the front of the grid: request b's
 // HT * max(1, n_split(b)) items (head tile major, split minor) follow those
@@ -252,11 +270,8 @@ __device__ __forceinline__ bool packed_item(const DecodeArgs &a, int B, int i, S
 {
     const DecodePlan &P = a.plan;
     const int lane = threadIdx.x & 63;
-    int n = 0;
-    if (lane < B) {
-        n = a.kv_lens[lane];
-        n = n < 0 ? 0 : (n > a.s_cap ? a.s_cap : n);
-    }
+    int n = 0, lo;
+    if (lane < B) n = windowed(a, request_len(a, lane), &lo);
     const int ns = (n + P.L - 1) / P.L;
     const int items = lane < B ? P.HT * (ns > 1 ? ns : 1) : 0;
     int incl = items;  // inclusive prefix sum over the lanes
@@ -370,9 +385,17 @@ __device__ __forceinline__ bool is_tagged2(tag_u2_t w) { return (w[0] & w[1] & 1
 // with a single split the output is written, otherwise the split's partial
 // is published with tagged device-scope stores (its outputs and its (max,
 // sum) pair), with no wait.
+// A sink logit (natural units of the scaled scores) in the log2 units of
+// the kernels' scores; -inf without sinks.
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float sink_log2(const DecodeArgs &a, int h)
+{
+    return a.sinks ? a.sinks[h] * kLog2e : kNegInf;
+}
+
 template <typename TQ, int D, int GT, int SOD = D>
 __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *so, const float *sm, const float *sl,
-                                             int col, int s, int n_split, TQ *out)
+                                             int col, int s, int n_split, TQ *out, int h0)
 {
     constexpr int NW = kDecodeThreads / 64;
     constexpr int NQ = GT * D / 4;  // 4-wide output items
@@ -392,6 +415,10 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *s
         }
 #pragma unroll
         for (int w = 0; w < NW; ++w) Mw = fmaxf(Mw, mw[w]);
+        // a single split normalises here, sink included; several publish
+        // their partials and the merge adds the sink
+        const float s2 = n_split == 1 ? sink_log2(a, h0 + qh) : kNegInf;
+        Mw = fmaxf(Mw, s2);
         if (n_split > 1) Mw = tagged_f32(Mw);  // finite: every split has a row
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
@@ -399,6 +426,7 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *s
             Lw += wt * lw[w];
             O0 += wt * xw[w].x; O1 += wt * xw[w].y; O2 += wt * xw[w].z; O3 += wt * xw[w].w;
         }
+        Lw += rel_weight(s2, Mw);
     }
     if (n_split == 1) {
         if (tid < NQ) store4(out + (size_t)qh * D + qd, O0 / Lw, O1 / Lw, O2 / Lw, O3 / Lw);
@@ -447,17 +475,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
     if (a.kv_lens && grid.B <= kDecodePackMaxB) {
         SplitItem it;
         if (!packed_item(a, grid.B, (int)blockIdx.x, &it)) return;
-        s = it.s; ht = it.ht; b = it.b; n = it.n;
+        s = it.s; ht = it.ht; b = it.b;
     } else {
         s = (int)blockIdx.x % grid.gx;
         ht = ((int)blockIdx.x / grid.gx) % P.HT;
         b = (int)blockIdx.x / (grid.gx * P.HT);
-        n = a.kv_len;
-        if (a.kv_lens) {
-            n = a.kv_lens[b];
-            n = n < 0 ? 0 : (n > a.s_cap ? a.s_cap : n);
-        }
     }
+    int lo;  // first visible row (a window's start)
+    n = windowed(a, request_len(a, b), &lo);
     const int n_split = (n + P.L - 1) / P.L;
     const int g = ht / P.ht_per_kv;
     const int h0 = g * P.G + (ht % P.ht_per_kv) * GT;
@@ -472,7 +497,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
     const int start = s * P.L;
     const int end = min(start + P.L, n);
 
-    const size_t head_row0 = ((size_t)b * a.Hkv + g) * (size_t)a.s_cap;
+    const size_t head_row0 = ((size_t)b * a.Hkv + g) * (size_t)a.s_cap + lo;
     const typename KV::Src src = KV::make_src(a, false, head_row0, end, lr);
     const typename KV::Src srcv = KV::make_src(a, true, head_row0, end, lr);
 
@@ -633,7 +658,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
     }
     __syncthreads();
 
-    finish_split<TQ, D, GT>(a, &so[0][0][0], &sm[0][0], &sl[0][0], col, s, n_split, out);
+    finish_split<TQ, D, GT>(a, &so[0][0][0], &sm[0][0], &sl[0][0], col, s, n_split, out, h0);
     if (n_split > 1) merge_tile<TQ, D, GT>(a, col, n_split, own, decision, 0, ticket);
 }
 
@@ -681,11 +706,8 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     const int col = m / GT;
     const int ht = col % P.HT;
     const int b = col / P.HT;
-    int n = a.kv_len;
-    if (a.kv_lens) {
-        n = a.kv_lens[b];
-        n = n < 0 ? 0 : (n > a.s_cap ? a.s_cap : n);
-    }
+    int lo;
+    const int n = windowed(a, request_len(a, b), &lo);
     const int n_split = (n + P.L - 1) / P.L;
     if (n_split <= 1) return;  // written directly by the streaming workgroup
     const int g = ht / P.ht_per_kv;
@@ -756,7 +778,8 @@ __device__ void merge_head(const DecodeArgs &a, int m)
         if (sg == 0) store4(out + d4 * 4, __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
         return;
     }
-    const float M = s_M;
+    const float s2 = sink_log2(a, h);
+    const float M = fmaxf(s_M, s2);
     float Ls = 0.0f;
     float4 R = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     float2 mlk[PER];  // all (max, sum) reads first (clamped to a valid split)
@@ -771,7 +794,7 @@ __device__ void merge_head(const DecodeArgs &a, int m)
             R.x += w * x.x; R.y += w * x.y; R.z += w * x.z; R.w += w * x.w;
         }
     }
-    Ls = colgroup_sum<CPW>(Ls);
+    Ls = colgroup_sum<CPW>(Ls) + rel_weight(s2, M);
     R.x = colgroup_sum<CPW>(R.x);
     R.y = colgroup_sum<CPW>(R.y);
     R.z = colgroup_sum<CPW>(R.z);
@@ -825,11 +848,8 @@ __device__ void merge_workgroup(const DecodeArgs &a, int m)
     __shared__ int s_go;
     const int col = m / GT, hh = m % GT;
     const int b = col / a.plan.HT;
-    int n = a.kv_len;
-    if (a.kv_lens) {
-        n = a.kv_lens[b];
-        n = n < 0 ? 0 : (n > a.s_cap ? a.s_cap : n);
-    }
+    int lo;
+    const int n = windowed(a, request_len(a, b), &lo);
     const int n_split = (n + a.plan.L - 1) / a.plan.L;
     if (n_split <= 1) return;  // written directly by the streaming workgroup
     if (threadIdx.x == 0) {
@@ -952,11 +972,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
     const int ht = ((int)blockIdx.x / grid.gx) % P.HT;
     const int b = (int)blockIdx.x / (grid.gx * P.HT);
 
-    int n = a.kv_len;
-    if (a.kv_lens) {
-        n = a.kv_lens[b];
-        n = n < 0 ? 0 : (n > a.s_cap ? a.s_cap : n);
-    }
+    int lo;
+    const int n = windowed(a, request_len(a, b), &lo);
     const int n_split = (n + P.L - 1) / P.L;
     const int g = ht / P.ht_per_kv;
     const int h0 = g * P.G + (ht % P.ht_per_kv) * GT;
@@ -974,7 +991,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
 
     // sources bounded to rows [0, end) of this (request, KV head): rows past
     // the split's end stage as zeros (and are masked below)
-    const size_t head_row0 = ((size_t)b * a.Hkv + g) * (size_t)a.s_cap;
+    const size_t head_row0 = ((size_t)b * a.Hkv + g) * (size_t)a.s_cap + lo;
     const BufDesc dk = buf_desc((const uint8_t *)a.k + head_row0 * S::ROWB, (size_t)end * S::ROWB);
     const BufDesc dv = buf_desc((const uint8_t *)a.v + head_row0 * S::ROWB, (size_t)end * S::ROWB);
     const BufDesc dks = buf_desc((const uint16_t *)a.k_scales + head_row0 * NG, (size_t)end * NG * 2);
@@ -1242,7 +1259,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
     unsigned ticket = kNoTicket;  // a group completer's tile word add (awaited at the end)
     if (n_split > 1 && tid == kTicketTid) ticket = group_done(a, col, s, n_split, gticket);
     __syncthreads();
-    finish_split<f16_t, D, GT, SOD>(a, so, sm, sl, col, s, n_split, out);
+    finish_split<f16_t, D, GT, SOD>(a, so, sm, sl, col, s, n_split, out, h0);
     if (n_split > 1) merge_tile<f16_t, D, GT>(a, col, n_split, own, decision, kTicketTid, ticket);
 }
 

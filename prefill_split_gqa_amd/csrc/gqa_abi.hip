@@ -76,8 +76,9 @@ int hip_status(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ERR_HIP; }
 
 bool dense_dtype(int dtype) { return dtype == GQA_F32 || dtype == GQA_BF16 || dtype == GQA_F16; }
 
+// plan_rows: the rows the split plan covers (s_cap, or a window's length)
 int check_decode_common(const void *q, const void *k, const void *v, void *out, int B, int Hq, int Hkv, int D,
-                        int s_cap, float scale, void *ws, size_t ws_bytes, DecodePlan *plan)
+                        int s_cap, float scale, void *ws, size_t ws_bytes, DecodePlan *plan, int plan_rows = 0)
 {
     if (!q || !k || !v || !out) return GQA_ERR_NULL;
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || s_cap < 1) return GQA_ERR_SHAPE;
@@ -85,7 +86,7 @@ int check_decode_common(const void *q, const void *k, const void *v, void *out, 
     if (D != 64 && D != 128) return GQA_ERR_UNSUPPORTED;
     // a KV head's rows are addressed with 32-bit buffer offsets
     if (B > 65535 || (size_t)s_cap * D * 4 >= ((size_t)1 << 31)) return GQA_ERR_SHAPE;
-    if (!plan_decode(B, Hq, Hkv, D, s_cap, plan)) return GQA_ERR_SHAPE;
+    if (!plan_decode(B, Hq, Hkv, D, plan_rows > 0 ? plan_rows : s_cap, plan)) return GQA_ERR_SHAPE;
     if (!ws || ws_bytes < plan->bytes) return GQA_ERR_WORKSPACE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(ws)) return GQA_ERR_ALIGN;
     return GQA_OK;
@@ -252,20 +253,52 @@ int gqa_decode_attend_batched(const void *q, const void *k, const void *v, void 
     return hip_status(launch_decode(dtype, D, B, a, (hipStream_t)stream));
 }
 
-size_t gqa_prefill_workspace_bytes(int B, int Hq, int Hkv, int D, int Tq, int Tk)
+int gqa_decode_attend_ex(const void *q, const void *k, const void *v, void *out, const int32_t *kv_lens, int B,
+                         int Hq, int Hkv, int D, int s_cap, float scale, int dtype, int window, const float *sinks,
+                         void *workspace, size_t workspace_bytes, void *stream)
 {
-    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Tq < 1 || Tq > Tk) return 0;
-    if (D != 64 && D != 128) return 0;
-    return prefill_workspace_bytes(B, Hq, D, Tq, Tk, plan_cus());
+    if (!kv_lens) return GQA_ERR_NULL;
+    if (window < 0) return GQA_ERR_SHAPE;
+    DecodePlan plan;
+    const int rows = window > 0 && window < s_cap ? window : s_cap;
+    if (int st = check_decode_common(q, k, v, out, B, Hq, Hkv, D, s_cap, scale, workspace, workspace_bytes, &plan,
+                                     rows))
+        return st;
+    if (!aligned16(kv_lens) || !aligned16(sinks)) return GQA_ERR_ALIGN;
+    if (!dense_dtype(dtype)) return GQA_ERR_UNSUPPORTED;
+    int cus = 0;
+    if (int st = check_device(&cus)) return st;
+    DecodeArgs a{};
+    a.n_cus = cus;
+    a.q = q; a.k = k; a.v = v; a.out = out;
+    a.kv_lens = kv_lens; a.kv_len = 0;
+    a.Hq = Hq; a.Hkv = Hkv; a.s_cap = s_cap; a.group = 0;
+    a.window = window; a.sinks = sinks;
+    a.qscale = scale * 1.4426950408889634f;
+    a.plan = plan;
+    fill_ws(a, workspace);
+    return hip_status(launch_decode(dtype, D, B, a, (hipStream_t)stream));
 }
 
-int gqa_prefill_causal(const void *q, const void *k, const void *v, void *out, int B, int Hq, int Hkv, int D,
-                       int Tq, int Tk, int s_cap, float scale, int dtype, void *workspace, size_t workspace_bytes,
-                       void *stream)
+size_t gqa_prefill_workspace_bytes_ex(int B, int Hq, int Hkv, int D, int Tq, int Tk, int window)
+{
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Tq < 1 || Tq > Tk || window < 0) return 0;
+    if (D != 64 && D != 128) return 0;
+    return prefill_workspace_bytes(B, Hq, D, Tq, Tk, window, plan_cus());
+}
+
+size_t gqa_prefill_workspace_bytes(int B, int Hq, int Hkv, int D, int Tq, int Tk)
+{
+    return gqa_prefill_workspace_bytes_ex(B, Hq, Hkv, D, Tq, Tk, 0);
+}
+
+int gqa_prefill_causal_ex(const void *q, const void *k, const void *v, void *out, int B, int Hq, int Hkv, int D,
+                          int Tq, int Tk, int s_cap, float scale, int dtype, int window, const float *sinks,
+                          void *workspace, size_t workspace_bytes, void *stream)
 {
     if (!q || !k || !v || !out) return GQA_ERR_NULL;
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return GQA_ERR_SHAPE;
-    if (Tq < 1 || Tq > Tk || Tk > s_cap) return GQA_ERR_SHAPE;
+    if (Tq < 1 || Tq > Tk || Tk > s_cap || window < 0) return GQA_ERR_SHAPE;
     if (!std::isfinite(scale)) return GQA_ERR_SHAPE;
     if (D != 64 && D != 128) return GQA_ERR_UNSUPPORTED;
     if (dtype != GQA_BF16 && dtype != GQA_F16) return GQA_ERR_UNSUPPORTED;
@@ -276,13 +309,22 @@ int gqa_prefill_causal(const void *q, const void *k, const void *v, void *out, i
     // addressed with 32-bit byte offsets
     if ((size_t)(s_cap + 512) * D * 2 >= ((size_t)1 << 31)) return GQA_ERR_SHAPE;
     const int cus = plan_cus();
-    const size_t need = prefill_workspace_bytes(B, Hq, D, Tq, Tk, cus);
+    const size_t need = prefill_workspace_bytes(B, Hq, D, Tq, Tk, window, cus);
     if (!workspace || workspace_bytes < need) return GQA_ERR_WORKSPACE;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace))
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace) ||
+        !aligned16(sinks))
         return GQA_ERR_ALIGN;
     if (int st = check_device()) return st;
-    return hip_status(launch_prefill(dtype, D, q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, workspace, cus,
-                                     (hipStream_t)stream));
+    return hip_status(launch_prefill(dtype, D, q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, workspace, window,
+                                     sinks, cus, (hipStream_t)stream));
+}
+
+int gqa_prefill_causal(const void *q, const void *k, const void *v, void *out, int B, int Hq, int Hkv, int D,
+                       int Tq, int Tk, int s_cap, float scale, int dtype, void *workspace, size_t workspace_bytes,
+                       void *stream)
+{
+    return gqa_prefill_causal_ex(q, k, v, out, B, Hq, Hkv, D, Tq, Tk, s_cap, scale, dtype, 0, nullptr, workspace,
+                                 workspace_bytes, stream);
 }
 
 int gqa_decode_attend_q4(const void *q, const uint8_t *k_codes, const void *k_scales, const void *k_biases,

@@ -210,7 +210,8 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D ==
                                                                     uint16_t *__restrict__ out, int Hq, int Hkv,
                                                                     int Tq, int Tk, int s_cap, float qscale,
                                                                     int n_rb, unsigned char *__restrict__ ws,
-                                                                    int B, PfItems items)
+                                                                    int B, int window, const float *__restrict__ sinks,
+                                                                    PfItems items)
 {
     typedef MfmaOps<T> Ops;
     typedef typename Ops::vec vec;
@@ -246,19 +247,30 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D ==
     const int rw0 = r0 + rw * 32;                   // first row of this wave
     const int row_hi = min(r0 + kPfBM, Tq);         // one past the last valid row of the block
     const int kend = min(Tk, row_hi + off);         // keys any valid row of the block can see
-    const int n_tiles = (kend + kPfBN - 1) / kPfBN;
+    // with a window, row i sees keys i + off - window < j <= i + off: the
+    // block's first row sets its first tile
+    const int t_lo = window > 0 ? max(0, r0 + off - window + 1) / kPfBN : 0;
+    const int n_tiles = (kend + kPfBN - 1) / kPfBN - t_lo;
     const int nc = (n_tiles + items.ch - 1) / items.ch;  // chunks of this row block
     const int per = (n_tiles + nc - 1) / nc;        // tiles per chunk
-    const int t_begin = min(n_tiles, chunk * per);
-    const int n = min(n_tiles, t_begin + per) - t_begin;
+    const int t_begin = t_lo + min(n_tiles, chunk * per);
+    const int n = min(n_tiles, chunk * per + per) - min(n_tiles, chunk * per);
     // Per wave (wave-uniform): tiles below n_full are visible in full to
     // every row of the wave, so they need no mask; tiles from w_end on are
     // masked for every row of the wave (or the wave has no valid row), so it
     // skips their arithmetic and only takes part in the loads and barriers.
-    const int n_full = min(n_tiles, (rw0 + off + 1) / kPfBN);
-    const int w_end = rw0 < row_hi ? min(n_tiles, (min(rw0 + 31, row_hi - 1) + off) / kPfBN + 1) : 0;
+    // With a window, tiles below w_begin are below every row's first visible
+    // key (skipped like those past w_end), and tiles below lo_full cross
+    // some row's first visible key (masked).
+    const int t_hi = t_lo + n_tiles;
+    const int n_full = min(t_hi, (rw0 + off + 1) / kPfBN);
+    const int w_end = rw0 < row_hi ? min(t_hi, (min(rw0 + 31, row_hi - 1) + off) / kPfBN + 1) : 0;
+    const int w_begin = window > 0 ? max(0, rw0 + off - window + 1) / kPfBN : 0;
+    const int lo_full =
+        window > 0 ? (max(0, min(rw0 + 31, max(row_hi - 1, rw0)) + off - window + 1) + kPfBN - 1) / kPfBN : 0;
     const int my_row = rw0 + ln;
     const int my_lim = my_row + off;  // last visible key of this lane's row
+    const int my_lo = window > 0 ? my_row + off - window + 1 : -0x7FFFFFFF;  // first visible key
 
     const uint16_t *qh = q + ((size_t)b * Hq + h) * (size_t)Tq * D;
     const uint16_t *kh = k + ((size_t)b * Hkv + g) * (size_t)s_cap * D;
@@ -362,7 +374,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D ==
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) st[u] = Ops::mfma(as_vec<vec>(k_frag(Kt, u, kb)), qreg[kb], st[u]);
         }
-        if (kt >= n_full) {
+        if (kt >= n_full || kt < lo_full) {
             // (kept a real branch: the empty asm stops the compiler from
             // turning the mask into selects executed on every tile)
             asm volatile("");
@@ -370,8 +382,10 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D ==
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    if (key0 + 32 * u + 8 * (j >> 2) + (j & 3) > my_lim) st[u][j] = NEG ? kInf : -kInf;
+                for (int j = 0; j < 16; ++j) {
+                    const int key = key0 + 32 * u + 8 * (j >> 2) + (j & 3);
+                    if (key > my_lim || key < my_lo) st[u][j] = NEG ? kInf : -kInf;
+                }
         }
     };
     // Probabilities exp2(s*qs + mq), rounded to 16 bits in four 16-key
@@ -438,12 +452,12 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D ==
     __syncthreads();
     for (int s = 0; s < n; s += 2) {  // unrolled by two: buffer indices are constants
         issue_tile_loads(t_begin + s + 1, 1);
-        if (t_begin + s < w_end) tile_step(t_begin + s, 0);
+        if (t_begin + s < w_end && t_begin + s >= w_begin) tile_step(t_begin + s, 0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (s + 1 < n) {
             issue_tile_loads(t_begin + s + 2, 0);
-            if (t_begin + s + 1 < w_end) tile_step(t_begin + s + 1, 1);
+            if (t_begin + s + 1 < w_end && t_begin + s + 1 >= w_begin) tile_step(t_begin + s + 1, 1);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
@@ -574,9 +588,18 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D ==
     }
 
     // ---- normalise and store: lane holds O^T[d][row] for d = 32db + 8i + 4lg + r ----
+    // A sink logit joins the normaliser: relative to the row's reference
+    // exponent it is e = sink * log2(e) - |qs| * m_run (log2 units); when
+    // e > 0 both the sum and the output are scaled by 2^-e first.
     const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
     if (my_row < Tq) {
-        const float inv = 1.0f / l_tot;
+        float inv = 1.0f / l_tot;
+        if (sinks) {
+            const float e = sinks[h] * 1.4426950408889634f - aq * m_run;
+            const float mx = fmaxf(e, 0.0f);
+            const float down = fast_exp2(-mx);
+            inv = down / __builtin_fmaf(l_tot, down, fast_exp2(e - mx));
+        }
         uint16_t *orow = out + (((size_t)b * Hq + h) * (size_t)Tq + my_row) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -592,11 +615,13 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D ==
 }
 
 // ---- work decomposition (host) ----
-// Key tiles of row block rb (the keys its valid rows can see).
-static int pf_row_tiles(int rb, int Tq, int Tk)
+// Key tiles of row block rb (the keys its valid rows can see; with a
+// window, from the first row's first visible key on).
+static int pf_row_tiles(int rb, int Tq, int Tk, int window)
 {
     const int row_hi = std::min((rb + 1) * kPfBM, Tq);
-    return (std::min(Tk, row_hi + Tk - Tq) + kPfBN - 1) / kPfBN;
+    const int t_lo = window > 0 ? std::max(0, rb * kPfBM + Tk - Tq - window + 1) / kPfBN : 0;
+    return (std::min(Tk, row_hi + Tk - Tq) + kPfBN - 1) / kPfBN - t_lo;
 }
 
 // Chunking of the causal triangle.  The most key tiles per chunk, ch, is
@@ -610,7 +635,7 @@ struct PfPlan {
     int n_rb, ch, rb0, max_nc, n_items;
 };
 
-static PfPlan pf_plan_for(int Tq, int Tk, int ch)
+static PfPlan pf_plan_for(int Tq, int Tk, int window, int ch)
 {
     PfPlan p;
     p.n_rb = (Tq + kPfBM - 1) / kPfBM;
@@ -619,7 +644,7 @@ static PfPlan pf_plan_for(int Tq, int Tk, int ch)
     p.max_nc = 1;
     p.n_items = 0;
     for (int rb = p.n_rb - 1; rb >= 0; --rb) {
-        const int nc = (pf_row_tiles(rb, Tq, Tk) + ch - 1) / ch;
+        const int nc = (pf_row_tiles(rb, Tq, Tk, window) + ch - 1) / ch;
         if (nc > 1) p.rb0 = rb;
         p.max_nc = std::max(p.max_nc, nc);
         p.n_items += nc;
@@ -634,31 +659,32 @@ static bool pf_plan_fits(const PfPlan &p, int B, int Hq)
 }
 
 // n_cus: compute units of the device the launch runs on.
-static PfPlan pf_plan(int B, int Hq, int D, int Tq, int Tk, int n_cus)
+static PfPlan pf_plan(int B, int Hq, int D, int Tq, int Tk, int window, int n_cus)
 {
     const int min_chunk = kPfMinChunk;
     const long slots = (long)(D == 64 ? 4 : 2) * n_cus;  // resident workgroups (VGPR budget)
     const int n_rb = (Tq + kPfBM - 1) / kPfBM;
     long total = 0;
-    for (int rb = 0; rb < n_rb; ++rb) total += pf_row_tiles(rb, Tq, Tk);
+    for (int rb = 0; rb < n_rb; ++rb) total += pf_row_tiles(rb, Tq, Tk, window);
     total *= (long)B * Hq;
     int lo = (int)std::min<long>(std::max((long)min_chunk, (total + slots - 1) / std::max(slots, 1L)), 1 << 30);
-    int hi = std::max(lo, pf_row_tiles(n_rb - 1, Tq, Tk));  // no split: always fits
-    if (pf_plan_fits(pf_plan_for(Tq, Tk, lo), B, Hq)) return pf_plan_for(Tq, Tk, lo);
+    int hi = lo;  // no split: always fits
+    for (int rb = 0; rb < n_rb; ++rb) hi = std::max(hi, pf_row_tiles(rb, Tq, Tk, window));
+    if (pf_plan_fits(pf_plan_for(Tq, Tk, window, lo), B, Hq)) return pf_plan_for(Tq, Tk, window, lo);
     while (hi - lo > 1) {  // invariant: lo does not fit, hi does
         const int mid = lo + (hi - lo) / 2;
-        if (pf_plan_fits(pf_plan_for(Tq, Tk, mid), B, Hq)) hi = mid; else lo = mid;
+        if (pf_plan_fits(pf_plan_for(Tq, Tk, window, mid), B, Hq)) hi = mid; else lo = mid;
     }
-    return pf_plan_for(Tq, Tk, hi);
+    return pf_plan_for(Tq, Tk, window, hi);
 }
 
 // The (row block, chunk) items sorted longest first (ties: longer row block
 // first, so that the chunks that merge run early), as the launch table.
-static void pf_items(const PfPlan &p, int Tq, int Tk, PfItems *it)
+static void pf_items(const PfPlan &p, int Tq, int Tk, int window, PfItems *it)
 {
     std::vector<std::pair<int, int>> v;  // (sort key, entry)
     for (int rb = 0; rb < p.n_rb; ++rb) {
-        const int nt = pf_row_tiles(rb, Tq, Tk);
+        const int nt = pf_row_tiles(rb, Tq, Tk, window);
         const int nc = (nt + p.ch - 1) / p.ch, per = (nt + nc - 1) / nc;
         for (int c = 0; c < nc; ++c) {
             const int t0 = std::min(nt, c * per), len = std::min(nt, t0 + per) - t0;
@@ -674,9 +700,9 @@ static void pf_items(const PfPlan &p, int Tq, int Tk, PfItems *it)
 }
 
 // Flag region, then one partial slot per chunk of every split row block.
-size_t prefill_workspace_bytes(int B, int Hq, int D, int Tq, int Tk, int n_cus)
+size_t prefill_workspace_bytes(int B, int Hq, int D, int Tq, int Tk, int window, int n_cus)
 {
-    const PfPlan p = pf_plan(B, Hq, D, Tq, Tk, n_cus);
+    const PfPlan p = pf_plan(B, Hq, D, Tq, Tk, window, n_cus);
     const size_t slot = D == 64 ? PfSlot<64>::BYTES : PfSlot<128>::BYTES;
     const size_t split_cols = (size_t)B * Hq * (p.n_rb - p.rb0);
     return kWsFlagBytes + (p.max_nc > 1 ? split_cols * p.max_nc * slot : 0);
@@ -684,11 +710,12 @@ size_t prefill_workspace_bytes(int B, int Hq, int D, int Tq, int Tk, int n_cus)
 
 template <typename T, int D>
 static hipError_t launch_pf(const void *q, const void *k, const void *v, void *out, int B, int Hq, int Hkv,
-                            int Tq, int Tk, int s_cap, float scale, void *ws, int n_cus, hipStream_t s)
+                            int Tq, int Tk, int s_cap, float scale, void *ws, int window, const float *sinks,
+                            int n_cus, hipStream_t s)
 {
-    const PfPlan plan = pf_plan(B, Hq, D, Tq, Tk, n_cus);
+    const PfPlan plan = pf_plan(B, Hq, D, Tq, Tk, window, n_cus);
     PfItems items;
-    pf_items(plan, Tq, Tk, &items);
+    pf_items(plan, Tq, Tk, window, &items);
     // A zero scale (uniform weights over the visible keys) is run as the
     // smallest normal scale: every exponent is then below 2^-80 in
     // magnitude, exp2 of it rounds to exactly 1, and masked keys (-inf)
@@ -699,24 +726,27 @@ static hipError_t launch_pf(const void *q, const void *k, const void *v, void *o
     if (qscale < 0.0f)
         hipLaunchKernelGGL((prefill_causal_kernel<T, D, true>), grid, dim3(kPfThreads), 0, s, (const uint16_t *)q,
                            (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)out, Hq, Hkv, Tq, Tk, s_cap,
-                           qscale, plan.n_rb, (unsigned char *)ws, B, items);
+                           qscale, plan.n_rb, (unsigned char *)ws, B, window, sinks, items);
     else
         hipLaunchKernelGGL((prefill_causal_kernel<T, D, false>), grid, dim3(kPfThreads), 0, s, (const uint16_t *)q,
                            (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)out, Hq, Hkv, Tq, Tk, s_cap,
-                           qscale, plan.n_rb, (unsigned char *)ws, B, items);
+                           qscale, plan.n_rb, (unsigned char *)ws, B, window, sinks, items);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill(int dtype, int D, const void *q, const void *k, const void *v, void *out, int B,
-                          int Hq, int Hkv, int Tq, int Tk, int s_cap, float scale, void *ws, int n_cus, hipStream_t s)
+                          int Hq, int Hkv, int Tq, int Tk, int s_cap, float scale, void *ws, int window,
+                          const float *sinks, int n_cus, hipStream_t s)
 {
+#define GQA_PF(T, DD) launch_pf<T, DD>(q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, ws, window, sinks, n_cus, s)
     if (dtype == 1) {
-        if (D == 64) return launch_pf<bf16_t, 64>(q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, ws, n_cus, s);
-        if (D == 128) return launch_pf<bf16_t, 128>(q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, ws, n_cus, s);
+        if (D == 64) return GQA_PF(bf16_t, 64);
+        if (D == 128) return GQA_PF(bf16_t, 128);
     } else if (dtype == 2) {
-        if (D == 64) return launch_pf<f16_t, 64>(q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, ws, n_cus, s);
-        if (D == 128) return launch_pf<f16_t, 128>(q, k, v, out, B, Hq, Hkv, Tq, Tk, s_cap, scale, ws, n_cus, s);
+        if (D == 64) return GQA_PF(f16_t, 64);
+        if (D == 128) return GQA_PF(f16_t, 128);
     }
+#undef GQA_PF
     return hipErrorInvalidValue;
 }
 

@@ -222,3 +222,26 @@ def test_append_validation(lib):
     assert q4(group=128, D=64) == gqa.GQA_ERR_SHAPE
     assert q4(dtype=9) == gqa.GQA_ERR_UNSUPPORTED
     assert q4(kn=FAKE_ODD) == gqa.GQA_ERR_ALIGN
+
+
+def test_window_sinks_validation(lib):
+    wsb = gqa.gqa_decode_workspace_bytes(2, 28, 4, 128, 64)
+
+    def dec(window=0, sinks=NULL, lens=FAKE):
+        return lib.gqa_decode_attend_ex(FAKE, FAKE, FAKE, FAKE, lens, 2, 28, 4, 128, 64, ctypes.c_float(0.1), 0,
+                                        window, sinks, FAKE, wsb, NULL)
+
+    assert dec(lens=NULL) == gqa.GQA_ERR_NULL
+    assert dec(window=-1) == gqa.GQA_ERR_SHAPE
+    assert dec(sinks=FAKE_ODD) == gqa.GQA_ERR_ALIGN
+    pwb = gqa.gqa_prefill_workspace_bytes_ex(1, 14, 2, 64, 8, 8, 3)
+    assert pwb >= MIB16 and gqa.gqa_prefill_workspace_bytes_ex(1, 14, 2, 64, 8, 8, -1) == 0
+    assert gqa.gqa_prefill_workspace_bytes_ex(1, 14, 2, 64, 300, 300, 0) == gqa.gqa_prefill_workspace_bytes(
+        1, 14, 2, 64, 300, 300)
+
+    def pf(window=0, sinks=NULL):
+        return lib.gqa_prefill_causal_ex(FAKE, FAKE, FAKE, FAKE, 1, 14, 2, 64, 8, 8, 8, ctypes.c_float(0.125), 1,
+                                         window, sinks, FAKE, pwb, NULL)
+
+    assert pf(window=-2) == gqa.GQA_ERR_SHAPE
+    assert pf(sinks=FAKE_ODD) == gqa.GQA_ERR_ALIGN
