@@ -9,13 +9,17 @@ the split-K decode kernel, captured once in a HIP graph and replayed.  The
 value is microseconds per layer (lower is better).
 
 Secondary metric: causal prefill attention with Qwen2.5-0.5B heads (14 / 2,
-dim 64), bf16, T = 4097, one step = 24 layers (that model's depth) captured
-in a HIP graph, reported per layer as TFLOP/s and as a fraction of the bf16
-matrix-core peak.  The other configurations of the workload set (decode at
-KV length 128 with 0.5B heads, batched bf16 decode with Qwen3-4B heads at
-B = 1, 2, 4, 8, 4-bit decode at KV length 2048 and 16384, and the chunked
-prefill of 256 queries at offset 3841) are reported the same way, each
-behind its own parity gate (skip them with --no-extra).
+dim 64), bf16, T = 513, 2049 and 4097, one step = 24 layers (that model's
+depth) captured in a HIP graph, reported per layer as TFLOP/s and as a
+fraction of the bf16 matrix-core peak.  The other configurations of the
+workload set are reported the same way, each behind its own parity gate:
+the 7B decode at KV lengths 128 ... 2048, decode at KV length 128 with 0.5B
+heads, batched bf16 decode with Qwen3-4B heads at B = 1, 2, 4, 8, 4-bit
+decode at KV length 2048 and 16384, the chunked prefill of 256 queries at
+offset 3841, the cache append (dense and 4-bit) that precedes each decode
+step, and the unfused torch-ROCm path the pages compare against (repeat the
+KV heads, matmul, scale and mask, softmax, matmul) for the 7B decode and the
+T = 4097 prefill.  --extras picks a subset, --no-extra skips them.
 
 Protocol: inputs are generated on the host from fixed seeds and copied to
 HBM before anything is timed; a parity gate compares sampled outputs with
@@ -25,7 +29,7 @@ of the step's inputs; HIP events on the launch stream bracket each step.
 ``cpu_baseline`` times the unmodified oracle on the host cores over a bounded
 sample of the same workload.
 
-Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--sweep]
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--extras a,b,...]
 """
 
 from __future__ import annotations
@@ -300,8 +304,9 @@ def hbm_entry(us, nbytes, gate_ok, gate_max_abs, kernel, traffic=None, **extra):
     return d
 
 
-EXTRAS = ("decode_0p5b_s128", "batched_qwen3_4b", "q4_decode_s2048", "q4_decode_s16384",
-          "prefill_0p5b_chunk256_at3841")
+EXTRAS = ("decode_7b_sweep", "prefill_0p5b_T513", "prefill_0p5b_T2049", "decode_0p5b_s128", "batched_qwen3_4b",
+          "q4_decode_s2048", "q4_decode_s16384", "prefill_0p5b_chunk256_at3841", "append_7b_s4096",
+          "append_q4_s16384", "naive_decode_7b_s4096", "naive_prefill_0p5b_t4097")
 
 
 def bench_extra(torch, gqa, oracle, W, steps, warmup, flush, names=EXTRAS):
@@ -312,6 +317,11 @@ def bench_extra(torch, gqa, oracle, W, steps, warmup, flush, names=EXTRAS):
     scaled (codes permuted for the 4-bit cache), so that every layer reads its
     own memory."""
     out = {}
+    if "decode_7b_sweep" in names:
+        out.update(extra_decode_sweep(torch, gqa, oracle, W, steps, warmup, flush))
+    for T in (513, 2049):
+        if "prefill_0p5b_T%d" % T in names:
+            out["prefill_0p5b_T%d" % T] = prefill_entry(bench_prefill(torch, gqa, oracle, W, T, steps, warmup, flush))
     if "decode_0p5b_s128" in names:
         out.update(extra_decode_small(torch, gqa, oracle, W, steps, warmup, flush))
     if "batched_qwen3_4b" in names:
@@ -321,6 +331,14 @@ def bench_extra(torch, gqa, oracle, W, steps, warmup, flush, names=EXTRAS):
         out.update(extra_q4(torch, gqa, oracle, W, steps, warmup, flush, sizes=sizes))
     if "prefill_0p5b_chunk256_at3841" in names:
         out.update(extra_chunked_prefill(torch, gqa, oracle, W, steps, warmup, flush))
+    if "append_7b_s4096" in names:
+        out.update(extra_append_dense(torch, gqa, oracle, W, steps, warmup, flush))
+    if "append_q4_s16384" in names:
+        out.update(extra_append_q4(torch, gqa, oracle, W, steps, warmup, flush))
+    if "naive_decode_7b_s4096" in names:
+        out.update(naive_decode(torch, oracle, W, steps, warmup, flush))
+    if "naive_prefill_0p5b_t4097" in names:
+        out.update(naive_prefill(torch, oracle, W, max(3, steps // 2), 1, flush))
     return out
 
 
@@ -464,6 +482,182 @@ def extra_chunked_prefill(torch, gqa, oracle, W, steps, warmup, flush):
     return out
 
 
+def prefill_entry(p, traffic=None, counters=None, gemm=None):
+    """The result entry of one prefill configuration."""
+    us = float(np.median(p["ms"])) * 1e3
+    tf = p["flops"] / (us * 1e-6) / 1e12
+    d = {"us": round(us, 2), "layers_per_step": p["layers"], "TFLOPs": round(tf, 2),
+         "score_matrix_bytes_avoided": score_matrix_bytes(p["T"]),
+         "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+         "roofline": {"bound": "mfma", "kernel": "prefill_causal_kernel<bf16_t,64,false>",
+                      "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                      "algorithmic_flop_per_launch": p["flops"], "launch_duration_us": round(us, 2)},
+         "parity_ok": p["gate_ok"], "parity_max_abs": p["gate_max_abs"]}
+    if counters is not None:
+        d["roofline"]["mfma_busy_counter_frac"] = counters
+    if gemm:
+        d["frac_of_gemm_bf16"] = round(tf / gemm, 4)
+    return d
+
+
+def extra_decode_sweep(torch, gqa, oracle, W, steps, warmup, flush, sizes=(128, 256, 512, 1024, 2048)):
+    """The 7B-geometry fp32 decode at the other KV lengths of the pages'
+    table, each timed like the headline (28 seeded layers, graph, flush)."""
+    out = {}
+    for S in sizes:
+        d = bench_decode(torch, gqa, oracle, W, S, 28, steps, warmup, flush, gate_layers=(0,))
+        us = float(np.median(d["graph_ms"])) * 1e3 / 28
+        out["decode_7b_s%d" % S] = hbm_entry(us, decode_bytes(S), d["gate_ok"], d["gate_max_abs"],
+                                             "decode_splitk_kernel<DenseKV<float,128>,float,128,7>",
+                                             layers_per_step=28,
+                                             eager_us_layer=round(float(np.median(d["eager_ms"])) * 1e3 / 28, 3))
+    return out
+
+
+def extra_append_dense(torch, gqa, oracle, W, steps, warmup, flush, S=4096):
+    """The dense append before a 7B-geometry fp32 decode step: one new
+    token's K and V rows (4 KV heads x 128) written at row S-1 of each of 28
+    layers' preallocated 4096-row caches; device lengths in and out.  Parity:
+    the caches after the append equal the oracle's placement bit for bit."""
+    w = W.by_name("decode_7b")
+    layers = 28
+    rng = np.random.default_rng(4096)
+    caches = [(torch.zeros((1, w.Hkv, S, w.D), device="cuda"), torch.zeros((1, w.Hkv, S, w.D), device="cuda"))
+              for _ in range(layers)]
+    new = [(torch.from_numpy(rng.standard_normal((1, w.Hkv, 1, w.D), dtype=np.float32)).cuda(),
+            torch.from_numpy(rng.standard_normal((1, w.Hkv, 1, w.D), dtype=np.float32)).cuda()) for _ in range(layers)]
+    lens = torch.tensor([S - 1], dtype=torch.int32, device="cuda")
+    new_lens = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def eager():
+        for (kc, vc), (kn, vn) in zip(caches, new):
+            gqa.gqa_kv_append(kn, vn, kc, vc, lens, new_lens)
+
+    eager()
+    torch.cuda.synchronize()
+    want, wl = oracle.kv_append(np.zeros((1, w.Hkv, S, w.D), np.float32), new[0][0].cpu().numpy(), [S - 1])
+    ok = bool(np.array_equal(caches[0][0].cpu().numpy(), want)) and int(new_lens.cpu()[0]) == int(wl[0])
+    g = graph_of(torch, eager)
+    us = float(np.median(time_steps(torch, g.replay, steps, warmup, flush))) * 1e3 / layers
+    nbytes = 2 * 2 * w.Hkv * w.D * 4  # new K and V rows read and written
+    return {"append_7b_s4096": hbm_entry(us, nbytes, ok, 0.0 if ok else None, "kv_append_kernel",
+                                         layers_per_step=layers, bit_exact=ok)}
+
+
+def extra_append_q4(torch, gqa, oracle, W, steps, warmup, flush, S=16384):
+    """The 4-bit append before a decode step of the 64/8-head workload: one
+    new token's f16 K and V rows (8 KV heads x 128) quantized into row S-1 of
+    each of 80 layers' 16384-row caches (codes, f16 scale and bias per group
+    of 64).  Parity: codes, scales and biases equal the oracle's quantizer
+    bit for bit."""
+    w = W.by_name("q4_decode")
+    layers = w.layers
+    rng = np.random.default_rng(16384)
+    G = w.D // w.group
+
+    def cache():
+        return [torch.zeros((1, w.Hkv, S, w.D // 2), dtype=torch.uint8, device="cuda"),
+                torch.zeros((1, w.Hkv, S, G), dtype=torch.float16, device="cuda"),
+                torch.zeros((1, w.Hkv, S, G), dtype=torch.float16, device="cuda")]
+
+    caches = [(cache(), cache()) for _ in range(layers)]
+    new = [(torch.from_numpy(rng.standard_normal((1, w.Hkv, 1, w.D), dtype=np.float32)).half().cuda(),
+            torch.from_numpy(rng.standard_normal((1, w.Hkv, 1, w.D), dtype=np.float32)).half().cuda())
+           for _ in range(layers)]
+    lens = torch.tensor([S - 1], dtype=torch.int32, device="cuda")
+
+    def eager():
+        for (kc, vc), (kn, vn) in zip(caches, new):
+            gqa.gqa_kv_append_q4(kn, vn, *kc, *vc, w.group, lens)
+
+    eager()
+    torch.cuda.synchronize()
+    c, sc, bi = oracle.q4_quantize(new[0][0].cpu(), w.group)
+    kc = caches[0][0]
+    ok = (np.array_equal(kc[0][:, :, S - 1:].cpu().numpy(), c)
+          and np.array_equal(kc[1][:, :, S - 1:].cpu().numpy().view(np.uint16), sc.view(np.uint16))
+          and np.array_equal(kc[2][:, :, S - 1:].cpu().numpy().view(np.uint16), bi.view(np.uint16)))
+    g = graph_of(torch, eager)
+    us = float(np.median(time_steps(torch, g.replay, steps, warmup, flush))) * 1e3 / layers
+    nbytes = 2 * w.Hkv * (w.D * 2 + w.D // 2 + 2 * 2 * G)  # f16 rows read; codes, scales, biases written
+    return {"append_q4_s16384": hbm_entry(us, nbytes, bool(ok), 0.0 if ok else None, "kv_append_q4_kernel<f16_t,128,64>",
+                                          layers_per_step=layers, bit_exact=bool(ok))}
+
+
+def time_eager(torch, run, steps, warmup, flush):
+    """Median ms per step of an eager sequence of launches, flush before each."""
+    return float(np.median(time_steps(torch, run, steps, warmup, flush)))
+
+
+def naive_decode(torch, oracle, W, steps, warmup, flush, S=4096):
+    """The unfused decode the Candle page replaces ("7x KV expansion" plus
+    matmul, softmax and matmul dispatches), in torch-ROCm on the same GPU:
+    repeat each KV head for its 7 query heads, Q K^T, scale, softmax, P V;
+    fp32, 28 seeded layers, eager, the cache flushed before each step."""
+    w = W.by_name("decode_7b")
+    layers = 28
+    dev = [tuple(t.cuda() for t in W.decode_inputs(w, S, l)) for l in range(layers)]
+    scale = w.scale()
+
+    def run():
+        outs = []
+        for q, k, v in dev:
+            kr = k.repeat_interleave(w.G, dim=1)
+            vr = v.repeat_interleave(w.G, dim=1)
+            p = torch.softmax(torch.matmul(q, kr.transpose(-1, -2)) * scale, dim=-1)
+            outs.append(torch.matmul(p, vr))
+        return outs
+
+    outs = run()
+    torch.cuda.synchronize()
+    err = float(np.abs(outs[0].cpu().double().numpy() - oracle.attend(*(t.cpu() for t in dev[0]), scale=scale)).max())
+    ms = time_eager(torch, run, steps, warmup, flush)
+    us = ms * 1e3 / layers
+    return {"naive_decode_7b_s4096": {
+        "us_layer": round(us, 3), "path": "torch repeat_interleave, matmul, scale, softmax, matmul (fp32, eager)",
+        "layers_per_step": layers, "algorithmic_bytes_per_layer": decode_bytes(S),
+        "expanded_kv_bytes_written_per_layer": expanded_kv_bytes(S),
+        "GBps_algorithmic": round(decode_bytes(S) / (us * 1e-6) / 1e9, 1), "max_abs_vs_oracle": err}}
+
+
+def naive_prefill(torch, oracle, W, steps, warmup, flush, T=4097, layers=24):
+    """The unfused prefill the Fornace page replaces: repeat_kv, a matmul
+    writing the [14, T, T] scores, scale, causal mask, softmax, a second
+    matmul, each its own kernel; bf16 in torch-ROCm on the same GPU, 24
+    layers (layer l: the seeded inputs scaled by 1 + l/64), eager."""
+    w = W.by_name("prefill_0p5b")
+    q, k, v = W.prefill_inputs(w, T)
+    q0, k0, v0 = q.cuda(), k.cuda(), v.cuda()
+    dev = [(q0, k0, v0)] + [tuple((x * (1.0 + l / 64.0)).contiguous() for x in (q0, k0, v0)) for l in range(1, layers)]
+    mask = torch.ones((T, T), dtype=torch.bool, device="cuda").tril()
+    scale = w.scale()
+
+    def run():
+        outs = []
+        for qq, kk, vv in dev:
+            kr = kk.repeat_interleave(w.G, dim=1)
+            vr = vv.repeat_interleave(w.G, dim=1)
+            s_ = torch.matmul(qq, kr.transpose(-1, -2).contiguous()) * scale
+            s_.masked_fill_(~mask, float("-inf"))
+            outs.append(torch.matmul(torch.softmax(s_, dim=-1), vr))
+        return outs[:1]
+
+    outs = run()
+    torch.cuda.synchronize()
+    err = 0.0
+    for i in (0, T // 2, T - 1):  # sampled rows: row i is decode over keys 0..i
+        want = oracle.attend(q[:, :, i:i + 1], k[:, :, :i + 1], v[:, :, :i + 1], scale=scale)
+        err = max(err, float(np.abs(outs[0][:, :, i:i + 1].float().cpu().double().numpy() - want).max()))
+    ms = time_eager(torch, run, steps, warmup, flush)
+    us = ms * 1e3 / layers
+    flops = prefill_flops(T, T)
+    return {"naive_prefill_0p5b_t4097": {
+        "us": round(us, 1), "path": "torch repeat_interleave, matmul, scale, masked_fill, softmax, matmul (bf16, eager)",
+        "layers_per_step": layers, "TFLOPs_algorithmic": round(flops / (us * 1e-6) / 1e12, 2),
+        "score_matrix_bytes_per_layer": score_matrix_bytes(T), "max_abs_vs_oracle_sampled_rows": err}}
+
+
 def cpu_baseline(oracle, host, scale, seconds, nthreads=0):
     """Time the oracle, as it stands, on the host cores (all of them, or
     `nthreads`) over whole layers of the headline workload until about
@@ -500,7 +694,6 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--S", type=int, default=4096, help="KV length of the headline decode workload")
-    ap.add_argument("--sweep", action="store_true", help="also time KV lengths 128..2048 and the other prefill sizes")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--extras", default=",".join(EXTRAS),
                     help="comma-separated extra configurations to time (default: all of " + ", ".join(EXTRAS) + ")")
@@ -588,40 +781,23 @@ def main():
             result["calibration"] = {"error": "%s: %s" % (type(e).__name__, e)}
 
     secondary = {}
-    if args.sweep:
-        sweep = {}
-        for S in (128, 256, 512, 1024, 2048):
-            ds = bench_decode(torch, gqa, oracle, W, S, layers, max(5, args.steps // 2), 2, flush, gate_layers=(0,))
-            u = float(np.median(ds["graph_ms"])) * 1e3 / layers
-            sweep[str(S)] = {"us_layer": round(u, 3), "GBps": round(decode_bytes(S) / (u * 1e-6) / 1e9, 1),
-                             "parity_ok": ds["gate_ok"]}
-        sweep[str(args.S)] = {"us_layer": round(us_layer, 3), "GBps": round(achieved, 1), "parity_ok": True}
-        secondary["decode_7b_sweep"] = sweep
     if not args.no_prefill:
-        for T in ((513, 2049, 4097) if args.sweep else (4097,)):
-            p = bench_prefill(torch, gqa, oracle, W, T, max(5, args.steps // 2), 2, flush)
-            us = float(np.median(p["ms"])) * 1e3
-            tf = p["flops"] / (us * 1e-6) / 1e12
-            secondary["prefill_0p5b_T%d" % T] = {
-                "us": round(us, 2), "layers_per_step": p["layers"], "TFLOPs": round(tf, 2),
-                "score_matrix_bytes_avoided": score_matrix_bytes(T),
-                "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
-                "roofline": {"bound": "mfma", "kernel": "prefill_causal_kernel<bf16_t,64,false>",
-                             "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                             "traffic": read_traffic(PREFILL_TRAFFIC_FILE, "prefill_source_sha256_16",
-                                                     PREFILL_SRCS) if T == 4097 else None,
-                             "algorithmic_flop_per_launch": p["flops"], "launch_duration_us": round(us, 2)},
-                "parity_ok": p["gate_ok"], "parity_max_abs": p["gate_max_abs"]}
-            if T == 4097:
-                # matrix-core busy cycles over all SIMD-cycles, from the committed counter pass
-                secondary["prefill_0p5b_T%d" % T]["roofline"]["mfma_busy_counter_frac"] = read_summary_value(
-                    PREFILL_COUNTERS_FILE, "prefill_source_sha256_16", PREFILL_SRCS, "mfma_busy_over_simd_cycles")
-            if "gemm_bf16" in result.get("calibration", {}):
-                secondary["prefill_0p5b_T%d" % T]["frac_of_gemm_bf16"] = round(
-                    tf / result["calibration"]["gemm_bf16"]["TFLOPs"], 4)
+        p = bench_prefill(torch, gqa, oracle, W, 4097, max(5, args.steps // 2), 2, flush)
+        gemm = result.get("calibration", {}).get("gemm_bf16", {}).get("TFLOPs")
+        secondary["prefill_0p5b_T4097"] = prefill_entry(
+            p, traffic=read_traffic(PREFILL_TRAFFIC_FILE, "prefill_source_sha256_16", PREFILL_SRCS),
+            counters=read_summary_value(PREFILL_COUNTERS_FILE, "prefill_source_sha256_16", PREFILL_SRCS,
+                                        "mfma_busy_over_simd_cycles"), gemm=gemm)
     if not args.no_extra:
         secondary.update(bench_extra(torch, gqa, oracle, W, max(5, args.steps // 2), 2, flush, extra_names))
+    # the pages' headline ratios on this GPU: the unfused torch path against the fused kernels
+    if "naive_decode_7b_s4096" in secondary:
+        nd = secondary["naive_decode_7b_s4096"]
+        nd["fused_speedup_graph"] = round(nd["us_layer"] / us_layer, 2)
+        nd["fused_speedup_eager"] = round(nd["us_layer"] / result["decode_detail"]["eager_us_layer"], 2)
+    if "naive_prefill_0p5b_t4097" in secondary and "prefill_0p5b_T4097" in secondary:
+        npf = secondary["naive_prefill_0p5b_t4097"]
+        npf["fused_speedup"] = round(npf["us"] / secondary["prefill_0p5b_T4097"]["us"], 2)
     if secondary:
         result["secondary"] = secondary
 

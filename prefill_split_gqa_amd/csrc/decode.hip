@@ -1035,17 +1035,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
         const BufDesc dq = buf_desc((const char *)a.q + ((size_t)b * a.Hq + h0) * D * 2, QB);
         lds_load16(dq, (unsigned)(uintptr_t)(lds_u8_t *)sq + 1024 * wave, 1024 * wave + 16 * lane);
     }
+    // The group add comes first (thread 0): the explicit waits below then at
+    // most also wait for it, never miss a load they count on.  Its result is
+    // used right after wave 0's last wait for all of its loads (the
+    // compiler, which cannot see the loads issued from assembly, waits for
+    // everything outstanding there anyway), so a group completer counts its
+    // group early in the split.
+    const int col = b * P.HT + ht;
+    unsigned gticket = 0u, ticket = kNoTicket;
+    if (n_split > 1 && tid == 0) gticket = group_add(a, col, s);
     const bool two = wave + kQ4Waves < nst;
     if (wave < nst) issue(wave, 0);
     if (two) issue(wave + kQ4Waves, 1);
-    // The group add comes from the last wave (not one that stages queries)
-    // after its loads: the explicit waits below then at most also wait for
-    // it, never miss a load they count on.  Its result is looked at once
-    // the wave's steps are done.
-    const int col = b * P.HT + ht;
-    constexpr int kTicketTid = kDecodeThreads - 64;
-    unsigned gticket = 0u;
-    if (n_split > 1 && tid == kTicketTid) gticket = group_add(a, col, s);
     if (wave < QDMA) {
         if (two)
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * S::NL) : "memory");
@@ -1224,10 +1225,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
     int it = 0;
     for (int st = wave; st < nst; st += kQ4Waves, ++it) {
         const int buf = it & 1;
-        if (st + kQ4Waves < nst)
+        if (st + kQ4Waves < nst) {
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(S::NL) : "memory");
-        else
+        } else {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (n_split > 1 && tid == 0) ticket = group_done(a, col, s, n_split, gticket);
+        }
         step(wbuf + buf * S::BYTES, start + st * kQ4Rows);
         if (st + 2 * kQ4Waves < nst) issue(st + 2 * kQ4Waves, buf);
     }
@@ -1256,11 +1259,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
             sl[wave * GT + j] = l_run;
         }
     }
-    unsigned ticket = kNoTicket;  // a group completer's tile word add (awaited at the end)
-    if (n_split > 1 && tid == kTicketTid) ticket = group_done(a, col, s, n_split, gticket);
     __syncthreads();
     finish_split<f16_t, D, GT, SOD>(a, so, sm, sl, col, s, n_split, out, h0);
-    if (n_split > 1) merge_tile<f16_t, D, GT>(a, col, n_split, own, decision, kTicketTid, ticket);
+    if (n_split > 1) merge_tile<f16_t, D, GT>(a, col, n_split, own, decision, 0, ticket);
 }
 
 // ---------------------------------------------------------------------------
