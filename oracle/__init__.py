@@ -243,3 +243,102 @@ def kv_append(cache, new, kv_lens):
         c[b, :, p:p + m] = n[b, :, :m]
         out_lens[b] = p + m
     return c, out_lens
+
+
+# ---------------------------------------------------------------------------
+# 4-bit cache with a float16 residual window.
+#
+# The VeloxQuant posts ("What this means in practice"; Part 4's caveats)
+# note that a production KIVI cache keeps the most recent tokens in float16
+# and only older ones quantized, which their test cache lacked.  Reading
+# taken here (block flush): with residual capacity R, a request of n tokens
+# holds positions [0, n_q) in the 4-bit arrays, n_q = R * floor(n / R), and
+# positions [n_q, n) as exact float16 rows in the residual buffer, position
+# p at slot p - n_q.  An append that fills the residual quantizes its rows
+# (and any new rows that age at once) as one block; every quantized row is
+# encoded on its own, with q4_quantize.
+# ---------------------------------------------------------------------------
+
+
+def q4r_split(n: int, R: int):
+    """(n_q, n_r): rows of an n-token request held 4-bit and held in float16."""
+    if R < 1:
+        raise ValueError("R must be positive")
+    n_q = R * (int(n) // R)
+    return n_q, int(n) - n_q
+
+
+def kv_append_q4r(state, k_new, v_new, kv_lens, group: int, R: int):
+    """Append float16 rows to a residual-window 4-bit cache.
+
+    state: dict with k_codes, v_codes (uint8 [B, H, s_cap, D/2]), k_scales,
+    k_biases, v_scales, v_biases (float16 [B, H, s_cap, D/group]) and k_res,
+    v_res (float16 [B, H, R, D]).  k_new, v_new: float16 [B, H, T_new, D].
+    Request b holds n = kv_lens[b] (clamped to [0, s_cap]) tokens; its new
+    rows take positions n .. n + T_new - 1, and rows at or past s_cap are
+    dropped.  Returns (updated copy of state, new lengths).
+
+    The request's recent rows, positions [n_q(n), n'), are the residual's
+    rows followed by the kept new rows; of those, positions [n_q(n), n_q(n'))
+    are encoded into the 4-bit arrays and positions [n_q(n'), n') become the
+    residual, from slot 0.  Other rows and slots are left as they were.
+    """
+    st = {key: np.array(val, copy=True) for key, val in state.items()}
+    kn = np.asarray(k_new)
+    vn = np.asarray(v_new)
+    if kn.dtype != np.float16 or vn.dtype != np.float16:
+        raise ValueError("new rows must be float16 (the residual's type)")
+    s_cap = st["k_codes"].shape[2]
+    if st["k_res"].shape[2] != R:
+        raise ValueError("residual buffers must hold R rows")
+    t_new = kn.shape[2]
+    out_lens = np.empty(st["k_codes"].shape[0], dtype=np.int32)
+    for b in range(st["k_codes"].shape[0]):
+        n = min(max(int(kv_lens[b]), 0), s_cap)
+        m = min(t_new, s_cap - n)
+        n2 = n + m
+        nq_old, nr_old = q4r_split(n, R)
+        nq_new, _ = q4r_split(n2, R)
+        for name, new in (("k", kn), ("v", vn)):
+            recent = np.concatenate([st[name + "_res"][b, :, :nr_old], new[b, :, :m]], axis=1)
+            aged = recent[:, :nq_new - nq_old]
+            if aged.shape[1] > 0:
+                codes, sc, bi = q4_quantize(aged.astype(np.float32), group)
+                st[name + "_codes"][b, :, nq_old:nq_new] = codes
+                st[name + "_scales"][b, :, nq_old:nq_new] = sc
+                st[name + "_biases"][b, :, nq_old:nq_new] = bi
+            keep = recent[:, nq_new - nq_old:]
+            st[name + "_res"][b, :, :keep.shape[1]] = keep
+        out_lens[b] = n2
+    return st, out_lens
+
+
+def q4r_view(state, kv_lens, group: int, R: int):
+    """The values a residual-window 4-bit cache holds, in position order:
+    float32 (K, V) [B, H, s_cap, D] with positions [0, n_q) dequantized
+    (q4_dequant), positions [n_q, n) the residual's float16 rows widened, and
+    zeros from n on."""
+    kc = np.asarray(state["k_codes"])
+    B, H, s_cap, half = kc.shape
+    D = 2 * half
+    out = []
+    for name in ("k", "v"):
+        x = np.zeros((B, H, s_cap, D), dtype=np.float32)
+        for b in range(B):
+            n = min(max(int(kv_lens[b]), 0), s_cap)
+            n_q, n_r = q4r_split(n, R)
+            if n_q > 0:
+                x[b, :, :n_q] = q4_dequant(state[name + "_codes"][b, :, :n_q], state[name + "_scales"][b, :, :n_q],
+                                           state[name + "_biases"][b, :, :n_q], group)
+            x[b, :, n_q:n] = np.asarray(state[name + "_res"][b, :, :n_r], dtype=np.float32)
+        out.append(x)
+    return out[0], out[1]
+
+
+def q4r_attend(q, state, kv_lens, group: int, R: int, causal: bool = False, scale: Optional[float] = None,
+               nthreads: int = 0):
+    """Attention over a residual-window 4-bit cache: its values in position
+    order (q4r_view), then attend (decode: one query row; causal: a prefill
+    chunk aligned to the end of each request's tokens)."""
+    k, v = q4r_view(state, kv_lens, group, R)
+    return attend(q, k, v, kv_lens=kv_lens, causal=causal, scale=scale, nthreads=nthreads)
