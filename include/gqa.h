@@ -346,6 +346,69 @@ int gqa_kv_append_q4(const void *k_new, const void *v_new, int dtype,
                      int B, int Hkv, int D, int group_size, int T_new, int s_cap, void *stream);
 
 /*
+ * 4-bit cache with a float16 residual window.
+ *
+ * The VeloxQuant posts ("What this means in practice", and the caveats
+ * after the real-model results) point out that a production KIVI cache
+ * keeps the most recent tokens in float16 and only older ones quantized,
+ * which their test cache did not.  Reading taken here (block flush): with
+ * residual capacity R, a request of n tokens holds positions [0, n_q),
+ * n_q = R * floor(n / R), in the 4-bit arrays (layouts as in
+ * gqa_decode_attend_q4, s_cap rows per KV head) and positions [n_q, n) as
+ * exact float16 rows at slots 0 .. n - n_q - 1 of
+ *
+ *   k_res, v_res   [B, Hkv, R, D]   f16
+ *
+ * kv_lens [B] int32 (DEVICE) holds n per request (clamped to [0, s_cap]).
+ * R must be a positive multiple of 64.
+ */
+
+/* Workspace bytes for gqa_decode_attend_q4r (0 if the sizes are invalid). */
+size_t gqa_decode_q4r_workspace_bytes(int B, int Hq, int Hkv, int D, int s_cap, int R);
+
+/*
+ * Decode over a residual-window 4-bit cache: attention of q [B, Hq, 1, D]
+ * f16 over every token of each request, the 4-bit rows dequantized as in
+ * gqa_decode_attend_q4 and the residual rows as they are; out [B, Hq, 1, D]
+ * f16.  Two launches on `stream`: the residual rows go through the dense
+ * decode kernel, whose normalised float32 output and log-sum-exp per query
+ * head (kept in the workspace) then join the 4-bit kernel's split merge as
+ * one more partial.  A request with no tokens gets zeros.  Requires D in
+ * {64, 128}, group_size in {32, 64, 128} dividing D, and a zero-initialised
+ * workspace of gqa_decode_q4r_workspace_bytes (calls leave it as they found
+ * it, so it is reused without clearing).
+ */
+int gqa_decode_attend_q4r(const void *q,
+                          const uint8_t *k_codes, const void *k_scales, const void *k_biases,
+                          const uint8_t *v_codes, const void *v_scales, const void *v_biases,
+                          const void *k_res, const void *v_res, void *out, const int32_t *kv_lens,
+                          int B, int Hq, int Hkv, int D, int group_size, int R, int s_cap, float scale,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Append new float16 rows k_new, v_new [B, Hkv, T_new, D] to a
+ * residual-window 4-bit cache (the VeloxQuant posts' "Part 4": encode only
+ * rows that age, never the whole history).  Request b's rows take
+ * positions n .. n + T_new - 1 (n = kv_lens[b] clamped to [0, s_cap]; rows
+ * at or past s_cap are dropped) and new_lens[b] (DEVICE, or NULL) receives
+ * n' = min(n + T_new, s_cap).  Positions [n_q(n), n_q(n')) are encoded
+ * into the 4-bit arrays with the quantizer of gqa_kv_append_q4 (from the
+ * residual, or straight from the new rows that age at once) and positions
+ * [max(n, n_q(n')), n') are copied to their residual slots; other rows and
+ * slots are left unchanged.  One workgroup per (request, KV head) encodes
+ * before it copies, so the update is exact whatever T_new is.  new_lens
+ * must not be kv_lens.  Requires D in {64, 128}, group_size in
+ * {32, 64, 128} dividing D, R a positive multiple of 64, T_new >= 1,
+ * finite inputs, 16-byte aligned pointers.
+ */
+int gqa_kv_append_q4r(const void *k_new, const void *v_new,
+                      uint8_t *k_codes, void *k_scales, void *k_biases,
+                      uint8_t *v_codes, void *v_scales, void *v_biases,
+                      void *k_res, void *v_res,
+                      const int32_t *kv_lens, int32_t *new_lens,
+                      int B, int Hkv, int D, int group_size, int R, int T_new, int s_cap, void *stream);
+
+/*
  * Dequantize n_rows cache rows to float32: s*c + b per element, rounded once
  * (a check hook for the encoding the 4-bit entry points share; its output
  * can be compared bit for bit with that definition).  The attention kernel

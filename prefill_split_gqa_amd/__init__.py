@@ -43,6 +43,9 @@ EXPORTED = (
     "gqa_dequant_q4",
     "gqa_kv_append",
     "gqa_kv_append_q4",
+    "gqa_decode_q4r_workspace_bytes",
+    "gqa_decode_attend_q4r",
+    "gqa_kv_append_q4r",
     "gqa_read_probe",
 )
 
@@ -96,6 +99,13 @@ def load() -> ctypes.CDLL:
     lib.gqa_kv_append.restype = i
     lib.gqa_kv_append_q4.argtypes = [vp, vp, i, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
     lib.gqa_kv_append_q4.restype = i
+    lib.gqa_decode_q4r_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.gqa_decode_q4r_workspace_bytes.restype = sz
+    lib.gqa_decode_attend_q4r.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz,
+                                          vp]
+    lib.gqa_decode_attend_q4r.restype = i
+    lib.gqa_kv_append_q4r.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
+    lib.gqa_kv_append_q4r.restype = i
     lib.gqa_read_probe.argtypes = [vp, sz, vp, vp]
     lib.gqa_read_probe.restype = i
     _lib = lib
@@ -427,6 +437,93 @@ def gqa_kv_append_q4(k_new, v_new, k_codes, k_scales, k_biases, v_codes, v_scale
                                    _ptr(k_scales), _ptr(k_biases), _ptr(v_codes), _ptr(v_scales), _ptr(v_biases),
                                    _ptr(kv_lens), _ptr(new_lens), B, Hkv, D, group_size, T_new, s_cap,
                                    _stream(k_new)), "gqa_kv_append_q4")
+
+
+def _q4r_cache_shapes(k_codes, v_codes, k_scales, k_biases, v_scales, v_biases, k_res, v_res, group_size: int):
+    """Checks a residual-window 4-bit cache; returns (B, Hkv, s_cap, D, R)."""
+    for n, t in (("k_codes", k_codes), ("v_codes", v_codes), ("k_scales", k_scales), ("k_biases", k_biases),
+                 ("v_scales", v_scales), ("v_biases", v_biases), ("k_res", k_res), ("v_res", v_res)):
+        _dense(n, t, 4)
+    B, Hkv, s_cap, half = k_codes.shape
+    D = 2 * half
+    R = k_res.shape[2]
+    if v_codes.shape != k_codes.shape or k_codes.dtype != torch.uint8 or v_codes.dtype != torch.uint8:
+        raise ValueError("codes must be uint8 [B,Hkv,s_cap,D/2], K and V alike")
+    gshape = (B, Hkv, s_cap, D // max(int(group_size), 1))
+    for n, t in (("k_scales", k_scales), ("k_biases", k_biases), ("v_scales", v_scales), ("v_biases", v_biases)):
+        if t.dtype != torch.float16 or tuple(t.shape) != gshape:
+            raise ValueError("%s must be float16 %s" % (n, gshape))
+    for n, t in (("k_res", k_res), ("v_res", v_res)):
+        if t.dtype != torch.float16 or tuple(t.shape) != (B, Hkv, R, D):
+            raise ValueError("%s must be float16 [B,Hkv,R,D]" % n)
+    _same_device(k_codes, v_codes=v_codes, k_scales=k_scales, k_biases=k_biases, v_scales=v_scales,
+                 v_biases=v_biases, k_res=k_res, v_res=v_res)
+    return B, Hkv, s_cap, D, R
+
+
+def gqa_decode_q4r_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, s_cap: int, R: int) -> int:
+    return int(load().gqa_decode_q4r_workspace_bytes(B, Hq, Hkv, D, s_cap, R))
+
+
+def make_q4r_workspace(B: int, Hq: int, Hkv: int, D: int, s_cap: int, R: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for gqa_decode_attend_q4r."""
+    n = gqa_decode_q4r_workspace_bytes(B, Hq, Hkv, D, s_cap, R)
+    if n == 0:
+        raise ValueError("invalid residual-window decode sizes")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def gqa_decode_attend_q4r(q, k_codes, k_scales, k_biases, v_codes, v_scales, v_biases, k_res, v_res, out,
+                          group_size: int, kv_lens, workspace, scale: Optional[float] = None) -> torch.Tensor:
+    """Decode over a residual-window 4-bit cache: q, out f16 [B,Hq,1,D]; 4-bit arrays as in
+    gqa_decode_attend_q4; k_res, v_res f16 [B,Hkv,R,D]; kv_lens int32 [B] (tokens per request)."""
+    B, Hkv, s_cap, D, R = _q4r_cache_shapes(k_codes, v_codes, k_scales, k_biases, v_scales, v_biases, k_res, v_res,
+                                            group_size)
+    _dense("q", q, 4)
+    _dense("out", out, 4)
+    _dense("kv_lens", kv_lens, 1)
+    if q.shape[0] != B or q.shape[2] != 1 or q.shape[3] != D or out.shape != q.shape:
+        raise ValueError("q and out must be [B,Hq,1,D]")
+    if q.dtype != torch.float16 or out.dtype != torch.float16:
+        raise ValueError("q and out must be float16")
+    if kv_lens.dtype != torch.int32 or kv_lens.numel() != B:
+        raise ValueError("kv_lens must be int32 [B]")
+    _same_device(q, out=out, k_codes=k_codes, kv_lens=kv_lens)
+    ws, ws_bytes = _workspace(workspace, q)
+    Hq = q.shape[1]
+    scale = default_scale(D) if scale is None else scale
+    _check(load().gqa_decode_attend_q4r(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(k_biases), _ptr(v_codes),
+                                        _ptr(v_scales), _ptr(v_biases), _ptr(k_res), _ptr(v_res), _ptr(out),
+                                        _ptr(kv_lens), B, Hq, Hkv, D, int(group_size), R, s_cap, float(scale), ws,
+                                        ws_bytes, _stream(q)), "gqa_decode_attend_q4r")
+    return out
+
+
+def gqa_kv_append_q4r(k_new, v_new, k_codes, k_scales, k_biases, v_codes, v_scales, v_biases, k_res, v_res,
+                      group_size: int, kv_lens, new_lens=None) -> None:
+    """Append f16 rows k_new, v_new [B,Hkv,T_new,D] to a residual-window 4-bit cache."""
+    B, Hkv, s_cap, D, R = _q4r_cache_shapes(k_codes, v_codes, k_scales, k_biases, v_scales, v_biases, k_res, v_res,
+                                            group_size)
+    _dense("k_new", k_new, 4)
+    _dense("v_new", v_new, 4)
+    _dense("kv_lens", kv_lens, 1)
+    T_new = k_new.shape[2]
+    if v_new.shape != k_new.shape or tuple(k_new.shape) != (B, Hkv, T_new, D):
+        raise ValueError("k_new, v_new must be [B,Hkv,T_new,D]")
+    if k_new.dtype != torch.float16 or v_new.dtype != torch.float16:
+        raise ValueError("new rows must be float16")
+    if kv_lens.dtype != torch.int32 or kv_lens.numel() != B:
+        raise ValueError("kv_lens must be int32 [B]")
+    if new_lens is not None:
+        _dense("new_lens", new_lens, 1)
+        if new_lens.dtype != torch.int32 or new_lens.numel() != B:
+            raise ValueError("new_lens must be int32 [B]")
+        _same_device(k_new, new_lens=new_lens)
+    _same_device(k_new, v_new=v_new, k_codes=k_codes, kv_lens=kv_lens)
+    _check(load().gqa_kv_append_q4r(_ptr(k_new), _ptr(v_new), _ptr(k_codes), _ptr(k_scales), _ptr(k_biases),
+                                    _ptr(v_codes), _ptr(v_scales), _ptr(v_biases), _ptr(k_res), _ptr(v_res),
+                                    _ptr(kv_lens), _ptr(new_lens), B, Hkv, D, int(group_size), R, T_new, s_cap,
+                                    _stream(k_new)), "gqa_kv_append_q4r")
 
 
 def gqa_read_probe(src: torch.Tensor, sink: torch.Tensor) -> None:

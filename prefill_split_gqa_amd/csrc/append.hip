@@ -19,7 +19,17 @@
 //    the scale is 0; a zero minimum or step is stored as +0).  Only the new
 //    rows are touched.
 //
-// Both are bound by HBM (a few hundred KB per call at the workloads' sizes);
+//  * 4-bit append with a float16 residual window: a request of n tokens
+//    holds positions [0, n_q) 4-bit, n_q = R * floor(n / R), and positions
+//    [n_q, n) as exact float16 rows in a residual buffer of R rows (slot p -
+//    n_q).  New float16 rows join the residual; when it fills, its rows and
+//    any new rows that age at once are encoded as one block (the VeloxQuant
+//    posts, "What this means in practice": a production KIVI cache keeps the
+//    recent tokens in float16).  One workgroup per (request, KV head) encodes
+//    the aged rows first and, after a barrier, writes the new residual rows,
+//    so a slot is read before it is overwritten.
+//
+// All are bound by HBM (a few hundred KB per call at the workloads' sizes);
 // one lane handles 8 consecutive elements of a row (one 16-byte load of
 // 16-bit inputs, two of fp32), the lanes of one group reduce its minimum and
 // maximum with butterfly shuffles, and each lane writes its 8 codes as one
@@ -101,6 +111,44 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x)
     return __builtin_bit_cast(uint16_t, h);
 }
 
+// Min-max encoding of the 8 elements x of one lane; the LPG lanes of a
+// group (aligned, a power of two) reduce its minimum and maximum together,
+// so every lane of a group must take part.  Returns the lane's 8 codes as
+// one word (element i: nibble i) and the group's f16 scale and bias.
+template <int LPG>
+__device__ __forceinline__ uint32_t q4_encode8(const float (&x)[8], uint16_t &sh, uint16_t &bh16)
+{
+    float lo = x[0], hi = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+        lo = fminf(lo, x[i]);
+        hi = fmaxf(hi, x[i]);
+    }
+#pragma unroll
+    for (int m = 1; m < LPG; m <<= 1) {
+        lo = fminf(lo, __shfl_xor(lo, m, 64));
+        hi = fmaxf(hi, __shfl_xor(hi, m, 64));
+    }
+    lo = lo == 0.0f ? 0.0f : lo;  // a zero minimum or step is stored as +0
+    float step = (hi - lo) / 15.0f;
+    step = step == 0.0f ? 0.0f : step;
+    sh = f32_to_f16_bits(step);
+    bh16 = f32_to_f16_bits(lo);
+    const float s = f16_bits_to_f32(sh);
+    const float bias = f16_bits_to_f32(bh16);
+    uint32_t word = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t c = 0u;
+        if (s != 0.0f) {
+            const float k = __builtin_rintf((x[i] - bias) / s);
+            c = k < 0.0f ? 0u : (k > 15.0f ? 15u : (uint32_t)k);
+        }
+        word |= c << (4 * i);  // element 8*lane8 + i: nibble i (low nibble = even element)
+    }
+    return word;
+}
+
 // One row of D elements per D/8 lanes; LPG = group/8 lanes per group (a
 // power of two, aligned within the wave), whose minimum and maximum are
 // reduced with xor shuffles.
@@ -134,34 +182,8 @@ __global__ __launch_bounds__(256) void kv_append_q4_kernel(const void *__restric
         const void *src = (const char *)(which ? v_new : k_new) + r * (long)D * sizeof(T);
         float x[8];
         Load8<T>::run(src, lane8, x);
-        float lo = x[0], hi = x[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) {
-            lo = fminf(lo, x[i]);
-            hi = fmaxf(hi, x[i]);
-        }
-#pragma unroll
-        for (int m = 1; m < LPG; m <<= 1) {
-            lo = fminf(lo, __shfl_xor(lo, m, 64));
-            hi = fmaxf(hi, __shfl_xor(hi, m, 64));
-        }
-        lo = lo == 0.0f ? 0.0f : lo;  // a zero minimum or step is stored as +0
-        float step = (hi - lo) / 15.0f;
-        step = step == 0.0f ? 0.0f : step;
-        const uint16_t sh = f32_to_f16_bits(step);
-        const uint16_t bh16 = f32_to_f16_bits(lo);
-        const float s = f16_bits_to_f32(sh);
-        const float bias = f16_bits_to_f32(bh16);
-        uint32_t word = 0u;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint32_t c = 0u;
-            if (s != 0.0f) {
-                const float k = __builtin_rintf((x[i] - bias) / s);
-                c = k < 0.0f ? 0u : (k > 15.0f ? 15u : (uint32_t)k);
-            }
-            word |= c << (4 * i);  // element 8*lane8 + i: nibble i (low nibble = even element)
-        }
+        uint16_t sh, bh16;
+        const uint32_t word = q4_encode8<LPG>(x, sh, bh16);
         if (store) {
             uint8_t *codes = which ? v_codes : k_codes;
             ((uint32_t *)(codes + dst * (D / 2)))[lane8] = word;
@@ -170,6 +192,77 @@ __global__ __launch_bounds__(256) void kv_append_q4_kernel(const void *__restric
                 (which ? v_scales : k_scales)[dst * NG + g] = sh;
                 (which ? v_biases : k_biases)[dst * NG + g] = bh16;
             }
+        }
+    }
+}
+
+// Residual-window append: one workgroup per (request b, KV head).  With n
+// the request's tokens before and n2 after the append, positions [n_q(n),
+// n_q(n2)) are encoded (from residual slot p - n_q(n) while p < n, else
+// from new row p - n), then positions [max(n, n_q(n2)), n2) are copied to
+// residual slot p - n_q(n2).  Rows are spread over the workgroup's lanes,
+// D/8 lanes per row; a lane past the last row of a pass shadows the row
+// before it and stores nothing.
+template <int D, int G>
+__global__ __launch_bounds__(256) void kv_append_q4r_kernel(const f16_t *__restrict__ k_new, const f16_t *__restrict__ v_new,
+                                                            uint8_t *__restrict__ k_codes, uint16_t *__restrict__ k_scales,
+                                                            uint16_t *__restrict__ k_biases, uint8_t *__restrict__ v_codes,
+                                                            uint16_t *__restrict__ v_scales, uint16_t *__restrict__ v_biases,
+                                                            uint4 *__restrict__ k_res, uint4 *__restrict__ v_res,
+                                                            const int32_t *__restrict__ kv_lens,
+                                                            int32_t *__restrict__ new_lens, int Hkv, int T_new,
+                                                            int s_cap, int R)
+{
+    constexpr int LPR = D / 8;   // lanes per row
+    constexpr int LPG = G / 8;   // lanes per group
+    constexpr int NG = D / G;    // groups per row
+    constexpr int RPP = 256 / LPR;  // rows per pass
+    static_assert(LPR <= 64 && (64 % LPR) == 0 && (LPG & (LPG - 1)) == 0 && LPG <= LPR, "lane layout");
+    const int bh = (int)blockIdx.x;
+    const int b = bh / Hkv;
+    const int n = clamp_len(kv_lens[b], s_cap);
+    const int n2 = min(n + T_new, s_cap);
+    const int nq_old = n - n % R, nq_new = n2 - n2 % R;
+    if (new_lens && threadIdx.x == 0 && bh % Hkv == 0) new_lens[b] = n2;
+    const int lane8 = (int)threadIdx.x % LPR;
+    const int rsub = (int)threadIdx.x / LPR;
+    const size_t res0 = (size_t)bh * R;        // residual row of slot 0
+    const size_t new0 = (size_t)bh * T_new;    // new row 0
+    const size_t cache0 = (size_t)bh * s_cap;  // cache row of position 0
+
+    // aged rows -> 4-bit
+    for (int p0 = nq_old; p0 < nq_new; p0 += RPP) {
+        const bool live = p0 + rsub < nq_new;
+        const int p = live ? p0 + rsub : nq_new - 1;
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            const f16_t *src = p < n ? (const f16_t *)(which ? v_res : k_res) + (res0 + (p - nq_old)) * D
+                                     : (which ? v_new : k_new) + (new0 + (p - n)) * D;
+            float x[8];
+            Load8<f16_t>::run(src, lane8, x);
+            uint16_t sh, bh16;
+            const uint32_t word = q4_encode8<LPG>(x, sh, bh16);
+            if (live) {
+                const size_t dst = cache0 + p;
+                ((uint32_t *)((which ? v_codes : k_codes) + dst * (D / 2)))[lane8] = word;
+                if ((lane8 % LPG) == 0) {
+                    (which ? v_scales : k_scales)[dst * NG + lane8 / LPG] = sh;
+                    (which ? v_biases : k_biases)[dst * NG + lane8 / LPG] = bh16;
+                }
+            }
+        }
+    }
+    __syncthreads();  // every aged residual slot has been read
+
+    // new rows that stay float16 -> residual
+    const int keep0 = max(n, nq_new);
+    for (int p0 = keep0; p0 < n2; p0 += RPP) {
+        const int p = p0 + rsub;
+        if (p < n2) {
+            const size_t src = (new0 + (p - n)) * LPR + lane8;  // 16-byte units
+            const size_t dst = (res0 + (p - nq_new)) * LPR + lane8;
+            k_res[dst] = ((const uint4 *)k_new)[src];
+            v_res[dst] = ((const uint4 *)v_new)[src];
         }
     }
 }
@@ -205,7 +298,40 @@ hipError_t launch_q4_append_t(int D, const void *kn, const void *vn, uint8_t *kc
     return hipErrorInvalidValue;
 }
 
+template <int D>
+hipError_t launch_q4r_append_d(const void *kn, const void *vn, uint8_t *kc, void *ks, void *kb, uint8_t *vc, void *vs,
+                               void *vb, void *kr, void *vr, const int32_t *lens, int32_t *new_lens, int B, int Hkv,
+                               int group, int R, int T_new, int s_cap, hipStream_t st)
+{
+#define GQA_Q4R(G)                                                                                                 \
+    hipLaunchKernelGGL((kv_append_q4r_kernel<D, G>), dim3(B * Hkv), dim3(256), 0, st, (const f16_t *)kn,          \
+                       (const f16_t *)vn, kc, (uint16_t *)ks, (uint16_t *)kb, vc, (uint16_t *)vs, (uint16_t *)vb, \
+                       (uint4 *)kr, (uint4 *)vr, lens, new_lens, Hkv, T_new, s_cap, R)
+    if (group == 32) GQA_Q4R(32);
+    else if (group == 64) GQA_Q4R(64);
+    else if constexpr (D == 128) {
+        if (group == 128) GQA_Q4R(128);
+        else return hipErrorInvalidValue;
+    } else return hipErrorInvalidValue;
+#undef GQA_Q4R
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_kv_append_q4r(const void *k_new, const void *v_new, uint8_t *k_codes, void *k_scales,
+                                void *k_biases, uint8_t *v_codes, void *v_scales, void *v_biases, void *k_res,
+                                void *v_res, const int32_t *kv_lens, int32_t *new_lens, int B, int Hkv, int D,
+                                int group, int R, int T_new, int s_cap, hipStream_t s)
+{
+    if (D == 64)
+        return launch_q4r_append_d<64>(k_new, v_new, k_codes, k_scales, k_biases, v_codes, v_scales, v_biases, k_res,
+                                       v_res, kv_lens, new_lens, B, Hkv, group, R, T_new, s_cap, s);
+    if (D == 128)
+        return launch_q4r_append_d<128>(k_new, v_new, k_codes, k_scales, k_biases, v_codes, v_scales, v_biases, k_res,
+                                        v_res, kv_lens, new_lens, B, Hkv, group, R, T_new, s_cap, s);
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_kv_append(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                             const int32_t *kv_lens, int32_t *new_lens, int B, int Hkv, int D, int T_new, int s_cap,

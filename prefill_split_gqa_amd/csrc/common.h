@@ -250,6 +250,17 @@ struct DecodeArgs {
     unsigned *poison;        // the workspace's poison word
     size_t ws_bytes;
     int n_cus;               // compute units of the device (launch shape)
+    // A 4-bit cache with a float16 residual window of res_cap rows: a
+    // request of n tokens (clamped to len_cap) holds n - n % res_cap rows
+    // 4-bit and n % res_cap rows in the residual.  len_mode 1: this launch
+    // sees the 4-bit rows; 2: the residual rows; 0: plain lengths.
+    int len_mode, len_cap, res_cap;
+    // Residual pass: instead of `out`, the normalised float32 output
+    // [B][Hq][D] and its log2-domain log-sum-exp [B][Hq] (units of qscale
+    // times the score; -inf for no rows).
+    float *x_out_o, *x_out_lse;
+    // 4-bit pass: that pair, folded in as one more partial (or nullptr).
+    const float *x_in_o, *x_in_lse;
 };
 
 // Launchers (defined in the .hip files; return a hipError_t).
@@ -268,6 +279,10 @@ hipError_t launch_kv_append_q4(int dtype, const void *k_new, const void *v_new, 
                                void *k_biases, uint8_t *v_codes, void *v_scales, void *v_biases,
                                const int32_t *kv_lens, int32_t *new_lens, int B, int Hkv, int D, int group, int T_new,
                                int s_cap, hipStream_t s);
+hipError_t launch_kv_append_q4r(const void *k_new, const void *v_new, uint8_t *k_codes, void *k_scales,
+                                void *k_biases, uint8_t *v_codes, void *v_scales, void *v_biases, void *k_res,
+                                void *v_res, const int32_t *kv_lens, int32_t *new_lens, int B, int Hkv, int D,
+                                int group, int R, int T_new, int s_cap, hipStream_t s);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_read_probe(const void *src, size_t bytes, void *sink, hipStream_t s);
 

@@ -242,10 +242,42 @@ __device__ __forceinline__ int request_len(const DecodeArgs &a, int b)
 {
     int n = a.kv_len;
     if (a.kv_lens) {
+        const int cap = a.len_mode ? a.len_cap : a.s_cap;
         n = a.kv_lens[b];
-        n = n < 0 ? 0 : (n > a.s_cap ? a.s_cap : n);
+        n = n < 0 ? 0 : (n > cap ? cap : n);
     }
+    if (a.len_mode == 1) n -= n % a.res_cap;  // whole blocks of the residual's size are 4-bit
+    else if (a.len_mode == 2) n %= a.res_cap; // the rest is float16
     return n;
+}
+
+// Final output of query head h of request b, 4 values at column d, with
+// the head's log2-domain log-sum-exp lse (taken from the lane with d = 0):
+// to the row `orow` of `out`, or, in the residual pass, to its float32
+// output and log-sum-exp arrays.
+template <int D, typename TQ>
+__device__ __forceinline__ void store_final(const DecodeArgs &a, TQ *orow, int b, int h, int d, float x0, float x1,
+                                            float x2, float x3, float lse)
+{
+    if (a.x_out_o) {
+        const size_t row = (size_t)b * a.Hq + h;
+        *(float4 *)(a.x_out_o + row * D + d) = make_float4(x0, x1, x2, x3);
+        if (d == 0) a.x_out_lse[row] = lse;
+    } else {
+        store4(orow + d, x0, x1, x2, x3);
+    }
+}
+
+// The residual pass's result for query head h of request b as one more
+// partial of the 4-bit pass: its log-sum-exp (-inf when there is none or
+// the residual is empty).
+__device__ __forceinline__ float extra_lse(const DecodeArgs &a, int b, int h)
+{
+    return a.x_in_lse ? a.x_in_lse[(size_t)b * a.Hq + h] : kNegInf;
+}
+__device__ __forceinline__ float4 extra_o(const DecodeArgs &a, int D, int b, int h, int d)
+{
+    return *(const float4 *)(a.x_in_o + ((size_t)b * a.Hq + h) * D + d);
 }
 __device__ __forceinline__ int windowed(const DecodeArgs &a, int n, int *lo)
 {
@@ -402,6 +434,7 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *s
     const DecodePlan &P = a.plan;
     const int tid = threadIdx.x;
     const int qh = tid / (D / 4), qd = (tid % (D / 4)) * 4;
+    const int b = col / P.HT;
     float Mw = kNegInf, Lw = 0.0f, O0 = 0.0f, O1 = 0.0f, O2 = 0.0f, O3 = 0.0f;
     if (tid < NQ) {
         // every read first, then the arithmetic
@@ -415,10 +448,11 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *s
         }
 #pragma unroll
         for (int w = 0; w < NW; ++w) Mw = fmaxf(Mw, mw[w]);
-        // a single split normalises here, sink included; several publish
-        // their partials and the merge adds the sink
+        // a single split normalises here, sink and residual partial
+        // included; several publish their partials and the merge adds them
         const float s2 = n_split == 1 ? sink_log2(a, h0 + qh) : kNegInf;
-        Mw = fmaxf(Mw, s2);
+        const float e2 = n_split == 1 ? extra_lse(a, b, h0 + qh) : kNegInf;
+        Mw = fmaxf(Mw, fmaxf(s2, e2));
         if (n_split > 1) Mw = tagged_f32(Mw);  // finite: every split has a row
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
@@ -427,9 +461,17 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *s
             O0 += wt * xw[w].x; O1 += wt * xw[w].y; O2 += wt * xw[w].z; O3 += wt * xw[w].w;
         }
         Lw += rel_weight(s2, Mw);
+        if (e2 != kNegInf) {
+            const float we = rel_weight(e2, Mw);
+            const float4 xe = extra_o(a, D, b, h0 + qh, qd);
+            Lw += we;
+            O0 += we * xe.x; O1 += we * xe.y; O2 += we * xe.z; O3 += we * xe.w;
+        }
     }
     if (n_split == 1) {
-        if (tid < NQ) store4(out + (size_t)qh * D + qd, O0 / Lw, O1 / Lw, O2 / Lw, O3 / Lw);
+        if (tid < NQ)
+            store_final<D>(a, out + (size_t)qh * D, b, h0 + qh, qd, O0 / Lw, O1 / Lw, O2 / Lw, O3 / Lw,
+                           Mw + __log2f(Lw));
         return;
     }
     const __amdgpu_buffer_rsrc_t ws_o =
@@ -489,8 +531,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
     TQ *out = (TQ *)a.out + ((size_t)b * a.Hq + h0) * D;
 
     if (n == 0) {  // empty request: defined as an all-zero output
-        if (s == 0)
-            for (int idx = tid; idx < GT * D; idx += kDecodeThreads) store_elem(out + idx, 0.0f);
+        if (s == 0) {
+            if (a.x_out_o) {  // residual pass: no rows, nothing to fold in
+                const size_t row0 = (size_t)b * a.Hq + h0;
+                for (int idx = tid; idx < GT * D; idx += kDecodeThreads) a.x_out_o[row0 * D + idx] = 0.0f;
+                if (tid < GT) a.x_out_lse[row0 + tid] = kNegInf;
+            } else {
+                for (int idx = tid; idx < GT * D; idx += kDecodeThreads) store_elem(out + idx, 0.0f);
+            }
+        }
         return;
     }
     if (s >= n_split) return;
@@ -775,11 +824,13 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     }
     __syncthreads();
     if (!s_go) {  // not reachable (see the file header); never pass silently
-        if (sg == 0) store4(out + d4 * 4, __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
+        const float nan = __builtin_nanf("");
+        if (sg == 0) store_final<D>(a, out, b, h, d4 * 4, nan, nan, nan, nan, nan);
         return;
     }
     const float s2 = sink_log2(a, h);
-    const float M = fmaxf(s_M, s2);
+    const float e2 = extra_lse(a, b, h);
+    const float M = fmaxf(fmaxf(s_M, s2), e2);
     float Ls = 0.0f;
     float4 R = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     float2 mlk[PER];  // all (max, sum) reads first (clamped to a valid split)
@@ -799,7 +850,15 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     R.y = colgroup_sum<CPW>(R.y);
     R.z = colgroup_sum<CPW>(R.z);
     R.w = colgroup_sum<CPW>(R.w);
-    if (sg == 0) store4(out + d4 * 4, R.x / Ls, R.y / Ls, R.z / Ls, R.w / Ls);
+    if (sg == 0) {
+        if (e2 != kNegInf) {
+            const float we = rel_weight(e2, M);
+            const float4 xe = extra_o(a, D, b, h, d4 * 4);
+            Ls += we;
+            R.x += we * xe.x; R.y += we * xe.y; R.z += we * xe.z; R.w += we * xe.w;
+        }
+        store_final<D>(a, out, b, h, d4 * 4, R.x / Ls, R.y / Ls, R.z / Ls, R.w / Ls, M + __log2f(Ls));
+    }
 }
 
 // The merges a split performs for (request, head tile) col once its own
@@ -979,9 +1038,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
     const int h0 = g * P.G + (ht % P.ht_per_kv) * GT;
     f16_t *out = (f16_t *)a.out + ((size_t)b * a.Hq + h0) * D;
 
-    if (n == 0) {  // empty request: defined as an all-zero output
-        if (s == 0)
-            for (int idx = tid; idx < GT * D; idx += kDecodeThreads) store_elem(out + idx, 0.0f);
+    if (n == 0) {  // no 4-bit rows: the residual's result, or (no rows at all) zeros
+        if (s == 0) {
+            const size_t row0 = (size_t)b * a.Hq + h0;
+            for (int idx = tid; idx < GT * D; idx += kDecodeThreads)
+                store_elem(out + idx, a.x_in_o ? a.x_in_o[row0 * D + idx] : 0.0f);
+        }
         return;
     }
     if (s >= n_split) return;

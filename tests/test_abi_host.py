@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gqa.gqa_abi_version() == 3
+    assert gqa.gqa_abi_version() == 4
     for st in range(8):
         assert gqa.status_string(st)
     assert gqa.status_string(99) == "unknown status"
@@ -245,3 +245,39 @@ def test_window_sinks_validation(lib):
 
     assert pf(window=-2) == gqa.GQA_ERR_SHAPE
     assert pf(sinks=FAKE_ODD) == gqa.GQA_ERR_ALIGN
+
+
+def test_q4r_validation(lib):
+    # residual capacity R: a positive multiple of 64
+    assert gqa.gqa_decode_q4r_workspace_bytes(2, 32, 8, 128, 4096, 128) > gqa.gqa_decode_workspace_bytes(
+        2, 32, 8, 128, 4096)
+    assert gqa.gqa_decode_q4r_workspace_bytes(2, 32, 8, 128, 4096, 100) == 0
+    assert gqa.gqa_decode_q4r_workspace_bytes(2, 32, 8, 128, 4096, 0) == 0
+    assert gqa.gqa_decode_q4r_workspace_bytes(2, 32, 8, 96, 4096, 128) == 0
+    wsb = gqa.gqa_decode_q4r_workspace_bytes(2, 32, 8, 128, 4096, 128)
+
+    def dec(res=FAKE, lens=FAKE, R=128, group=64, D=128, ws_bytes=wsb, ks=FAKE):
+        return lib.gqa_decode_attend_q4r(FAKE, FAKE, ks, FAKE, FAKE, FAKE, FAKE, res, FAKE, FAKE, lens, 2, 32, 8, D,
+                                         group, R, 4096, ctypes.c_float(0.1), FAKE, ws_bytes, NULL)
+
+    assert dec(res=NULL) == gqa.GQA_ERR_NULL
+    assert dec(lens=NULL) == gqa.GQA_ERR_NULL
+    assert dec(R=96) == gqa.GQA_ERR_SHAPE
+    assert dec(group=48) == gqa.GQA_ERR_UNSUPPORTED
+    assert dec(group=128, D=64) == gqa.GQA_ERR_SHAPE
+    assert dec(ws_bytes=wsb - 256) == gqa.GQA_ERR_WORKSPACE
+    assert dec(ks=FAKE_ODD) == gqa.GQA_ERR_ALIGN
+    assert dec(res=FAKE_ODD) == gqa.GQA_ERR_ALIGN
+
+    def app(kn=FAKE, res=FAKE, lens=FAKE, new=NULL, R=128, group=64, D=128, T=1):
+        return lib.gqa_kv_append_q4r(kn, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, res, FAKE, lens, new, 2, 8, D,
+                                     group, R, T, 4096, NULL)
+
+    assert app(kn=NULL) == gqa.GQA_ERR_NULL
+    assert app(res=NULL) == gqa.GQA_ERR_NULL
+    assert app(T=0) == gqa.GQA_ERR_SHAPE
+    assert app(R=32) == gqa.GQA_ERR_SHAPE
+    assert app(new=FAKE) == gqa.GQA_ERR_SHAPE                         # same pointer as kv_lens
+    assert app(group=48) == gqa.GQA_ERR_UNSUPPORTED
+    assert app(D=96) == gqa.GQA_ERR_UNSUPPORTED
+    assert app(res=FAKE_ODD) == gqa.GQA_ERR_ALIGN
