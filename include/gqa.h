@@ -409,6 +409,32 @@ int gqa_kv_append_q4r(const void *k_new, const void *v_new,
                       int B, int Hkv, int D, int group_size, int R, int T_new, int s_cap, void *stream);
 
 /*
+ * Causal prefill of a chunk over a residual-window 4-bit cache (the
+ * VeloxQuant posts' caveats above, with the chunked prefill of the Fornace
+ * page's "Cause and workaround": a chunk of Tq queries at the end of Tk
+ * tokens sees every earlier token).  Every request holds Tk tokens (the
+ * chunk's own rows already appended, e.g. by gqa_kv_append_q4r), so
+ * positions [0, n_q), n_q = R * floor(Tk / R), are read from the 4-bit
+ * arrays and [n_q, Tk) from the residual.  Query row i attends to
+ * positions j <= i + Tk - Tq.
+ *
+ *   q, out   [B, Hq, Tq, D]  f16
+ *
+ * The kernel is gqa_prefill_causal's with the 4-bit tiles dequantized on
+ * the way into LDS: each value s*c + b is formed in float32 (one rounding,
+ * as gqa_dequant_q4) and rounded to f16, the type the matrix cores read.
+ * Workspace: gqa_prefill_workspace_bytes(B, Hq, Hkv, D, Tq, Tk).  Requires
+ * D in {64, 128}, group_size in {32, 64, 128} dividing D, R a positive
+ * multiple of 64, 1 <= Tq <= Tk <= s_cap.
+ */
+int gqa_prefill_causal_q4r(const void *q,
+                           const uint8_t *k_codes, const void *k_scales, const void *k_biases,
+                           const uint8_t *v_codes, const void *v_scales, const void *v_biases,
+                           const void *k_res, const void *v_res, void *out,
+                           int B, int Hq, int Hkv, int D, int group_size, int R, int Tq, int Tk, int s_cap,
+                           float scale, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Dequantize n_rows cache rows to float32: s*c + b per element, rounded once
  * (a check hook for the encoding the 4-bit entry points share; its output
  * can be compared bit for bit with that definition).  The attention kernel

@@ -46,6 +46,7 @@ EXPORTED = (
     "gqa_decode_q4r_workspace_bytes",
     "gqa_decode_attend_q4r",
     "gqa_kv_append_q4r",
+    "gqa_prefill_causal_q4r",
     "gqa_read_probe",
 )
 
@@ -106,6 +107,9 @@ def load() -> ctypes.CDLL:
     lib.gqa_decode_attend_q4r.restype = i
     lib.gqa_kv_append_q4r.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
     lib.gqa_kv_append_q4r.restype = i
+    lib.gqa_prefill_causal_q4r.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, vp,
+                                           sz, vp]
+    lib.gqa_prefill_causal_q4r.restype = i
     lib.gqa_read_probe.argtypes = [vp, sz, vp, vp]
     lib.gqa_read_probe.restype = i
     _lib = lib
@@ -524,6 +528,30 @@ def gqa_kv_append_q4r(k_new, v_new, k_codes, k_scales, k_biases, v_codes, v_scal
                                     _ptr(v_codes), _ptr(v_scales), _ptr(v_biases), _ptr(k_res), _ptr(v_res),
                                     _ptr(kv_lens), _ptr(new_lens), B, Hkv, D, int(group_size), R, T_new, s_cap,
                                     _stream(k_new)), "gqa_kv_append_q4r")
+
+
+def gqa_prefill_causal_q4r(q, k_codes, k_scales, k_biases, v_codes, v_scales, v_biases, k_res, v_res, out,
+                           group_size: int, Tk: int, workspace=None, scale: Optional[float] = None) -> torch.Tensor:
+    """Causal prefill of q, out f16 [B,Hq,Tq,D] (the last Tq of Tk tokens) over a residual-window 4-bit cache."""
+    B, Hkv, s_cap, D, R = _q4r_cache_shapes(k_codes, v_codes, k_scales, k_biases, v_scales, v_biases, k_res, v_res,
+                                            group_size)
+    _dense("q", q, 4)
+    _dense("out", out, 4)
+    if q.shape[0] != B or q.shape[3] != D or out.shape != q.shape:
+        raise ValueError("q and out must be [B,Hq,Tq,D]")
+    if q.dtype != torch.float16 or out.dtype != torch.float16:
+        raise ValueError("q and out must be float16")
+    _same_device(q, out=out, k_codes=k_codes)
+    Hq, Tq = q.shape[1], q.shape[2]
+    if workspace is None:
+        workspace = make_prefill_workspace(B, Hq, Hkv, D, Tq, int(Tk), device=q.device)
+    ws, ws_bytes = _workspace(workspace, q)
+    scale = default_scale(D) if scale is None else scale
+    _check(load().gqa_prefill_causal_q4r(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(k_biases), _ptr(v_codes),
+                                         _ptr(v_scales), _ptr(v_biases), _ptr(k_res), _ptr(v_res), _ptr(out), B, Hq,
+                                         Hkv, D, int(group_size), R, Tq, int(Tk), s_cap, float(scale), ws, ws_bytes,
+                                         _stream(q)), "gqa_prefill_causal_q4r")
+    return out
 
 
 def gqa_read_probe(src: torch.Tensor, sink: torch.Tensor) -> None:

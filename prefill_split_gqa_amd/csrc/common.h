@@ -117,7 +117,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, si
 // inline assembly so that the compiler does not treat them as pending LDS
 // stores (it would otherwise wait for every one of them at each workgroup
 // barrier); the kernels wait for them themselves (s_waitcnt vmcnt) before
-// the data is read.
+// the data is read.  The compiler's hazard recognizer cannot see inside
+// inline assembly, so each block starts with the wait states a vector
+// memory instruction needs after a VALU write of an SGPR it reads (5: the
+// descriptor or M0 may have just been reloaded with v_readlane) and after
+// an SALU write of M0 (1).
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 struct BufDesc { u32x4_t w; };
 
@@ -134,12 +138,14 @@ __device__ __forceinline__ BufDesc buf_desc(const void *base, size_t bytes)
 
 __device__ __forceinline__ void lds_load16(const BufDesc &d, unsigned lds_base, int voff)
 {
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(d.w), "{m0}"(lds_base) : "memory");
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(d.w), "{m0}"(lds_base)
+                 : "memory");
 }
 
 __device__ __forceinline__ void lds_load_u16(const BufDesc &d, unsigned lds_base, int voff)
 {
-    asm volatile("buffer_load_ushort %0, %1, 0 offen lds" ::"v"(voff), "s"(d.w), "{m0}"(lds_base) : "memory");
+    asm volatile("s_nop 4\n\tbuffer_load_ushort %0, %1, 0 offen lds" ::"v"(voff), "s"(d.w), "{m0}"(lds_base)
+                 : "memory");
 }
 
 // ---------------------------------------------------------------------------
@@ -272,6 +278,18 @@ hipError_t launch_prefill(int dtype, int D, const void *q, const void *k, const 
                           int B, int Hq, int Hkv, int Tq, int Tk, int s_cap, float scale, void *ws, int window,
                           const float *sinks, int n_cus, hipStream_t s);
 size_t prefill_workspace_bytes(int B, int Hq, int D, int Tq, int Tk, int window, int n_cus);
+// A 4-bit cache with a float16 residual as the prefill kernel reads it:
+// key positions [0, n_q) from the 4-bit arrays (s_cap rows per KV head,
+// group-affine, f16 scale and bias per group), later positions from the
+// float16 residual rows (passed as k and v, R rows per KV head).
+struct Q4Source {
+    const uint8_t *k_codes, *v_codes;
+    const uint16_t *k_scales, *k_biases, *v_scales, *v_biases;
+    int n_q, group, s_cap;
+};
+hipError_t launch_prefill_q4r(int D, const void *q, const void *k_res, const void *v_res, void *out, int B, int Hq,
+                              int Hkv, int Tq, int Tk, int R, float scale, void *ws, const Q4Source &src, int n_cus,
+                              hipStream_t s);
 hipError_t launch_kv_append(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                             const int32_t *kv_lens, int32_t *new_lens, int B, int Hkv, int D, int T_new, int s_cap,
                             int elem_bytes, hipStream_t s);

@@ -238,16 +238,23 @@ struct DecodeGrid {
 // Rows of request b that its query sees: its length (device lengths are
 // clamped to [0, s_cap]); with a window, only the last `window` of them,
 // which start at row *lo.
+// What a launch reads of a residual-window 4-bit cache (a compile-time
+// mode, so that plain launches carry none of it): kResNone a plain cache;
+// kResQ4 the 4-bit rows, folding in the residual pass's result; kResDense
+// the float16 residual rows, writing that result.
+enum ResMode { kResNone = 0, kResQ4 = 1, kResDense = 2 };
+
+template <int RES>
 __device__ __forceinline__ int request_len(const DecodeArgs &a, int b)
 {
     int n = a.kv_len;
     if (a.kv_lens) {
-        const int cap = a.len_mode ? a.len_cap : a.s_cap;
+        const int cap = RES != kResNone ? a.len_cap : a.s_cap;
         n = a.kv_lens[b];
         n = n < 0 ? 0 : (n > cap ? cap : n);
     }
-    if (a.len_mode == 1) n -= n % a.res_cap;  // whole blocks of the residual's size are 4-bit
-    else if (a.len_mode == 2) n %= a.res_cap; // the rest is float16
+    if constexpr (RES == kResQ4) n -= n % a.res_cap;  // whole blocks of the residual's size are 4-bit
+    if constexpr (RES == kResDense) n %= a.res_cap;   // the rest is float16
     return n;
 }
 
@@ -255,11 +262,11 @@ __device__ __forceinline__ int request_len(const DecodeArgs &a, int b)
 // the head's log2-domain log-sum-exp lse (taken from the lane with d = 0):
 // to the row `orow` of `out`, or, in the residual pass, to its float32
 // output and log-sum-exp arrays.
-template <int D, typename TQ>
+template <int D, int RES, typename TQ>
 __device__ __forceinline__ void store_final(const DecodeArgs &a, TQ *orow, int b, int h, int d, float x0, float x1,
                                             float x2, float x3, float lse)
 {
-    if (a.x_out_o) {
+    if constexpr (RES == kResDense) {
         const size_t row = (size_t)b * a.Hq + h;
         *(float4 *)(a.x_out_o + row * D + d) = make_float4(x0, x1, x2, x3);
         if (d == 0) a.x_out_lse[row] = lse;
@@ -271,9 +278,10 @@ __device__ __forceinline__ void store_final(const DecodeArgs &a, TQ *orow, int b
 // The residual pass's result for query head h of request b as one more
 // partial of the 4-bit pass: its log-sum-exp (-inf when there is none or
 // the residual is empty).
-__device__ __forceinline__ float extra_lse(const DecodeArgs &a, int b, int h)
+template <int RES> __device__ __forceinline__ float extra_lse(const DecodeArgs &a, int b, int h)
 {
-    return a.x_in_lse ? a.x_in_lse[(size_t)b * a.Hq + h] : kNegInf;
+    if constexpr (RES == kResQ4) return a.x_in_lse[(size_t)b * a.Hq + h];
+    return kNegInf;
 }
 __device__ __forceinline__ float4 extra_o(const DecodeArgs &a, int D, int b, int h, int d)
 {
@@ -298,12 +306,13 @@ constexpr int kDecodePackMaxB = 64;
 struct SplitItem {
     int b, ht, s, n;  // request, head tile, split, clamped length
 };
+template <int RES>
 __device__ __forceinline__ bool packed_item(const DecodeArgs &a, int B, int i, SplitItem *it)
 {
     const DecodePlan &P = a.plan;
     const int lane = threadIdx.x & 63;
     int n = 0, lo;
-    if (lane < B) n = windowed(a, request_len(a, lane), &lo);
+    if (lane < B) n = windowed(a, request_len<RES>(a, lane), &lo);
     const int ns = (n + P.L - 1) / P.L;
     const int items = lane < B ? P.HT * (ns > 1 ? ns : 1) : 0;
     int incl = items;  // inclusive prefix sum over the lanes
@@ -325,12 +334,12 @@ __device__ __forceinline__ bool packed_item(const DecodeArgs &a, int B, int i, S
     return true;
 }
 
-template <typename TQ, int D, int GT>
+template <typename TQ, int D, int GT, int RES>
 __device__ void merge_head(const DecodeArgs &a, int m);
-template <typename TQ, int D, int GT>
+template <typename TQ, int D, int GT, int RES>
 __device__ void merge_tile(const DecodeArgs &a, int col, int n_split, unsigned own_heads, unsigned decision,
                            int ticket_tid, unsigned ticket);
-template <typename TQ, int D, int GT>
+template <typename TQ, int D, int GT, int RES>
 __device__ void merge_workgroup(const DecodeArgs &a, int m);
 
 // Control words (see the file header): the tile word of (request, head
@@ -425,7 +434,7 @@ __device__ __forceinline__ float sink_log2(const DecodeArgs &a, int h)
     return a.sinks ? a.sinks[h] * kLog2e : kNegInf;
 }
 
-template <typename TQ, int D, int GT, int SOD = D>
+template <typename TQ, int D, int GT, int RES, int SOD = D>
 __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *so, const float *sm, const float *sl,
                                              int col, int s, int n_split, TQ *out, int h0)
 {
@@ -434,7 +443,7 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *s
     const DecodePlan &P = a.plan;
     const int tid = threadIdx.x;
     const int qh = tid / (D / 4), qd = (tid % (D / 4)) * 4;
-    const int b = col / P.HT;
+    const int b = RES != kResNone ? col / P.HT : 0;
     float Mw = kNegInf, Lw = 0.0f, O0 = 0.0f, O1 = 0.0f, O2 = 0.0f, O3 = 0.0f;
     if (tid < NQ) {
         // every read first, then the arithmetic
@@ -451,7 +460,7 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *s
         // a single split normalises here, sink and residual partial
         // included; several publish their partials and the merge adds them
         const float s2 = n_split == 1 ? sink_log2(a, h0 + qh) : kNegInf;
-        const float e2 = n_split == 1 ? extra_lse(a, b, h0 + qh) : kNegInf;
+        const float e2 = n_split == 1 ? extra_lse<RES>(a, b, h0 + qh) : kNegInf;
         Mw = fmaxf(Mw, fmaxf(s2, e2));
         if (n_split > 1) Mw = tagged_f32(Mw);  // finite: every split has a row
 #pragma unroll
@@ -461,7 +470,7 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *s
             O0 += wt * xw[w].x; O1 += wt * xw[w].y; O2 += wt * xw[w].z; O3 += wt * xw[w].w;
         }
         Lw += rel_weight(s2, Mw);
-        if (e2 != kNegInf) {
+        if (RES == kResQ4 && e2 != kNegInf) {
             const float we = rel_weight(e2, Mw);
             const float4 xe = extra_o(a, D, b, h0 + qh, qd);
             Lw += we;
@@ -470,8 +479,8 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *s
     }
     if (n_split == 1) {
         if (tid < NQ)
-            store_final<D>(a, out + (size_t)qh * D, b, h0 + qh, qd, O0 / Lw, O1 / Lw, O2 / Lw, O3 / Lw,
-                           Mw + __log2f(Lw));
+            store_final<D, RES>(a, out + (size_t)qh * D, b, h0 + qh, qd, O0 / Lw, O1 / Lw, O2 / Lw, O3 / Lw,
+                                RES == kResDense ? Mw + __log2f(Lw) : 0.0f);
         return;
     }
     const __amdgpu_buffer_rsrc_t ws_o =
@@ -492,7 +501,7 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *s
     }
 }
 
-template <class KV, typename TQ, int D, int GT>
+template <class KV, typename TQ, int D, int GT, int RES>
 __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArgs a, DecodeGrid grid)
 {
     constexpr int EPL = D / kDecodeLPR;
@@ -505,7 +514,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
     static_assert(NF % 2 == 0 && NQ <= kDecodeThreads && kDecodeLPR == 32, "tile shape");
 
     if ((int)blockIdx.x >= grid.n_stream) {
-        merge_workgroup<TQ, D, GT>(a, (int)blockIdx.x - grid.n_stream);
+        merge_workgroup<TQ, D, GT, RES>(a, (int)blockIdx.x - grid.n_stream);
         return;
     }
 
@@ -516,7 +525,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
     int s, ht, b, n;
     if (a.kv_lens && grid.B <= kDecodePackMaxB) {
         SplitItem it;
-        if (!packed_item(a, grid.B, (int)blockIdx.x, &it)) return;
+        if (!packed_item<RES>(a, grid.B, (int)blockIdx.x, &it)) return;
         s = it.s; ht = it.ht; b = it.b;
     } else {
         s = (int)blockIdx.x % grid.gx;
@@ -524,7 +533,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
         b = (int)blockIdx.x / (grid.gx * P.HT);
     }
     int lo;  // first visible row (a window's start)
-    n = windowed(a, request_len(a, b), &lo);
+    n = windowed(a, request_len<RES>(a, b), &lo);
     const int n_split = (n + P.L - 1) / P.L;
     const int g = ht / P.ht_per_kv;
     const int h0 = g * P.G + (ht % P.ht_per_kv) * GT;
@@ -532,7 +541,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
 
     if (n == 0) {  // empty request: defined as an all-zero output
         if (s == 0) {
-            if (a.x_out_o) {  // residual pass: no rows, nothing to fold in
+            if constexpr (RES == kResDense) {  // residual pass: no rows, nothing to fold in
                 const size_t row0 = (size_t)b * a.Hq + h0;
                 for (int idx = tid; idx < GT * D; idx += kDecodeThreads) a.x_out_o[row0 * D + idx] = 0.0f;
                 if (tid < GT) a.x_out_lse[row0 + tid] = kNegInf;
@@ -707,8 +716,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
     }
     __syncthreads();
 
-    finish_split<TQ, D, GT>(a, &so[0][0][0], &sm[0][0], &sl[0][0], col, s, n_split, out, h0);
-    if (n_split > 1) merge_tile<TQ, D, GT>(a, col, n_split, own, decision, 0, ticket);
+    finish_split<TQ, D, GT, RES>(a, &so[0][0][0], &sm[0][0], &sl[0][0], col, s, n_split, out, h0);
+    if (n_split > 1) merge_tile<TQ, D, GT, RES>(a, col, n_split, own, decision, 0, ticket);
 }
 
 // Sum over the lanes of a wave that share lane % CPW (CPW a power of two
@@ -732,7 +741,7 @@ template <int CPW> __device__ __forceinline__ float colgroup_sum(float x)
 // split j) and leaves them and their maximum in LDS; each wave then forms
 // its weights and sums its lanes with cross-lane steps.
 //
-template <typename TQ, int D, int GT>
+template <typename TQ, int D, int GT, int RES>
 __device__ void merge_head(const DecodeArgs &a, int m)
 {
     constexpr int D4 = D / 4;                     // 4-wide output columns
@@ -756,7 +765,7 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     const int ht = col % P.HT;
     const int b = col / P.HT;
     int lo;
-    const int n = windowed(a, request_len(a, b), &lo);
+    const int n = windowed(a, request_len<RES>(a, b), &lo);
     const int n_split = (n + P.L - 1) / P.L;
     if (n_split <= 1) return;  // written directly by the streaming workgroup
     const int g = ht / P.ht_per_kv;
@@ -825,11 +834,11 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     __syncthreads();
     if (!s_go) {  // not reachable (see the file header); never pass silently
         const float nan = __builtin_nanf("");
-        if (sg == 0) store_final<D>(a, out, b, h, d4 * 4, nan, nan, nan, nan, nan);
+        if (sg == 0) store_final<D, RES>(a, out, b, h, d4 * 4, nan, nan, nan, nan, nan);
         return;
     }
     const float s2 = sink_log2(a, h);
-    const float e2 = extra_lse(a, b, h);
+    const float e2 = extra_lse<RES>(a, b, h);
     const float M = fmaxf(fmaxf(s_M, s2), e2);
     float Ls = 0.0f;
     float4 R = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -851,13 +860,14 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     R.z = colgroup_sum<CPW>(R.z);
     R.w = colgroup_sum<CPW>(R.w);
     if (sg == 0) {
-        if (e2 != kNegInf) {
+        if (RES == kResQ4 && e2 != kNegInf) {
             const float we = rel_weight(e2, M);
             const float4 xe = extra_o(a, D, b, h, d4 * 4);
             Ls += we;
             R.x += we * xe.x; R.y += we * xe.y; R.z += we * xe.z; R.w += we * xe.w;
         }
-        store_final<D>(a, out, b, h, d4 * 4, R.x / Ls, R.y / Ls, R.z / Ls, R.w / Ls, M + __log2f(Ls));
+        store_final<D, RES>(a, out, b, h, d4 * 4, R.x / Ls, R.y / Ls, R.z / Ls, R.w / Ls,
+                            RES == kResDense ? M + __log2f(Ls) : 0.0f);
     }
 }
 
@@ -868,7 +878,7 @@ __device__ void merge_head(const DecodeArgs &a, int m)
 // add (thread ticket_tid holds the result; kNoTicket if it completed no
 // group) counted the last group, the heads whose designated mergers
 // decided before that.
-template <typename TQ, int D, int GT>
+template <typename TQ, int D, int GT, int RES>
 __device__ void merge_tile(const DecodeArgs &a, int col, int n_split, unsigned own_heads, unsigned decision,
                            int ticket_tid, unsigned ticket)
 {
@@ -894,21 +904,21 @@ __device__ void merge_tile(const DecodeArgs &a, int col, int n_split, unsigned o
     __syncthreads();
     const unsigned heads = s_heads;
     for (int hh = 0; hh < GT; ++hh)
-        if (heads & (1u << hh)) merge_head<TQ, D, GT>(a, col * GT + hh);
+        if (heads & (1u << hh)) merge_head<TQ, D, GT, RES>(a, col * GT + hh);
 }
 
 // A merge workgroup (placed after every split in the grid): the designated
 // merger of item m = (request, head tile) * GT + head.  Thread 0 waits a
 // bounded time for the tile word to count every group (it waits for starts
 // only that long), then decides with its one add.
-template <typename TQ, int D, int GT>
+template <typename TQ, int D, int GT, int RES>
 __device__ void merge_workgroup(const DecodeArgs &a, int m)
 {
     __shared__ int s_go;
     const int col = m / GT, hh = m % GT;
     const int b = col / a.plan.HT;
     int lo;
-    const int n = windowed(a, request_len(a, b), &lo);
+    const int n = windowed(a, request_len<RES>(a, b), &lo);
     const int n_split = (n + a.plan.L - 1) / a.plan.L;
     if (n_split <= 1) return;  // written directly by the streaming workgroup
     if (threadIdx.x == 0) {
@@ -924,7 +934,7 @@ __device__ void merge_workgroup(const DecodeArgs &a, int m)
         s_go = (old & kTwGroups) == n_groups ? 1 : 0;
     }
     __syncthreads();
-    if (s_go) merge_head<TQ, D, GT>(a, m);
+    if (s_go) merge_head<TQ, D, GT, RES>(a, m);
 }
 
 // ===========================================================================
@@ -1008,7 +1018,7 @@ __device__ __forceinline__ q4f16x8_t q4_operand(uint32_t w)
     return __builtin_bit_cast(q4f16x8_t, x);
 }
 
-template <int D, int G, int GT>
+template <int D, int G, int GT, int RES>
 __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a, DecodeGrid grid)
 {
     typedef Q4Stage<D, G> S;
@@ -1019,7 +1029,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
     static_assert(GT <= 16 && G % 32 == 0 && D % G == 0, "tile shape");
 
     if ((int)blockIdx.x >= grid.n_stream) {
-        merge_workgroup<f16_t, D, GT>(a, (int)blockIdx.x - grid.n_stream);
+        merge_workgroup<f16_t, D, GT, RES>(a, (int)blockIdx.x - grid.n_stream);
         return;
     }
 
@@ -1032,7 +1042,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
     const int b = (int)blockIdx.x / (grid.gx * P.HT);
 
     int lo;
-    const int n = windowed(a, request_len(a, b), &lo);
+    const int n = windowed(a, request_len<RES>(a, b), &lo);
     const int n_split = (n + P.L - 1) / P.L;
     const int g = ht / P.ht_per_kv;
     const int h0 = g * P.G + (ht % P.ht_per_kv) * GT;
@@ -1042,7 +1052,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
         if (s == 0) {
             const size_t row0 = (size_t)b * a.Hq + h0;
             for (int idx = tid; idx < GT * D; idx += kDecodeThreads)
-                store_elem(out + idx, a.x_in_o ? a.x_in_o[row0 * D + idx] : 0.0f);
+                store_elem(out + idx, RES == kResQ4 ? a.x_in_o[row0 * D + idx] : 0.0f);
         }
         return;
     }
@@ -1322,8 +1332,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
         }
     }
     __syncthreads();
-    finish_split<f16_t, D, GT, SOD>(a, so, sm, sl, col, s, n_split, out, h0);
-    if (n_split > 1) merge_tile<f16_t, D, GT>(a, col, n_split, own, decision, 0, ticket);
+    finish_split<f16_t, D, GT, RES, SOD>(a, so, sm, sl, col, s, n_split, out, h0);
+    if (n_split > 1) merge_tile<f16_t, D, GT, RES>(a, col, n_split, own, decision, 0, ticket);
 }
 
 // ---------------------------------------------------------------------------
@@ -1345,28 +1355,28 @@ static int decode_grid(int B, int GT, const DecodeArgs &a, DecodeGrid *g)
     return several && !g->inplace ? B * a.plan.HT * GT : 0;
 }
 
-template <class KV, typename TQ, int D, int GT>
+template <class KV, typename TQ, int D, int GT, int RES>
 static hipError_t launch_one(int B, const DecodeArgs &a, hipStream_t stream)
 {
     DecodeGrid g;
     const int n_merge = decode_grid(B, GT, a, &g);
-    hipLaunchKernelGGL((decode_splitk_kernel<KV, TQ, D, GT>), dim3(g.n_stream + n_merge), dim3(kDecodeThreads), 0,
-                       stream, a, g);
+    hipLaunchKernelGGL((decode_splitk_kernel<KV, TQ, D, GT, RES>), dim3(g.n_stream + n_merge), dim3(kDecodeThreads),
+                       0, stream, a, g);
     return hipGetLastError();
 }
 
-template <class KV, typename TQ, int D>
+template <class KV, typename TQ, int D, int RES>
 static hipError_t dispatch_gt(int B, const DecodeArgs &a, hipStream_t s)
 {
     switch (a.plan.GT) {
-    case 1: return launch_one<KV, TQ, D, 1>(B, a, s);
-    case 2: return launch_one<KV, TQ, D, 2>(B, a, s);
-    case 3: return launch_one<KV, TQ, D, 3>(B, a, s);
-    case 4: return launch_one<KV, TQ, D, 4>(B, a, s);
-    case 5: return launch_one<KV, TQ, D, 5>(B, a, s);
-    case 6: return launch_one<KV, TQ, D, 6>(B, a, s);
-    case 7: return launch_one<KV, TQ, D, 7>(B, a, s);
-    case 8: return launch_one<KV, TQ, D, 8>(B, a, s);
+    case 1: return launch_one<KV, TQ, D, 1, RES>(B, a, s);
+    case 2: return launch_one<KV, TQ, D, 2, RES>(B, a, s);
+    case 3: return launch_one<KV, TQ, D, 3, RES>(B, a, s);
+    case 4: return launch_one<KV, TQ, D, 4, RES>(B, a, s);
+    case 5: return launch_one<KV, TQ, D, 5, RES>(B, a, s);
+    case 6: return launch_one<KV, TQ, D, 6, RES>(B, a, s);
+    case 7: return launch_one<KV, TQ, D, 7, RES>(B, a, s);
+    case 8: return launch_one<KV, TQ, D, 8, RES>(B, a, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1374,11 +1384,18 @@ static hipError_t dispatch_gt(int B, const DecodeArgs &a, hipStream_t s)
 template <typename T, int D>
 static hipError_t dispatch_dense(int B, const DecodeArgs &a, hipStream_t s)
 {
-    return dispatch_gt<DenseKV<T, D>, T, D>(B, a, s);
+    return dispatch_gt<DenseKV<T, D>, T, D, kResNone>(B, a, s);
 }
 
 hipError_t launch_decode(int dtype, int D, int B, const DecodeArgs &a, hipStream_t s)
 {
+    if (a.len_mode == kResDense) {  // the float16 residual of a 4-bit cache
+        if (dtype != 2 || !a.x_out_o || !a.x_out_lse) return hipErrorInvalidValue;
+        if (D == 128) return dispatch_gt<DenseKV<f16_t, 128>, f16_t, 128, kResDense>(B, a, s);
+        if (D == 64) return dispatch_gt<DenseKV<f16_t, 64>, f16_t, 64, kResDense>(B, a, s);
+        return hipErrorInvalidValue;
+    }
+    if (a.len_mode != kResNone) return hipErrorInvalidValue;
     if (D == 128) {
         if (dtype == 0) return dispatch_dense<float, 128>(B, a, s);
         if (dtype == 1) return dispatch_dense<bf16_t, 128>(B, a, s);
@@ -1391,30 +1408,41 @@ hipError_t launch_decode(int dtype, int D, int B, const DecodeArgs &a, hipStream
     return hipErrorInvalidValue;
 }
 
-template <int D, int G, int GT>
+template <int D, int G, int GT, int RES>
 static hipError_t launch_q4(int B, const DecodeArgs &a, hipStream_t stream)
 {
     DecodeGrid g;
     const int n_merge = decode_grid(B, GT, a, &g);
-    hipLaunchKernelGGL((decode_q4_kernel<D, G, GT>), dim3(g.n_stream + n_merge), dim3(kDecodeThreads), 0, stream, a,
-                       g);
+    hipLaunchKernelGGL((decode_q4_kernel<D, G, GT, RES>), dim3(g.n_stream + n_merge), dim3(kDecodeThreads), 0,
+                       stream, a, g);
     return hipGetLastError();
+}
+
+template <int D, int G, int RES>
+static hipError_t dispatch_q4_gt(int B, const DecodeArgs &a, hipStream_t s)
+{
+    switch (a.plan.GT) {
+    case 1: return launch_q4<D, G, 1, RES>(B, a, s);
+    case 2: return launch_q4<D, G, 2, RES>(B, a, s);
+    case 3: return launch_q4<D, G, 3, RES>(B, a, s);
+    case 4: return launch_q4<D, G, 4, RES>(B, a, s);
+    case 5: return launch_q4<D, G, 5, RES>(B, a, s);
+    case 6: return launch_q4<D, G, 6, RES>(B, a, s);
+    case 7: return launch_q4<D, G, 7, RES>(B, a, s);
+    case 8: return launch_q4<D, G, 8, RES>(B, a, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <int D, int G>
 static hipError_t dispatch_q4(int B, const DecodeArgs &a, hipStream_t s)
 {
-    switch (a.plan.GT) {
-    case 1: return launch_q4<D, G, 1>(B, a, s);
-    case 2: return launch_q4<D, G, 2>(B, a, s);
-    case 3: return launch_q4<D, G, 3>(B, a, s);
-    case 4: return launch_q4<D, G, 4>(B, a, s);
-    case 5: return launch_q4<D, G, 5>(B, a, s);
-    case 6: return launch_q4<D, G, 6>(B, a, s);
-    case 7: return launch_q4<D, G, 7>(B, a, s);
-    case 8: return launch_q4<D, G, 8>(B, a, s);
-    default: return hipErrorInvalidValue;
+    if (a.len_mode == kResQ4) {  // the 4-bit rows of a residual-window cache
+        if (!a.x_in_o || !a.x_in_lse) return hipErrorInvalidValue;
+        return dispatch_q4_gt<D, G, kResQ4>(B, a, s);
     }
+    if (a.len_mode != kResNone) return hipErrorInvalidValue;
+    return dispatch_q4_gt<D, G, kResNone>(B, a, s);
 }
 
 hipError_t launch_decode_q4(int D, int group, int B, const DecodeArgs &a, hipStream_t s)

@@ -334,6 +334,41 @@ int gqa_prefill_causal_ex(const void *q, const void *k, const void *v, void *out
                                      sinks, cus, (hipStream_t)stream));
 }
 
+int gqa_prefill_causal_q4r(const void *q, const uint8_t *k_codes, const void *k_scales, const void *k_biases,
+                           const uint8_t *v_codes, const void *v_scales, const void *v_biases, const void *k_res,
+                           const void *v_res, void *out, int B, int Hq, int Hkv, int D, int group_size, int R, int Tq,
+                           int Tk, int s_cap, float scale, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!q || !k_codes || !k_scales || !k_biases || !v_codes || !v_scales || !v_biases || !k_res || !v_res || !out)
+        return GQA_ERR_NULL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return GQA_ERR_SHAPE;
+    if (Tq < 1 || Tq > Tk || Tk > s_cap) return GQA_ERR_SHAPE;
+    if (!std::isfinite(scale)) return GQA_ERR_SHAPE;
+    if (D != 64 && D != 128) return GQA_ERR_UNSUPPORTED;
+    if (group_size != 32 && group_size != 64 && group_size != 128) return GQA_ERR_UNSUPPORTED;
+    if (D % group_size != 0 || !q4r_residual_ok(D, R)) return GQA_ERR_SHAPE;
+    if (Tq > 1024 * 128 || (long)B * Hq * 1024 >= (1L << 31)) return GQA_ERR_SHAPE;
+    if ((size_t)(s_cap + 512) * D * 2 >= ((size_t)1 << 31) || (size_t)(R + 512) * D * 2 >= ((size_t)1 << 31))
+        return GQA_ERR_SHAPE;
+    const int cus = plan_cus();
+    const size_t need = prefill_workspace_bytes(B, Hq, D, Tq, Tk, 0, cus);
+    if (!workspace || workspace_bytes < need) return GQA_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(k_scales) || !aligned16(k_biases) ||
+        !aligned16(v_scales) || !aligned16(v_biases) || !aligned16(k_res) || !aligned16(v_res) || !aligned16(out) ||
+        !aligned16(workspace))
+        return GQA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    Q4Source src;
+    src.k_codes = k_codes; src.v_codes = v_codes;
+    src.k_scales = (const uint16_t *)k_scales; src.k_biases = (const uint16_t *)k_biases;
+    src.v_scales = (const uint16_t *)v_scales; src.v_biases = (const uint16_t *)v_biases;
+    src.n_q = Tk - Tk % R;
+    src.group = group_size;
+    src.s_cap = s_cap;
+    return hip_status(launch_prefill_q4r(D, q, k_res, v_res, out, B, Hq, Hkv, Tq, Tk, R, scale, workspace, src, cus,
+                                         (hipStream_t)stream));
+}
+
 int gqa_prefill_causal(const void *q, const void *k, const void *v, void *out, int B, int Hq, int Hkv, int D,
                        int Tq, int Tk, int s_cap, float scale, int dtype, void *workspace, size_t workspace_bytes,
                        void *stream)

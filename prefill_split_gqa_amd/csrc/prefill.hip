@@ -203,15 +203,15 @@ __device__ __forceinline__ float softmax_max(const f32x16_t (&st)[2], f32x16_t (
     return m_run == -kInf ? 0.0f : -fabsf(qs) * m_run;
 }
 
-template <typename T, int D, bool NEG>
-__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2))) void prefill_causal_kernel(const uint16_t *__restrict__ q,
+template <typename T, int D, bool NEG, bool Q4 = false>
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? (Q4 ? 3 : 4) : 2))) void prefill_causal_kernel(const uint16_t *__restrict__ q,
                                                                     const uint16_t *__restrict__ k,
                                                                     const uint16_t *__restrict__ v,
                                                                     uint16_t *__restrict__ out, int Hq, int Hkv,
                                                                     int Tq, int Tk, int s_cap, float qscale,
                                                                     int n_rb, unsigned char *__restrict__ ws,
                                                                     int B, int window, const float *__restrict__ sinks,
-                                                                    PfItems items)
+                                                                    PfItems items, Q4Source q4)
 {
     typedef MfmaOps<T> Ops;
     typedef typename Ops::vec vec;
@@ -275,10 +275,13 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D ==
     const uint16_t *qh = q + ((size_t)b * Hq + h) * (size_t)Tq * D;
     const uint16_t *kh = k + ((size_t)b * Hkv + g) * (size_t)s_cap * D;
     const uint16_t *vh = v + ((size_t)b * Hkv + g) * (size_t)s_cap * D;
+    // With a 4-bit cache, k and v hold the float16 residual: key position
+    // p >= n_q is its row p - n_q.
+    const int row_base = Q4 ? q4.n_q : 0;
     // rows at or past Tq (queries) and Tk (keys) read as zeros
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qh, (size_t)Tq * D * 2);
-    const BufDesc dk = buf_desc(kh, (size_t)Tk * D * 2);
-    const BufDesc dv = buf_desc(vh, (size_t)Tk * D * 2);
+    const BufDesc dk = buf_desc(kh, (size_t)(Tk - row_base) * D * 2);
+    const BufDesc dv = buf_desc(vh, (size_t)(Tk - row_base) * D * 2);
 
     // Q rows of this wave as MFMA B operands: lane (row ln, group lg) holds
     // dims [16*kb + 8*lg, +8) of its row.
@@ -306,11 +309,89 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D ==
         dma_lds[ii] = (unsigned)(uintptr_t)(lds_void_t *)(smem + (loads_v ? 2 : 0) * L::TILE +
                                                           (row_first >> 3) * L::GROUP + (row_first & 7) * L::ROW);
     }
-    auto issue_tile_loads = [&](int kt, int buf) {
-        const int toff = kt * kPfBN * D * 2;
+    auto issue_dma = [&](int kt, int buf) {
+        const int toff = (kt * kPfBN - row_base) * D * 2;
 #pragma unroll
         for (int ii = 0; ii < IPW; ++ii)
             lds_load16(loads_v ? dv : dk, dma_lds[ii] + buf * L::TILE, dma_voff[ii] + toff);
+    };
+
+    // ---- 4-bit tiles: HBM -> registers -> dequantized f16 in LDS ----
+    // Tiles below n_q (a multiple of the tile) are 4-bit.  Their codes,
+    // scales and biases are loaded into registers when the tile's loads are
+    // issued, and dequantized (s * c + b in fp32, one rounding, then to f16)
+    // into the tile buffer at the end of the step, in the layout the DMA
+    // path writes.  Thread t handles 8-element chunks t + 256 i of the tile
+    // (16 consecutive threads cover one row's codes, coalesced).
+    constexpr int QCPT = Q4 ? D / 32 : 1;  // chunks per thread and tile (K or V)
+    constexpr int QLPR = D / 8;            // chunks per row
+    const int q4_ng = Q4 ? D / q4.group : 1;
+    const int q4_gshift = Q4 ? __builtin_ctz((unsigned)q4.group / 8u) : 0;  // chunk -> group
+    // (without a 4-bit cache these resources are empty and never used)
+    const size_t q4_head = Q4 ? ((size_t)b * Hkv + g) * (size_t)q4.s_cap : 0;
+    const size_t q4_nq = Q4 ? (size_t)q4.n_q : 0;
+    auto q4_rsrc = [&](const void *base, size_t per_row) {
+        return Q4 ? make_rsrc((const char *)base + q4_head * per_row, q4_nq * per_row) : make_rsrc(kh, 0);
+    };
+    const __amdgpu_buffer_rsrc_t rkc = q4_rsrc(q4.k_codes, D / 2), rvc = q4_rsrc(q4.v_codes, D / 2);
+    const __amdgpu_buffer_rsrc_t rks = q4_rsrc(q4.k_scales, q4_ng * 2), rkb = q4_rsrc(q4.k_biases, q4_ng * 2);
+    const __amdgpu_buffer_rsrc_t rvs = q4_rsrc(q4.v_scales, q4_ng * 2), rvb = q4_rsrc(q4.v_biases, q4_ng * 2);
+    // (scales and biases stay in registers of their own: combining them
+    // at issue would wait for the loads there)
+    uint32_t qk_w[QCPT], qv_w[QCPT];
+    uint32_t qk_s[QCPT], qk_b[QCPT], qv_s[QCPT], qv_b[QCPT];
+    bool q4_pending = false;
+    auto issue_q4 = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < QCPT; ++i) {
+            const int c = tid + 256 * i;
+            const int row = kt * kPfBN + c / QLPR, cc = c % QLPR;
+            const int coff = row * (D / 2) + cc * 4;
+            const int soff = (row * q4_ng + (cc >> q4_gshift)) * 2;
+            qk_w[i] = __builtin_amdgcn_raw_buffer_load_b32(rkc, coff, 0, 0);
+            qv_w[i] = __builtin_amdgcn_raw_buffer_load_b32(rvc, coff, 0, 0);
+            qk_s[i] = __builtin_amdgcn_raw_buffer_load_b16(rks, soff, 0, 0);
+            qk_b[i] = __builtin_amdgcn_raw_buffer_load_b16(rkb, soff, 0, 0);
+            qv_s[i] = __builtin_amdgcn_raw_buffer_load_b16(rvs, soff, 0, 0);
+            qv_b[i] = __builtin_amdgcn_raw_buffer_load_b16(rvb, soff, 0, 0);
+        }
+    };
+    auto commit_q4 = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < QCPT; ++i) {
+            const int c = tid + 256 * i;
+            const int row = c / QLPR, cc = c % QLPR;
+#pragma unroll
+            for (int which = 0; which < 2; ++which) {
+                const uint32_t w = which ? qv_w[i] : qk_w[i];
+                const float sc = f16_bits_to_f32(which ? qv_s[i] : qk_s[i]);
+                const float bi = f16_bits_to_f32(which ? qv_b[i] : qk_b[i]);
+                f32x8_t x;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(sc, (float)((w >> (4 * e)) & 15u), bi);
+                *(uint4 *)(smem + (2 * which + buf) * L::TILE + tile_off<D>(row, cc)) = MfmaOps<f16_t>::pack8(x);
+            }
+        }
+    };
+    auto issue_tile_loads = [&](int kt, int buf) {
+        if constexpr (Q4) {
+            if (kt * kPfBN < row_base) {
+                issue_q4(kt);
+                q4_pending = true;
+                return;
+            }
+        }
+        issue_dma(kt, buf);
+    };
+    // end of a step: a 4-bit tile whose loads were issued goes into buffer buf
+    auto finish_tile_loads = [&](int buf) {
+        if constexpr (Q4) {
+            if (q4_pending) {
+                commit_q4(buf);
+                q4_pending = false;
+            }
+        }
+        (void)buf;
     };
 
     f32x16_t acc[NDB];
@@ -448,16 +529,19 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D ==
     // computed from the other buffer; the step ends by waiting for its own
     // loads and a barrier.
     if (n > 0) issue_tile_loads(t_begin, 0);
+    finish_tile_loads(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int s = 0; s < n; s += 2) {  // unrolled by two: buffer indices are constants
         issue_tile_loads(t_begin + s + 1, 1);
         if (t_begin + s < w_end && t_begin + s >= w_begin) tile_step(t_begin + s, 0);
+        finish_tile_loads(1);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (s + 1 < n) {
             issue_tile_loads(t_begin + s + 2, 0);
             if (t_begin + s + 1 < w_end && t_begin + s + 1 >= w_begin) tile_step(t_begin + s + 1, 1);
+            finish_tile_loads(0);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
@@ -708,10 +792,10 @@ size_t prefill_workspace_bytes(int B, int Hq, int D, int Tq, int Tk, int window,
     return kWsFlagBytes + (p.max_nc > 1 ? split_cols * p.max_nc * slot : 0);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool Q4 = false>
 static hipError_t launch_pf(const void *q, const void *k, const void *v, void *out, int B, int Hq, int Hkv,
                             int Tq, int Tk, int s_cap, float scale, void *ws, int window, const float *sinks,
-                            int n_cus, hipStream_t s)
+                            int n_cus, hipStream_t s, Q4Source src = Q4Source{})
 {
     const PfPlan plan = pf_plan(B, Hq, D, Tq, Tk, window, n_cus);
     PfItems items;
@@ -724,13 +808,13 @@ static hipError_t launch_pf(const void *q, const void *k, const void *v, void *o
     if (qscale == 0.0f) qscale = 1.17549435e-38f;
     dim3 grid((unsigned)(items.n * B * Hq));
     if (qscale < 0.0f)
-        hipLaunchKernelGGL((prefill_causal_kernel<T, D, true>), grid, dim3(kPfThreads), 0, s, (const uint16_t *)q,
-                           (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)out, Hq, Hkv, Tq, Tk, s_cap,
-                           qscale, plan.n_rb, (unsigned char *)ws, B, window, sinks, items);
+        hipLaunchKernelGGL((prefill_causal_kernel<T, D, true, Q4>), grid, dim3(kPfThreads), 0, s,
+                           (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)out, Hq, Hkv,
+                           Tq, Tk, s_cap, qscale, plan.n_rb, (unsigned char *)ws, B, window, sinks, items, src);
     else
-        hipLaunchKernelGGL((prefill_causal_kernel<T, D, false>), grid, dim3(kPfThreads), 0, s, (const uint16_t *)q,
-                           (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)out, Hq, Hkv, Tq, Tk, s_cap,
-                           qscale, plan.n_rb, (unsigned char *)ws, B, window, sinks, items);
+        hipLaunchKernelGGL((prefill_causal_kernel<T, D, false, Q4>), grid, dim3(kPfThreads), 0, s,
+                           (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)out, Hq, Hkv,
+                           Tq, Tk, s_cap, qscale, plan.n_rb, (unsigned char *)ws, B, window, sinks, items, src);
     return hipGetLastError();
 }
 
@@ -747,6 +831,19 @@ hipError_t launch_prefill(int dtype, int D, const void *q, const void *k, const 
         if (D == 128) return GQA_PF(f16_t, 128);
     }
 #undef GQA_PF
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_q4r(int D, const void *q, const void *k_res, const void *v_res, void *out, int B, int Hq,
+                              int Hkv, int Tq, int Tk, int R, float scale, void *ws, const Q4Source &src, int n_cus,
+                              hipStream_t s)
+{
+    if (D == 64)
+        return launch_pf<f16_t, 64, true>(q, k_res, v_res, out, B, Hq, Hkv, Tq, Tk, R, scale, ws, 0, nullptr, n_cus, s,
+                                          src);
+    if (D == 128)
+        return launch_pf<f16_t, 128, true>(q, k_res, v_res, out, B, Hq, Hkv, Tq, Tk, R, scale, ws, 0, nullptr, n_cus,
+                                           s, src);
     return hipErrorInvalidValue;
 }
 

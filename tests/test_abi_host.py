@@ -281,3 +281,20 @@ def test_q4r_validation(lib):
     assert app(group=48) == gqa.GQA_ERR_UNSUPPORTED
     assert app(D=96) == gqa.GQA_ERR_UNSUPPORTED
     assert app(res=FAKE_ODD) == gqa.GQA_ERR_ALIGN
+
+    wsp = gqa.gqa_prefill_workspace_bytes(1, 14, 2, 64, 256, 4097)
+
+    def pf(res=FAKE, R=128, group=32, D=64, Tq=256, Tk=4097, s_cap=4097, ws_bytes=wsp, out=FAKE):
+        return lib.gqa_prefill_causal_q4r(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, res, FAKE, out, 1, 14, 2, D, group,
+                                          R, Tq, Tk, s_cap, ctypes.c_float(0.125), FAKE, ws_bytes, NULL)
+
+    assert pf(res=NULL) == gqa.GQA_ERR_NULL
+    assert pf(out=NULL) == gqa.GQA_ERR_NULL
+    assert pf(Tq=4098) == gqa.GQA_ERR_SHAPE
+    assert pf(s_cap=4000) == gqa.GQA_ERR_SHAPE
+    assert pf(R=100) == gqa.GQA_ERR_SHAPE
+    assert pf(group=128) == gqa.GQA_ERR_SHAPE                         # group larger than D
+    assert pf(group=16) == gqa.GQA_ERR_UNSUPPORTED
+    assert pf(D=96) == gqa.GQA_ERR_UNSUPPORTED
+    assert pf(ws_bytes=0) == gqa.GQA_ERR_WORKSPACE
+    assert pf(res=FAKE_ODD) == gqa.GQA_ERR_ALIGN

@@ -13,6 +13,12 @@
   decode over the residual; a cache grown one token at a time across a
   flush matches the oracle at every step; the 4-bit decode workload's
   geometry at 16k keys.
+* gqa_prefill_causal_q4r: a chunk of queries at the end of each request's
+  tokens, causal, over 4-bit and residual rows (chunks that start inside the
+  4-bit rows, a whole prompt, one query, an empty residual) within the f16
+  bound; with no 4-bit rows bit-identical to gqa_prefill_causal over the
+  residual; the pages' 256-query chunk after 3841 tokens on the 0.5B
+  geometry.
 """
 
 import numpy as np
@@ -197,3 +203,59 @@ def test_decode_q4_workload_geometry_16k(gpu_lib):
     note("q4r decode %d/%d heads, D=%d, n=%d (n_q=%d n_r=%d)" % (Hq, H, D, n, n_q, n_r))
     got = _decode(gpu_lib, dev, q.cuda(), [n], group, gpu_lib.make_q4r_workspace(1, Hq, H, D, s_cap, R))
     assert_close(got, oracle.q4r_attend(q, st, [n], group, R), TOL_16, "q4r 16k")
+
+
+def _prefill(gpu_lib, dev, q, Tk, group, scale=None):
+    out = torch.empty_like(q)
+    gpu_lib.gqa_prefill_causal_q4r(q, dev["k_codes"], dev["k_scales"], dev["k_biases"], dev["v_codes"],
+                                   dev["v_scales"], dev["v_biases"], dev["k_res"], dev["v_res"], out, group, Tk,
+                                   scale=scale)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("D,group,R,Tk,Tq", [(64, 32, 64, 229, 100), (128, 64, 128, 700, 700), (128, 128, 64, 640, 77),
+                                             (64, 64, 192, 1000, 1), (128, 32, 64, 385, 385)])
+def test_prefill_chunk_over_q4r_cache(gpu_lib, D, group, R, Tk, Tq):
+    rng = np.random.default_rng(D + group + R + Tk + Tq)
+    B, Hq, H, s_cap = 2, 4, 2, Tk + 64
+    st = _grown_state(rng, B, H, s_cap, D, group, R, [Tk, Tk])
+    dev = _to_dev(st)
+    q = torch.from_numpy((rng.standard_normal((B, Hq, Tq, D)) * 0.8).astype(np.float16)).cuda()
+    n_q, n_r = oracle.q4r_split(Tk, R)
+    note("q4r prefill D=%d group=%d R=%d Tk=%d Tq=%d (n_q=%d n_r=%d)" % (D, group, R, Tk, Tq, n_q, n_r))
+    got = _prefill(gpu_lib, dev, q, Tk, group)
+    want = oracle.q4r_attend(q.cpu(), st, [Tk, Tk], group, R, causal=True)
+    assert_close(got, want, TOL_16, "q4r prefill Tk=%d Tq=%d" % (Tk, Tq))
+
+
+def test_prefill_without_4bit_rows_is_the_f16_prefill(gpu_lib):
+    rng = np.random.default_rng(41)
+    B, Hq, H, D, group, R = 1, 4, 2, 128, 64, 256
+    Tk, Tq = 200, 120  # Tk < R: every token in the residual
+    st = _grown_state(rng, B, H, 512, D, group, R, [Tk])
+    dev = _to_dev(st)
+    q = torch.from_numpy(rng.standard_normal((B, Hq, Tq, D)).astype(np.float16)).cuda()
+    note("q4r prefill == f16 prefill Tk=%d Tq=%d" % (Tk, Tq))
+    got = _prefill(gpu_lib, dev, q, Tk, group)
+    ref = torch.empty_like(q)
+    gpu_lib.gqa_prefill_causal(q, dev["k_res"], dev["v_res"], ref, gpu_lib.make_prefill_workspace(B, Hq, H, D, Tq, Tk),
+                               Tk)
+    torch.cuda.synchronize()
+    assert_close(got, oracle.q4r_attend(q.cpu(), st, [Tk], group, R, causal=True), TOL_16, "q4r prefill no 4-bit")
+    assert torch.equal(got, ref)
+
+
+def test_prefill_chunk_at_3841_of_4097(gpu_lib):
+    # the pages' chunked-prefill case (256 queries after 3841 tokens) on
+    # the 0.5B geometry, over a 4-bit cache with a 128-row residual
+    w = W.by_name("prefill_0p5b")
+    rng = np.random.default_rng(43)
+    Hq, H, D, group, R = w.Hq, w.Hkv, w.D, 32, 128
+    Tk, Tq = 4097, 256
+    st = _grown_state(rng, 1, H, Tk, D, group, R, [Tk])
+    dev = _to_dev(st)
+    q = torch.from_numpy(rng.standard_normal((1, Hq, Tq, D)).astype(np.float16)).cuda()
+    note("q4r prefill chunk Tk=%d Tq=%d heads %d/%d D=%d" % (Tk, Tq, Hq, H, D))
+    got = _prefill(gpu_lib, dev, q, Tk, group)
+    assert_close(got, oracle.q4r_attend(q.cpu(), st, [Tk], group, R, causal=True), TOL_16, "q4r chunk at 3841")
