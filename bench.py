@@ -306,7 +306,8 @@ def hbm_entry(us, nbytes, gate_ok, gate_max_abs, kernel, traffic=None, **extra):
 
 EXTRAS = ("decode_7b_sweep", "prefill_0p5b_T513", "prefill_0p5b_T2049", "decode_0p5b_s128", "batched_qwen3_4b",
           "q4_decode_s2048", "q4_decode_s16384", "prefill_0p5b_chunk256_at3841", "append_7b_s4096",
-          "append_q4_s16384", "naive_decode_7b_s4096", "naive_prefill_0p5b_t4097")
+          "append_q4_s16384", "q4r_decode_s16448_r128", "q4r_prefill_0p5b_chunk256_at3841_r128",
+          "append_q4r_r128", "naive_decode_7b_s4096", "naive_prefill_0p5b_t4097")
 
 
 def bench_extra(torch, gqa, oracle, W, steps, warmup, flush, names=EXTRAS):
@@ -335,6 +336,12 @@ def bench_extra(torch, gqa, oracle, W, steps, warmup, flush, names=EXTRAS):
         out.update(extra_append_dense(torch, gqa, oracle, W, steps, warmup, flush))
     if "append_q4_s16384" in names:
         out.update(extra_append_q4(torch, gqa, oracle, W, steps, warmup, flush))
+    if "q4r_decode_s16448_r128" in names:
+        out.update(extra_q4r_decode(torch, gqa, oracle, W, steps, warmup, flush))
+    if "q4r_prefill_0p5b_chunk256_at3841_r128" in names:
+        out.update(extra_q4r_prefill(torch, gqa, oracle, W, steps, warmup, flush))
+    if "append_q4r_r128" in names:
+        out.update(extra_append_q4r(torch, gqa, oracle, W, steps, warmup, flush))
     if "naive_decode_7b_s4096" in names:
         out.update(naive_decode(torch, oracle, W, steps, warmup, flush))
     if "naive_prefill_0p5b_t4097" in names:
@@ -583,6 +590,163 @@ def extra_append_q4(torch, gqa, oracle, W, steps, warmup, flush, S=16384):
     nbytes = 2 * w.Hkv * (w.D * 2 + w.D // 2 + 2 * 2 * G)  # f16 rows read; codes, scales, biases written
     return {"append_q4_s16384": hbm_entry(us, nbytes, bool(ok), 0.0 if ok else None, "kv_append_q4_kernel<f16_t,128,64>",
                                           layers_per_step=layers, bit_exact=bool(ok))}
+
+
+Q4R_NAMES = ("k_codes", "k_scales", "k_biases", "v_codes", "v_scales", "v_biases", "k_res", "v_res")
+
+
+def _q4r_layers(torch, d0, layers):
+    """Device copies of one residual-window cache state, one per layer
+    (codes permuted, float values scaled), so that every layer reads its own
+    memory."""
+    dev = [d0]
+    for l in range(1, layers):
+        dl = {}
+        for n, t in d0.items():
+            dl[n] = (t ^ (l & 0xFF)) if t.dtype == torch.uint8 else (t * (1.0 + l / 64.0)).contiguous()
+        dev.append(dl)
+    return dev
+
+
+def extra_q4r_decode(torch, gqa, oracle, W, steps, warmup, flush, n=16448, R=128):
+    """Decode over a 4-bit cache with a float16 residual window (the 64/8-head
+    workload, group 64, 80 layers): 16448 tokens = 16384 4-bit rows (the
+    q4_decode_s16384 cache) plus 64 float16 residual rows (R = 128).  Two
+    launches per layer: the dense kernel over the residual, then the 4-bit
+    kernel, which folds the residual's result into its merge."""
+    w = W.by_name("q4_decode")
+    rng = np.random.default_rng(16448)
+    n_q, n_r = oracle.q4r_split(n, R)
+    s_cap = n_q + R  # capacity for the request's positions; rows past n_q are never read
+    x = W.q4_inputs(w, n_q, 0, s_cap=s_cap)
+    st = {k: x[k] for k in Q4R_NAMES[:6]}
+    st["k_res"] = torch.from_numpy(rng.standard_normal((1, w.Hkv, R, w.D)).astype(np.float16))
+    st["v_res"] = torch.from_numpy(rng.standard_normal((1, w.Hkv, R, w.D)).astype(np.float16))
+    q = x["q"]
+    dev = _q4r_layers(torch, {k: v.cuda() for k, v in st.items()}, w.layers)
+    qs = [(q.cuda() * (1.0 + l / 64.0)).contiguous() for l in range(w.layers)]
+    outs = [torch.empty_like(qs[0]) for _ in dev]
+    lens = torch.tensor([n], dtype=torch.int32, device="cuda")
+    ws = gqa.make_q4r_workspace(1, w.Hq, w.Hkv, w.D, s_cap, R)
+
+    def eager():
+        for dl, qq, oo in zip(dev, qs, outs):
+            gqa.gqa_decode_attend_q4r(qq, *(dl[k] for k in Q4R_NAMES), oo, w.group, lens, ws)
+
+    eager()
+    torch.cuda.synchronize()
+    stn = {k: v.numpy() for k, v in st.items()}
+    want = oracle.q4r_attend(q, stn, [n], w.group, R)
+    err = float(np.abs(outs[0].float().cpu().double().numpy() - want).max())
+    ref = [t.clone() for t in outs]
+    g = graph_of(torch, eager)
+    us = float(np.median(time_steps(torch, g.replay, steps, warmup, flush))) * 1e3 / w.layers
+    ok = err <= 2e-2 and all(torch.equal(a, b) for a, b in zip(outs, ref))
+    nbytes = (n_q * w.Hkv * 2 * (w.D // 2 + 2 * 2 * (w.D // w.group)) + n_r * w.Hkv * 2 * w.D * 2
+              + 2 * w.Hq * w.D * 2)
+    return {"q4r_decode_s16448_r128": hbm_entry(
+        us, nbytes, ok, err, "decode_splitk_kernel<DenseKV<f16_t,128>,f16_t,128,8,2> + decode_q4_kernel<128,64,8,1>",
+        layers_per_step=w.layers, n_q=n_q, n_r=n_r, launches_per_layer=2)}
+
+
+def extra_q4r_prefill(torch, gqa, oracle, W, steps, warmup, flush, Tk=4097, Tq=256, R=128, group=32):
+    """Chunked prefill over a residual-window 4-bit cache: the last 256 queries
+    of a 4097-token prompt on the 0.5B geometry (14/2 heads, D = 64, f16),
+    the cache holding 4096 4-bit rows (group 32) and 1 float16 residual row;
+    24 layers.  Parity: sampled chunk rows against the oracle over the
+    cache's values."""
+    w = W.by_name("prefill_0p5b")
+    rng = np.random.default_rng(3841)
+    k = rng.standard_normal((1, w.Hkv, Tk, w.D)).astype(np.float16)
+    v = rng.standard_normal((1, w.Hkv, Tk, w.D)).astype(np.float16)
+    st = {"k_codes": np.zeros((1, w.Hkv, Tk, w.D // 2), np.uint8), "v_codes": np.zeros((1, w.Hkv, Tk, w.D // 2), np.uint8),
+          "k_scales": np.zeros((1, w.Hkv, Tk, w.D // group), np.float16),
+          "k_biases": np.zeros((1, w.Hkv, Tk, w.D // group), np.float16),
+          "v_scales": np.zeros((1, w.Hkv, Tk, w.D // group), np.float16),
+          "v_biases": np.zeros((1, w.Hkv, Tk, w.D // group), np.float16),
+          "k_res": np.zeros((1, w.Hkv, R, w.D), np.float16), "v_res": np.zeros((1, w.Hkv, R, w.D), np.float16)}
+    st, _ = oracle.kv_append_q4r(st, k, v, [0], group, R)
+    q = rng.standard_normal((1, w.Hq, Tq, w.D)).astype(np.float16)
+    dev = _q4r_layers(torch, {n: torch.from_numpy(t).cuda() for n, t in st.items()}, 24)
+    qs = [(torch.from_numpy(q).cuda() * (1.0 + l / 64.0)).contiguous() for l in range(24)]
+    outs = [torch.empty_like(qs[0]) for _ in dev]
+    ws = gqa.make_prefill_workspace(1, w.Hq, w.Hkv, w.D, Tq, Tk)
+
+    def eager():
+        for dl, qq, oo in zip(dev, qs, outs):
+            gqa.gqa_prefill_causal_q4r(qq, *(dl[n] for n in Q4R_NAMES), oo, group, Tk, ws)
+
+    eager()
+    torch.cuda.synchronize()
+    kv, vv = oracle.q4r_view(st, [Tk], group, R)
+    rows = sorted(set([0, 1, Tq - 1] + list(np.random.default_rng(257).integers(0, Tq, 13))))
+    err = 0.0
+    for i in rows:
+        n_vis = Tk - Tq + i + 1
+        want = oracle.attend(q[:, :, i:i + 1], kv[:, :, :n_vis], vv[:, :, :n_vis], scale=w.scale())
+        err = max(err, float(np.abs(outs[0][:, :, i:i + 1].float().cpu().double().numpy() - want).max()))
+    ref = [t.clone() for t in outs]
+    g = graph_of(torch, eager)
+    us = float(np.median(time_steps(torch, g.replay, steps, warmup, flush))) * 1e3 / len(dev)
+    flops = prefill_flops(Tq, Tk)
+    tf = flops / (us * 1e-6) / 1e12
+    return {"q4r_prefill_0p5b_chunk256_at3841_r128": {
+        "us": round(us, 2), "layers_per_step": len(dev), "TFLOPs": round(tf, 2),
+        "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": "prefill_causal_kernel<f16_t,64,false,true>", "achieved": round(tf, 1),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flop_per_launch": flops, "launch_duration_us": round(us, 2)},
+        "parity_ok": err <= 2e-2 and all(torch.equal(a, b) for a, b in zip(outs, ref)), "parity_max_abs": err}}
+
+
+def extra_append_q4r(torch, gqa, oracle, W, steps, warmup, flush, R=128):
+    """The residual-window 4-bit append before a decode step of the 64/8-head
+    workload, 80 layers, one new f16 token per layer: at 16447 tokens (the
+    row joins the residual, no encoding) and at 16511 tokens (the residual
+    fills: its 128 rows are encoded as a block).  Parity: every array equals
+    the oracle's append bit for bit (layer 0)."""
+    w = W.by_name("q4_decode")
+    rng = np.random.default_rng(16511)
+    G = w.D // w.group
+    s_cap = 16640
+    out = {}
+    for name, n in (("append_q4r_r128", 16447), ("append_q4r_r128_flush", 16511)):
+        st = {"k_codes": rng.integers(0, 256, (1, w.Hkv, s_cap, w.D // 2), dtype=np.uint8),
+              "v_codes": rng.integers(0, 256, (1, w.Hkv, s_cap, w.D // 2), dtype=np.uint8),
+              "k_scales": rng.random((1, w.Hkv, s_cap, G)).astype(np.float16),
+              "k_biases": rng.random((1, w.Hkv, s_cap, G)).astype(np.float16),
+              "v_scales": rng.random((1, w.Hkv, s_cap, G)).astype(np.float16),
+              "v_biases": rng.random((1, w.Hkv, s_cap, G)).astype(np.float16),
+              "k_res": rng.standard_normal((1, w.Hkv, R, w.D)).astype(np.float16),
+              "v_res": rng.standard_normal((1, w.Hkv, R, w.D)).astype(np.float16)}
+        kn = rng.standard_normal((1, w.Hkv, 1, w.D)).astype(np.float16)
+        vn = rng.standard_normal((1, w.Hkv, 1, w.D)).astype(np.float16)
+        want, _ = oracle.kv_append_q4r(st, kn, vn, [n], w.group, R)
+        dev = _q4r_layers(torch, {k: torch.from_numpy(v).cuda() for k, v in st.items()}, w.layers)
+        knd, vnd = torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda()
+        lens = torch.tensor([n], dtype=torch.int32, device="cuda")
+        new_lens = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+        def eager(dev=dev):
+            for dl in dev:
+                gqa.gqa_kv_append_q4r(knd, vnd, *(dl[k] for k in Q4R_NAMES), w.group, lens, new_lens)
+
+        eager()
+        torch.cuda.synchronize()
+        ok = all(np.array_equal(dev[0][k].cpu().numpy().view(np.uint8), want[k].view(np.uint8)) for k in Q4R_NAMES)
+        ok = ok and int(new_lens.cpu()[0]) == n + 1
+        g = graph_of(torch, eager)
+        us = float(np.median(time_steps(torch, g.replay, steps, warmup, flush))) * 1e3 / w.layers
+        n_q0, n_r0 = oracle.q4r_split(n, R)
+        n_q1, _ = oracle.q4r_split(n + 1, R)
+        aged = n_q1 - n_q0
+        # new f16 rows read; aged rows read from the residual and encoded; kept rows written
+        nbytes = 2 * w.Hkv * (w.D * 2 + aged * (w.D * 2 + w.D // 2 + 2 * 2 * G) + (1 if aged == 0 else 0) * w.D * 2)
+        out[name] = hbm_entry(us, nbytes, bool(ok), 0.0 if ok else None, "kv_append_q4r_kernel<128,64>",
+                              layers_per_step=w.layers, bit_exact=bool(ok), tokens_before=n, rows_encoded=aged)
+        del dev
+        torch.cuda.empty_cache()
+    return out
 
 
 def time_eager(torch, run, steps, warmup, flush):

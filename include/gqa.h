@@ -395,8 +395,11 @@ int gqa_decode_attend_q4r(const void *q,
  * into the 4-bit arrays with the quantizer of gqa_kv_append_q4 (from the
  * residual, or straight from the new rows that age at once) and positions
  * [max(n, n_q(n')), n') are copied to their residual slots; other rows and
- * slots are left unchanged.  One workgroup per (request, KV head) encodes
- * before it copies, so the update is exact whatever T_new is.  new_lens
+ * slots are left unchanged.  Several workgroups per (request, KV head)
+ * share the encoding; when the copies would overwrite residual slots that
+ * the encoding reads (a flush that keeps new rows, old residual not empty),
+ * one workgroup encodes and then copies, so the update is exact whatever
+ * T_new is.  new_lens
  * must not be kv_lens.  Requires D in {64, 128}, group_size in
  * {32, 64, 128} dividing D, R a positive multiple of 64, T_new >= 1,
  * finite inputs, 16-byte aligned pointers.

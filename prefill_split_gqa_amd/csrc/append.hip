@@ -25,9 +25,10 @@
 //    n_q).  New float16 rows join the residual; when it fills, its rows and
 //    any new rows that age at once are encoded as one block (the VeloxQuant
 //    posts, "What this means in practice": a production KIVI cache keeps the
-//    recent tokens in float16).  One workgroup per (request, KV head) encodes
-//    the aged rows first and, after a barrier, writes the new residual rows,
-//    so a slot is read before it is overwritten.
+//    recent tokens in float16).  Several workgroups per (request, KV head)
+//    share the encoding; a slot that is both read (aged) and rewritten (new)
+//    in one append is handled by a single workgroup, read before a barrier
+//    and written after it.
 //
 // All are bound by HBM (a few hundred KB per call at the workloads' sizes);
 // one lane handles 8 consecutive elements of a row (one 16-byte load of
@@ -35,6 +36,8 @@
 // maximum with butterfly shuffles, and each lane writes its 8 codes as one
 // 32-bit word.  Device lengths are read by every lane that needs them; the
 // host cannot check them, so they are clamped.
+
+#include <algorithm>
 
 #include "common.h"
 
@@ -196,13 +199,18 @@ __global__ __launch_bounds__(256) void kv_append_q4_kernel(const void *__restric
     }
 }
 
-// Residual-window append: one workgroup per (request b, KV head).  With n
-// the request's tokens before and n2 after the append, positions [n_q(n),
-// n_q(n2)) are encoded (from residual slot p - n_q(n) while p < n, else
-// from new row p - n), then positions [max(n, n_q(n2)), n2) are copied to
-// residual slot p - n_q(n2).  Rows are spread over the workgroup's lanes,
-// D/8 lanes per row; a lane past the last row of a pass shadows the row
-// before it and stores nothing.
+// Residual-window append: workgroups (request b, KV head, j), j < NB.  With
+// n the request's tokens before and n2 after the append, positions
+// [n_q(n), n_q(n2)) are encoded (from residual slot p - n_q(n) while p < n,
+// else from new row p - n), then positions [max(n, n_q(n2)), n2) are copied
+// to residual slot p - n_q(n2).  The copies overwrite slots the encoding
+// reads only when a flush keeps new rows in the residual and the old
+// residual was not empty (an append of several rows); then workgroup j = 0
+// does both in order, with a barrier between, and the others stop.
+// Otherwise the NB workgroups share the encoding row by row and j = 0 also
+// copies.  Rows are spread over a workgroup's lanes, D/8 lanes per row; a
+// lane past the last row of a pass shadows the row before it and stores
+// nothing.
 template <int D, int G>
 __global__ __launch_bounds__(256) void kv_append_q4r_kernel(const f16_t *__restrict__ k_new, const f16_t *__restrict__ v_new,
                                                             uint8_t *__restrict__ k_codes, uint16_t *__restrict__ k_scales,
@@ -219,11 +227,15 @@ __global__ __launch_bounds__(256) void kv_append_q4r_kernel(const f16_t *__restr
     constexpr int RPP = 256 / LPR;  // rows per pass
     static_assert(LPR <= 64 && (64 % LPR) == 0 && (LPG & (LPG - 1)) == 0 && LPG <= LPR, "lane layout");
     const int bh = (int)blockIdx.x;
+    const int j = (int)blockIdx.y, nb = (int)gridDim.y;
     const int b = bh / Hkv;
     const int n = clamp_len(kv_lens[b], s_cap);
     const int n2 = min(n + T_new, s_cap);
     const int nq_old = n - n % R, nq_new = n2 - n2 % R;
-    if (new_lens && threadIdx.x == 0 && bh % Hkv == 0) new_lens[b] = n2;
+    const bool ordered = nq_new > nq_old && n > nq_old && n2 > nq_new;
+    if (ordered && j != 0) return;
+    const int step = ordered ? 1 : nb;  // passes of this workgroup: j, j + step, ...
+    if (new_lens && j == 0 && threadIdx.x == 0 && bh % Hkv == 0) new_lens[b] = n2;
     const int lane8 = (int)threadIdx.x % LPR;
     const int rsub = (int)threadIdx.x / LPR;
     const size_t res0 = (size_t)bh * R;        // residual row of slot 0
@@ -231,7 +243,7 @@ __global__ __launch_bounds__(256) void kv_append_q4r_kernel(const f16_t *__restr
     const size_t cache0 = (size_t)bh * s_cap;  // cache row of position 0
 
     // aged rows -> 4-bit
-    for (int p0 = nq_old; p0 < nq_new; p0 += RPP) {
+    for (int p0 = nq_old + j * RPP; p0 < nq_new; p0 += step * RPP) {
         const bool live = p0 + rsub < nq_new;
         const int p = live ? p0 + rsub : nq_new - 1;
 #pragma unroll
@@ -252,7 +264,8 @@ __global__ __launch_bounds__(256) void kv_append_q4r_kernel(const f16_t *__restr
             }
         }
     }
-    __syncthreads();  // every aged residual slot has been read
+    if (j != 0) return;
+    __syncthreads();  // (ordered) every aged residual slot has been read
 
     // new rows that stay float16 -> residual
     const int keep0 = max(n, nq_new);
@@ -303,8 +316,12 @@ hipError_t launch_q4r_append_d(const void *kn, const void *vn, uint8_t *kc, void
                                void *vb, void *kr, void *vr, const int32_t *lens, int32_t *new_lens, int B, int Hkv,
                                int group, int R, int T_new, int s_cap, hipStream_t st)
 {
+    // workgroups per (request, KV head): enough passes for the most rows one
+    // append can encode (a full residual plus the new rows), at most 64
+    const long rows = (long)R + T_new;
+    const unsigned nb = (unsigned)std::min<long>(64, (rows + 256 / (D / 8) - 1) / (256 / (D / 8)));
 #define GQA_Q4R(G)                                                                                                 \
-    hipLaunchKernelGGL((kv_append_q4r_kernel<D, G>), dim3(B * Hkv), dim3(256), 0, st, (const f16_t *)kn,          \
+    hipLaunchKernelGGL((kv_append_q4r_kernel<D, G>), dim3(B * Hkv, nb), dim3(256), 0, st, (const f16_t *)kn,      \
                        (const f16_t *)vn, kc, (uint16_t *)ks, (uint16_t *)kb, vc, (uint16_t *)vs, (uint16_t *)vb, \
                        (uint4 *)kr, (uint4 *)vr, lens, new_lens, Hkv, T_new, s_cap, R)
     if (group == 32) GQA_Q4R(32);

@@ -134,6 +134,15 @@ unsigned char *scratch_address(hipStream_t stream)
 // the two plans.  Returns the bytes needed; *off_o, *off_lse their places.
 bool q4r_residual_ok(int D, int R) { return R >= 64 && R % 64 == 0 && (size_t)R * D * 4 < ((size_t)1 << 31); }
 
+// The residual pass reads at most R rows per KV head: one split per (request,
+// head tile), so that its result needs no cross-split merge (a merge costs
+// more than streaming a few hundred rows on one CU).
+bool plan_residual(int B, int Hq, int Hkv, int D, int R, DecodePlan *p)
+{
+    if (!make_decode_plan(B, Hq, Hkv, D, R, kDecodeTargetWGs, 1, p)) return false;
+    return p->HT <= 65535 && p->n_split_max == 1 && p->bytes < ((size_t)1 << 31);
+}
+
 size_t q4r_layout(const DecodePlan &pq, const DecodePlan &pr, int B, int Hq, int D, size_t *off_o, size_t *off_lse)
 {
     const size_t o = align_up(pq.bytes > pr.bytes ? pq.bytes : pr.bytes, 256);
@@ -410,7 +419,7 @@ size_t gqa_decode_q4r_workspace_bytes(int B, int Hq, int Hkv, int D, int s_cap, 
 {
     if ((D != 64 && D != 128) || !q4r_residual_ok(D, R)) return 0;
     DecodePlan pq, pr;
-    if (!plan_decode(B, Hq, Hkv, D, s_cap, &pq) || !plan_decode(B, Hq, Hkv, D, R, &pr)) return 0;
+    if (!plan_decode(B, Hq, Hkv, D, s_cap, &pq) || !plan_residual(B, Hq, Hkv, D, R, &pr)) return 0;
     return q4r_layout(pq, pr, B, Hq, D, nullptr, nullptr);
 }
 
@@ -425,7 +434,7 @@ int gqa_decode_attend_q4r(const void *q, const uint8_t *k_codes, const void *k_s
     if (int st = check_decode_common(q, k_codes, v_codes, out, B, Hq, Hkv, D, s_cap, scale, workspace,
                                      workspace_bytes, &pq))
         return st;
-    if (!q4r_residual_ok(D, R) || !plan_decode(B, Hq, Hkv, D, R, &pr)) return GQA_ERR_SHAPE;
+    if (!q4r_residual_ok(D, R) || !plan_residual(B, Hq, Hkv, D, R, &pr)) return GQA_ERR_SHAPE;
     if (group_size != 32 && group_size != 64 && group_size != 128) return GQA_ERR_UNSUPPORTED;
     if (D % group_size != 0) return GQA_ERR_SHAPE;
     size_t off_o = 0, off_lse = 0;
