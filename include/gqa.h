@@ -370,13 +370,13 @@ size_t gqa_decode_q4r_workspace_bytes(int B, int Hq, int Hkv, int D, int s_cap, 
  * Decode over a residual-window 4-bit cache: attention of q [B, Hq, 1, D]
  * f16 over every token of each request, the 4-bit rows dequantized as in
  * gqa_decode_attend_q4 and the residual rows as they are; out [B, Hq, 1, D]
- * f16.  Two launches on `stream`: the residual rows go through the dense
- * decode kernel, whose normalised float32 output and log-sum-exp per query
- * head (kept in the workspace) then join the 4-bit kernel's split merge as
- * one more partial.  A request with no tokens gets zeros.  Requires D in
- * {64, 128}, group_size in {32, 64, 128} dividing D, and a zero-initialised
- * workspace of gqa_decode_q4r_workspace_bytes (calls leave it as they found
- * it, so it is reused without clearing).
+ * f16.  One launch: the 4-bit rows are split as in gqa_decode_attend_q4,
+ * and the residual rows of each (request, head tile) are one more split,
+ * streamed as float16 rows by the dense decode path and merged with the
+ * others.  A request with no tokens gets zeros.  Requires D in {64, 128},
+ * group_size in {32, 64, 128} dividing D, and a zero-initialised workspace
+ * of gqa_decode_q4r_workspace_bytes (calls leave it as they found it, so it
+ * is reused without clearing).
  */
 int gqa_decode_attend_q4r(const void *q,
                           const uint8_t *k_codes, const void *k_scales, const void *k_biases,

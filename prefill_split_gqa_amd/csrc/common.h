@@ -200,8 +200,10 @@ constexpr int kCtrlWords = 1 + kDecodeMaxSplits / kSplitGroup;
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// extra_splits: splits per (request, head tile) beyond those of the rows
+// (a residual-window cache's float16 residual is one).
 inline bool make_decode_plan(int B, int Hq, int Hkv, int D, int s_cap, int target_wgs, int max_splits,
-                             DecodePlan *p)
+                             DecodePlan *p, int extra_splits = 0)
 {
     if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || s_cap < 1 || Hq % Hkv || target_wgs < 1 || max_splits < 1)
         return false;
@@ -211,7 +213,7 @@ inline bool make_decode_plan(int B, int Hq, int Hkv, int D, int s_cap, int targe
         if (p->G % t == 0) { p->GT = t; break; }
     p->ht_per_kv = p->G / p->GT;
     p->HT = Hkv * p->ht_per_kv;
-    long ns = target_wgs / p->HT;
+    long ns = target_wgs / p->HT - extra_splits;  // the extra splits count against the target
     if (ns < 1) ns = 1;
     if (ns > max_splits) ns = max_splits;
     const long rows = kDecodeRowGroups;
@@ -223,7 +225,7 @@ inline bool make_decode_plan(int B, int Hq, int Hkv, int D, int s_cap, int targe
     // 32 two-row splits 8.41 us per layer).
     if (per < 2 && (s_cap + 2 * rows - 1) / (2 * rows) >= p->GT) per = 2;
     p->L = (int)(per * rows);
-    p->n_split_max = (int)((s_cap + p->L - 1) / p->L);
+    p->n_split_max = (int)((s_cap + p->L - 1) / p->L) + extra_splits;
     const size_t parts = (size_t)B * p->HT * p->n_split_max * p->GT;  // (request, query head, split)
     p->ml_bytes = parts * 2 * 4;
     p->off_ctrl = align_up(p->ml_bytes, 128);
@@ -256,17 +258,11 @@ struct DecodeArgs {
     unsigned *poison;        // the workspace's poison word
     size_t ws_bytes;
     int n_cus;               // compute units of the device (launch shape)
-    // A 4-bit cache with a float16 residual window of res_cap rows: a
-    // request of n tokens (clamped to len_cap) holds n - n % res_cap rows
-    // 4-bit and n % res_cap rows in the residual.  len_mode 1: this launch
-    // sees the 4-bit rows; 2: the residual rows; 0: plain lengths.
-    int len_mode, len_cap, res_cap;
-    // Residual pass: instead of `out`, the normalised float32 output
-    // [B][Hq][D] and its log2-domain log-sum-exp [B][Hq] (units of qscale
-    // times the score; -inf for no rows).
-    float *x_out_o, *x_out_lse;
-    // 4-bit pass: that pair, folded in as one more partial (or nullptr).
-    const float *x_in_o, *x_in_lse;
+    // A 4-bit cache with a float16 residual window (res_cap > 0 rows per KV
+    // head in k_res / v_res): a request of n tokens (clamped to s_cap) holds
+    // n - n % res_cap rows 4-bit and n % res_cap rows in the residual.
+    int res_cap;
+    const void *k_res, *v_res;
 };
 
 // Launchers (defined in the .hip files; return a hipError_t).

@@ -112,9 +112,9 @@ struct DenseKV {
     struct Src {
         __amdgpu_buffer_rsrc_t rs;  // rows [0, end) of this (request, KV head)
     };
-    __device__ __forceinline__ static Src make_src(const DecodeArgs &a, bool is_v, size_t head_row0, int end, int)
+    __device__ __forceinline__ static Src make_src(const void *base, size_t head_row0, int end)
     {
-        return Src{make_rsrc((const T *)(is_v ? a.v : a.k) + head_row0 * D, (size_t)end * ROW)};
+        return Src{make_rsrc((const T *)base + head_row0 * D, (size_t)end * ROW)};
     }
 
     __device__ __forceinline__ static void load(Raw &r, const Src &s, int row, int lr)
@@ -238,55 +238,43 @@ struct DecodeGrid {
 // Rows of request b that its query sees: its length (device lengths are
 // clamped to [0, s_cap]); with a window, only the last `window` of them,
 // which start at row *lo.
-// What a launch reads of a residual-window 4-bit cache (a compile-time
-// mode, so that plain launches carry none of it): kResNone a plain cache;
-// kResQ4 the 4-bit rows, folding in the residual pass's result; kResDense
-// the float16 residual rows, writing that result.
-enum ResMode { kResNone = 0, kResQ4 = 1, kResDense = 2 };
+// The cache a launch reads (a compile-time mode, so that plain launches
+// carry none of it): kResNone a plain cache; kResQ4 a 4-bit cache with a
+// float16 residual window, whose residual rows are one more split.
+enum ResMode { kResNone = 0, kResQ4 = 1 };
 
+// Rows of request b the splits of length L cover (with a residual window:
+// its 4-bit rows, whole blocks of the residual's size).
 template <int RES>
 __device__ __forceinline__ int request_len(const DecodeArgs &a, int b)
 {
     int n = a.kv_len;
     if (a.kv_lens) {
-        const int cap = RES != kResNone ? a.len_cap : a.s_cap;
         n = a.kv_lens[b];
-        n = n < 0 ? 0 : (n > cap ? cap : n);
+        n = n < 0 ? 0 : (n > a.s_cap ? a.s_cap : n);
     }
-    if constexpr (RES == kResQ4) n -= n % a.res_cap;  // whole blocks of the residual's size are 4-bit
-    if constexpr (RES == kResDense) n %= a.res_cap;   // the rest is float16
+    if constexpr (RES == kResQ4) n -= n % a.res_cap;
     return n;
 }
 
-// Final output of query head h of request b, 4 values at column d, with
-// the head's log2-domain log-sum-exp lse (taken from the lane with d = 0):
-// to the row `orow` of `out`, or, in the residual pass, to its float32
-// output and log-sum-exp arrays.
-template <int D, int RES, typename TQ>
-__device__ __forceinline__ void store_final(const DecodeArgs &a, TQ *orow, int b, int h, int d, float x0, float x1,
-                                            float x2, float x3, float lse)
+// Float16 residual rows of request b (kResQ4): the rest of its tokens.
+__device__ __forceinline__ int residual_rows(const DecodeArgs &a, int b)
 {
-    if constexpr (RES == kResDense) {
-        const size_t row = (size_t)b * a.Hq + h;
-        *(float4 *)(a.x_out_o + row * D + d) = make_float4(x0, x1, x2, x3);
-        if (d == 0) a.x_out_lse[row] = lse;
-    } else {
-        store4(orow + d, x0, x1, x2, x3);
-    }
+    int n = a.kv_lens[b];
+    n = n < 0 ? 0 : (n > a.s_cap ? a.s_cap : n);
+    return n % a.res_cap;
 }
 
-// The residual pass's result for query head h of request b as one more
-// partial of the 4-bit pass: its log-sum-exp (-inf when there is none or
-// the residual is empty).
-template <int RES> __device__ __forceinline__ float extra_lse(const DecodeArgs &a, int b, int h)
+// Splits of request b, whose split-covered rows are n: pieces of L rows, and
+// with a residual window one more for the residual rows if there are any.
+template <int RES>
+__device__ __forceinline__ int request_splits(const DecodeArgs &a, int b, int n)
 {
-    if constexpr (RES == kResQ4) return a.x_in_lse[(size_t)b * a.Hq + h];
-    return kNegInf;
+    const int ns = (n + a.plan.L - 1) / a.plan.L;
+    if constexpr (RES == kResQ4) return ns + (residual_rows(a, b) > 0 ? 1 : 0);
+    return ns;
 }
-__device__ __forceinline__ float4 extra_o(const DecodeArgs &a, int D, int b, int h, int d)
-{
-    return *(const float4 *)(a.x_in_o + ((size_t)b * a.Hq + h) * D + d);
-}
+
 __device__ __forceinline__ int windowed(const DecodeArgs &a, int n, int *lo)
 {
     *lo = a.window > 0 && n > a.window ? n - a.window : 0;
@@ -443,7 +431,6 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *s
     const DecodePlan &P = a.plan;
     const int tid = threadIdx.x;
     const int qh = tid / (D / 4), qd = (tid % (D / 4)) * 4;
-    const int b = RES != kResNone ? col / P.HT : 0;
     float Mw = kNegInf, Lw = 0.0f, O0 = 0.0f, O1 = 0.0f, O2 = 0.0f, O3 = 0.0f;
     if (tid < NQ) {
         // every read first, then the arithmetic
@@ -457,11 +444,10 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *s
         }
 #pragma unroll
         for (int w = 0; w < NW; ++w) Mw = fmaxf(Mw, mw[w]);
-        // a single split normalises here, sink and residual partial
-        // included; several publish their partials and the merge adds them
+        // a single split normalises here, sink included; several publish
+        // their partials and the merge adds the sink
         const float s2 = n_split == 1 ? sink_log2(a, h0 + qh) : kNegInf;
-        const float e2 = n_split == 1 ? extra_lse<RES>(a, b, h0 + qh) : kNegInf;
-        Mw = fmaxf(Mw, fmaxf(s2, e2));
+        Mw = fmaxf(Mw, s2);
         if (n_split > 1) Mw = tagged_f32(Mw);  // finite: every split has a row
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
@@ -470,17 +456,9 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *s
             O0 += wt * xw[w].x; O1 += wt * xw[w].y; O2 += wt * xw[w].z; O3 += wt * xw[w].w;
         }
         Lw += rel_weight(s2, Mw);
-        if (RES == kResQ4 && e2 != kNegInf) {
-            const float we = rel_weight(e2, Mw);
-            const float4 xe = extra_o(a, D, b, h0 + qh, qd);
-            Lw += we;
-            O0 += we * xe.x; O1 += we * xe.y; O2 += we * xe.z; O3 += we * xe.w;
-        }
     }
     if (n_split == 1) {
-        if (tid < NQ)
-            store_final<D, RES>(a, out + (size_t)qh * D, b, h0 + qh, qd, O0 / Lw, O1 / Lw, O2 / Lw, O3 / Lw,
-                                RES == kResDense ? Mw + __log2f(Lw) : 0.0f);
+        if (tid < NQ) store4(out + (size_t)qh * D + qd, O0 / Lw, O1 / Lw, O2 / Lw, O3 / Lw);
         return;
     }
     const __amdgpu_buffer_rsrc_t ws_o =
@@ -501,8 +479,15 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *s
     }
 }
 
+// One split of a dense KV cache (or of a 4-bit cache's float16 residual):
+// rows [start, end) of the KV head whose row 0 is row head_row0 of kbase /
+// vbase, for query heads h0 .. h0 + GT - 1 of request b (head tile ht);
+// split s of the (request, head tile)'s n_split.  Streams the rows,
+// publishes the split's partial and takes part in the merge.
 template <class KV, typename TQ, int D, int GT, int RES>
-__global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArgs a, DecodeGrid grid)
+__device__ __forceinline__ void dense_split(const DecodeArgs &a, const DecodeGrid &grid, const void *kbase,
+                                            const void *vbase, size_t head_row0, int s, int n_split, int start,
+                                            int end, int b, int ht, int h0, TQ *out)
 {
     constexpr int EPL = D / kDecodeLPR;
     constexpr int RC = 2;                     // rows per row-group per chunk
@@ -513,51 +498,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
     static_assert(KV::EPL == EPL, "lane layout mismatch");
     static_assert(NF % 2 == 0 && NQ <= kDecodeThreads && kDecodeLPR == 32, "tile shape");
 
-    if ((int)blockIdx.x >= grid.n_stream) {
-        merge_workgroup<TQ, D, GT, RES>(a, (int)blockIdx.x - grid.n_stream);
-        return;
-    }
-
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, rgq = lane >> 5, lr = lane & 31;
     const int rg = wave * 2 + rgq;  // row-group (half wave) within the workgroup
     const DecodePlan &P = a.plan;
-    int s, ht, b, n;
-    if (a.kv_lens && grid.B <= kDecodePackMaxB) {
-        SplitItem it;
-        if (!packed_item<RES>(a, grid.B, (int)blockIdx.x, &it)) return;
-        s = it.s; ht = it.ht; b = it.b;
-    } else {
-        s = (int)blockIdx.x % grid.gx;
-        ht = ((int)blockIdx.x / grid.gx) % P.HT;
-        b = (int)blockIdx.x / (grid.gx * P.HT);
-    }
-    int lo;  // first visible row (a window's start)
-    n = windowed(a, request_len<RES>(a, b), &lo);
-    const int n_split = (n + P.L - 1) / P.L;
-    const int g = ht / P.ht_per_kv;
-    const int h0 = g * P.G + (ht % P.ht_per_kv) * GT;
-    TQ *out = (TQ *)a.out + ((size_t)b * a.Hq + h0) * D;
 
-    if (n == 0) {  // empty request: defined as an all-zero output
-        if (s == 0) {
-            if constexpr (RES == kResDense) {  // residual pass: no rows, nothing to fold in
-                const size_t row0 = (size_t)b * a.Hq + h0;
-                for (int idx = tid; idx < GT * D; idx += kDecodeThreads) a.x_out_o[row0 * D + idx] = 0.0f;
-                if (tid < GT) a.x_out_lse[row0 + tid] = kNegInf;
-            } else {
-                for (int idx = tid; idx < GT * D; idx += kDecodeThreads) store_elem(out + idx, 0.0f);
-            }
-        }
-        return;
-    }
-    if (s >= n_split) return;
-    const int start = s * P.L;
-    const int end = min(start + P.L, n);
-
-    const size_t head_row0 = ((size_t)b * a.Hkv + g) * (size_t)a.s_cap + lo;
-    const typename KV::Src src = KV::make_src(a, false, head_row0, end, lr);
-    const typename KV::Src srcv = KV::make_src(a, true, head_row0, end, lr);
+    const typename KV::Src src = KV::make_src(kbase, head_row0, end);
+    const typename KV::Src srcv = KV::make_src(vbase, head_row0, end);
 
     typename KV::Raw kr[2][RC], vr[2][RC];
     auto load_chunk = [&](int buf, int c0) {
@@ -720,6 +667,47 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
     if (n_split > 1) merge_tile<TQ, D, GT, RES>(a, col, n_split, own, decision, 0, ticket);
 }
 
+template <class KV, typename TQ, int D, int GT>
+__global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArgs a, DecodeGrid grid)
+{
+    constexpr int RES = kResNone;
+    if ((int)blockIdx.x >= grid.n_stream) {
+        merge_workgroup<TQ, D, GT, RES>(a, (int)blockIdx.x - grid.n_stream);
+        return;
+    }
+
+    const int tid = threadIdx.x;
+    const DecodePlan &P = a.plan;
+    int s, ht, b, n;
+    if (a.kv_lens && grid.B <= kDecodePackMaxB) {
+        SplitItem it;
+        if (!packed_item<RES>(a, grid.B, (int)blockIdx.x, &it)) return;
+        s = it.s; ht = it.ht; b = it.b;
+    } else {
+        s = (int)blockIdx.x % grid.gx;
+        ht = ((int)blockIdx.x / grid.gx) % P.HT;
+        b = (int)blockIdx.x / (grid.gx * P.HT);
+    }
+    int lo;  // first visible row (a window's start)
+    n = windowed(a, request_len<RES>(a, b), &lo);
+    const int n_split = (n + P.L - 1) / P.L;
+    const int g = ht / P.ht_per_kv;
+    const int h0 = g * P.G + (ht % P.ht_per_kv) * GT;
+    TQ *out = (TQ *)a.out + ((size_t)b * a.Hq + h0) * D;
+
+    if (n == 0) {  // empty request: defined as an all-zero output
+        if (s == 0)
+            for (int idx = tid; idx < GT * D; idx += kDecodeThreads) store_elem(out + idx, 0.0f);
+        return;
+    }
+    if (s >= n_split) return;
+    const int start = s * P.L;
+    const int end = min(start + P.L, n);
+
+    const size_t head_row0 = ((size_t)b * a.Hkv + g) * (size_t)a.s_cap + lo;
+    dense_split<KV, TQ, D, GT, RES>(a, grid, a.k, a.v, head_row0, s, n_split, start, end, b, ht, h0, out);
+}
+
 // Sum over the lanes of a wave that share lane % CPW (CPW a power of two
 // below 16): rotations by CPW, 2 CPW, ... inside each 16-lane row, then the
 // two row swaps.  Every lane of the group ends with the same value.
@@ -766,7 +754,7 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     const int b = col / P.HT;
     int lo;
     const int n = windowed(a, request_len<RES>(a, b), &lo);
-    const int n_split = (n + P.L - 1) / P.L;
+    const int n_split = request_splits<RES>(a, b, n);
     if (n_split <= 1) return;  // written directly by the streaming workgroup
     const int g = ht / P.ht_per_kv;
     const int h = g * P.G + (ht % P.ht_per_kv) * GT + hh;
@@ -833,13 +821,11 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     }
     __syncthreads();
     if (!s_go) {  // not reachable (see the file header); never pass silently
-        const float nan = __builtin_nanf("");
-        if (sg == 0) store_final<D, RES>(a, out, b, h, d4 * 4, nan, nan, nan, nan, nan);
+        if (sg == 0) store4(out + d4 * 4, __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
         return;
     }
     const float s2 = sink_log2(a, h);
-    const float e2 = extra_lse<RES>(a, b, h);
-    const float M = fmaxf(fmaxf(s_M, s2), e2);
+    const float M = fmaxf(s_M, s2);
     float Ls = 0.0f;
     float4 R = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     float2 mlk[PER];  // all (max, sum) reads first (clamped to a valid split)
@@ -859,16 +845,7 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     R.y = colgroup_sum<CPW>(R.y);
     R.z = colgroup_sum<CPW>(R.z);
     R.w = colgroup_sum<CPW>(R.w);
-    if (sg == 0) {
-        if (RES == kResQ4 && e2 != kNegInf) {
-            const float we = rel_weight(e2, M);
-            const float4 xe = extra_o(a, D, b, h, d4 * 4);
-            Ls += we;
-            R.x += we * xe.x; R.y += we * xe.y; R.z += we * xe.z; R.w += we * xe.w;
-        }
-        store_final<D, RES>(a, out, b, h, d4 * 4, R.x / Ls, R.y / Ls, R.z / Ls, R.w / Ls,
-                            RES == kResDense ? M + __log2f(Ls) : 0.0f);
-    }
+    if (sg == 0) store4(out + d4 * 4, R.x / Ls, R.y / Ls, R.z / Ls, R.w / Ls);
 }
 
 // The merges a split performs for (request, head tile) col once its own
@@ -919,7 +896,7 @@ __device__ void merge_workgroup(const DecodeArgs &a, int m)
     const int b = col / a.plan.HT;
     int lo;
     const int n = windowed(a, request_len<RES>(a, b), &lo);
-    const int n_split = (n + a.plan.L - 1) / a.plan.L;
+    const int n_split = request_splits<RES>(a, b, n);
     if (n_split <= 1) return;  // written directly by the streaming workgroup
     if (threadIdx.x == 0) {
         const unsigned n_groups = split_groups(n_split);
@@ -1043,20 +1020,28 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
 
     int lo;
     const int n = windowed(a, request_len<RES>(a, b), &lo);
-    const int n_split = (n + P.L - 1) / P.L;
+    const int n_split = request_splits<RES>(a, b, n);
     const int g = ht / P.ht_per_kv;
     const int h0 = g * P.G + (ht % P.ht_per_kv) * GT;
     f16_t *out = (f16_t *)a.out + ((size_t)b * a.Hq + h0) * D;
 
-    if (n == 0) {  // no 4-bit rows: the residual's result, or (no rows at all) zeros
-        if (s == 0) {
-            const size_t row0 = (size_t)b * a.Hq + h0;
-            for (int idx = tid; idx < GT * D; idx += kDecodeThreads)
-                store_elem(out + idx, RES == kResQ4 ? a.x_in_o[row0 * D + idx] : 0.0f);
-        }
+    if (n_split == 0) {  // empty request: defined as an all-zero output
+        if (s == 0)
+            for (int idx = tid; idx < GT * D; idx += kDecodeThreads) store_elem(out + idx, 0.0f);
         return;
     }
     if (s >= n_split) return;
+    if constexpr (RES == kResQ4) {
+        // the last split of a residual-window cache: its float16 residual
+        // rows, through the dense path (the same partial and merge)
+        const int n_r = residual_rows(a, b);
+        if (n_r > 0 && s == n_split - 1) {
+            dense_split<DenseKV<f16_t, D>, f16_t, D, GT, RES>(a, grid, a.k_res, a.v_res,
+                                                              ((size_t)b * a.Hkv + g) * (size_t)a.res_cap, s,
+                                                              n_split, 0, n_r, b, ht, h0, out);
+            return;
+        }
+    }
     const int start = s * P.L;
     const int end = min(start + P.L, n);
     const int nst = (end - start + kQ4Rows - 1) / kQ4Rows;
@@ -1355,28 +1340,28 @@ static int decode_grid(int B, int GT, const DecodeArgs &a, DecodeGrid *g)
     return several && !g->inplace ? B * a.plan.HT * GT : 0;
 }
 
-template <class KV, typename TQ, int D, int GT, int RES>
+template <class KV, typename TQ, int D, int GT>
 static hipError_t launch_one(int B, const DecodeArgs &a, hipStream_t stream)
 {
     DecodeGrid g;
     const int n_merge = decode_grid(B, GT, a, &g);
-    hipLaunchKernelGGL((decode_splitk_kernel<KV, TQ, D, GT, RES>), dim3(g.n_stream + n_merge), dim3(kDecodeThreads),
-                       0, stream, a, g);
+    hipLaunchKernelGGL((decode_splitk_kernel<KV, TQ, D, GT>), dim3(g.n_stream + n_merge), dim3(kDecodeThreads), 0,
+                       stream, a, g);
     return hipGetLastError();
 }
 
-template <class KV, typename TQ, int D, int RES>
+template <class KV, typename TQ, int D>
 static hipError_t dispatch_gt(int B, const DecodeArgs &a, hipStream_t s)
 {
     switch (a.plan.GT) {
-    case 1: return launch_one<KV, TQ, D, 1, RES>(B, a, s);
-    case 2: return launch_one<KV, TQ, D, 2, RES>(B, a, s);
-    case 3: return launch_one<KV, TQ, D, 3, RES>(B, a, s);
-    case 4: return launch_one<KV, TQ, D, 4, RES>(B, a, s);
-    case 5: return launch_one<KV, TQ, D, 5, RES>(B, a, s);
-    case 6: return launch_one<KV, TQ, D, 6, RES>(B, a, s);
-    case 7: return launch_one<KV, TQ, D, 7, RES>(B, a, s);
-    case 8: return launch_one<KV, TQ, D, 8, RES>(B, a, s);
+    case 1: return launch_one<KV, TQ, D, 1>(B, a, s);
+    case 2: return launch_one<KV, TQ, D, 2>(B, a, s);
+    case 3: return launch_one<KV, TQ, D, 3>(B, a, s);
+    case 4: return launch_one<KV, TQ, D, 4>(B, a, s);
+    case 5: return launch_one<KV, TQ, D, 5>(B, a, s);
+    case 6: return launch_one<KV, TQ, D, 6>(B, a, s);
+    case 7: return launch_one<KV, TQ, D, 7>(B, a, s);
+    case 8: return launch_one<KV, TQ, D, 8>(B, a, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1384,18 +1369,12 @@ static hipError_t dispatch_gt(int B, const DecodeArgs &a, hipStream_t s)
 template <typename T, int D>
 static hipError_t dispatch_dense(int B, const DecodeArgs &a, hipStream_t s)
 {
-    return dispatch_gt<DenseKV<T, D>, T, D, kResNone>(B, a, s);
+    return dispatch_gt<DenseKV<T, D>, T, D>(B, a, s);
 }
 
 hipError_t launch_decode(int dtype, int D, int B, const DecodeArgs &a, hipStream_t s)
 {
-    if (a.len_mode == kResDense) {  // the float16 residual of a 4-bit cache
-        if (dtype != 2 || !a.x_out_o || !a.x_out_lse) return hipErrorInvalidValue;
-        if (D == 128) return dispatch_gt<DenseKV<f16_t, 128>, f16_t, 128, kResDense>(B, a, s);
-        if (D == 64) return dispatch_gt<DenseKV<f16_t, 64>, f16_t, 64, kResDense>(B, a, s);
-        return hipErrorInvalidValue;
-    }
-    if (a.len_mode != kResNone) return hipErrorInvalidValue;
+    if (a.res_cap != 0) return hipErrorInvalidValue;
     if (D == 128) {
         if (dtype == 0) return dispatch_dense<float, 128>(B, a, s);
         if (dtype == 1) return dispatch_dense<bf16_t, 128>(B, a, s);
@@ -1437,11 +1416,10 @@ static hipError_t dispatch_q4_gt(int B, const DecodeArgs &a, hipStream_t s)
 template <int D, int G>
 static hipError_t dispatch_q4(int B, const DecodeArgs &a, hipStream_t s)
 {
-    if (a.len_mode == kResQ4) {  // the 4-bit rows of a residual-window cache
-        if (!a.x_in_o || !a.x_in_lse) return hipErrorInvalidValue;
+    if (a.res_cap > 0) {  // a residual-window cache: device lengths, residual rows
+        if (!a.kv_lens || !a.k_res || !a.v_res) return hipErrorInvalidValue;
         return dispatch_q4_gt<D, G, kResQ4>(B, a, s);
     }
-    if (a.len_mode != kResNone) return hipErrorInvalidValue;
     return dispatch_q4_gt<D, G, kResNone>(B, a, s);
 }
 

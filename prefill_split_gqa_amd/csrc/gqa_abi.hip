@@ -128,28 +128,15 @@ unsigned char *scratch_address(hipStream_t stream)
     return addr[dev];
 }
 
-// Residual-window 4-bit decode: both passes (float16 residual, then 4-bit
-// rows) share one workspace -- each leaves the words it used at zero -- and
-// the residual pass's float32 outputs and log-sum-exps follow the larger of
-// the two plans.  Returns the bytes needed; *off_o, *off_lse their places.
+// Residual-window 4-bit decode: one launch, whose splits are those of the
+// 4-bit rows plus one for the float16 residual rows (at most 63 + 1, so the
+// merge still reads every partial in one round).
 bool q4r_residual_ok(int D, int R) { return R >= 64 && R % 64 == 0 && (size_t)R * D * 4 < ((size_t)1 << 31); }
 
-// The residual pass reads at most R rows per KV head: one split per (request,
-// head tile), so that its result needs no cross-split merge (a merge costs
-// more than streaming a few hundred rows on one CU).
-bool plan_residual(int B, int Hq, int Hkv, int D, int R, DecodePlan *p)
+bool plan_q4r(int B, int Hq, int Hkv, int D, int s_cap, DecodePlan *p)
 {
-    if (!make_decode_plan(B, Hq, Hkv, D, R, kDecodeTargetWGs, 1, p)) return false;
-    return p->HT <= 65535 && p->n_split_max == 1 && p->bytes < ((size_t)1 << 31);
-}
-
-size_t q4r_layout(const DecodePlan &pq, const DecodePlan &pr, int B, int Hq, int D, size_t *off_o, size_t *off_lse)
-{
-    const size_t o = align_up(pq.bytes > pr.bytes ? pq.bytes : pr.bytes, 256);
-    const size_t l = align_up(o + (size_t)B * Hq * D * 4, 256);
-    if (off_o) *off_o = o;
-    if (off_lse) *off_lse = l;
-    return align_up(l + (size_t)B * Hq * 4, 256);
+    if (!make_decode_plan(B, Hq, Hkv, D, s_cap, kDecodeTargetWGs, kDecodeMaxSplits - 1, p, 1)) return false;
+    return p->HT <= 65535 && p->n_split_max <= kDecodeMaxSplits && p->bytes < ((size_t)1 << 31);
 }
 
 void fill_ws(DecodeArgs &a, void *ws)
@@ -418,9 +405,9 @@ int gqa_decode_attend_q4(const void *q, const uint8_t *k_codes, const void *k_sc
 size_t gqa_decode_q4r_workspace_bytes(int B, int Hq, int Hkv, int D, int s_cap, int R)
 {
     if ((D != 64 && D != 128) || !q4r_residual_ok(D, R)) return 0;
-    DecodePlan pq, pr;
-    if (!plan_decode(B, Hq, Hkv, D, s_cap, &pq) || !plan_residual(B, Hq, Hkv, D, R, &pr)) return 0;
-    return q4r_layout(pq, pr, B, Hq, D, nullptr, nullptr);
+    DecodePlan p;
+    if (!plan_q4r(B, Hq, Hkv, D, s_cap, &p)) return 0;
+    return p.bytes;
 }
 
 int gqa_decode_attend_q4r(const void *q, const uint8_t *k_codes, const void *k_scales, const void *k_biases,
@@ -430,46 +417,29 @@ int gqa_decode_attend_q4r(const void *q, const uint8_t *k_codes, const void *k_s
                           void *stream)
 {
     if (!k_scales || !k_biases || !v_scales || !v_biases || !k_res || !v_res || !kv_lens) return GQA_ERR_NULL;
-    DecodePlan pq, pr;
+    DecodePlan plan;
+    // (the common checks, with the workspace size checked against this plan below)
     if (int st = check_decode_common(q, k_codes, v_codes, out, B, Hq, Hkv, D, s_cap, scale, workspace,
-                                     workspace_bytes, &pq))
+                                     ~(size_t)0, &plan))
         return st;
-    if (!q4r_residual_ok(D, R) || !plan_residual(B, Hq, Hkv, D, R, &pr)) return GQA_ERR_SHAPE;
+    if (!q4r_residual_ok(D, R) || !plan_q4r(B, Hq, Hkv, D, s_cap, &plan)) return GQA_ERR_SHAPE;
     if (group_size != 32 && group_size != 64 && group_size != 128) return GQA_ERR_UNSUPPORTED;
     if (D % group_size != 0) return GQA_ERR_SHAPE;
-    size_t off_o = 0, off_lse = 0;
-    if (workspace_bytes < q4r_layout(pq, pr, B, Hq, D, &off_o, &off_lse)) return GQA_ERR_WORKSPACE;
+    if (workspace_bytes < plan.bytes) return GQA_ERR_WORKSPACE;
     if (!aligned16(k_scales) || !aligned16(k_biases) || !aligned16(v_scales) || !aligned16(v_biases) ||
         !aligned16(k_res) || !aligned16(v_res) || !aligned16(kv_lens))
         return GQA_ERR_ALIGN;
     int cus = 0;
     if (int st = check_device(&cus)) return st;
-    float *x_o = (float *)((char *)workspace + off_o);
-    float *x_lse = (float *)((char *)workspace + off_lse);
-    const float qscale = scale * 1.4426950408889634f;
-    // pass 1: the float16 residual rows, to float32 outputs and log-sum-exps
-    DecodeArgs r{};
-    r.n_cus = cus;
-    r.q = q; r.k = k_res; r.v = v_res; r.out = nullptr;
-    r.kv_lens = kv_lens; r.kv_len = 0;
-    r.Hq = Hq; r.Hkv = Hkv; r.s_cap = R; r.group = 0;
-    r.len_mode = 2; r.len_cap = s_cap; r.res_cap = R;
-    r.x_out_o = x_o; r.x_out_lse = x_lse;
-    r.qscale = qscale;
-    r.plan = pr;
-    fill_ws(r, workspace);
-    if (int st = hip_status(launch_decode(GQA_F16, D, B, r, (hipStream_t)stream))) return st;
-    // pass 2: the 4-bit rows, with pass 1's result folded in as one more partial
     DecodeArgs a{};
     a.n_cus = cus;
     a.q = q; a.k = k_codes; a.v = v_codes; a.out = out;
     a.k_scales = k_scales; a.k_biases = k_biases; a.v_scales = v_scales; a.v_biases = v_biases;
     a.kv_lens = kv_lens; a.kv_len = 0;
     a.Hq = Hq; a.Hkv = Hkv; a.s_cap = s_cap; a.group = group_size;
-    a.len_mode = 1; a.len_cap = s_cap; a.res_cap = R;
-    a.x_in_o = x_o; a.x_in_lse = x_lse;
-    a.qscale = qscale;
-    a.plan = pq;
+    a.res_cap = R; a.k_res = k_res; a.v_res = v_res;
+    a.qscale = scale * 1.4426950408889634f;
+    a.plan = plan;
     fill_ws(a, workspace);
     return hip_status(launch_decode_q4(D, group_size, B, a, (hipStream_t)stream));
 }

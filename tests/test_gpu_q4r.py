@@ -133,6 +133,8 @@ def test_decode_ragged_lengths(gpu_lib, D, group, R):
 @pytest.mark.parametrize("D,group,R", [(128, 64, 128), (64, 32, 64)])
 def test_decode_reduces_to_plain_kernels(gpu_lib, D, group, R):
     rng = np.random.default_rng(17 + D + R)
+    # (at these sizes both plans cut the rows into the same splits; the
+    # residual-window plan keeps one more for the residual)
     Hq, H, s_cap = 8, 2, 8 * R
     # empty residual (n a multiple of R): bit-identical to the plain 4-bit decode
     n = 5 * R
