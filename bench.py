@@ -50,12 +50,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 matrix peak (256 CU x 2.4 GHz x 4096 FLOP/clk)
 PAGES_M2_US_PER_LAYER_7B_S4096 = 264.82  # Apple M2 fused Metal SDPA (context only)
 DECODE_SRCS = [os.path.join(ROOT, "prefill_split_gqa_amd", "csrc", f) for f in ("decode.hip", "common.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_7b_s4096_traffic.txt")
 PREFILL_SRCS = [os.path.join(ROOT, "prefill_split_gqa_amd", "csrc", f) for f in ("prefill.hip", "common.h")]
-PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_0p5b_t4097_traffic.txt")
-PREFILL_COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_0p5b_t4097_counters.txt")
-Q4_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4_decode_s16384_traffic.txt")
-BATCHED_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "batched_qwen3_4b_traffic.txt")
+APPEND_SRCS = [os.path.join(ROOT, "prefill_split_gqa_amd", "csrc", f) for f in ("append.hip", "common.h")]
+PROFILES = os.path.join(ROOT, "profiles")
+PREFILL_COUNTERS_FILE = os.path.join(PROFILES, "prefill_0p5b_T4097_counters.txt")
 
 
 def decode_bytes(S: int, Hq: int = 28, Hkv: int = 4, D: int = 128, elem: int = 4) -> int:
@@ -69,6 +67,12 @@ def prefill_flops(Tq: int, Tk: int, Hq: int = 14, D: int = 64) -> int:
     off = Tk - Tq
     pairs = sum(min(i + off + 1, Tk) for i in range(Tq))
     return 4 * D * Hq * pairs
+
+
+def prefill_bytes(Tq: int, Tk: int, Hq: int = 14, Hkv: int = 2, D: int = 64, elem: int = 2) -> int:
+    """Compulsory HBM bytes of one prefill launch: Q read and O written once,
+    K and V read once."""
+    return 2 * Hq * Tq * D * elem + 2 * Hkv * Tk * D * elem
 
 
 def decode_bytes_generic(B, Hq, Hkv, D, lens, elem):
@@ -114,10 +118,29 @@ def read_summary_value(path, key, srcs, field):
         return None
 
 
-def read_traffic(path=TRAFFIC_FILE, key="decode_source_sha256_16", srcs=DECODE_SRCS):
-    """HBM bytes per launch from a committed counter summary (FETCH_SIZE +
-    WRITE_SIZE, calibrated), or None when it does not match the source."""
-    return read_summary_value(path, key, srcs, "hbm_bytes_per_launch")
+def sources_of(kernel: str):
+    """The source files a kernel is built from (a summary taken on other
+    sources does not describe it)."""
+    if "prefill" in kernel:
+        return PREFILL_SRCS
+    if "append" in kernel:
+        return APPEND_SRCS
+    return DECODE_SRCS
+
+
+def attach_traffic(name: str, entry: dict) -> None:
+    """Fill roofline.traffic (HBM bytes per launch, FETCH_SIZE + WRITE_SIZE
+    calibrated) from the committed counter summary profiles/<name>_traffic.txt
+    when it was taken on the current kernel sources; otherwise leave null."""
+    rl = entry.get("roofline") if isinstance(entry, dict) else None
+    if not rl or rl.get("traffic") is not None:
+        return
+    t = read_summary_value(os.path.join(PROFILES, name + "_traffic.txt"), "source_sha256_16",
+                           sources_of(rl["kernel"]), "hbm_bytes_per_launch")
+    rl["traffic"] = t
+    base = rl.get("algorithmic_bytes_per_launch") or rl.get("compulsory_bytes_per_launch")
+    if t is not None and base:
+        rl["traffic_over_algorithmic"] = round(t / base, 3)
 
 
 class Flusher:
@@ -318,34 +341,55 @@ def bench_extra(torch, gqa, oracle, W, steps, warmup, flush, names=EXTRAS):
     scaled (codes permuted for the 4-bit cache), so that every layer reads its
     own memory."""
     out = {}
+    t0 = time.time()
+
+    def done(what):
+        sys.stderr.write("bench: %s done (%.0f s)\n" % (what, time.time() - t0))
+        sys.stderr.flush()
+
     if "decode_7b_sweep" in names:
         out.update(extra_decode_sweep(torch, gqa, oracle, W, steps, warmup, flush))
+        done("decode_7b_sweep")
     for T in (513, 2049):
         if "prefill_0p5b_T%d" % T in names:
             out["prefill_0p5b_T%d" % T] = prefill_entry(bench_prefill(torch, gqa, oracle, W, T, steps, warmup, flush))
+            done("prefill_0p5b_T%d" % T)
     if "decode_0p5b_s128" in names:
         out.update(extra_decode_small(torch, gqa, oracle, W, steps, warmup, flush))
+        done("decode_0p5b_s128")
     if "batched_qwen3_4b" in names:
         out.update(extra_batched(torch, gqa, oracle, W, steps, warmup, flush))
+        done("batched_qwen3_4b")
     sizes = tuple(S for S in (2048, 16384) if "q4_decode_s%d" % S in names)
     if sizes:
         out.update(extra_q4(torch, gqa, oracle, W, steps, warmup, flush, sizes=sizes))
+        done("q4_decode")
     if "prefill_0p5b_chunk256_at3841" in names:
         out.update(extra_chunked_prefill(torch, gqa, oracle, W, steps, warmup, flush))
+        done("prefill_0p5b_chunk256_at3841")
     if "append_7b_s4096" in names:
         out.update(extra_append_dense(torch, gqa, oracle, W, steps, warmup, flush))
+        done("append_7b_s4096")
     if "append_q4_s16384" in names:
         out.update(extra_append_q4(torch, gqa, oracle, W, steps, warmup, flush))
+        done("append_q4_s16384")
     if "q4r_decode_s16448_r128" in names:
         out.update(extra_q4r_decode(torch, gqa, oracle, W, steps, warmup, flush))
+        done("q4r_decode_s16448_r128")
     if "q4r_prefill_0p5b_chunk256_at3841_r128" in names:
         out.update(extra_q4r_prefill(torch, gqa, oracle, W, steps, warmup, flush))
+        done("q4r_prefill_0p5b_chunk256_at3841_r128")
     if "append_q4r_r128" in names:
         out.update(extra_append_q4r(torch, gqa, oracle, W, steps, warmup, flush))
+        done("append_q4r_r128")
     if "naive_decode_7b_s4096" in names:
         out.update(naive_decode(torch, oracle, W, steps, warmup, flush))
+        done("naive_decode_7b_s4096")
     if "naive_prefill_0p5b_t4097" in names:
         out.update(naive_prefill(torch, oracle, W, max(3, steps // 2), 1, flush))
+        done("naive_prefill_0p5b_t4097")
+    for name, entry in out.items():
+        attach_traffic(name, entry)
     return out
 
 
@@ -404,8 +448,6 @@ def extra_batched(torch, gqa, oracle, W, steps, warmup, flush):
         out["batched_qwen3_4b_B%d" % B] = hbm_entry(
             us, decode_bytes_generic(B, w.Hq, w.Hkv, w.D, [int(x) for x in lens], 2), ok, err,
             "decode_splitk_kernel<DenseKV<bf16_t,128>,bf16_t,128,4>",
-            traffic=read_summary_value(BATCHED_TRAFFIC_FILE, "decode_source_sha256_16", DECODE_SRCS,
-                                       "hbm_bytes_per_launch_B%d" % B),
             layers_per_step=w.layers, kv_lens=[int(x) for x in lens])
         del dev, outs, ref, g
         torch.cuda.empty_cache()
@@ -443,8 +485,7 @@ def extra_q4(torch, gqa, oracle, W, steps, warmup, flush, sizes=(2048, 16384)):
         us = float(np.median(time_steps(torch, g.replay, steps, warmup, flush))) * 1e3 / w.layers
         ok = err <= 2e-2 and all(torch.equal(a, b) for a, b in zip(outs, ref))
         nbytes = S * w.Hkv * 2 * (w.D // 2 + 2 * 2 * (w.D // w.group)) + 2 * w.Hq * w.D * 2
-        traffic = read_traffic(Q4_TRAFFIC_FILE, "decode_source_sha256_16", DECODE_SRCS) if S == 16384 else None
-        out["q4_decode_s%d" % S] = hbm_entry(us, nbytes, ok, err, "decode_q4_kernel<128,64,8>", traffic=traffic,
+        out["q4_decode_s%d" % S] = hbm_entry(us, nbytes, ok, err, "decode_q4_kernel<128,64,8>",
                                              layers_per_step=w.layers)
         del dev, outs, ref, g
         torch.cuda.empty_cache()
@@ -484,7 +525,8 @@ def extra_chunked_prefill(torch, gqa, oracle, W, steps, warmup, flush):
         "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
         "roofline": {"bound": "mfma", "kernel": "prefill_causal_kernel<bf16_t,64,false>", "achieved": round(tf, 1),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "algorithmic_flop_per_launch": flops, "launch_duration_us": round(us, 2)},
+                     "traffic": None, "algorithmic_flop_per_launch": flops,
+                     "compulsory_bytes_per_launch": prefill_bytes(256, 4097), "launch_duration_us": round(us, 2)},
         "parity_ok": err <= 2e-2 and all(torch.equal(a, b) for a, b in zip(outs, ref)), "parity_max_abs": err}
     return out
 
@@ -499,7 +541,8 @@ def prefill_entry(p, traffic=None, counters=None, gemm=None):
          "roofline": {"bound": "mfma", "kernel": "prefill_causal_kernel<bf16_t,64,false>",
                       "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                       "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
-                      "algorithmic_flop_per_launch": p["flops"], "launch_duration_us": round(us, 2)},
+                      "algorithmic_flop_per_launch": p["flops"],
+                      "compulsory_bytes_per_launch": prefill_bytes(p["T"], p["T"]), "launch_duration_us": round(us, 2)},
          "parity_ok": p["gate_ok"], "parity_max_abs": p["gate_max_abs"]}
     if counters is not None:
         d["roofline"]["mfma_busy_counter_frac"] = counters
@@ -917,7 +960,6 @@ def main():
     us_layer = ms_step * 1e3 / layers
     nbytes = decode_bytes(args.S)
     achieved = nbytes / (us_layer * 1e-6) / 1e9
-    traffic = read_traffic() if args.S == 4096 else None
     result.update({
         "value": round(us_layer, 3),
         "ms_per_step": round(ms_step, 4),
@@ -927,7 +969,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "decode_splitk_kernel<DenseKV<float,128>,float,128,7>",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,
+                     "traffic": None, "algorithmic_bytes_per_launch": nbytes,
                      "launch_duration_us": round(us_layer, 3)},
         "decode_detail": {"expanded_kv_bytes_avoided": expanded_kv_bytes(args.S),
                           "p10_us_layer": round(float(np.percentile(d["graph_ms"], 10)) * 1e3 / layers, 3),
@@ -935,6 +977,8 @@ def main():
                           "eager_us_layer": round(float(np.median(d["eager_ms"])) * 1e3 / layers, 3),
                           "parity_max_abs": d["gate_max_abs"]},
     })
+
+    attach_traffic("decode_7b_s%d" % args.S, result)
 
     if not args.no_calibration:
         try:  # auxiliary: a failure here must not cost the benchmark line
@@ -949,9 +993,11 @@ def main():
         p = bench_prefill(torch, gqa, oracle, W, 4097, max(5, args.steps // 2), 2, flush)
         gemm = result.get("calibration", {}).get("gemm_bf16", {}).get("TFLOPs")
         secondary["prefill_0p5b_T4097"] = prefill_entry(
-            p, traffic=read_traffic(PREFILL_TRAFFIC_FILE, "prefill_source_sha256_16", PREFILL_SRCS),
-            counters=read_summary_value(PREFILL_COUNTERS_FILE, "prefill_source_sha256_16", PREFILL_SRCS,
-                                        "mfma_busy_over_simd_cycles"), gemm=gemm)
+            p, counters=read_summary_value(PREFILL_COUNTERS_FILE, "source_sha256_16", PREFILL_SRCS,
+                                           "mfma_busy_over_simd_cycles"), gemm=gemm)
+        attach_traffic("prefill_0p5b_T4097", secondary["prefill_0p5b_T4097"])
+        sys.stderr.write("bench: prefill_0p5b_T4097 done\n")
+        sys.stderr.flush()
     if not args.no_extra:
         secondary.update(bench_extra(torch, gqa, oracle, W, max(5, args.steps // 2), 2, flush, extra_names))
     # the pages' headline ratios on this GPU: the unfused torch path against the fused kernels
