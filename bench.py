@@ -75,6 +75,14 @@ def prefill_bytes(Tq: int, Tk: int, Hq: int = 14, Hkv: int = 2, D: int = 64, ele
     return 2 * Hq * Tq * D * elem + 2 * Hkv * Tk * D * elem
 
 
+def q4r_prefill_bytes(Tq, Tk, Hq, Hkv, D, group, R) -> int:
+    """Compulsory HBM bytes of a prefill chunk over a residual-window 4-bit
+    cache: f16 Q read and O written once; per KV head the 4-bit rows' codes,
+    scales and biases and the float16 residual rows of K and V read once."""
+    n_q = Tk - Tk % R
+    return 2 * Hq * Tq * D * 2 + 2 * Hkv * (n_q * (D // 2 + 2 * 2 * (D // group)) + (Tk - n_q) * D * 2)
+
+
 def decode_bytes_generic(B, Hq, Hkv, D, lens, elem):
     """Algorithmic bytes of one decode launch: each request's valid K and V
     rows read once, its queries read and outputs written once."""
@@ -738,7 +746,9 @@ def extra_q4r_prefill(torch, gqa, oracle, W, steps, warmup, flush, Tk=4097, Tq=2
         "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
         "roofline": {"bound": "mfma", "kernel": "prefill_causal_kernel<f16_t,64,false,true>", "achieved": round(tf, 1),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "algorithmic_flop_per_launch": flops, "launch_duration_us": round(us, 2)},
+                     "traffic": None, "algorithmic_flop_per_launch": flops,
+                     "compulsory_bytes_per_launch": q4r_prefill_bytes(Tq, Tk, w.Hq, w.Hkv, w.D, group, R),
+                     "launch_duration_us": round(us, 2)},
         "parity_ok": err <= 2e-2 and all(torch.equal(a, b) for a, b in zip(outs, ref)), "parity_max_abs": err}}
 
 
