@@ -38,6 +38,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -101,11 +102,21 @@ def score_matrix_bytes(T: int, Hq: int = 14, elem: int = 2) -> int:
     return Hq * T * T * elem
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source with comments removed and whitespace collapsed: what a
+    counter summary must match (a comment edit does not change a kernel).
+    String literals in these sources hold no comment markers."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest(paths) -> str:
+    """Digest of the code (comments and whitespace aside) of the given sources."""
     h = hashlib.sha256()
     for p in paths:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -74,7 +74,16 @@
 // The 4-bit cache variant (VeloxQuant-MLX "attention" posts, Part 4: codes,
 // scales, biases and the group size go to the kernel, which dequantizes
 // inside it) has a kernel of its own on the matrix cores (below); the split
-// plan, the partials and the merge are shared.
+// plan, the partials and the merge are shared.  With a float16 residual
+// window (the same posts, "What this means in practice": recent tokens kept
+// unquantized), the residual rows of each (request, head tile) are one more
+// split of that launch, streamed by the dense path (dense_split) and merged
+// with the 4-bit splits.
+//
+// Sliding window and sinks (the Fornace prefill page, "What this does not
+// prove", and the SDPA signature in the VeloxQuant posts, Part 4): a window
+// moves each request's first visible row (the splits cover only the window),
+// and a sink logit joins the normaliser where the partials are combined.
 
 #include "common.h"
 

@@ -41,6 +41,14 @@
 // over.  Only tiles that cross a wave's diagonal are masked, and a wave
 // skips the arithmetic of tiles it cannot see at all (the end of a row
 // block's diagonal, or a last row block with fewer than 128 valid rows).
+//
+// Sliding window and sinks: tiles wholly before a wave's first visible key
+// are skipped, tiles across it masked, and a sink logit joins the final
+// normaliser.  A 4-bit cache with a float16 residual window (VeloxQuant
+// posts; a chunked prefill reading the quantized cache): key tiles below
+// the 4-bit row count are loaded as codes, scales and biases into registers
+// and dequantized into the tile buffers at the end of the step; the others
+// come from the residual rows by the same LDS DMA as a dense cache.
 
 #include <algorithm>
 #include <type_traits>
