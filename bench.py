@@ -436,7 +436,7 @@ def extra_decode_small(torch, gqa, oracle, W, steps, warmup, flush):
     us = float(np.median(time_steps(torch, g.replay, steps, warmup, flush))) * 1e3 / len(dev)
     ok = err <= 2e-5 and all(torch.equal(a, b) for a, b in zip(outs, ref))
     out["decode_0p5b_s128"] = hbm_entry(us, decode_bytes_generic(1, w.Hq, w.Hkv, w.D, [128], 4), ok, err,
-                                        "decode_splitk_kernel<DenseKV<float,64>,float,64,7>",
+                                        "decode_mfma_kernel<float,64,7>",
                                         layers_per_step=len(dev))
     return out
 
@@ -466,7 +466,7 @@ def extra_batched(torch, gqa, oracle, W, steps, warmup, flush):
         ok = err <= 2e-2 and all(torch.equal(a, b) for a, b in zip(outs, ref))
         out["batched_qwen3_4b_B%d" % B] = hbm_entry(
             us, decode_bytes_generic(B, w.Hq, w.Hkv, w.D, [int(x) for x in lens], 2), ok, err,
-            "decode_splitk_kernel<DenseKV<bf16_t,128>,bf16_t,128,4>",
+            "decode_mfma_kernel<bf16_t,128,4>",
             layers_per_step=w.layers, kv_lens=[int(x) for x in lens])
         del dev, outs, ref, g
         torch.cuda.empty_cache()
@@ -578,7 +578,7 @@ def extra_decode_sweep(torch, gqa, oracle, W, steps, warmup, flush, sizes=(128, 
         d = bench_decode(torch, gqa, oracle, W, S, 28, steps, warmup, flush, gate_layers=(0,))
         us = float(np.median(d["graph_ms"])) * 1e3 / 28
         out["decode_7b_s%d" % S] = hbm_entry(us, decode_bytes(S), d["gate_ok"], d["gate_max_abs"],
-                                             "decode_splitk_kernel<DenseKV<float,128>,float,128,7>",
+                                             "decode_mfma_kernel<float,128,7>",
                                              layers_per_step=28,
                                              eager_us_layer=round(float(np.median(d["eager_ms"])) * 1e3 / 28, 3))
     return out
@@ -673,9 +673,9 @@ def _q4r_layers(torch, d0, layers):
 def extra_q4r_decode(torch, gqa, oracle, W, steps, warmup, flush, n=16448, R=128):
     """Decode over a 4-bit cache with a float16 residual window (the 64/8-head
     workload, group 64, 80 layers): 16448 tokens = 16384 4-bit rows (the
-    q4_decode_s16384 cache) plus 64 float16 residual rows (R = 128).  Two
-    launches per layer: the dense kernel over the residual, then the 4-bit
-    kernel, which folds the residual's result into its merge."""
+    q4_decode_s16384 cache) plus 64 float16 residual rows (R = 128).  One
+    launch per layer: the 4-bit kernel, whose last split streams the
+    residual rows and is merged with the others."""
     w = W.by_name("q4_decode")
     rng = np.random.default_rng(16448)
     n_q, n_r = oracle.q4r_split(n, R)
@@ -707,8 +707,8 @@ def extra_q4r_decode(torch, gqa, oracle, W, steps, warmup, flush, n=16448, R=128
     nbytes = (n_q * w.Hkv * 2 * (w.D // 2 + 2 * 2 * (w.D // w.group)) + n_r * w.Hkv * 2 * w.D * 2
               + 2 * w.Hq * w.D * 2)
     return {"q4r_decode_s16448_r128": hbm_entry(
-        us, nbytes, ok, err, "decode_splitk_kernel<DenseKV<f16_t,128>,f16_t,128,8,2> + decode_q4_kernel<128,64,8,1>",
-        layers_per_step=w.layers, n_q=n_q, n_r=n_r, launches_per_layer=2)}
+        us, nbytes, ok, err, "decode_q4_kernel<128,64,8,1>",
+        layers_per_step=w.layers, n_q=n_q, n_r=n_r, launches_per_layer=1)}
 
 
 def extra_q4r_prefill(torch, gqa, oracle, W, steps, warmup, flush, Tk=4097, Tq=256, R=128, group=32):
@@ -987,7 +987,7 @@ def main():
         "vs_baseline": round(us_layer / PAGES_M2_US_PER_LAYER_7B_S4096, 5) if args.S == 4096 else None,
         "baseline_context": "pages' fused Metal figure 264.82 us/layer on an Apple M2 10-core GPU "
                             "(same geometry and context); lower ratio = faster",
-        "roofline": {"bound": "hbm", "kernel": "decode_splitk_kernel<DenseKV<float,128>,float,128,7>",
+        "roofline": {"bound": "hbm", "kernel": "decode_mfma_kernel<float,128,7>",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "algorithmic_bytes_per_launch": nbytes,

@@ -1,27 +1,34 @@
 // decode.hip -- split-K single-token grouped-query attention for gfx950.
 //
-// One workgroup (8 waves, 512 lanes) handles one split of the KV length for
-// one KV head and GT of the query heads that share it ("Why It Matters: 7x
-// KV Expansion" on the Candle decode page: the fused kernel reads each KV
-// head once through a GQA stride; here the heads of a group share the load).
+// Every decode launch splits the KV length of each (request, KV head) into
+// splits of L rows; one workgroup handles one split for GT of the query
+// heads that share the KV head ("Why It Matters: 7x KV Expansion" on the
+// Candle decode page: the fused kernel reads each KV head once through a GQA
+// stride; here the heads of a group share the load).  Each split publishes
+// one (max, sum, output) partial per query head, and the partials are merged
+// in the same launch (below).
 //
-// Lane layout: each key row is read by a 32-lane row-group with 16-byte
-// (or 8-byte) coalesced loads; a wave reads 2 rows per load instruction and
-// the workgroup 16 rows per step.  Each lane owns D/32 elements of the row;
-// a dot product is finished with four DPP steps inside a 16-lane row and one
+// Dense caches (fp32, bf16, f16) run on the matrix cores: decode_mfma_kernel,
+// 4 waves, each taking 16-row blocks of the split (its comment has the
+// operand layouts).
+//
+// The float16 residual rows of a residual-window 4-bit cache are one split of
+// the 4-bit kernel's launch, streamed on the SIMD lanes (dense_split, 8
+// waves): each key row is read by a 32-lane row-group with 16-byte (or
+// 8-byte) coalesced loads; a wave reads 2 rows per load instruction and the
+// workgroup 16 rows per step.  Each lane owns D/32 elements of the row; a
+// dot product is finished with four DPP steps inside a 16-lane row and one
 // gfx950 row swap (v_permlane16_swap).  Each row-group keeps its own
-// online-softmax state (reference max, sum, output slice) in registers; the
-// reference max is only raised when a score exceeds it by more than 2^8
-// (log2 domain), so the rescale of the output registers is rare and the
-// result is exact up to rounding.  The GT query rows are staged in LDS once
-// per workgroup.  Two 32-row chunks of K and V are in flight per workgroup,
-// read through buffer resources bounded to the split, so a row past the end
-// reads as zeros and every load is issued unconditionally.
+// online-softmax state in registers; the two row-groups of a wave are merged
+// with the gfx950 cross-half lane swap (v_permlane32_swap), the eight waves
+// through LDS.
 //
-// End of a workgroup: the two row-groups of a wave are merged with the
-// gfx950 cross-half lane swap (v_permlane32_swap, a reduce-scatter: each
-// lane then owns half of the wave's output slice), the eight waves through
-// LDS, giving one (max, sum, output) partial per split.
+// In both, the reference maximum of the online softmax is only raised when a
+// score exceeds it by more than 2^8 (log2 domain), so the rescale of the
+// output registers is rare and the result is exact up to rounding; the query
+// rows are staged in LDS once per workgroup; K and V are read through buffer
+// resources bounded to the split, so a row past its end reads as zeros and
+// loads are issued unconditionally.
 //
 // Cross-split merge: one CU can pull only ~70 GB/s, so a single workgroup
 // reading every split's partial would be the tail of the launch.  Instead
@@ -86,6 +93,8 @@
 // and a sink logit joins the normaliser where the partials are combined.
 
 #include "common.h"
+
+#include <type_traits>
 
 namespace gqa {
 
@@ -331,12 +340,12 @@ __device__ __forceinline__ bool packed_item(const DecodeArgs &a, int B, int i, S
     return true;
 }
 
-template <typename TQ, int D, int GT, int RES>
+template <typename TQ, int D, int GT, int RES, int NT = kDecodeThreads>
 __device__ void merge_head(const DecodeArgs &a, int m);
-template <typename TQ, int D, int GT, int RES>
+template <typename TQ, int D, int GT, int RES, int NT = kDecodeThreads>
 __device__ void merge_tile(const DecodeArgs &a, int col, int n_split, unsigned own_heads, unsigned decision,
                            int ticket_tid, unsigned ticket);
-template <typename TQ, int D, int GT, int RES>
+template <typename TQ, int D, int GT, int RES, int NT = kDecodeThreads>
 __device__ void merge_workgroup(const DecodeArgs &a, int m);
 
 // Control words (see the file header): the tile word of (request, head
@@ -431,12 +440,13 @@ __device__ __forceinline__ float sink_log2(const DecodeArgs &a, int h)
     return a.sinks ? a.sinks[h] * kLog2e : kNegInf;
 }
 
-template <typename TQ, int D, int GT, int RES, int SOD = D>
+template <typename TQ, int D, int GT, int RES, int SOD = D, int NT = kDecodeThreads>
 __device__ __forceinline__ void finish_split(const DecodeArgs &a, const float *so, const float *sm, const float *sl,
                                              int col, int s, int n_split, TQ *out, int h0)
 {
-    constexpr int NW = kDecodeThreads / 64;
+    constexpr int NW = NT / 64;
     constexpr int NQ = GT * D / 4;  // 4-wide output items
+    static_assert(NQ <= NT, "one output item per thread");
     const DecodePlan &P = a.plan;
     const int tid = threadIdx.x;
     const int qh = tid / (D / 4), qd = (tid % (D / 4)) * 4;
@@ -676,18 +686,176 @@ __device__ __forceinline__ void dense_split(const DecodeArgs &a, const DecodeGri
     if (n_split > 1) merge_tile<TQ, D, GT, RES>(a, col, n_split, own, decision, 0, ticket);
 }
 
-template <class KV, typename TQ, int D, int GT>
-__global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArgs a, DecodeGrid grid)
+// ===========================================================================
+// Dense KV cache on the matrix cores
+// ===========================================================================
+//
+// One workgroup of 4 waves (one per SIMD) per (request, head tile, split),
+// with the split plan, the partials and the merge above.  Wave w takes the
+// 16-row blocks w, w + 4, ... of the split, two blocks in flight, read
+// straight from HBM into registers in the layouts the matrix instructions
+// take, so that no key or value ever moves between lanes.  With lane l,
+// j = l % 16 and k = l / 16:
+//   S^T[row][head] = K Q^T: A = K row j of the block (16-byte pieces k,
+//     k + 4, ... of the row), B = query head j in the same element order
+//     (zero past the tile's heads).  fp32 caches take
+//     v_mfma_f32_16x16x4_f32 (one element of each piece per instruction),
+//     16-bit caches v_mfma_f32_16x16x32_{bf16,f16} (a whole piece).  The
+//     lane then holds head j, rows 4k .. 4k + 3 of the block.
+//   Online softmax (log2 domain) with the lazy reference maximum, shared by
+//     the four lanes of a head.
+//   O^T[d][head] += V^T P^T with v_mfma_f32_16x16x4_f32, in four steps v
+//     over the rows 4k + v: A = V[row 4k + v][the lane's dimensions] (16
+//     lanes read a whole row, 16 or 8 consecutive bytes each), B = the
+//     lane's own p of that row.  Values of 16-bit caches are widened to
+//     fp32 in registers; p stays fp32.
+// At the end each wave holds, per head, its reference maximum, its sum of
+// weights and its output row; the workgroup combines the 4 waves as the
+// kernel above does.
+constexpr int kMfThreads = 256;
+constexpr int kMfWaves = kMfThreads / 64;
+constexpr int kMfRows = 16;  // rows per block
+
+typedef float mf_f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 mf_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 mf_f16x8_t __attribute__((ext_vector_type(8)));
+
+template <typename T, int D>
+struct MfKV {
+    static constexpr int ES = (int)sizeof(T);
+    static constexpr int ROW = D * ES;                         // bytes per row
+    static constexpr int KE = 16 / ES;                         // elements per 16-byte K piece
+    static constexpr int NK = D / (4 * KE);                    // K pieces per lane (of the lane's row)
+    static constexpr int VU = ROW / 16 >= 16 ? 16 : ROW / 16;  // bytes per V load
+    static constexpr int NVL = ROW / 16 / VU;                  // V loads per lane and row
+    static constexpr int VE = VU / ES;                         // elements per V load
+    static constexpr int NTILE = D / 16;                       // 16-dimension output tiles
+    static_assert(NK >= 1 && NVL * VE * 16 == D && NTILE == NVL * VE, "operand layout");
+    struct Blk {
+        u32x4_t k[NK];
+        uint32_t v[4][NVL][VU / 4];
+    };
+    // Block of rows r0 .. r0 + 15 (rows at or past the resources' end read
+    // as zeros): lane (j, k) reads K row r0 + j, pieces k + 4t, and V rows
+    // r0 + 4k + v, bytes VU * (16h + j) .. of each.
+    __device__ __forceinline__ static void load(Blk &bk, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                                int r0, int j, int k)
+    {
+#pragma unroll
+        for (int t = 0; t < NK; ++t)
+            bk.k[t] = __builtin_bit_cast(u32x4_t,
+                                         __builtin_amdgcn_raw_buffer_load_b128(rk, (r0 + j) * ROW + 64 * t + 16 * k, 0, 0));
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int h = 0; h < NVL; ++h) {
+                const int off = (r0 + 4 * k + v) * ROW + VU * (16 * h + j);
+                if constexpr (VU == 16) {
+                    const auto x = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+                    bk.v[v][h][0] = x[0]; bk.v[v][h][1] = x[1]; bk.v[v][h][2] = x[2]; bk.v[v][h][3] = x[3];
+                } else {
+                    const auto x = __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, 0);
+                    bk.v[v][h][0] = x[0]; bk.v[v][h][1] = x[1];
+                }
+            }
+    }
+    // element e of V load (v, h), widened to fp32
+    __device__ __forceinline__ static float v_elem(const Blk &bk, int v, int h, int e)
+    {
+        if constexpr (ES == 4) {
+            return __uint_as_float(bk.v[v][h][e]);
+        } else if constexpr (__is_same(T, bf16_t)) {
+            const uint32_t w = bk.v[v][h][e / 2];
+            return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+        } else {
+            const uint32_t w = bk.v[v][h][e / 2];
+            return f16_bits_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+        }
+    }
+};
+
+// S^T of one block: fp32 elements one per instruction, 16-bit pieces whole.
+template <typename T, int D>
+struct MfQK;
+template <int D>
+struct MfQK<float, D> {
+    typedef MfKV<float, D> M;
+    float q[M::NK][4];  // query element 4(k + 4t) + e of head j, times scale * log2(e)
+    __device__ __forceinline__ void init(const uint32_t *sq, int j, int k, bool valid, float qscale)
+    {
+#pragma unroll
+        for (int t = 0; t < M::NK; ++t) {
+            const uint4 x = *(const uint4 *)(sq + j * D + 4 * (k + 4 * t));
+            q[t][0] = valid ? __uint_as_float(x.x) * qscale : 0.0f;
+            q[t][1] = valid ? __uint_as_float(x.y) * qscale : 0.0f;
+            q[t][2] = valid ? __uint_as_float(x.z) * qscale : 0.0f;
+            q[t][3] = valid ? __uint_as_float(x.w) * qscale : 0.0f;
+        }
+    }
+    __device__ __forceinline__ mf_f32x4_t scores(const typename M::Blk &bk) const
+    {
+        mf_f32x4_t c0 = {0.0f, 0.0f, 0.0f, 0.0f}, c1 = c0;
+#pragma unroll
+        for (int t = 0; t < M::NK; ++t) {
+            c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(bk.k[t][0]), q[t][0], c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(bk.k[t][1]), q[t][1], c1, 0, 0, 0);
+            c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(bk.k[t][2]), q[t][2], c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(bk.k[t][3]), q[t][3], c1, 0, 0, 0);
+        }
+        return c0 + c1;
+    }
+};
+template <typename T16, int D>
+struct MfQK16 {
+    typedef MfKV<T16, D> M;
+    typedef typename std::conditional<__is_same(T16, bf16_t), mf_bf16x8_t, mf_f16x8_t>::type op_t;
+    op_t q[M::NK];  // query elements 8(k + 4t) .. + 7 of head j
+    float qscale;
+    __device__ __forceinline__ void init(const uint32_t *sq, int j, int k, bool valid, float qs)
+    {
+#pragma unroll
+        for (int t = 0; t < M::NK; ++t) {
+            uint4 x = *(const uint4 *)(sq + (j * D) / 2 + 4 * (k + 4 * t));
+            if (!valid) x = make_uint4(0u, 0u, 0u, 0u);
+            q[t] = __builtin_bit_cast(op_t, x);
+        }
+        qscale = qs;
+    }
+    __device__ __forceinline__ mf_f32x4_t scores(const typename M::Blk &bk) const
+    {
+        mf_f32x4_t c0 = {0.0f, 0.0f, 0.0f, 0.0f}, c1 = c0;
+#pragma unroll
+        for (int t = 0; t < M::NK; ++t) {
+            if constexpr (__is_same(T16, bf16_t)) {
+                if (t & 1) c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(op_t, bk.k[t]), q[t], c1, 0, 0, 0);
+                else c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(op_t, bk.k[t]), q[t], c0, 0, 0, 0);
+            } else {
+                if (t & 1) c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(op_t, bk.k[t]), q[t], c1, 0, 0, 0);
+                else c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(op_t, bk.k[t]), q[t], c0, 0, 0, 0);
+            }
+        }
+        return (c0 + c1) * qscale;
+    }
+};
+template <int D> struct MfQK<bf16_t, D> : MfQK16<bf16_t, D> {};
+template <int D> struct MfQK<f16_t, D> : MfQK16<f16_t, D> {};
+
+template <typename T, int D, int GT>
+__global__ __launch_bounds__(kMfThreads) void decode_mfma_kernel(DecodeArgs a, DecodeGrid grid)
 {
     constexpr int RES = kResNone;
+    typedef MfKV<T, D> M;
+    static_assert(GT <= 16, "one matrix column per query head");
     if ((int)blockIdx.x >= grid.n_stream) {
-        merge_workgroup<TQ, D, GT, RES>(a, (int)blockIdx.x - grid.n_stream);
+        merge_workgroup<T, D, GT, RES, kMfThreads>(a, (int)blockIdx.x - grid.n_stream);
         return;
     }
 
     const int tid = threadIdx.x;
+    const int lane = tid & 63, j = lane & 15, k = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const DecodePlan &P = a.plan;
-    int s, ht, b, n;
+    int s, ht, b;
     if (a.kv_lens && grid.B <= kDecodePackMaxB) {
         SplitItem it;
         if (!packed_item<RES>(a, grid.B, (int)blockIdx.x, &it)) return;
@@ -698,23 +866,130 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_splitk_kernel(DecodeArg
         b = (int)blockIdx.x / (grid.gx * P.HT);
     }
     int lo;  // first visible row (a window's start)
-    n = windowed(a, request_len<RES>(a, b), &lo);
+    const int n = windowed(a, request_len<RES>(a, b), &lo);
     const int n_split = (n + P.L - 1) / P.L;
-    const int g = ht / P.ht_per_kv;
-    const int h0 = g * P.G + (ht % P.ht_per_kv) * GT;
-    TQ *out = (TQ *)a.out + ((size_t)b * a.Hq + h0) * D;
+    const int gk = ht / P.ht_per_kv;
+    const int h0 = gk * P.G + (ht % P.ht_per_kv) * GT;
+    T *out = (T *)a.out + ((size_t)b * a.Hq + h0) * D;
 
     if (n == 0) {  // empty request: defined as an all-zero output
         if (s == 0)
-            for (int idx = tid; idx < GT * D; idx += kDecodeThreads) store_elem(out + idx, 0.0f);
+            for (int idx = tid; idx < GT * D; idx += kMfThreads) store_elem(out + idx, 0.0f);
         return;
     }
     if (s >= n_split) return;
     const int start = s * P.L;
     const int end = min(start + P.L, n);
+    const int nblk = (end - start + kMfRows - 1) / kMfRows;
 
-    const size_t head_row0 = ((size_t)b * a.Hkv + g) * (size_t)a.s_cap + lo;
-    dense_split<KV, TQ, D, GT, RES>(a, grid, a.k, a.v, head_row0, s, n_split, start, end, b, ht, h0, out);
+    const size_t head_row0 = ((size_t)b * a.Hkv + gk) * (size_t)a.s_cap + lo;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc((const T *)a.k + head_row0 * D, (size_t)end * M::ROW);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const T *)a.v + head_row0 * D, (size_t)end * M::ROW);
+
+    // The query rows first (one 16-byte load per thread, staged in LDS), then
+    // this split's group add, then the first two blocks of every wave, all
+    // before anything is consumed; the loads are unconditional (a block past
+    // the split reads zeros without touching memory) so that the compiler's
+    // in-order wait counts stay exact.
+    constexpr int QB = GT * D * (int)sizeof(T);
+    static_assert(QB <= 16 * kMfThreads, "query rows: one 16-byte load per thread");
+    __shared__ __attribute__((aligned(16))) uint32_t sq[QB / 4];
+    const bool q_loader = tid < QB / 16;
+    const uint4 qv = *((const uint4 *)((const char *)a.q + ((size_t)b * a.Hq + h0) * D * sizeof(T)) +
+                       (q_loader ? tid : 0));
+    const int col = b * P.HT + ht;
+    unsigned gticket = 0u;
+    if (n_split > 1 && tid == 0) gticket = group_add(a, col, s);
+    asm volatile("" ::: "memory");
+    typename M::Blk bk0, bk1;
+    M::load(bk0, rk, rv, start + wave * kMfRows, j, k);
+    M::load(bk1, rk, rv, start + (wave + kMfWaves) * kMfRows, j, k);
+    if (q_loader) *((uint4 *)sq + tid) = qv;
+    __syncthreads();
+    unsigned ticket = kNoTicket;  // a group completer's tile word add (awaited at the end)
+    if (n_split > 1 && tid == 0) ticket = group_done(a, col, s, n_split, gticket);
+
+    MfQK<T, D> qk;
+    qk.init(sq, j < GT ? j : 0, k, j < GT, a.qscale);
+
+    mf_f32x4_t o[M::NTILE];
+#pragma unroll
+    for (int t = 0; t < M::NTILE; ++t) o[t] = mf_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_ref = kNegInf, l_run = 0.0f;
+
+    auto block = [&](const typename M::Blk &bk, int r0) {
+        const mf_f32x4_t sv = qk.scores(bk);
+        float sc[4] = {sv[0], sv[1], sv[2], sv[3]};
+        if (r0 + kMfRows > end) {  // the split's last block: rows past its end
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                if (r0 + 4 * k + v >= end) sc[v] = kNegInf;
+        }
+        const float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        if (__any(bm > m_ref + kLazyRescale)) {
+            const float mn = fmaxf(m_ref, max4q(bm));  // finite: the block's first row is valid
+            const float al = rel_weight(m_ref, mn);
+            m_ref = mn;
+            l_run *= al;
+#pragma unroll
+            for (int t = 0; t < M::NTILE; ++t) o[t] *= al;
+        }
+        float p[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            p[v] = fast_exp2(sc[v] - m_ref);
+            l_run += p[v];
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int h = 0; h < M::NVL; ++h)
+#pragma unroll
+                for (int e = 0; e < M::VE; ++e)
+                    o[h * M::VE + e] =
+                        __builtin_amdgcn_mfma_f32_16x16x4f32(M::v_elem(bk, v, h, e), p[v], o[h * M::VE + e], 0, 0, 0);
+    };
+
+    // Two-deep register pipeline over this wave's blocks; the refills are
+    // unconditional too (past the split they read zeros).
+    for (int kb = wave; kb < nblk; kb += 2 * kMfWaves) {
+        block(bk0, start + kb * kMfRows);
+        M::load(bk0, rk, rv, start + (kb + 2 * kMfWaves) * kMfRows, j, k);
+        if (kb + kMfWaves >= nblk) break;
+        block(bk1, start + (kb + kMfWaves) * kMfRows);
+        M::load(bk1, rk, rv, start + (kb + 3 * kMfWaves) * kMfRows, j, k);
+    }
+
+    // in place, split s is the designated merger of heads s, s + n_split, ...
+    const unsigned own = n_split > 1 && grid.inplace ? inplace_heads<GT>(s, n_split) : 0u;
+    unsigned decision = 0u;
+    if (tid == 0 && own != 0u) decision = decide(a, col, own);
+
+    // ---- the 4 waves' partials through LDS ----
+    constexpr int SOD = D + 4;  // row stride (floats): the heads' rows start in distinct banks
+    __shared__ __attribute__((aligned(16))) float so[kMfWaves * GT * SOD];
+    __shared__ float sm[kMfWaves * GT], sl[kMfWaves * GT];
+    l_run = sum4q(l_run);
+    if (j < GT) {
+        float *row = so + (wave * GT + j) * SOD;
+#pragma unroll
+        for (int h = 0; h < M::NVL; ++h)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int e4 = 0; e4 < M::VE; e4 += 4)
+                    *(float4 *)&row[16 * M::VE * h + M::VE * (4 * k + v) + e4] =
+                        make_float4(o[h * M::VE + e4][v], o[h * M::VE + e4 + 1][v], o[h * M::VE + e4 + 2][v],
+                                    o[h * M::VE + e4 + 3][v]);
+        if (k == 0) {
+            sm[wave * GT + j] = m_ref;
+            sl[wave * GT + j] = l_run;
+        }
+    }
+    __syncthreads();
+
+    finish_split<T, D, GT, RES, SOD, kMfThreads>(a, so, sm, sl, col, s, n_split, out, h0);
+    if (n_split > 1) merge_tile<T, D, GT, RES, kMfThreads>(a, col, n_split, own, decision, 0, ticket);
 }
 
 // Sum over the lanes of a wave that share lane % CPW (CPW a power of two
@@ -738,11 +1013,11 @@ template <int CPW> __device__ __forceinline__ float colgroup_sum(float x)
 // split j) and leaves them and their maximum in LDS; each wave then forms
 // its weights and sums its lanes with cross-lane steps.
 //
-template <typename TQ, int D, int GT, int RES>
+template <typename TQ, int D, int GT, int RES, int NT>
 __device__ void merge_head(const DecodeArgs &a, int m)
 {
     constexpr int D4 = D / 4;                     // 4-wide output columns
-    constexpr int NW = kDecodeThreads / 64;       // waves
+    constexpr int NW = NT / 64;                   // waves
     constexpr int CPW = D4 / NW;                  // columns per wave
     constexpr int LPC = 64 / CPW;                 // lanes per column
     constexpr int PER = kDecodeMaxSplits / LPC;   // splits per lane
@@ -864,7 +1139,7 @@ __device__ void merge_head(const DecodeArgs &a, int m)
 // add (thread ticket_tid holds the result; kNoTicket if it completed no
 // group) counted the last group, the heads whose designated mergers
 // decided before that.
-template <typename TQ, int D, int GT, int RES>
+template <typename TQ, int D, int GT, int RES, int NT>
 __device__ void merge_tile(const DecodeArgs &a, int col, int n_split, unsigned own_heads, unsigned decision,
                            int ticket_tid, unsigned ticket)
 {
@@ -890,14 +1165,14 @@ __device__ void merge_tile(const DecodeArgs &a, int col, int n_split, unsigned o
     __syncthreads();
     const unsigned heads = s_heads;
     for (int hh = 0; hh < GT; ++hh)
-        if (heads & (1u << hh)) merge_head<TQ, D, GT, RES>(a, col * GT + hh);
+        if (heads & (1u << hh)) merge_head<TQ, D, GT, RES, NT>(a, col * GT + hh);
 }
 
 // A merge workgroup (placed after every split in the grid): the designated
 // merger of item m = (request, head tile) * GT + head.  Thread 0 waits a
 // bounded time for the tile word to count every group (it waits for starts
 // only that long), then decides with its one add.
-template <typename TQ, int D, int GT, int RES>
+template <typename TQ, int D, int GT, int RES, int NT>
 __device__ void merge_workgroup(const DecodeArgs &a, int m)
 {
     __shared__ int s_go;
@@ -920,7 +1195,7 @@ __device__ void merge_workgroup(const DecodeArgs &a, int m)
         s_go = (old & kTwGroups) == n_groups ? 1 : 0;
     }
     __syncthreads();
-    if (s_go) merge_head<TQ, D, GT, RES>(a, m);
+    if (s_go) merge_head<TQ, D, GT, RES, NT>(a, m);
 }
 
 // ===========================================================================
@@ -1349,36 +1624,29 @@ static int decode_grid(int B, int GT, const DecodeArgs &a, DecodeGrid *g)
     return several && !g->inplace ? B * a.plan.HT * GT : 0;
 }
 
-template <class KV, typename TQ, int D, int GT>
-static hipError_t launch_one(int B, const DecodeArgs &a, hipStream_t stream)
+template <typename T, int D, int GT>
+static hipError_t launch_dense(int B, const DecodeArgs &a, hipStream_t stream)
 {
     DecodeGrid g;
     const int n_merge = decode_grid(B, GT, a, &g);
-    hipLaunchKernelGGL((decode_splitk_kernel<KV, TQ, D, GT>), dim3(g.n_stream + n_merge), dim3(kDecodeThreads), 0,
-                       stream, a, g);
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D, GT>), dim3(g.n_stream + n_merge), dim3(kMfThreads), 0, stream, a, g);
     return hipGetLastError();
-}
-
-template <class KV, typename TQ, int D>
-static hipError_t dispatch_gt(int B, const DecodeArgs &a, hipStream_t s)
-{
-    switch (a.plan.GT) {
-    case 1: return launch_one<KV, TQ, D, 1>(B, a, s);
-    case 2: return launch_one<KV, TQ, D, 2>(B, a, s);
-    case 3: return launch_one<KV, TQ, D, 3>(B, a, s);
-    case 4: return launch_one<KV, TQ, D, 4>(B, a, s);
-    case 5: return launch_one<KV, TQ, D, 5>(B, a, s);
-    case 6: return launch_one<KV, TQ, D, 6>(B, a, s);
-    case 7: return launch_one<KV, TQ, D, 7>(B, a, s);
-    case 8: return launch_one<KV, TQ, D, 8>(B, a, s);
-    default: return hipErrorInvalidValue;
-    }
 }
 
 template <typename T, int D>
 static hipError_t dispatch_dense(int B, const DecodeArgs &a, hipStream_t s)
 {
-    return dispatch_gt<DenseKV<T, D>, T, D>(B, a, s);
+    switch (a.plan.GT) {
+    case 1: return launch_dense<T, D, 1>(B, a, s);
+    case 2: return launch_dense<T, D, 2>(B, a, s);
+    case 3: return launch_dense<T, D, 3>(B, a, s);
+    case 4: return launch_dense<T, D, 4>(B, a, s);
+    case 5: return launch_dense<T, D, 5>(B, a, s);
+    case 6: return launch_dense<T, D, 6>(B, a, s);
+    case 7: return launch_dense<T, D, 7>(B, a, s);
+    case 8: return launch_dense<T, D, 8>(B, a, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_decode(int dtype, int D, int B, const DecodeArgs &a, hipStream_t s)
