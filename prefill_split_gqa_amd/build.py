@@ -31,6 +31,11 @@ COMMON_FLAGS = [
     # matrix-core accumulators live in ordinary VGPRs, so the softmax and the
     # rescale of the running output need no AGPR<->VGPR copies
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # every atomic here is issued by one lane, so the compiler's cross-lane
+    # atomic combining gains nothing; its expansion also reads the result at
+    # once, which makes the issuing wave wait for the atomic's round trip
+    # before its next loads
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I", os.path.join(ROOT, "include"),
 ]
 
