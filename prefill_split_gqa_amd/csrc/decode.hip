@@ -1071,6 +1071,8 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     // outside the resources' ranges: they read zero and touch no memory.
     unsigned pend = need;
     for (unsigned it = 0;; ++it) {
+        // the words change under this loop: every poll must read memory again
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int k = 0; k < PER; ++k)
             po[k] = __builtin_bit_cast(tag_u4_t, __builtin_amdgcn_raw_buffer_load_b128(ws_o, o_off(k), 0, kSC1));
