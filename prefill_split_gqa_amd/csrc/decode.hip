@@ -341,7 +341,7 @@ __device__ __forceinline__ bool packed_item(const DecodeArgs &a, int B, int i, S
 }
 
 template <typename TQ, int D, int GT, int RES, int NT = kDecodeThreads>
-__device__ void merge_head(const DecodeArgs &a, int m);
+__device__ void merge_head(const DecodeArgs &a, int m, int n_split);
 template <typename TQ, int D, int GT, int RES, int NT = kDecodeThreads>
 __device__ void merge_tile(const DecodeArgs &a, int col, int n_split, unsigned own_heads, unsigned decision,
                            int ticket_tid, unsigned ticket);
@@ -1008,8 +1008,8 @@ template <int CPW> __device__ __forceinline__ float colgroup_sum(float x)
 }
 
 // Merge of item m = (request b, head tile ht) * GT + hh: the partials of
-// every split for query head h0 + hh, combined by a whole workgroup (one
-// that has published its own split, or a merge workgroup).  Wave w owns the
+// the n_split splits of (b, ht) for query head h0 + hh, combined by a whole
+// workgroup (one that has published its own split, or a merge workgroup).  Wave w owns the
 // 4-wide output columns w*CPW .. w*CPW + CPW - 1; lane (c = lane % CPW,
 // sg = lane / CPW) handles column c of the splits sg + k*LPC and polls
 // those output slices itself.  Wave 0 polls the (max, sum) pairs (lane j:
@@ -1017,7 +1017,7 @@ template <int CPW> __device__ __forceinline__ float colgroup_sum(float x)
 // its weights and sums its lanes with cross-lane steps.
 //
 template <typename TQ, int D, int GT, int RES, int NT>
-__device__ void merge_head(const DecodeArgs &a, int m)
+__device__ void merge_head(const DecodeArgs &a, int m, int n_split)
 {
     constexpr int D4 = D / 4;                     // 4-wide output columns
     constexpr int NW = NT / 64;                   // waves
@@ -1039,9 +1039,6 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     const int col = m / GT;
     const int ht = col % P.HT;
     const int b = col / P.HT;
-    int lo;
-    const int n = windowed(a, request_len<RES>(a, b), &lo);
-    const int n_split = request_splits<RES>(a, b, n);
     if (n_split <= 1) return;  // written directly by the streaming workgroup
     const int g = ht / P.ht_per_kv;
     const int h = g * P.G + (ht % P.ht_per_kv) * GT + hh;
@@ -1058,8 +1055,10 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     auto o_off = [&](int k) { return (int)(((((size_t)sg + (size_t)k * LPC) * GT + hh) * D + d4 * 4) * 4); };
     if (tid == 0) s_go = 1;
     __syncthreads();
-    // a poisoned workspace (an earlier merge gave up) is not trusted
-    const unsigned poisoned = tid == 0 ? __hip_atomic_load(a.poison, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    // a poisoned workspace (an earlier merge gave up) is not trusted; every
+    // thread reads the word (one line), so that its round trip overlaps the
+    // first poll's instead of preceding it
+    const unsigned poisoned = __hip_atomic_load(a.poison, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     tag_u4_t po[PER];
     tag_u2_t mlw = {0u, 0u};
     unsigned need = tid < n_split ? 1u << PER : 0u;  // bit k: slice k, bit PER: the pair
@@ -1120,14 +1119,15 @@ __device__ void merge_head(const DecodeArgs &a, int m)
     float2 mlk[PER];  // all (max, sum) reads first (clamped to a valid split)
 #pragma unroll
     for (int k = 0; k < PER; ++k) mlk[k] = sml[min(sg + k * LPC, n_split - 1)];
+    // branch-free: a slot past the splits gets weight 0 (its words read as
+    // zero); every split's maximum is finite (each split has a row)
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-        if (sg + k * LPC < n_split) {
-            const float w = rel_weight(mlk[k].x, M);
-            const float4 x = __builtin_bit_cast(float4, po[k]);
-            Ls += w * mlk[k].y;
-            R.x += w * x.x; R.y += w * x.y; R.z += w * x.z; R.w += w * x.w;
-        }
+        const float e = fast_exp2(mlk[k].x - M);
+        const float w = sg + k * LPC < n_split ? e : 0.0f;
+        const float4 x = __builtin_bit_cast(float4, po[k]);
+        Ls += w * mlk[k].y;
+        R.x += w * x.x; R.y += w * x.y; R.z += w * x.z; R.w += w * x.w;
     }
     Ls = colgroup_sum<CPW>(Ls) + rel_weight(s2, M);
     R.x = colgroup_sum<CPW>(R.x);
@@ -1170,7 +1170,7 @@ __device__ void merge_tile(const DecodeArgs &a, int col, int n_split, unsigned o
     __syncthreads();
     const unsigned heads = s_heads;
     for (int hh = 0; hh < GT; ++hh)
-        if (heads & (1u << hh)) merge_head<TQ, D, GT, RES, NT>(a, col * GT + hh);
+        if (heads & (1u << hh)) merge_head<TQ, D, GT, RES, NT>(a, col * GT + hh, n_split);
 }
 
 // A merge workgroup (placed after every split in the grid): the designated
@@ -1200,7 +1200,7 @@ __device__ void merge_workgroup(const DecodeArgs &a, int m)
         s_go = (old & kTwGroups) == n_groups ? 1 : 0;
     }
     __syncthreads();
-    if (s_go) merge_head<TQ, D, GT, RES, NT>(a, m);
+    if (s_go) merge_head<TQ, D, GT, RES, NT>(a, m, n_split);
 }
 
 // ===========================================================================
