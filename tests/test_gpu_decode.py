@@ -275,8 +275,9 @@ def test_batched_many_requests(gpu_lib, B):
     # the grid (each workgroup derives its request, head tile and split from
     # all the lengths); past 64 the grid is strided over (request, head tile,
     # split).  Both must match the oracle, with empty and full requests mixed
-    # in, and each request must equal its own single-request call.
-    Hq, Hkv, D, s_cap = 8, 2, 64, 96
+    # in, and each request must equal its own single-request call.  (160 rows
+    # of 64: large enough for several splits per request.)
+    Hq, Hkv, D, s_cap = 8, 2, 64, 160
     rng = np.random.default_rng(B)
     q = torch.from_numpy(rng.standard_normal((B, Hq, 1, D), dtype=np.float32)).to(torch.bfloat16)
     k = torch.from_numpy(rng.standard_normal((B, Hkv, s_cap, D), dtype=np.float32)).to(torch.bfloat16)
