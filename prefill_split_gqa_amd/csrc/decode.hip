@@ -1013,8 +1013,9 @@ template <int CPW> __device__ __forceinline__ float colgroup_sum(float x)
 // 4-wide output columns w*CPW .. w*CPW + CPW - 1; lane (c = lane % CPW,
 // sg = lane / CPW) handles column c of the splits sg + k*LPC and polls
 // those output slices itself.  Wave 0 polls the (max, sum) pairs (lane j:
-// split j) and leaves them and their maximum in LDS; each wave then forms
-// its weights and sums its lanes with cross-lane steps.
+// split j) and leaves each split's weight and the reciprocal of the total
+// weight in LDS; each wave then scales its slices and sums its lanes with
+// cross-lane steps.
 //
 template <typename TQ, int D, int GT, int RES, int NT>
 __device__ void merge_head(const DecodeArgs &a, int m, int n_split)
@@ -1026,9 +1027,9 @@ __device__ void merge_head(const DecodeArgs &a, int m, int n_split)
     constexpr int PER = kDecodeMaxSplits / LPC;   // splits per lane
     static_assert(CPW * NW == D4 && CPW < 16 && LPC * PER == kDecodeMaxSplits, "merge layout");
     static_assert(kDecodeMaxSplits <= 64, "every split's (max, sum) pair is polled by a lane of wave 0");
-    __shared__ float2 sml[kDecodeMaxSplits];
+    __shared__ __attribute__((aligned(16))) float sw[LPC][PER];  // weight of split sg + k * LPC at [sg][k]
     __shared__ int s_go;
-    __shared__ float s_M;
+    __shared__ float s_inv;
     const DecodePlan &P = a.plan;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -1097,44 +1098,54 @@ __device__ void merge_head(const DecodeArgs &a, int m, int n_split)
                 __builtin_amdgcn_raw_buffer_store_b128(tag_u4_t{0u, 0u, 0u, 0u}, ws_o, o_off(k), 0, kSC1);
         if (tid < n_split) __builtin_amdgcn_raw_buffer_store_b64(tag_u2_t{0u, 0u}, ws_ml, (tid * GT + hh) * 8, 0, kSC1);
     }
-    if (tid < n_split) sml[tid] = __builtin_bit_cast(float2, mlw);
-    if (tid < 64) {  // the maximum over the splits, reduced within wave 0
-        float mx = tid < n_split ? __builtin_bit_cast(float2, mlw).x : kNegInf;
+    // Wave 0 (lane j: split j) forms the maximum over the splits (and the
+    // sink), each split's weight and the reciprocal of the total weight, and
+    // leaves them in LDS, weights [sg][k] for split sg + k * LPC; every
+    // thread then scales and adds its output slices.
+    if (tid < 64) {
+        const float2 ml = __builtin_bit_cast(float2, mlw);
+        const bool in = tid < n_split;
+        float mx = in ? ml.x : kNegInf;
         mx = fmaxf(mx, dpp_f32<0xB1>(mx));
         mx = fmaxf(mx, dpp_f32<0x4E>(mx));
         mx = fmaxf(mx, dpp_f32<0x141>(mx));
         mx = fmaxf(mx, dpp_f32<0x140>(mx));
         mx = max4q(mx);
-        if (tid == 0) s_M = mx;
+        const float s2 = sink_log2(a, h);
+        const float M = fmaxf(mx, s2);
+        const float w = in ? fast_exp2(ml.x - M) : 0.0f;  // every split's maximum is finite
+        sw[tid % LPC][tid / LPC] = w;
+        float lw = w * ml.y;
+        lw = row16_sum(lw);
+        {
+            float lo, hi;
+            swap16(lw, lw, lo, hi);
+            lw = lo + hi;
+            swap32(lw, lw, lo, hi);
+            lw = lo + hi;
+        }
+        if (tid == 0) s_inv = 1.0f / (lw + rel_weight(s2, M));
     }
     __syncthreads();
     if (!s_go) {  // not reachable (see the file header); never pass silently
         if (sg == 0) store4(out + d4 * 4, __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
         return;
     }
-    const float s2 = sink_log2(a, h);
-    const float M = fmaxf(s_M, s2);
-    float Ls = 0.0f;
     float4 R = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    float2 mlk[PER];  // all (max, sum) reads first (clamped to a valid split)
+    float wk[PER];  // slots past the splits have weight 0 (and their words read as zero)
 #pragma unroll
-    for (int k = 0; k < PER; ++k) mlk[k] = sml[min(sg + k * LPC, n_split - 1)];
-    // branch-free: a slot past the splits gets weight 0 (its words read as
-    // zero); every split's maximum is finite (each split has a row)
+    for (int k = 0; k < PER; ++k) wk[k] = sw[sg][k];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-        const float e = fast_exp2(mlk[k].x - M);
-        const float w = sg + k * LPC < n_split ? e : 0.0f;
         const float4 x = __builtin_bit_cast(float4, po[k]);
-        Ls += w * mlk[k].y;
-        R.x += w * x.x; R.y += w * x.y; R.z += w * x.z; R.w += w * x.w;
+        R.x += wk[k] * x.x; R.y += wk[k] * x.y; R.z += wk[k] * x.z; R.w += wk[k] * x.w;
     }
-    Ls = colgroup_sum<CPW>(Ls) + rel_weight(s2, M);
     R.x = colgroup_sum<CPW>(R.x);
     R.y = colgroup_sum<CPW>(R.y);
     R.z = colgroup_sum<CPW>(R.z);
     R.w = colgroup_sum<CPW>(R.w);
-    if (sg == 0) store4(out + d4 * 4, R.x / Ls, R.y / Ls, R.z / Ls, R.w / Ls);
+    const float inv = s_inv;
+    if (sg == 0) store4(out + d4 * 4, R.x * inv, R.y * inv, R.z * inv, R.w * inv);
 }
 
 // The merges a split performs for (request, head tile) col once its own
