@@ -1394,9 +1394,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
     }
     // The group add comes first (thread 0), and wave 0 waits for it (and
     // its query piece) before issuing its steps (measured: 1 us faster at
-    // 16384 rows than letting it overlap them).  Its result is used right
-    // after wave 0's last wait for all of its loads, so a group completer
-    // counts its group early in the split.
+    // 16384 rows than letting it overlap them); its result is used right
+    // after the query barrier.
     const int col = b * P.HT + ht;
     unsigned gticket = 0u, ticket = kNoTicket;
     if (n_split > 1 && tid == 0) {
@@ -1415,6 +1414,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __syncthreads();
+    // the group add's result is in (waited above): a group completer counts
+    // its group now, early in the split
+    if (n_split > 1 && tid == 0) ticket = group_done(a, col, s, n_split, gticket);
 
     // B operands of the first product: head j, slot order of q4_operand,
     // entries facing a 16c slot divided by 16; and per group the sum of the
@@ -1584,12 +1586,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
     int it = 0;
     for (int st = wave; st < nst; st += kQ4Waves, ++it) {
         const int buf = it & 1;
-        if (st + kQ4Waves < nst) {
+        if (st + kQ4Waves < nst)
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(S::NL) : "memory");
-        } else {
+        else
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            if (n_split > 1 && tid == 0) ticket = group_done(a, col, s, n_split, gticket);
-        }
         step(wbuf + buf * S::BYTES, start + st * kQ4Rows);
         if (st + 2 * kQ4Waves < nst) issue(st + 2 * kQ4Waves, buf);
     }
