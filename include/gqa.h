@@ -135,7 +135,7 @@ int gqa_workspace_init(void *workspace, size_t bytes, void *stream);
  * 1 <= kv_len <= s_cap, dtype in {GQA_F32, GQA_BF16, GQA_F16},
  * workspace_bytes >= gqa_decode_workspace_bytes(B, Hq, Hkv, D, s_cap) and a
  * workspace prepared as described at gqa_workspace_init.
- * The split of the KV length depends only on (s_cap, Hq, Hkv), so the output
+ * The split of the KV length depends only on (s_cap, Hq, Hkv, D), so the output
  * for request b is bit-identical to gqa_decode_attend_batched with
  * kv_lens[b] = kv_len and the same s_cap.
  */

@@ -151,7 +151,7 @@ __device__ __forceinline__ void lds_load_u16(const BufDesc &d, unsigned lds_base
 // ---------------------------------------------------------------------------
 // Decode split plan.  The host sizes the workspace and the grid from it and
 // the kernel derives every index from the same numbers, so a request's split
-// boundaries depend only on (s_cap, Hq, Hkv) -- never on B or on the other
+// boundaries depend only on (s_cap, Hq, Hkv, D) -- never on B or on the other
 // requests' lengths.
 // ---------------------------------------------------------------------------
 constexpr int kDecodeThreads = 512;     // 8 waves
