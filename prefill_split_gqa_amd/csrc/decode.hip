@@ -343,8 +343,7 @@ __device__ __forceinline__ bool packed_item(const DecodeArgs &a, int B, int i, S
 template <typename TQ, int D, int GT, int RES, int NT = kDecodeThreads>
 __device__ void merge_head(const DecodeArgs &a, int m, int n_split);
 template <typename TQ, int D, int GT, int RES, int NT = kDecodeThreads>
-__device__ void merge_tile(const DecodeArgs &a, int col, int n_split, unsigned own_heads, unsigned decision,
-                           int ticket_tid, unsigned ticket);
+__device__ void merge_heads(const DecodeArgs &a, int col, int n_split, unsigned heads);
 template <typename TQ, int D, int GT, int RES, int NT = kDecodeThreads>
 __device__ void merge_workgroup(const DecodeArgs &a, int m);
 
@@ -411,6 +410,34 @@ template <int GT> __device__ __forceinline__ unsigned inplace_heads(int s, int n
     unsigned h = 0u;
     for (int hh = s; hh < GT; hh += n_split) h |= 1u << hh;
     return h;
+}
+
+// The heads a split of (request, head tile) col merges once it has published
+// (see the file header), from the results of its adds to the tile word
+// (thread 0): the heads it is the designated merger of (own_heads, in
+// place), if its decision add (result `decision`) found every group
+// counted; and, if its group completion (`ticket`; kNoTicket if it
+// completed no group) counted the last group, the heads whose designated
+// mergers decided before that.  Called before the workgroup's last barrier
+// ahead of the publish: waiting there for the adds' round trips does not
+// also wait for the publish stores.
+template <int GT>
+__device__ __forceinline__ unsigned tile_heads(const DecodeArgs &a, int col, int n_split, unsigned own_heads,
+                                               unsigned decision, unsigned ticket)
+{
+    const unsigned all = (1u << GT) - 1u;
+    const unsigned n_groups = split_groups(n_split);
+    unsigned heads = 0u;
+    if (ticket != kNoTicket) {
+        const unsigned after = ticket + 1u;
+        if ((after & kTwGroups) == n_groups) heads |= (ticket >> kTwHeadShift) & all;  // left to this split
+        tile_word_last<GT>(a, col, n_split, after);
+    }
+    if (own_heads != 0u) {
+        if ((decision & kTwGroups) == n_groups) heads |= own_heads;
+        tile_word_last<GT>(a, col, n_split, decision + tile_decision_add(own_heads));
+    }
+    return heads;
 }
 
 // Published partials carry a tag: every fp32 word is written with its
@@ -650,8 +677,8 @@ __device__ __forceinline__ void dense_split(const DecodeArgs &a, const DecodeGri
     }
 
     // in place, split s is the designated merger of heads s, s + n_split, ...,
-    // and decides for them now (the add's result is first needed after the
-    // split has published)
+    // and decides for them now (the add's result is needed at the last
+    // barrier)
     const unsigned own = n_split > 1 && grid.inplace ? inplace_heads<GT>(s, n_split) : 0u;
     unsigned decision = 0u;
     if (tid == 0 && own != 0u) decision = decide(a, col, own);
@@ -680,10 +707,12 @@ __device__ __forceinline__ void dense_split(const DecodeArgs &a, const DecodeGri
             so[wave][ff / EPL][KV::dim(lr, ff % EPL)] = lo + hi;
         }
     }
+    __shared__ unsigned s_heads;
+    if (tid == 0) s_heads = n_split > 1 ? tile_heads<GT>(a, col, n_split, own, decision, ticket) : 0u;
     __syncthreads();
 
     finish_split<TQ, D, GT, RES>(a, &so[0][0][0], &sm[0][0], &sl[0][0], col, s, n_split, out, h0);
-    if (n_split > 1) merge_tile<TQ, D, GT, RES>(a, col, n_split, own, decision, 0, ticket);
+    if (n_split > 1) merge_heads<TQ, D, GT, RES>(a, col, n_split, s_heads);
 }
 
 // ===========================================================================
@@ -989,10 +1018,12 @@ __global__ __launch_bounds__(kMfThreads) void decode_mfma_kernel(DecodeArgs a, D
             sl[wave * GT + j] = l_run;
         }
     }
+    __shared__ unsigned s_heads;
+    if (tid == 0) s_heads = n_split > 1 ? tile_heads<GT>(a, col, n_split, own, decision, ticket) : 0u;
     __syncthreads();
 
     finish_split<T, D, GT, RES, SOD, kMfThreads>(a, so, sm, sl, col, s, n_split, out, h0);
-    if (n_split > 1) merge_tile<T, D, GT, RES, kMfThreads>(a, col, n_split, own, decision, 0, ticket);
+    if (n_split > 1) merge_heads<T, D, GT, RES, kMfThreads>(a, col, n_split, s_heads);
 }
 
 // Sum over the lanes of a wave that share lane % CPW (CPW a power of two
@@ -1148,38 +1179,11 @@ __device__ void merge_head(const DecodeArgs &a, int m, int n_split)
     if (sg == 0) store4(out + d4 * 4, R.x * inv, R.y * inv, R.z * inv, R.w * inv);
 }
 
-// The merges a split performs for (request, head tile) col once its own
-// partial is published (see the file header): the heads it is the
-// designated merger of (own_heads, in place), if its decision add (result
-// `decision`, thread 0) found every group counted; and, if its tile word
-// add (thread ticket_tid holds the result; kNoTicket if it completed no
-// group) counted the last group, the heads whose designated mergers
-// decided before that.
+// The merges of heads (a bit per head of the tile) by a split that has
+// published its own partial.
 template <typename TQ, int D, int GT, int RES, int NT>
-__device__ void merge_tile(const DecodeArgs &a, int col, int n_split, unsigned own_heads, unsigned decision,
-                           int ticket_tid, unsigned ticket)
+__device__ void merge_heads(const DecodeArgs &a, int col, int n_split, unsigned heads)
 {
-    __shared__ unsigned s_ticket, s_heads;
-    if ((int)threadIdx.x == ticket_tid) s_ticket = ticket;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned all = (1u << GT) - 1u;
-        const unsigned n_groups = split_groups(n_split);
-        unsigned heads = 0u;
-        const unsigned t = ticket_tid >= 0 ? s_ticket : kNoTicket;
-        if (t != kNoTicket) {
-            const unsigned after = t + 1u;
-            if ((after & kTwGroups) == n_groups) heads |= (t >> kTwHeadShift) & all;  // left to this split
-            tile_word_last<GT>(a, col, n_split, after);
-        }
-        if (own_heads != 0u) {
-            if ((decision & kTwGroups) == n_groups) heads |= own_heads;
-            tile_word_last<GT>(a, col, n_split, decision + tile_decision_add(own_heads));
-        }
-        s_heads = heads;
-    }
-    __syncthreads();
-    const unsigned heads = s_heads;
     for (int hh = 0; hh < GT; ++hh)
         if (heads & (1u << hh)) merge_head<TQ, D, GT, RES, NT>(a, col * GT + hh, n_split);
 }
@@ -1618,9 +1622,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_q4_kernel(DecodeArgs a,
             sl[wave * GT + j] = l_run;
         }
     }
+    __shared__ unsigned s_heads;
+    if (tid == 0) s_heads = n_split > 1 ? tile_heads<GT>(a, col, n_split, own, decision, ticket) : 0u;
     __syncthreads();
     finish_split<f16_t, D, GT, RES, SOD>(a, so, sm, sl, col, s, n_split, out, h0);
-    if (n_split > 1) merge_tile<f16_t, D, GT, RES>(a, col, n_split, own, decision, 0, ticket);
+    if (n_split > 1) merge_heads<f16_t, D, GT, RES>(a, col, n_split, s_heads);
 }
 
 // ---------------------------------------------------------------------------
