@@ -739,8 +739,8 @@ __device__ __forceinline__ void dense_split(const DecodeArgs &a, const DecodeGri
 //     lane's own p of that row.  Values of 16-bit caches are widened to
 //     fp32 in registers; p stays fp32.
 // At the end each wave holds, per head, its reference maximum, its sum of
-// weights and its output row; the workgroup combines the 4 waves as the
-// kernel above does.
+// weights and its output row; the workgroup combines the 4 waves through
+// LDS (finish_split) and publishes the split's partial.
 constexpr int kMfThreads = 256;
 constexpr int kMfWaves = kMfThreads / 64;
 constexpr int kMfRows = 16;  // rows per block
