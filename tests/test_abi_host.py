@@ -157,6 +157,16 @@ def test_decode_workspace_layout():
     assert gqa.gqa_decode_workspace_bytes(886, 28, 4, 128, 4096) == 0
 
 
+def test_decode_small_heads_are_one_split():
+    # a KV head of at most 8192 elements per K and V is one split (no merge):
+    # 14/2 heads of 64 at s_cap = 128 -> one partial slot per (column, head);
+    # at 129 rows, or at 128 rows of 128, the split plan keeps several
+    assert gqa.gqa_decode_workspace_bytes(1, 14, 2, 64, 128) == MIB16 + 2 * 1 * 7 * 64 * 4
+    assert gqa.gqa_decode_workspace_bytes(1, 14, 2, 64, 129) > MIB16 + 2 * 1 * 7 * 64 * 4
+    assert gqa.gqa_decode_workspace_bytes(1, 28, 4, 128, 128) > MIB16 + 4 * 1 * 7 * 128 * 4
+    assert gqa.gqa_decode_workspace_bytes(1, 28, 4, 128, 64) == MIB16 + 4 * 1 * 7 * 128 * 4
+
+
 def test_q4_validation(lib):
     wsb = gqa.gqa_decode_workspace_bytes(1, 64, 8, 128, 64)
 
