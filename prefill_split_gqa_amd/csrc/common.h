@@ -159,7 +159,12 @@ constexpr int kDecodeLPR = 32;          // lanes per key row (a row-group)
 constexpr int kDecodeRowGroups = kDecodeThreads / kDecodeLPR;
 constexpr int kDecodeMaxSplits = 64;    // partials merged by one workgroup (one round trip)
 constexpr long kDecodeOneSplitElems = 8192;  // a KV head this small is one split (see make_decode_plan)
-constexpr int kDecodeTargetWGs = 256;   // one workgroup per CU at full length
+// Workgroups a plan aims for at full length: the matrix-core dense kernel's
+// 4-wave workgroups co-reside 2 or 3 per CU (measured best, batched Qwen3-4B
+// geometry, B = 1..8: 320 against 256, 384 and 512); the 4-bit kernel's
+// 8-wave ones one per CU.
+constexpr int kDecodeTargetWGs = 320;
+constexpr int kDecodeQ4TargetWGs = 256;
 
 // Every workspace begins with a flag region of fixed size.  The words that
 // workgroups use to meet one another (decode (max, sum) words, prefill
