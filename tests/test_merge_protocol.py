@@ -30,8 +30,12 @@ GROUP = 8
 
 
 class Model:
-    def __init__(self, n_split, GT, inplace, rng):
+    # decide_after: a designated merger in place makes its decision add after
+    # publishing its own partial (the matrix-core kernel) instead of before
+    # (the SIMD-lane and 4-bit kernels)
+    def __init__(self, n_split, GT, inplace, rng, decide_after=False):
         self.n, self.GT, self.inplace, self.rng = n_split, GT, inplace, rng
+        self.decide_after = decide_after
         self.n_groups = (n_split + GROUP - 1) // GROUP
         self.group = [0] * self.n_groups
         self.tile = 0
@@ -62,13 +66,12 @@ class Model:
             ticket = self.tile; self.tile += 1          # tile add
             yield "tile add"
         decision = None
-        if own:
-            add = (len(own) << 4) | sum(1 << (8 + h) for h in own)
-            decision = self.tile; self.tile += add      # decision add (after streaming)
-            self.decided.update(own)
-            yield "decision add"
+        if own and not self.decide_after:
+            decision = yield from self.decide(own)      # after streaming
         self.published.add(s)
         yield "publish"
+        if own and self.decide_after:
+            decision = yield from self.decide(own)      # after publishing
         heads = []
         if ticket is not None:
             after = ticket + 1
@@ -81,6 +84,13 @@ class Model:
             self.last_check(decision + ((len(own) << 4) | sum(1 << (8 + h) for h in own)))
         for h in heads:
             yield from self.merge(h, who=("split", s))
+
+    def decide(self, own):
+        add = (len(own) << 4) | sum(1 << (8 + h) for h in own)
+        decision = self.tile; self.tile += add          # decision add
+        self.decided.update(own)
+        yield "decision add"
+        return decision
 
     def merge_wg(self, h):
         for _ in range(self.rng.randrange(0, 4)):       # bounded reads of the tile word
@@ -105,9 +115,9 @@ class Model:
         yield "merge"
 
 
-def run(n_split, GT, inplace, seed):
+def run(n_split, GT, inplace, seed, decide_after=False):
     rng = random.Random(seed)
-    m = Model(n_split, GT, inplace, rng)
+    m = Model(n_split, GT, inplace, rng, decide_after)
     pending = [m.split(s) for s in range(n_split)]
     if not inplace:
         pending += [m.merge_wg(h) for h in range(GT)]
@@ -131,20 +141,22 @@ def run(n_split, GT, inplace, seed):
     return m
 
 
+@pytest.mark.parametrize("decide_after", [False, True])
 @pytest.mark.parametrize("inplace", [True, False])
 @pytest.mark.parametrize("n_split,GT", [(2, 1), (3, 7), (7, 7), (8, 4), (9, 8), (17, 3), (64, 7), (64, 8), (5, 8)])
-def test_protocol_random_schedules(n_split, GT, inplace):
+def test_protocol_random_schedules(n_split, GT, inplace, decide_after):
     for seed in range(150):
-        run(n_split, GT, inplace, seed)
+        run(n_split, GT, inplace, seed, decide_after)
 
 
-def test_declined_heads_fall_to_the_last_group_completer():
+@pytest.mark.parametrize("decide_after", [False, True])
+def test_declined_heads_fall_to_the_last_group_completer(decide_after):
     # with few slots, designated mergers often decide before every split has
     # started; the split that completes the last group then merges the
     # declined heads
     declined = 0
     for seed in range(300):
-        m = run(9, 4, seed % 2 == 0, seed)
+        m = run(9, 4, seed % 2 == 0, seed, decide_after)
         declined += sum(1 for who in m.merged.values() if who[0] == "split" and m.inplace is False)
         declined += sum(1 for h, who in m.merged.items() if m.inplace and who != ("split", h % m.n))
     assert declined > 0
