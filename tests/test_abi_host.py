@@ -187,6 +187,22 @@ def test_q4_validation(lib):
     assert lib.gqa_dequant_q4(FAKE, FAKE, FAKE, FAKE, 4, 64, 128, NULL) == gqa.GQA_ERR_SHAPE
 
 
+def test_q4_plan_fits_the_decode_workspace(lib):
+    # the 4-bit kernel's split plan aims at fewer workgroups than the dense
+    # kernels' (fewer splits), so gqa_decode_workspace_bytes covers it: with
+    # exactly that many bytes the call gets past the workspace check (and
+    # stops at the misaligned query pointer, before any launch)
+    for B in (1, 3, 8):
+        for Hq, Hkv in ((64, 8), (32, 8), (28, 4), (14, 2), (16, 16)):
+            for D in (64, 128):
+                for s_cap in (64, 1000, 2048, 16384):
+                    wsb = gqa.gqa_decode_workspace_bytes(B, Hq, Hkv, D, s_cap)
+                    assert wsb > 0
+                    st = lib.gqa_decode_attend_q4(FAKE_ODD, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, Hq, Hkv, D,
+                                                  32, s_cap, s_cap, ctypes.c_float(0.1), FAKE, wsb, NULL)
+                    assert st == gqa.GQA_ERR_ALIGN, (B, Hq, Hkv, D, s_cap, st)
+
+
 def test_workspace_init_validation(lib):
     assert lib.gqa_workspace_init(NULL, 256, NULL) == gqa.GQA_ERR_NULL
     assert lib.gqa_workspace_init(FAKE_ODD, 256, NULL) == gqa.GQA_ERR_ALIGN
