@@ -374,9 +374,18 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D ==
                 const uint32_t w = which ? qv_w[i] : qk_w[i];
                 const float sc = f16_bits_to_f32(which ? qv_s[i] : qk_s[i]);
                 const float bi = f16_bits_to_f32(which ? qv_b[i] : qk_b[i]);
+                // even nibbles to the bytes of lo, odd ones to those of hi:
+                // each code then converts with one byte-to-float instruction
+                // (the masks are opaque to the compiler, which would
+                // otherwise fold them back into one bit-field extract per
+                // code)
+                uint32_t lo, hi;
+                asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(w));
+                asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(hi) : "v"(w >> 4));
                 f32x8_t x;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(sc, (float)((w >> (4 * e)) & 15u), bi);
+                for (int e = 0; e < 8; ++e)
+                    x[e] = __builtin_fmaf(sc, (float)((((e & 1) ? hi : lo) >> (8 * (e >> 1))) & 0xFFu), bi);
                 *(uint4 *)(smem + (2 * which + buf) * L::TILE + tile_off<D>(row, cc)) = MfmaOps<f16_t>::pack8(x);
             }
         }
