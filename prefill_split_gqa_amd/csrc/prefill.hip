@@ -10,8 +10,8 @@
 // one query head (32 rows per wave) and a contiguous range ("chunk") of the
 // 64-key tiles those rows can see.  Short row blocks are one chunk; the long
 // ones near the end of the causal triangle are cut into chunks of at most
-// ch tiles, ch chosen so that the launch has about one workgroup per
-// workgroup slot of the device (4 per CU).  The host sorts the (row block,
+// ch tiles, ch chosen so that the launch has about three workgroups per CU
+// for D = 64 (four are resident).  The host sorts the (row block,
 // chunk) items longest first into a table passed with the launch, so the
 // long items start first and the short ones fill in behind them.  The
 // chunks of a split row block meet through the workspace: each stores its
@@ -727,7 +727,7 @@ static int pf_row_tiles(int rb, int Tq, int Tk, int window)
 
 // Chunking of the causal triangle.  The most key tiles per chunk, ch, is
 // the smallest value that gives about one slot's share of the tiles per
-// chunk (4 workgroup slots per CU for D = 64, 2 for D = 128; the items,
+// chunk (3 shares per CU for D = 64, 2 for D = 128; the items,
 // issued longest first, then finish close together), but at least
 // kPfMinChunk tiles, with the launch table's item count, the chunks per row
 // block and the split row blocks' counters within their limits.  Every
@@ -763,7 +763,10 @@ static bool pf_plan_fits(const PfPlan &p, int B, int Hq)
 static PfPlan pf_plan(int B, int Hq, int D, int Tq, int Tk, int window, int n_cus)
 {
     const int min_chunk = kPfMinChunk;
-    const long slots = (long)(D == 64 ? 4 : 2) * n_cus;  // resident workgroups (VGPR budget)
+    // Shares of 3 workgroups per CU for D = 64, although 4 are resident:
+    // longer chunks and fewer merges measured 0.8 us faster at T = 4097
+    // (0.5B geometry), the same at T = 2049 and for a 256-query chunk.
+    const long slots = (long)(D == 64 ? 3 : 2) * n_cus;
     const int n_rb = (Tq + kPfBM - 1) / kPfBM;
     long total = 0;
     for (int rb = 0; rb < n_rb; ++rb) total += pf_row_tiles(rb, Tq, Tk, window);

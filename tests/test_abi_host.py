@@ -129,10 +129,11 @@ def test_prefill_workspace_size():
     # The flag region, then one partial slot per possible chunk of every
     # split row block.  B=2, 14 heads, T=4097: row block rb (< 32) sees
     # 2(rb+1) key tiles of 64, the last one 65, 1121 tiles a head, 31388 in
-    # all; about one workgroup per slot (1024) gives chunks of at most 31
-    # tiles, so row blocks 15..32 (18 of them) are split, at most 3 ways.
+    # all; a share for each of 3 workgroups per CU (768 on 256 CUs) gives
+    # chunks of at most 41 tiles, so row blocks 20..32 (13 of them) are
+    # split, at most 2 ways.
     slot64 = (4 * 2 * 16 * 64 + 4 * 64 * 2) * 4
-    assert gqa.gqa_prefill_workspace_bytes(2, 14, 2, 64, 4097, 4097) == MIB16 + 2 * 14 * 18 * 3 * slot64
+    assert gqa.gqa_prefill_workspace_bytes(2, 14, 2, 64, 4097, 4097) == MIB16 + 2 * 14 * 13 * 2 * slot64
     # nothing is split: the flag region alone (chunks hold at least 8 tiles)
     assert gqa.gqa_prefill_workspace_bytes(1, 14, 2, 64, 8, 8) == MIB16
     assert gqa.gqa_prefill_workspace_bytes(1, 14, 2, 128, 200, 300) == MIB16
