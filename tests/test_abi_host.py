@@ -150,12 +150,12 @@ def test_decode_workspace_layout():
     # keys at s_cap = 4096; one 128-float partial per (column, split, head)
     # after the flag region
     assert gqa.gqa_decode_workspace_bytes(1, 28, 4, 128, 4096) == MIB16 + 4 * 64 * 7 * 128 * 4
-    # the (max, sum) words, 8 bytes per partial, and nine control words on
-    # lines of their own (1152 bytes) per (request, head tile) must fit the
-    # flag region less its 64-byte tail: 28 * 64 * 8 + 4 * 1152 bytes a
-    # request allow 885 requests
-    assert gqa.gqa_decode_workspace_bytes(885, 28, 4, 128, 4096) > 0
-    assert gqa.gqa_decode_workspace_bytes(886, 28, 4, 128, 4096) == 0
+    # the (max, sum) words, 8 bytes per partial, and five control words on
+    # lines of their own (640 bytes) per (request, head tile) must fit the
+    # flag region less its 64-byte tail: 28 * 64 * 8 + 4 * 640 bytes a
+    # request allow 992 requests
+    assert gqa.gqa_decode_workspace_bytes(992, 28, 4, 128, 4096) > 0
+    assert gqa.gqa_decode_workspace_bytes(993, 28, 4, 128, 4096) == 0
 
 
 def test_decode_small_heads_are_one_split():

@@ -26,7 +26,7 @@ import random
 
 import pytest
 
-GROUP = 8
+GROUP = 16  # splits per group word (the kernels' kSplitGroup)
 
 
 class Model:
@@ -143,7 +143,7 @@ def run(n_split, GT, inplace, seed, decide_after=False):
 
 @pytest.mark.parametrize("decide_after", [False, True])
 @pytest.mark.parametrize("inplace", [True, False])
-@pytest.mark.parametrize("n_split,GT", [(2, 1), (3, 7), (7, 7), (8, 4), (9, 8), (17, 3), (64, 7), (64, 8), (5, 8)])
+@pytest.mark.parametrize("n_split,GT", [(2, 1), (3, 7), (7, 7), (8, 4), (9, 8), (17, 3), (33, 5), (40, 4), (64, 7), (64, 8), (5, 8)])
 def test_protocol_random_schedules(n_split, GT, inplace, decide_after):
     for seed in range(150):
         run(n_split, GT, inplace, seed, decide_after)
