@@ -211,8 +211,9 @@ __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a -
 
 // extra_splits: splits per (request, head tile) beyond those of the rows
 // (a residual-window cache's float16 residual is one).
+// min_per: the fewest rows per row-group a split gets (see below).
 inline bool make_decode_plan(int B, int Hq, int Hkv, int D, int s_cap, int target_wgs, int max_splits,
-                             DecodePlan *p, int extra_splits = 0)
+                             DecodePlan *p, int extra_splits = 0, int min_per = 2)
 {
     if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || s_cap < 1 || Hq % Hkv || target_wgs < 1 || max_splits < 1)
         return false;
@@ -232,12 +233,13 @@ inline bool make_decode_plan(int B, int Hq, int Hkv, int D, int s_cap, int targe
     if (ns > max_splits) ns = max_splits;
     const long rows = kDecodeRowGroups;
     long per = (s_cap + rows * ns - 1) / (rows * ns);  // rows per row-group per split
-    // At least two rows per row-group (one full chunk) as long as that still
-    // gives every query head of a tile a split to merge it: one-row splits
-    // leave half of each chunk's loads empty and double the partials
-    // (measured at 7B geometry, KV length 1024: 64 one-row splits 8.85 us,
-    // 32 two-row splits 8.41 us per layer).
-    if (per < 2 && (s_cap + 2 * rows - 1) / (2 * rows) >= p->GT) per = 2;
+    // At least min_per rows per row-group as long as that still gives every
+    // query head of a tile a split to merge it.  The 4-bit kernel takes 2
+    // (32-row steps: shorter splits would leave half of each step's loads
+    // empty); the matrix-core dense kernel takes 1 (16-row blocks: at 7B
+    // geometry 16-row splits measured 0.1 us faster at KV lengths 512 and
+    // 1024 than 32-row ones, and the same elsewhere).
+    if (per < min_per && (s_cap + min_per * rows - 1) / (min_per * rows) >= p->GT) per = min_per;
     p->L = (int)(per * rows);
     p->n_split_max = (int)((s_cap + p->L - 1) / p->L) + extra_splits;
     const size_t parts = (size_t)B * p->HT * p->n_split_max * p->GT;  // (request, query head, split)

@@ -23,11 +23,13 @@ constexpr int kAbiVersion = 4;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-// target_wgs: kDecodeTargetWGs for the dense kernels, kDecodeQ4TargetWGs for
-// the 4-bit kernel (fewer splits, so a dense plan's workspace fits it too)
-bool plan_decode(int B, int Hq, int Hkv, int D, int s_cap, DecodePlan *p, int target_wgs = kDecodeTargetWGs)
+// four_bit: the 4-bit kernel's plan (fewer workgroups and at least two rows
+// per row-group: never more splits, so a dense plan's workspace fits it too)
+bool plan_decode(int B, int Hq, int Hkv, int D, int s_cap, DecodePlan *p, bool four_bit = false)
 {
-    if (!make_decode_plan(B, Hq, Hkv, D, s_cap, target_wgs, kDecodeMaxSplits, p)) return false;
+    if (!make_decode_plan(B, Hq, Hkv, D, s_cap, four_bit ? kDecodeQ4TargetWGs : kDecodeTargetWGs, kDecodeMaxSplits,
+                          p, 0, four_bit ? 2 : 1))
+        return false;
     // grid limits, and buffer-resource ranges of the partial arrays
     return p->HT <= 65535 && p->n_split_max <= 65535 && p->bytes < ((size_t)1 << 31);
 }
@@ -81,7 +83,7 @@ bool dense_dtype(int dtype) { return dtype == GQA_F32 || dtype == GQA_BF16 || dt
 // plan_rows: the rows the split plan covers (s_cap, or a window's length)
 int check_decode_common(const void *q, const void *k, const void *v, void *out, int B, int Hq, int Hkv, int D,
                         int s_cap, float scale, void *ws, size_t ws_bytes, DecodePlan *plan, int plan_rows = 0,
-                        int target_wgs = kDecodeTargetWGs)
+                        bool four_bit = false)
 {
     if (!q || !k || !v || !out) return GQA_ERR_NULL;
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || s_cap < 1) return GQA_ERR_SHAPE;
@@ -89,7 +91,7 @@ int check_decode_common(const void *q, const void *k, const void *v, void *out, 
     if (D != 64 && D != 128) return GQA_ERR_UNSUPPORTED;
     // a KV head's rows are addressed with 32-bit buffer offsets
     if (B > 65535 || (size_t)s_cap * D * 4 >= ((size_t)1 << 31)) return GQA_ERR_SHAPE;
-    if (!plan_decode(B, Hq, Hkv, D, plan_rows > 0 ? plan_rows : s_cap, plan, target_wgs)) return GQA_ERR_SHAPE;
+    if (!plan_decode(B, Hq, Hkv, D, plan_rows > 0 ? plan_rows : s_cap, plan, four_bit)) return GQA_ERR_SHAPE;
     if (!ws || ws_bytes < plan->bytes) return GQA_ERR_WORKSPACE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(ws)) return GQA_ERR_ALIGN;
     return GQA_OK;
@@ -384,7 +386,7 @@ int gqa_decode_attend_q4(const void *q, const uint8_t *k_codes, const void *k_sc
     if (!k_scales || !k_biases || !v_scales || !v_biases) return GQA_ERR_NULL;
     DecodePlan plan;
     if (int st = check_decode_common(q, k_codes, v_codes, out, B, Hq, Hkv, D, s_cap, scale, workspace,
-                                     workspace_bytes, &plan, 0, kDecodeQ4TargetWGs))
+                                     workspace_bytes, &plan, 0, true))
         return st;
     if (kv_len < 1 || kv_len > s_cap) return GQA_ERR_SHAPE;
     if (group_size != 32 && group_size != 64 && group_size != 128) return GQA_ERR_UNSUPPORTED;
