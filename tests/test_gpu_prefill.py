@@ -10,7 +10,8 @@ D = 128, f16, several group sizes and B > 1.  Bound: max-abs 2e-2 (bf16/f16
 outputs); every 16-bit comparison also reports the per-row error in units
 in the last place at the row's largest |output|.  Row 0 of a square prefill
 sees one key and must equal that key's value row exactly; the chunk must
-match the tail of the full prefill within the bound.
+match the tail of the full prefill within the bound.  Runs on two streams at
+once, each with its own workspace, must equal a serial run bit for bit.
 
 Seam cases: long rows are split into chunks of 64-key tiles merged through
 the workspace, and on plain N(0,1) inputs one key more or less at a chunk
@@ -162,6 +163,40 @@ def test_prefill_deterministic(gpu_lib, T):
     torch.cuda.synchronize()
     for r in range(1, 10):
         assert torch.equal(outs[r], outs[0]), "run %d differs" % r
+
+
+def test_prefill_concurrent_streams_separate_workspaces(gpu_lib):
+    # The full prefill at T=4097 and the 256-query chunk at offset 3841 run
+    # concurrently on two streams (default priority), each with its own
+    # workspace, three calls per stream and round, five rounds.  The chunk
+    # merge takes a ticket and never waits, so competing launches only change
+    # which chunk merges; every output must equal a serial run bit for bit.
+    w = W.by_name("prefill_0p5b")
+    q, k, v = (t.cuda() for t in W.prefill_inputs(w, 4097))
+    qc = q[:, :, 4097 - 256:].contiguous()
+    ws_full, ws_chunk = prefill_ws(gpu_lib, q, k), prefill_ws(gpu_lib, qc, k)
+    want_full, want_chunk = torch.empty_like(q), torch.empty_like(qc)
+    gpu_lib.gqa_prefill_causal(q, k, v, want_full, ws_full)
+    gpu_lib.gqa_prefill_causal(qc, k, v, want_chunk, ws_chunk)
+    outs_full = [torch.empty_like(q) for _ in range(3)]
+    outs_chunk = [torch.empty_like(qc) for _ in range(3)]
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for r in range(5):
+        note("concurrent prefill round %d" % r)
+        with torch.cuda.stream(s1):
+            for o in outs_full:
+                gpu_lib.gqa_prefill_causal(q, k, v, o, ws_full)
+        with torch.cuda.stream(s2):
+            for o in outs_chunk:
+                gpu_lib.gqa_prefill_causal(qc, k, v, o, ws_chunk)
+        torch.cuda.synchronize()
+        for i, o in enumerate(outs_full):
+            assert torch.equal(o, want_full), "round %d full call %d" % (r, i)
+        for i, o in enumerate(outs_chunk):
+            assert torch.equal(o, want_chunk), "round %d chunk call %d" % (r, i)
+    assert_workspace_ready(ws_full, "full prefill workspace after the concurrent rounds")
+    assert_workspace_ready(ws_chunk, "chunk workspace after the concurrent rounds")
 
 
 def test_prefill_workspace_reuse(gpu_lib):
