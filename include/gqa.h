@@ -188,7 +188,10 @@ int gqa_decode_attend_batched(const void *q, const void *k, const void *v, void 
  * 0 when the sizes are invalid.  The value depends on the arguments and on
  * the compute-unit count of the current HIP device (the chunking sizes the
  * launch to the device; 256 when no device can be queried), so size the
- * workspace with the device current that the call will run on.
+ * workspace with the device current that the call will run on.  It is not
+ * monotone in Tq and Tk (a shorter prompt may be cut into more key chunks):
+ * a workspace shared by calls of several sizes takes the largest of their
+ * values.
  * Like the decode workspace it must start zero-filled (torch.zeros, or
  * gqa_workspace_init once per allocation).
  */

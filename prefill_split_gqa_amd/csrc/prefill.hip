@@ -125,7 +125,8 @@ constexpr int kPfBM = 128;       // query rows per workgroup: 4 row-waves of 32 
 constexpr int kPfBN = 64;        // keys per tile
 constexpr int kPfThreads = 256;  // 4 waves
 constexpr int kPfMaxItems = 1024;     // (row block, key chunk) work items in the launch table
-constexpr int kPfMinChunk = 10;       // fewest key tiles per chunk: a chunk's partial costs a write and a read
+constexpr int kPfMinChunk = 3;        // fewest key tiles per chunk
+constexpr int kPfMaxSplit = 7;        // most chunks of a row block the floor allows: each partial costs a write and a read
 constexpr float kPfSumLimit = 1024.0f;  // a lane's probability sum that needs the exact path
 
 // The launch's work items, longest first: entry r is (row block << 6) |
@@ -729,7 +730,8 @@ static int pf_row_tiles(int rb, int Tq, int Tk, int window)
 // the smallest value that gives about one slot's share of the tiles per
 // chunk (3 shares per CU for D = 64, 2 for D = 128; the items,
 // issued longest first, then finish close together), but at least
-// kPfMinChunk tiles, with the launch table's item count, the chunks per row
+// kPfMinChunk tiles and a 1/kPfMaxSplit share of the longest row block,
+// with the launch table's item count, the chunks per row
 // block and the split row blocks' counters within their limits.  Every
 // limit is monotone in ch and met once no row block is split.
 struct PfPlan {
@@ -762,18 +764,27 @@ static bool pf_plan_fits(const PfPlan &p, int B, int Hq)
 // n_cus: compute units of the device the launch runs on.
 static PfPlan pf_plan(int B, int Hq, int D, int Tq, int Tk, int window, int n_cus)
 {
-    const int min_chunk = kPfMinChunk;
     // Shares of 3 workgroups per CU for D = 64, although 4 are resident:
     // longer chunks and fewer merges measured 0.8 us faster at T = 4097
     // (0.5B geometry), the same at T = 2049 and for a 256-query chunk.
     const long slots = (long)(D == 64 ? 3 : 2) * n_cus;
     const int n_rb = (Tq + kPfBM - 1) / kPfBM;
     long total = 0;
-    for (int rb = 0; rb < n_rb; ++rb) total += pf_row_tiles(rb, Tq, Tk, window);
+    int max_nt = 0;
+    for (int rb = 0; rb < n_rb; ++rb) {
+        const int nt = pf_row_tiles(rb, Tq, Tk, window);
+        total += nt;
+        max_nt = std::max(max_nt, nt);
+    }
     total *= (long)B * Hq;
-    int lo = (int)std::min<long>(std::max((long)min_chunk, (total + slots - 1) / std::max(slots, 1L)), 1 << 30);
-    int hi = lo;  // no split: always fits
-    for (int rb = 0; rb < n_rb; ++rb) hi = std::max(hi, pf_row_tiles(rb, Tq, Tk, window));
+    // The floor: short prompts split into short chunks (T = 513, 0.5B
+    // geometry: 154 workgroups of at most 3 tiles instead of 70 whole row
+    // blocks, 10.7 us against 11.6), but no row block into more than
+    // kPfMaxSplit chunks (without that cap, a 256-query chunk's 65-tile rows
+    // split 22 ways and took 28.5 us against 18.7).
+    const long min_chunk = std::max<long>(kPfMinChunk, (max_nt + kPfMaxSplit - 1) / kPfMaxSplit);
+    int lo = (int)std::min<long>(std::max(min_chunk, (total + slots - 1) / std::max(slots, 1L)), 1 << 30);
+    int hi = std::max(lo, max_nt);  // no split: always fits
     if (pf_plan_fits(pf_plan_for(Tq, Tk, window, lo), B, Hq)) return pf_plan_for(Tq, Tk, window, lo);
     while (hi - lo > 1) {  // invariant: lo does not fit, hi does
         const int mid = lo + (hi - lo) / 2;

@@ -134,9 +134,15 @@ def test_prefill_workspace_size():
     # split, at most 2 ways.
     slot64 = (4 * 2 * 16 * 64 + 4 * 64 * 2) * 4
     assert gqa.gqa_prefill_workspace_bytes(2, 14, 2, 64, 4097, 4097) == MIB16 + 2 * 14 * 13 * 2 * slot64
-    # nothing is split: the flag region alone (chunks hold at least 8 tiles)
+    # one key tile: nothing is split, the flag region alone
     assert gqa.gqa_prefill_workspace_bytes(1, 14, 2, 64, 8, 8) == MIB16
-    assert gqa.gqa_prefill_workspace_bytes(1, 14, 2, 128, 200, 300) == MIB16
+    # a short prompt splits into chunks of the 3-tile floor: Tq=200 of 300
+    # keys gives row blocks of 4 and 5 tiles, 2 chunks each, 14 heads
+    slot128 = (4 * 4 * 16 * 64 + 4 * 64 * 2) * 4
+    assert gqa.gqa_prefill_workspace_bytes(1, 14, 2, 128, 200, 300) == MIB16 + 14 * 2 * 2 * slot128
+    # the 256-query chunk at offset 3841: rows of 65 tiles, at most 7 chunks
+    # of 10 (the cap on chunks per row block sets the floor), 2 row blocks
+    assert gqa.gqa_prefill_workspace_bytes(1, 14, 2, 64, 256, 4097) == MIB16 + 14 * 2 * 7 * slot64
     # a large batch fills the GPU without splitting
     assert gqa.gqa_prefill_workspace_bytes(64, 32, 8, 128, 2048, 2048) == MIB16
     # invalid sizes give 0

@@ -204,14 +204,19 @@ def test_prefill_workspace_reuse(gpu_lib):
     # to arrive merges and returns the slots and the counter to zero.  Many
     # calls in a row on one workspace, with changing inputs and lengths, must
     # each match a fresh run, and leave the workspace ready for the next call.
+    # The workspace is sized for the largest of the calls (the size is not
+    # monotone in the lengths: a shorter prompt may be cut into more chunks).
     w = W.by_name("prefill_0p5b")
     q0, k0, v0 = (t.cuda() for t in W.prefill_inputs(w, 2049))
     Hq, Hkv, D = q0.shape[1], k0.shape[1], q0.shape[3]
-    ws = gpu_lib.make_prefill_workspace(1, Hq, Hkv, D, 2049, 2049)
     rng = np.random.default_rng(29)
+    sizes = []
     for it in range(12):
         Tq = int(rng.integers(1, 2049))
-        Tk = int(rng.integers(Tq, 2050))
+        sizes.append((Tq, int(rng.integers(Tq, 2050))))
+    ws = torch.zeros(max(gpu_lib.gqa_prefill_workspace_bytes(1, Hq, Hkv, D, Tq, Tk) for Tq, Tk in sizes),
+                     dtype=torch.uint8, device="cuda")
+    for it, (Tq, Tk) in enumerate(sizes):
         q = (q0[:, :, :Tq] * (1 + 0.1 * it)).contiguous()
         k = (k0 * (1 - 0.05 * it)).contiguous()
         note("prefill reuse it=%d Tq=%d Tk=%d" % (it, Tq, Tk))
@@ -230,10 +235,11 @@ def test_workspace_shared_by_decode_and_prefill(gpu_lib):
     w = W.by_name("prefill_0p5b")
     q0, k0, v0 = (t.cuda() for t in W.prefill_inputs(w, 2049))
     Hq, Hkv, D = q0.shape[1], k0.shape[1], q0.shape[3]
-    ws = torch.zeros(max(gpu_lib.gqa_prefill_workspace_bytes(1, Hq, Hkv, D, 2049, 2049),
-                         gpu_lib.gqa_decode_workspace_bytes(4, Hq, Hkv, D, 2049)), dtype=torch.uint8, device="cuda")
+    calls = [(2049, 2049, 4), (300, 1900, 1), (1500, 1500, 3), (77, 2049, 2)]
+    ws = torch.zeros(max([gpu_lib.gqa_prefill_workspace_bytes(1, Hq, Hkv, D, Tq, Tk) for Tq, Tk, _ in calls] +
+                         [gpu_lib.gqa_decode_workspace_bytes(4, Hq, Hkv, D, 2049)]), dtype=torch.uint8, device="cuda")
     gen = torch.Generator().manual_seed(43)
-    for it, (Tq, Tk, B) in enumerate([(2049, 2049, 4), (300, 1900, 1), (1500, 1500, 3), (77, 2049, 2)]):
+    for it, (Tq, Tk, B) in enumerate(calls):
         note("shared workspace it=%d prefill Tq=%d Tk=%d, decode B=%d" % (it, Tq, Tk, B))
         q = q0[:, :, :Tq].contiguous()
         got = torch.empty_like(q)
